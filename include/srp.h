@@ -1,0 +1,186 @@
+/*
+ * srp.h -- C ABI of libsrp.so, the selective-recompute prefill layer ("KV cache
+ * fusor") for AMD MI355X (gfx950).
+ *
+ * One layer of the method: the concatenated, independently precomputed KV caches
+ * of retrieved chunks are moved to their global positions, a subset of token rows is
+ * recomputed, chosen by KV deviation, their fresh K/V overwrite the cache, and the
+ * selected rows attend over the whole fused cache (CacheBlend walkthrough,
+ * "Selective KV recompute" and "Implementation"; CacheClip paper, sections 4.1-4.3).
+ *
+ * Conventions for every entry point:
+ *  - Tensor arguments are DEVICE pointers owned by the caller, row-major and
+ *    contiguous. The library keeps no pointer after a call returns.
+ *  - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream). No
+ *    entry point synchronises the host except srp_validate_batch. Outputs are valid
+ *    once the caller has synchronised with the stream.
+ *  - Return value: SRP_OK (0) or a negative srp_status. Host-checkable errors are
+ *    reported before anything is enqueued; srp_last_error() returns a message for
+ *    the last failure on the calling thread. No exception or abort crosses the ABI.
+ *  - Device arrays (offsets, positions, candidate lists) are trusted: malformed
+ *    contents give undefined results. srp_validate_batch checks them on request.
+ *  - Identical inputs give bitwise-identical outputs (no floating-point atomics).
+ */
+#ifndef SRP_H_
+#define SRP_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t *srp_stream_t; /* hipStream_t */
+
+typedef enum {
+  SRP_OK = 0,
+  SRP_E_INVALID = -1,     /* bad argument (shape, dtype, ratio, null pointer...)  */
+  SRP_E_WORKSPACE = -2,   /* workspace smaller than srp_workspace_size()          */
+  SRP_E_UNSUPPORTED = -3, /* valid but not implemented (e.g. head_dim 96)          */
+  SRP_E_HIP = -4,         /* a HIP runtime call failed                            */
+  SRP_E_BATCH = -5        /* srp_validate_batch found malformed device arrays     */
+} srp_status;
+
+typedef enum { SRP_F32 = 0, SRP_BF16 = 1 } srp_dtype;
+
+/* Selection modes (CacheBlend walkthrough, "Implementation": a per-layer
+ * check_flag says whether the layer selects tokens by deviation or uses the
+ * indices it was given). */
+typedef enum {
+  SRP_SEL_TOPK = 0, /* score candidates by KV deviation, keep the top k      */
+  SRP_SEL_GIVEN = 1 /* keep the candidates as given (no scoring)            */
+} srp_sel_mode;
+
+/* What the deviation measures (the CacheBlend walkthrough compares K and V; the
+ * CacheClip paper's account of CacheBlend compares value matrices only). */
+typedef enum { SRP_DEV_KV = 0, SRP_DEV_V = 1 } srp_dev_mode;
+
+/* Model shape of one layer. Weights W_qkv are [(nh + 2 nkv) * d, hidden]: the
+ * n_heads*d query rows, then n_kv_heads*d key rows, then n_kv_heads*d value rows,
+ * each row one output feature (so Q = X W_q^T). Rotary embedding: rotate-half
+ * pairing (i, i + d/2), angle p * rope_base^(-2i/d). Supported: head_dim 64 or
+ * 128, n_heads a multiple of n_kv_heads, hidden a multiple of 64. */
+typedef struct {
+  int32_t hidden;
+  int32_t n_heads;
+  int32_t n_kv_heads;
+  int32_t head_dim;
+  double rope_base;
+  int32_t dtype; /* srp_dtype: storage and compute type of every tensor */
+} srp_dims;
+
+/* A varlen batch of total_rows token rows (CacheClip paper 4.1: concatenated chunk
+ * caches with rearranged position IDs). Rows are partitioned into requests and,
+ * independently, into segments; every segment lies inside one request. A segment
+ * is a cached chunk whose first row was encoded at position chunk_src_pos[c] (its
+ * rows at consecutive positions), or a fresh segment (chunk_src_pos[c] = -1: the
+ * query tail or a chunk whose cache is missing), whose rows are always recomputed
+ * and whose input cache rows are ignored. */
+typedef struct {
+  int32_t n_req;        /* host: number of requests (>= 1)                         */
+  int32_t n_chunks;     /* host: number of segments (>= 1)                         */
+  int32_t total_rows;   /* host: T (>= 0)                                          */
+  int32_t max_req_rows; /* host: upper bound on the rows of any one request        */
+  int32_t max_position; /* host: every position, encode position and |pos - src|
+                           is < max_position (sizes the rotary tables)            */
+  const int32_t *req_offsets;   /* device [n_req+1], req_offsets[0] = 0,
+                                   req_offsets[n_req] = T, non-decreasing          */
+  const int32_t *chunk_offsets; /* device [n_chunks+1], same rules               */
+  const int32_t *chunk_src_pos; /* device [n_chunks], >= 0 cached, -1 fresh       */
+  const int32_t *positions;     /* device [T], global positions, strictly
+                                   increasing inside each request                 */
+} srp_batch;
+
+/* Token selection of one layer. k = round(ratio * N_ctx) per request (halves up),
+ * N_ctx = the request's cached rows, clamped to its candidate count (CacheClip
+ * walkthrough 6.2). Ties in deviation go to the lower row index. window > 0 turns
+ * on sliding-window grouping (CacheClip paper 4.3): over the request's cached rows
+ * in order, a window of `window` rows starting on a top-k row that holds at least
+ * `tau` top-k rows is recomputed whole; top-k rows covered by no such window are
+ * dropped. Grouping requires cand == NULL. Candidates (gradual filtering across
+ * layers, CacheBlend walkthrough "The chicken-and-egg problem"): cand == NULL means
+ * every cached row; otherwise cand/cand_offsets is a CSR list per request of row
+ * ids, ascending inside each request -- the sel_idx/sel_offsets of the previous
+ * layer can be passed as is (fresh rows in it are ignored, they are always
+ * recomputed). */
+typedef struct {
+  int32_t mode;     /* srp_sel_mode                                             */
+  double ratio;     /* in [0, 1]                                                */
+  int32_t window;   /* 0 = no grouping                                          */
+  int32_t tau;      /* grouping threshold, 1 <= tau <= window                   */
+  int32_t dev_mode; /* srp_dev_mode                                             */
+  const int32_t *cand;        /* device, NULL = all cached rows                  */
+  const int32_t *cand_offsets; /* device [n_req+1], required with cand            */
+} srp_select;
+
+/* Bytes of scratch that srp_fuse_layer needs for these arguments. */
+int srp_workspace_size(const srp_dims *dims, const srp_batch *batch,
+                       const srp_select *sel, size_t *bytes);
+
+/* One fused layer (CacheBlend walkthrough, "Selective KV recompute": mask the input
+ * to the selected rows, project Q/K/V, expand K/V with the reused rows, attend).
+ *   hidden    [T, hidden]                 layer input
+ *   w_qkv     [(nh+2nkv)*d, hidden]       weights (layout above)
+ *   k_cache   [T, nkv, d]  in/out         in: K of cached rows at their encode
+ *             positions; out: fused K (re-rotated cache rows, fresh K on
+ *             selected rows)
+ *   v_cache   [T, nkv, d]  in/out         in: cached V; out: fused V
+ *   sel_idx   [T] out                     selected rows, ascending per request,
+ *             fresh rows included; only the first sel_offsets[n_req] are written
+ *   sel_offsets [n_req+1] out             CSR offsets of sel_idx per request
+ *   attn_out  [T, nh, d] out              attention output of selected row
+ *             sel_idx[s] in row s; rows past sel_offsets[n_req] are not written
+ *   dev_out   [T] out, optional (NULL)    fp32 deviation per row, NaN where the
+ *             row was not scored
+ *   workspace device scratch of workspace_bytes >= srp_workspace_size()
+ * k_cache/v_cache are updated in place: a caller that must keep its stored chunk
+ * caches intact passes a copy (Cache-Craft summary, section 4: the fixed cache is
+ * swapped in only after use). */
+int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch,
+                   const srp_select *sel, const void *hidden, const void *w_qkv,
+                   void *k_cache, void *v_cache, int32_t *sel_idx,
+                   int32_t *sel_offsets, void *attn_out, float *dev_out,
+                   void *workspace, size_t workspace_bytes, srp_stream_t stream);
+
+/* Offline chunk encoding (CacheClip walkthrough, Figure 4, offline phase: each
+ * chunk's KV cache is computed once, at chunk-local positions):
+ *   k_out[j] = R(positions[j]) W_k hidden[j],  v_out[j] = W_v hidden[j]
+ * for j < n_rows. hidden [n_rows, hidden], positions device [n_rows] with
+ * 0 <= positions[j] < max_position; k_out, v_out [n_rows, nkv, d]. */
+int srp_encode_kv(const srp_dims *dims, int32_t n_rows, int32_t max_position,
+                  const void *hidden, const void *w_qkv, const int32_t *positions,
+                  void *k_out, void *v_out, srp_stream_t stream);
+
+/* Positional recovery alone (CacheBlend walkthrough, "Selective KV recompute";
+ * SpecCache notes 2.1): every cached row's K is rotated in place from its encode
+ * position to its global position, K <- R(pos - src) K. Fresh rows and V are not
+ * touched. Equals srp_fuse_layer's cache output at ratio 0 without fresh rows. */
+int srp_rerotate_kv(const srp_dims *dims, const srp_batch *batch, void *k_cache,
+                    srp_stream_t stream);
+
+/* Chain step between stacked layers (gradual filtering): for every selected row
+ * j = sel_idx[s], s < sel_offsets[n_req]:
+ *   hidden[j] <- y / sqrt(mean(y^2) + eps),  y = hidden[j] + attn_out[s]
+ * (unit-weight RMSNorm after the residual; requires n_heads * head_dim == hidden).
+ * sel_capacity bounds sel_offsets[n_req] (normally T). */
+int srp_residual_rmsnorm(const srp_dims *dims, void *hidden, const void *attn_out,
+                         const int32_t *sel_idx, const int32_t *sel_offsets,
+                         int32_t n_req, int32_t sel_capacity, float eps,
+                         srp_stream_t stream);
+
+/* Debug check of a batch's device arrays against the rules of srp_batch (copies
+ * them to the host and synchronises). SRP_OK or SRP_E_BATCH with a message. */
+int srp_validate_batch(const srp_batch *batch, srp_stream_t stream);
+
+/* Message for the last failing call on this thread ("" if none). */
+const char *srp_last_error(void);
+
+/* Library version string. */
+const char *srp_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SRP_H_ */

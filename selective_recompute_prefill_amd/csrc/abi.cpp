@@ -1,0 +1,360 @@
+// C ABI of libsrp (include/srp.h): argument checks, rotary tables, workspace
+// carve-up and the launch sequence of one fused layer on the caller's stream.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <tuple>
+#include <vector>
+
+#include "kernels.hpp"
+
+using namespace srp;
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char *fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define SRP_HIP(call)                                                             \
+  do {                                                                            \
+    hipError_t e_ = (call);                                                       \
+    if (e_ != hipSuccess)                                                         \
+      return fail(SRP_E_HIP, "%s failed: %s", #call, hipGetErrorString(e_));      \
+  } while (0)
+
+// ------------------------------------------------------------------------- //
+// rotary tables: one per (device, head_dim, base), grown on demand. cos/sin of
+// p * base^(-2i/d) are evaluated in double on the host and rounded to float.
+// Superseded tables stay allocated so in-flight work never reads freed memory.
+// ------------------------------------------------------------------------- //
+struct Table {
+  float *cos_t = nullptr, *sin_t = nullptr;
+  int max_pos = 0;
+};
+std::mutex g_mu;
+std::map<std::tuple<int, int, double>, Table> g_tables;
+std::vector<void *> g_retired;
+
+int get_table(int d, double base, int max_pos, RopeTable *out) {
+  int dev = 0;
+  SRP_HIP(hipGetDevice(&dev));
+  std::lock_guard<std::mutex> lk(g_mu);
+  Table &t = g_tables[std::make_tuple(dev, d, base)];
+  if (t.max_pos < max_pos) {
+    int cap = max_pos > 2 * t.max_pos ? max_pos : 2 * t.max_pos;
+    cap = (cap + 1023) / 1024 * 1024;
+    const int half = d / 2;
+    std::vector<float> c((size_t)cap * half), s((size_t)cap * half);
+    for (int i = 0; i < half; ++i) {
+      const double f = std::pow(base, -2.0 * i / d);
+      for (int p = 0; p < cap; ++p) {
+        const double th = (double)p * f;
+        c[(size_t)p * half + i] = (float)std::cos(th);
+        s[(size_t)p * half + i] = (float)std::sin(th);
+      }
+    }
+    float *dc = nullptr, *ds = nullptr;
+    SRP_HIP(hipMalloc(&dc, c.size() * sizeof(float)));
+    SRP_HIP(hipMalloc(&ds, s.size() * sizeof(float)));
+    SRP_HIP(hipMemcpy(dc, c.data(), c.size() * sizeof(float), hipMemcpyHostToDevice));
+    SRP_HIP(hipMemcpy(ds, s.data(), s.size() * sizeof(float), hipMemcpyHostToDevice));
+    if (t.cos_t) {
+      g_retired.push_back(t.cos_t);
+      g_retired.push_back(t.sin_t);
+    }
+    t.cos_t = dc;
+    t.sin_t = ds;
+    t.max_pos = cap;
+  }
+  *out = RopeTable{t.cos_t, t.sin_t, d / 2, t.max_pos};
+  return SRP_OK;
+}
+
+// ------------------------------------------------------------------------- //
+// argument checks
+// ------------------------------------------------------------------------- //
+int check_dims(const srp_dims *d) {
+  if (!d) return fail(SRP_E_INVALID, "dims is NULL");
+  if (d->dtype != SRP_F32 && d->dtype != SRP_BF16) return fail(SRP_E_INVALID, "dtype %d unknown", d->dtype);
+  if (d->hidden <= 0 || d->hidden % 64) return fail(SRP_E_INVALID, "hidden %d must be a positive multiple of 64", d->hidden);
+  if (d->n_kv_heads <= 0 || d->n_heads <= 0 || d->n_heads % d->n_kv_heads)
+    return fail(SRP_E_INVALID, "n_heads %d must be a positive multiple of n_kv_heads %d", d->n_heads, d->n_kv_heads);
+  if (d->n_heads / d->n_kv_heads > 8) return fail(SRP_E_UNSUPPORTED, "more than 8 query heads per KV head");
+  if (d->head_dim != 64 && d->head_dim != 128) return fail(SRP_E_UNSUPPORTED, "head_dim %d (64 or 128 supported)", d->head_dim);
+  if (!(d->rope_base > 1.0) || !std::isfinite(d->rope_base)) return fail(SRP_E_INVALID, "rope_base must be > 1");
+  return SRP_OK;
+}
+
+int check_batch(const srp_batch *b) {
+  if (!b) return fail(SRP_E_INVALID, "batch is NULL");
+  if (b->n_req < 1 || b->n_chunks < 1 || b->total_rows < 0 || b->max_req_rows < 0 || b->max_position < 1)
+    return fail(SRP_E_INVALID, "batch sizes out of range (n_req %d, n_chunks %d, rows %d, max_req_rows %d, max_position %d)",
+                b->n_req, b->n_chunks, b->total_rows, b->max_req_rows, b->max_position);
+  if (b->total_rows > 0 && b->max_req_rows < 1) return fail(SRP_E_INVALID, "max_req_rows must be >= 1");
+  if (!b->req_offsets || !b->chunk_offsets || !b->chunk_src_pos || (b->total_rows > 0 && !b->positions))
+    return fail(SRP_E_INVALID, "batch device arrays must not be NULL");
+  return SRP_OK;
+}
+
+int check_select(const srp_select *s) {
+  if (!s) return fail(SRP_E_INVALID, "select is NULL");
+  if (s->mode != SRP_SEL_TOPK && s->mode != SRP_SEL_GIVEN) return fail(SRP_E_INVALID, "selection mode %d unknown", s->mode);
+  if (!(s->ratio >= 0.0 && s->ratio <= 1.0)) return fail(SRP_E_INVALID, "ratio must lie in [0, 1]");
+  if (s->dev_mode != SRP_DEV_KV && s->dev_mode != SRP_DEV_V) return fail(SRP_E_INVALID, "dev_mode %d unknown", s->dev_mode);
+  if (s->window < 0) return fail(SRP_E_INVALID, "window must be >= 0");
+  if (s->window > 0) {
+    if (s->tau < 1 || s->tau > s->window) return fail(SRP_E_INVALID, "tau must lie in [1, window]");
+    if (s->cand) return fail(SRP_E_INVALID, "grouping scans every cached row: cand must be NULL");
+  }
+  if (s->cand && !s->cand_offsets) return fail(SRP_E_INVALID, "cand needs cand_offsets");
+  if (s->mode == SRP_SEL_GIVEN && !s->cand) return fail(SRP_E_INVALID, "SRP_SEL_GIVEN needs a candidate list");
+  return SRP_OK;
+}
+
+#define CHECK(x)            \
+  do {                      \
+    int rc_ = (x);          \
+    if (rc_ != SRP_OK) return rc_; \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char *srp_last_error(void) { return g_err.c_str(); }
+const char *srp_version(void) { return "libsrp 0.1 gfx950"; }
+
+int srp_workspace_size(const srp_dims *dims, const srp_batch *batch, const srp_select *sel, size_t *bytes) {
+  CHECK(check_dims(dims));
+  CHECK(check_batch(batch));
+  CHECK(check_select(sel));
+  if (!bytes) return fail(SRP_E_INVALID, "bytes is NULL");
+  *bytes = carve(*dims, *batch, nullptr).bytes;
+  return SRP_OK;
+}
+
+int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_select *sel,
+                   const void *hidden, const void *w_qkv, void *k_cache, void *v_cache,
+                   int32_t *sel_idx, int32_t *sel_offsets, void *attn_out, float *dev_out,
+                   void *workspace, size_t workspace_bytes, srp_stream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(dims));
+  CHECK(check_batch(batch));
+  CHECK(check_select(sel));
+  const srp_dims &d = *dims;
+  const srp_batch &b = *batch;
+  const int T = b.total_rows;
+  if (T > 0 && (!hidden || !w_qkv || !k_cache || !v_cache || !sel_idx || !attn_out))
+    return fail(SRP_E_INVALID, "tensor arguments must not be NULL");
+  if (!sel_offsets) return fail(SRP_E_INVALID, "sel_offsets must not be NULL");
+  const size_t need = carve(d, b, nullptr).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(SRP_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  RopeTable rt;
+  CHECK(get_table(d.head_dim, d.rope_base, b.max_position, &rt));
+  const Workspace w = carve(d, b, (char *)workspace);
+  const int kvd = d.n_kv_heads * d.head_dim, qd = d.n_heads * d.head_dim;
+  const size_t es = d.dtype == SRP_BF16 ? 2 : 4;
+
+  SelectArgs sa{};
+  sa.n_req = b.n_req;
+  sa.T = T;
+  sa.max_req_rows = b.max_req_rows;
+  sa.req_offsets = b.req_offsets;
+  sa.chunk_offsets = b.chunk_offsets;
+  sa.chunk_src_pos = b.chunk_src_pos;
+  sa.positions = b.positions;
+  sa.n_chunks = b.n_chunks;
+  sa.mode = sel->mode;
+  sa.window = sel->window;
+  sa.tau = sel->tau;
+  sa.dev_mode = sel->dev_mode;
+  sa.ratio = sel->ratio;
+  sa.cand = sel->cand;
+  sa.cand_offsets = sel->cand_offsets;
+  sa.nkv = d.n_kv_heads;
+  sa.dev_out = dev_out;
+
+  // 1. row metadata; candidate list and the recomputed rows R when given
+  SRP_HIP(launch_prepare(sa, w, s));
+  // 2. positional recovery of cached rows outside R (inside R the projection
+  //    epilogue rotates them next to the deviation)
+  if (sel->cand && T > 0)
+    SRP_HIP(launch_rerotate(d.dtype, T, d.n_kv_heads, d.head_dim, b.chunk_offsets, b.n_chunks,
+                            b.chunk_src_pos, b.positions, w.rowflag, rt, k_cache, s));
+  // 3. K/V projection of R with the rotation / deviation epilogue
+  GemmArgs g{};
+  g.dtype = d.dtype;
+  g.A = hidden;
+  g.K = d.hidden;
+  g.a_rows = sel->cand ? w.rlist : nullptr;
+  g.M_host = T;
+  g.M_dev = sel->cand ? w.ctr + kCtrREntries : nullptr;
+  g.M_cap = T;
+  g.B = (const char *)w_qkv + (size_t)qd * d.hidden * es;
+  g.N = 2 * kvd;
+  g.mode = EPI_KV;
+  g.nh = d.n_heads;
+  g.nkv = d.n_kv_heads;
+  g.d = d.head_dim;
+  g.positions = b.positions;
+  g.row_delta = w.row_delta;
+  g.rope = rt;
+  g.k_cache = k_cache;
+  g.v_cache = v_cache;
+  g.fresh = w.fresh_kv;
+  g.dev_part = w.dev_part;
+  SRP_HIP(launch_gemm(g, s));
+  // 4. top-k / grouping per request, CSR offsets, attention tiles
+  SRP_HIP(launch_select(sa, w, s));
+  SRP_HIP(launch_finalize(sa, w, sel_offsets, s));
+  // 5. sel_idx and the scatter of fresh K/V into the cache
+  SRP_HIP(launch_compact_scatter(sa, w, d.dtype, kvd, sel_idx, sel_offsets, k_cache, v_cache, s));
+  // 6. Q projection of the selected rows
+  GemmArgs gq = g;
+  gq.a_rows = sel_idx;
+  gq.M_dev = w.ctr + kCtrTotalSel;
+  gq.B = w_qkv;
+  gq.N = qd;
+  gq.mode = EPI_Q;
+  gq.q_out = w.q;
+  SRP_HIP(launch_gemm(gq, s));
+  // 7. attention of the selected rows over the fused cache
+  AttnArgs aa{};
+  aa.dtype = d.dtype;
+  aa.nh = d.n_heads;
+  aa.nkv = d.n_kv_heads;
+  aa.d = d.head_dim;
+  aa.q = w.q;
+  aa.sel_idx = sel_idx;
+  aa.req_offsets = b.req_offsets;
+  aa.tiles = w.tiles;
+  aa.n_tiles = w.ctr + kCtrTiles;
+  aa.max_tiles = max_attn_tiles(T, b.n_req);
+  aa.k_cache = k_cache;
+  aa.v_cache = v_cache;
+  aa.out = attn_out;
+  if (T > 0) SRP_HIP(launch_attention(aa, s));
+  return SRP_OK;
+}
+
+int srp_encode_kv(const srp_dims *dims, int32_t n_rows, int32_t max_position, const void *hidden,
+                  const void *w_qkv, const int32_t *positions, void *k_out, void *v_out,
+                  srp_stream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(dims));
+  if (n_rows < 0 || max_position < 1) return fail(SRP_E_INVALID, "n_rows / max_position out of range");
+  if (n_rows == 0) return SRP_OK;
+  if (!hidden || !w_qkv || !positions || !k_out || !v_out) return fail(SRP_E_INVALID, "NULL tensor argument");
+  const srp_dims &d = *dims;
+  RopeTable rt;
+  CHECK(get_table(d.head_dim, d.rope_base, max_position, &rt));
+  const size_t es = d.dtype == SRP_BF16 ? 2 : 4;
+  GemmArgs g{};
+  g.dtype = d.dtype;
+  g.A = hidden;
+  g.K = d.hidden;
+  g.M_host = n_rows;
+  g.M_cap = n_rows;
+  g.B = (const char *)w_qkv + (size_t)d.n_heads * d.head_dim * d.hidden * es;
+  g.N = 2 * d.n_kv_heads * d.head_dim;
+  g.mode = EPI_ENC;
+  g.nh = d.n_heads;
+  g.nkv = d.n_kv_heads;
+  g.d = d.head_dim;
+  g.positions = positions;
+  g.rope = rt;
+  g.k_cache = k_out;
+  g.v_cache = v_out;
+  SRP_HIP(launch_gemm(g, (hipStream_t)stream));
+  return SRP_OK;
+}
+
+int srp_rerotate_kv(const srp_dims *dims, const srp_batch *batch, void *k_cache, srp_stream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(dims));
+  CHECK(check_batch(batch));
+  if (batch->total_rows == 0) return SRP_OK;
+  if (!k_cache) return fail(SRP_E_INVALID, "k_cache is NULL");
+  RopeTable rt;
+  CHECK(get_table(dims->head_dim, dims->rope_base, batch->max_position, &rt));
+  SRP_HIP(launch_rerotate(dims->dtype, batch->total_rows, dims->n_kv_heads, dims->head_dim,
+                          batch->chunk_offsets, batch->n_chunks, batch->chunk_src_pos,
+                          batch->positions, nullptr, rt, k_cache, (hipStream_t)stream));
+  return SRP_OK;
+}
+
+int srp_residual_rmsnorm(const srp_dims *dims, void *hidden, const void *attn_out,
+                         const int32_t *sel_idx, const int32_t *sel_offsets, int32_t n_req,
+                         int32_t sel_capacity, float eps, srp_stream_t stream) {
+  g_err.clear();
+  CHECK(check_dims(dims));
+  if (dims->n_heads * dims->head_dim != dims->hidden)
+    return fail(SRP_E_INVALID, "residual needs n_heads * head_dim == hidden");
+  if (n_req < 1 || sel_capacity < 0 || !(eps >= 0.f)) return fail(SRP_E_INVALID, "n_req / sel_capacity / eps out of range");
+  if (sel_capacity == 0) return SRP_OK;
+  if (!hidden || !attn_out || !sel_idx || !sel_offsets) return fail(SRP_E_INVALID, "NULL tensor argument");
+  SRP_HIP(launch_residual_rmsnorm(dims->dtype, dims->hidden, hidden, attn_out, sel_idx,
+                                  sel_offsets + n_req, sel_capacity, eps, (hipStream_t)stream));
+  return SRP_OK;
+}
+
+int srp_validate_batch(const srp_batch *batch, srp_stream_t stream) {
+  g_err.clear();
+  CHECK(check_batch(batch));
+  const srp_batch &b = *batch;
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<int32_t> ro(b.n_req + 1), co(b.n_chunks + 1), cs(b.n_chunks), pos(b.total_rows);
+  SRP_HIP(hipMemcpyAsync(ro.data(), b.req_offsets, ro.size() * 4, hipMemcpyDeviceToHost, s));
+  SRP_HIP(hipMemcpyAsync(co.data(), b.chunk_offsets, co.size() * 4, hipMemcpyDeviceToHost, s));
+  SRP_HIP(hipMemcpyAsync(cs.data(), b.chunk_src_pos, cs.size() * 4, hipMemcpyDeviceToHost, s));
+  if (b.total_rows)
+    SRP_HIP(hipMemcpyAsync(pos.data(), b.positions, pos.size() * 4, hipMemcpyDeviceToHost, s));
+  SRP_HIP(hipStreamSynchronize(s));
+  const int T = b.total_rows;
+  if (ro[0] != 0 || ro[b.n_req] != T) return fail(SRP_E_BATCH, "req_offsets must run from 0 to total_rows");
+  if (co[0] != 0 || co[b.n_chunks] != T) return fail(SRP_E_BATCH, "chunk_offsets must run from 0 to total_rows");
+  for (int r = 0; r < b.n_req; ++r) {
+    if (ro[r + 1] < ro[r]) return fail(SRP_E_BATCH, "req_offsets decrease at %d", r);
+    if (ro[r + 1] - ro[r] > b.max_req_rows) return fail(SRP_E_BATCH, "request %d has more than max_req_rows rows", r);
+    for (int j = ro[r] + 1; j < ro[r + 1]; ++j)
+      if (pos[j] <= pos[j - 1]) return fail(SRP_E_BATCH, "positions not strictly increasing at row %d", j);
+  }
+  for (int j = 0; j < T; ++j)
+    if (pos[j] < 0 || pos[j] >= b.max_position) return fail(SRP_E_BATCH, "position of row %d outside [0, max_position)", j);
+  int r = 0;
+  for (int c = 0; c < b.n_chunks; ++c) {
+    if (co[c + 1] < co[c]) return fail(SRP_E_BATCH, "chunk_offsets decrease at %d", c);
+    if (co[c + 1] == co[c]) continue;
+    while (r < b.n_req && ro[r + 1] <= co[c]) ++r;
+    if (r >= b.n_req || co[c] < ro[r] || co[c + 1] > ro[r + 1])
+      return fail(SRP_E_BATCH, "segment %d crosses a request boundary", c);
+    if (cs[c] < -1) return fail(SRP_E_BATCH, "chunk_src_pos[%d] < -1", c);
+    if (cs[c] >= 0) {
+      const long last = (long)cs[c] + (co[c + 1] - co[c]) - 1;
+      if (last >= b.max_position) return fail(SRP_E_BATCH, "segment %d encoded past max_position", c);
+      for (int j = co[c]; j < co[c + 1]; ++j) {
+        const long delta = (long)pos[j] - (cs[c] + (j - co[c]));
+        if (delta >= b.max_position || -delta >= b.max_position)
+          return fail(SRP_E_BATCH, "|pos - src| of row %d reaches max_position", j);
+      }
+    }
+  }
+  return SRP_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,219 @@
+// Shared definitions of libsrp's HIP kernels and host code (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+#include "../../include/srp.h"
+
+namespace srp {
+
+constexpr int kFresh = INT32_MIN;  // row_delta of a row without a cache
+constexpr int kWave = 64;
+
+// Per R-entry flags.
+constexpr uint8_t kCand = 1;   // cached row that is scored (candidate)
+constexpr uint8_t kFreshF = 2; // fresh row: always recomputed and selected
+constexpr uint8_t kTop = 4;    // chosen by top-k
+constexpr uint8_t kSel = 8;    // in the final selection
+
+// Attention query tile (selected rows per work-group).
+constexpr int kQT = 32;
+
+// ------------------------------------------------------------------------- //
+// bf16 storage
+// ------------------------------------------------------------------------- //
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// float -> bf16, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> struct Elem;
+template <> struct Elem<float> {
+  __device__ static __forceinline__ float ld(const float *p) { return *p; }
+  __device__ static __forceinline__ void st(float *p, float v) { *p = v; }
+};
+template <> struct Elem<uint16_t> {
+  __device__ static __forceinline__ float ld(const uint16_t *p) { return bf2f(*p); }
+  __device__ static __forceinline__ void st(uint16_t *p, float v) { *p = f2bf(v); }
+};
+
+// Load / store 4 consecutive elements as floats.
+__device__ __forceinline__ void ld4(const float *p, float v[4]) {
+  float4 t = *reinterpret_cast<const float4 *>(p);
+  v[0] = t.x; v[1] = t.y; v[2] = t.z; v[3] = t.w;
+}
+__device__ __forceinline__ void ld4(const uint16_t *p, float v[4]) {
+  uint2 t = *reinterpret_cast<const uint2 *>(p);
+  v[0] = __uint_as_float(t.x << 16); v[1] = __uint_as_float(t.x & 0xffff0000u);
+  v[2] = __uint_as_float(t.y << 16); v[3] = __uint_as_float(t.y & 0xffff0000u);
+}
+__device__ __forceinline__ void st4(float *p, const float v[4]) {
+  *reinterpret_cast<float4 *>(p) = make_float4(v[0], v[1], v[2], v[3]);
+}
+__device__ __forceinline__ void st4(uint16_t *p, const float v[4]) {
+  uint2 t;
+  t.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  t.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<uint2 *>(p) = t;
+}
+
+// ------------------------------------------------------------------------- //
+// wave / block primitives (wave64)
+// ------------------------------------------------------------------------- //
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan over the block (blockDim.x a multiple of 64, <= 1024).
+// `sh` needs 17 ints of LDS. Returns the exclusive prefix; *total = block sum.
+__device__ __forceinline__ int block_excl_scan(int v, int *sh, int *total) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int inc = wave_incl_scan(v);
+  if (lane == 63) sh[wid] = inc;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    int run = 0;
+    for (int w = 0; w < nw; ++w) { int t = sh[w]; sh[w] = run; run += t; }
+    sh[16] = run;
+  }
+  __syncthreads();
+  int res = sh[wid] + inc - v;
+  *total = sh[16];
+  __syncthreads();
+  return res;
+}
+
+__device__ __forceinline__ int block_sum(int v, int *sh) {
+  int tot;
+  block_excl_scan(v, sh, &tot);
+  return tot;
+}
+
+// Largest i in [0, n) with a[i] <= x, for a non-decreasing a with a[0] <= x.
+__device__ __forceinline__ int upper_index(const int32_t *a, int n, int x) {
+  int lo = 0, hi = n - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// ------------------------------------------------------------------------- //
+// rotary tables: cos/sin of p * base^(-2i/d), p < max_position, i < d/2,
+// computed in fp64 on the host and stored as fp32 [max_position][d/2].
+// ------------------------------------------------------------------------- //
+struct RopeTable {
+  const float *cos_t;
+  const float *sin_t;
+  int half;
+  int max_pos;
+};
+
+// Rotate 4 rotation pairs (a[i], b[i]) = (x_i, x_{i+d/2}) by angle index p,
+// p may be negative (rotation by -|p|).
+__device__ __forceinline__ void rope4(float a[4], float b[4], const RopeTable &t, int p, int i0) {
+  int ap = p < 0 ? -p : p;
+  ap = ap < t.max_pos ? ap : t.max_pos - 1;  // never read past the table
+  float c[4], s[4];
+  ld4(t.cos_t + (size_t)ap * t.half + i0, c);
+  ld4(t.sin_t + (size_t)ap * t.half + i0, s);
+  const float sg = p < 0 ? -1.f : 1.f;
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    float sk = sg * s[k];
+    float x = a[k], y = b[k];
+    a[k] = x * c[k] - y * sk;
+    b[k] = y * c[k] + x * sk;
+  }
+}
+
+// ------------------------------------------------------------------------- //
+// workspace carve-up
+// ------------------------------------------------------------------------- //
+struct Workspace {
+  int32_t *row_delta;  // [T] pos - src, kFresh for fresh rows
+  int32_t *row_req;    // [T]
+  uint8_t *rowflag;    // [T] candidate marks by row (candidate-list mode)
+  int32_t *rlist;      // [T] R entry -> row (candidate-list mode)
+  int32_t *roff;       // [n_req+1] R offsets (candidate-list mode)
+  int32_t *blkcnt;     // compaction block counts; later per-request tile counts
+  float *dev_part;     // [T][2 nkv] per-head squared-deviation partials
+  void *fresh_kv;      // [T][2 kvdim] recomputed K (roped) and V, storage type
+  uint32_t *keys;      // [T] fp32 bit patterns of squared deviations
+  uint8_t *eflag;      // [T] per R-entry flags
+  int32_t *seq_ent;    // [T] grouping: sequence slot -> entry
+  int32_t *seq_pre;    // [T] grouping: prefix counts
+  uint8_t *seq_flag;   // [T] grouping: top-k / passing-window flags
+  int32_t *tsel_row;   // [T] selection per request, at the request's R offset
+  int32_t *tsel_ent;   // [T]
+  int32_t *sel_cnt;    // [n_req]
+  int32_t *sel_ent;    // [T] compact: R entry of each selected row
+  void *q;             // [T][qdim] roped queries of the selected rows
+  int32_t *tiles;      // [3 * max_tiles] attention tiles (first sel, count, req)
+  int32_t *ctr;        // [16] device counters (see kCtr*)
+  size_t bytes;
+};
+constexpr int kCtrTotalSel = 0;
+constexpr int kCtrTiles = 1;
+constexpr int kCtrREntries = 2;
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+inline int blocks_per_req(int max_req_rows) { return (max_req_rows + 1023) / 1024 > 0 ? (max_req_rows + 1023) / 1024 : 1; }
+inline int max_attn_tiles(int T, int n_req) { return T / kQT + n_req + 1; }
+
+// Lays the workspace out from `base` (nullptr: just measure).
+inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base) {
+  const size_t T = (size_t)(b.total_rows > 0 ? b.total_rows : 1);
+  const size_t nr = (size_t)b.n_req;
+  const size_t es = d.dtype == SRP_BF16 ? 2 : 4;
+  const size_t kvd = (size_t)d.n_kv_heads * d.head_dim, qd = (size_t)d.n_heads * d.head_dim;
+  Workspace w{};
+  size_t off = 0;
+  auto take = [&](size_t n) -> char * {
+    char *p = base ? base + off : nullptr;
+    off = align_up(off + n, 256);
+    return p;
+  };
+  w.row_delta = (int32_t *)take(T * 4);
+  w.row_req = (int32_t *)take(T * 4);
+  w.rowflag = (uint8_t *)take(T);
+  w.rlist = (int32_t *)take(T * 4);
+  w.roff = (int32_t *)take((nr + 1) * 4);
+  {
+    const size_t nb = nr * (size_t)blocks_per_req(b.max_req_rows) + 1;
+    w.blkcnt = (int32_t *)take((nb > 2 * nr + 2 ? nb : 2 * nr + 2) * 4);
+  }
+  w.dev_part = (float *)take(T * 2 * d.n_kv_heads * 4);
+  w.fresh_kv = take(T * 2 * kvd * es);
+  w.keys = (uint32_t *)take(T * 4);
+  w.eflag = (uint8_t *)take(T);
+  w.seq_ent = (int32_t *)take(T * 4);
+  w.seq_pre = (int32_t *)take(T * 4);
+  w.seq_flag = (uint8_t *)take(T);
+  w.tsel_row = (int32_t *)take(T * 4);
+  w.tsel_ent = (int32_t *)take(T * 4);
+  w.sel_cnt = (int32_t *)take(nr * 4);
+  w.sel_ent = (int32_t *)take(T * 4);
+  w.q = take(T * qd * es);
+  w.tiles = (int32_t *)take((size_t)3 * max_attn_tiles((int)T, (int)nr) * 4);
+  w.ctr = (int32_t *)take(16 * 4);
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace srp

@@ -1,0 +1,108 @@
+// Streaming kernels outside the projection: standalone positional recovery of the
+// cached keys, and the residual + RMSNorm step between stacked layers (gfx950).
+#include "kernels.hpp"
+
+namespace srp {
+
+// K[j] <- R(pos_j - src_j) K[j] for cached rows. One thread per 4 rotation pairs of
+// one head of one row: consecutive threads cover consecutive 8-byte (bf16) or
+// 16-byte (fp32) pieces of the two halves of a head, so the row streams coalesced.
+template <typename T>
+__global__ __launch_bounds__(256) void rerotate_kernel(int T_rows, int nkv, int d,
+                                                      const int32_t *chunk_offsets, int n_chunks,
+                                                      const int32_t *chunk_src_pos,
+                                                      const int32_t *positions, const uint8_t *skip,
+                                                      RopeTable rt, T *k_cache) {
+  const int half = d >> 1, per_head = half >> 2, per_row = nkv * per_head;
+  const long n = (long)T_rows * per_row;
+  for (long it = blockIdx.x * (long)blockDim.x + threadIdx.x; it < n; it += (long)gridDim.x * blockDim.x) {
+    const int j = (int)(it / per_row);
+    const int rem = (int)(it - (long)j * per_row);
+    const int gh = rem / per_head, i0 = (rem - gh * per_head) * 4;
+    if (skip && skip[j]) continue;
+    const int c = upper_index(chunk_offsets, n_chunks + 1, j);
+    const int src0 = chunk_src_pos[c];
+    if (src0 < 0) continue;
+    const int delta = positions[j] - (src0 + j - chunk_offsets[c]);
+    if (delta == 0) continue;
+    T *p = k_cache + ((size_t)j * nkv + gh) * d;
+    float a[4], b[4];
+    ld4(p + i0, a);
+    ld4(p + half + i0, b);
+    rope4(a, b, rt, delta, i0);
+    st4(p + i0, a);
+    st4(p + half + i0, b);
+  }
+}
+
+hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *chunk_offsets,
+                           int n_chunks, const int32_t *chunk_src_pos, const int32_t *positions,
+                           const uint8_t *skip, const RopeTable &rt, void *k_cache, hipStream_t s) {
+  const long n = (long)T * nkv * (d / 8);
+  if (n <= 0) return hipSuccess;
+  long grid = (n + 255) / 256;
+  grid = grid < 8192 ? grid : 8192;
+  if (dtype == SRP_BF16)
+    hipLaunchKernelGGL(rerotate_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, s, T, nkv, d,
+                       chunk_offsets, n_chunks, chunk_src_pos, positions, skip, rt,
+                       (uint16_t *)k_cache);
+  else
+    hipLaunchKernelGGL(rerotate_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, T, nkv, d,
+                       chunk_offsets, n_chunks, chunk_src_pos, positions, skip, rt,
+                       (float *)k_cache);
+  return hipGetLastError();
+}
+
+// hidden[j] <- y / sqrt(mean(y^2) + eps), y = hidden[j] + attn[s], j = sel_idx[s].
+// One work-group per selected row; fixed-order reduction.
+template <typename T>
+__global__ __launch_bounds__(256) void residual_rmsnorm_kernel(int H, T *hidden, const T *attn,
+                                                              const int32_t *sel_idx,
+                                                              const int32_t *total_dev, float eps) {
+  __shared__ float red[4];
+  const int total = *total_dev;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  for (int s = blockIdx.x; s < total; s += gridDim.x) {
+    const int j = sel_idx[s];
+    T *x = hidden + (size_t)j * H;
+    const T *o = attn + (size_t)s * H;
+    float ss = 0.f;
+    for (int i = tid * 4; i < H; i += 1024) {
+      float a[4], b[4];
+      ld4(x + i, a);
+      ld4(o + i, b);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { const float y = a[k] + b[k]; ss = fmaf(y, y, ss); }
+    }
+    for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
+    if (lane == 0) red[w] = ss;
+    __syncthreads();
+    const float tot = (red[0] + red[1]) + (red[2] + red[3]);
+    const float sc = 1.f / sqrtf(tot / (float)H + eps);
+    for (int i = tid * 4; i < H; i += 1024) {
+      float a[4], b[4];
+      ld4(x + i, a);
+      ld4(o + i, b);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) a[k] = (a[k] + b[k]) * sc;
+      st4(x + i, a);
+    }
+    __syncthreads();
+  }
+}
+
+hipError_t launch_residual_rmsnorm(int dtype, int H, void *hidden, const void *attn,
+                                   const int32_t *sel_idx, const int32_t *total_dev, int cap,
+                                   float eps, hipStream_t s) {
+  if (cap <= 0) return hipSuccess;
+  const int grid = cap < 2048 ? cap : 2048;
+  if (dtype == SRP_BF16)
+    hipLaunchKernelGGL(residual_rmsnorm_kernel<uint16_t>, dim3(grid), dim3(256), 0, s, H,
+                       (uint16_t *)hidden, (const uint16_t *)attn, sel_idx, total_dev, eps);
+  else
+    hipLaunchKernelGGL(residual_rmsnorm_kernel<float>, dim3(grid), dim3(256), 0, s, H,
+                       (float *)hidden, (const float *)attn, sel_idx, total_dev, eps);
+  return hipGetLastError();
+}
+
+}  // namespace srp

@@ -1,0 +1,85 @@
+// Host-side launchers of libsrp's kernels (internal to the library).
+#pragma once
+
+#include "common.hpp"
+
+namespace srp {
+
+enum EpiMode { EPI_KV = 0, EPI_Q = 1, EPI_ENC = 2 };
+
+// C[m, n] = sum_k A[row(m), k] * B[n, k], followed by an epilogue on each
+// head-sized unit of a row:
+//  EPI_KV : n < kvdim are K heads (roped at the row's global position), the rest
+//           V heads. Fresh K/V go to `fresh` [m][2 kvdim]. For cached rows the
+//           cached K is rotated by the row's delta (written back in place) and the
+//           squared deviation of each head goes to dev_part [m][2 nkv].
+//  EPI_Q  : n are Q heads, roped; written to q_out [m][qdim].
+//  EPI_ENC: like EPI_KV's layout, K roped at positions[m]; K -> k_cache[m],
+//           V -> v_cache[m].
+struct GemmArgs {
+  int dtype;
+  const void *A;       // [*, K]
+  int K;
+  const int32_t *a_rows;  // m -> row of A (NULL: identity)
+  int M_host;
+  const int32_t *M_dev;   // device M (overrides M_host when set)
+  int M_cap;              // upper bound of M (grid sizing)
+  const void *B;       // [N, K]
+  int N;
+  int mode;
+  int nh, nkv, d;
+  const int32_t *positions;
+  const int32_t *row_delta;
+  RopeTable rope;
+  void *k_cache, *v_cache;
+  void *fresh;
+  float *dev_part;
+  void *q_out;
+};
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
+
+struct SelectArgs {
+  int n_req, T, max_req_rows;
+  const int32_t *req_offsets, *chunk_offsets, *chunk_src_pos, *positions;
+  int n_chunks;
+  int mode, window, tau, dev_mode;
+  double ratio;
+  const int32_t *cand, *cand_offsets;
+  int nkv;
+  float *dev_out;
+};
+// Row metadata (delta, request), dev_out prefill with NaN, candidate marking and
+// the R list (candidate rows plus fresh rows, per request) when cand is given.
+hipError_t launch_prepare(const SelectArgs &a, const Workspace &w, hipStream_t s);
+hipError_t launch_select(const SelectArgs &a, const Workspace &w, hipStream_t s);
+hipError_t launch_finalize(const SelectArgs &a, const Workspace &w, int32_t *sel_offsets,
+                           hipStream_t s);
+hipError_t launch_compact_scatter(const SelectArgs &a, const Workspace &w, int dtype, int kvdim,
+                                  int32_t *sel_idx, const int32_t *sel_offsets, void *k_cache,
+                                  void *v_cache, hipStream_t s);
+// Re-rotation of cached rows; with `skip` (row flags) rows flagged as candidates
+// are left alone (the projection epilogue rotates those).
+hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *chunk_offsets,
+                           int n_chunks, const int32_t *chunk_src_pos,
+                           const int32_t *positions, const uint8_t *skip, const RopeTable &rt,
+                           void *k_cache, hipStream_t s);
+
+struct AttnArgs {
+  int dtype;
+  int nh, nkv, d;
+  const void *q;           // [n_sel][nh][d]
+  const int32_t *sel_idx;  // [n_sel]
+  const int32_t *req_offsets;
+  const int32_t *tiles;    // [3 * max_tiles]: first selected row, count, request
+  const int32_t *n_tiles;  // device
+  int max_tiles;
+  const void *k_cache, *v_cache;
+  void *out;               // [n_sel][nh][d]
+};
+hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
+
+hipError_t launch_residual_rmsnorm(int dtype, int H, void *hidden, const void *attn,
+                                   const int32_t *sel_idx, const int32_t *total_dev,
+                                   int cap, float eps, hipStream_t s);
+
+}  // namespace srp

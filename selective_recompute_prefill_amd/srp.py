@@ -1,0 +1,161 @@
+"""ctypes binding of libsrp.so (include/srp.h), with the same entry-point names.
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels. torch tensors are accepted for device memory and streams; their data
+pointers and the current HIP stream are passed through unchanged. There is no
+fallback: if libsrp.so is missing or fails to load, every call raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libsrp.so")
+
+SRP_OK, SRP_E_INVALID, SRP_E_WORKSPACE, SRP_E_UNSUPPORTED, SRP_E_HIP, SRP_E_BATCH = 0, -1, -2, -3, -4, -5
+SRP_F32, SRP_BF16 = 0, 1
+SRP_SEL_TOPK, SRP_SEL_GIVEN = 0, 1
+SRP_DEV_KV, SRP_DEV_V = 0, 1
+
+EXPORTS = ("srp_workspace_size", "srp_fuse_layer", "srp_encode_kv", "srp_rerotate_kv",
+           "srp_residual_rmsnorm", "srp_validate_batch", "srp_last_error", "srp_version")
+
+
+class SrpError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libsrp error {code}: {msg}")
+        self.code = code
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("hidden", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("rope_base", ctypes.c_double), ("dtype", ctypes.c_int32)]
+
+
+class Batch(ctypes.Structure):
+    _fields_ = [("n_req", ctypes.c_int32), ("n_chunks", ctypes.c_int32),
+                ("total_rows", ctypes.c_int32), ("max_req_rows", ctypes.c_int32),
+                ("max_position", ctypes.c_int32),
+                ("req_offsets", ctypes.c_void_p), ("chunk_offsets", ctypes.c_void_p),
+                ("chunk_src_pos", ctypes.c_void_p), ("positions", ctypes.c_void_p)]
+
+
+class Select(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("ratio", ctypes.c_double),
+                ("window", ctypes.c_int32), ("tau", ctypes.c_int32),
+                ("dev_mode", ctypes.c_int32), ("cand", ctypes.c_void_p),
+                ("cand_offsets", ctypes.c_void_p)]
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded library; raises if it is not built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is not built (run selective_recompute_prefill_amd.build)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+        P = ctypes.POINTER
+        L.srp_workspace_size.argtypes = [P(Dims), P(Batch), P(Select), P(sz)]
+        L.srp_fuse_layer.argtypes = [P(Dims), P(Batch), P(Select), vp, vp, vp, vp, vp, vp, vp, vp,
+                                     vp, sz, vp]
+        L.srp_encode_kv.argtypes = [P(Dims), i32, i32, vp, vp, vp, vp, vp, vp]
+        L.srp_rerotate_kv.argtypes = [P(Dims), P(Batch), vp, vp]
+        L.srp_residual_rmsnorm.argtypes = [P(Dims), vp, vp, vp, vp, i32, i32, ctypes.c_float, vp]
+        L.srp_validate_batch.argtypes = [P(Batch), vp]
+        for f in ("srp_workspace_size", "srp_fuse_layer", "srp_encode_kv", "srp_rerotate_kv",
+                  "srp_residual_rmsnorm", "srp_validate_batch"):
+            getattr(L, f).restype = ctypes.c_int
+        L.srp_last_error.restype = ctypes.c_char_p
+        L.srp_version.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(rc: int) -> int:
+    if rc != SRP_OK:
+        raise SrpError(rc, lib().srp_last_error().decode())
+    return rc
+
+
+def _ptr(t) -> Optional[int]:
+    """Device pointer of a tensor (or None / an int passed through)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def make_dims(hidden, n_heads, n_kv_heads, head_dim, rope_base=10000.0, dtype=SRP_BF16) -> Dims:
+    return Dims(hidden, n_heads, n_kv_heads, head_dim, float(rope_base), dtype)
+
+
+def make_batch(req_offsets, chunk_offsets, chunk_src_pos, positions, *, total_rows: int,
+               max_req_rows: int, max_position: int) -> Batch:
+    """Batch descriptor over int32 device tensors (sizes are host ints)."""
+    return Batch(len(req_offsets) - 1, len(chunk_offsets) - 1, int(total_rows), int(max_req_rows),
+                 int(max_position), _ptr(req_offsets), _ptr(chunk_offsets), _ptr(chunk_src_pos),
+                 _ptr(positions))
+
+
+def make_select(ratio: float, *, mode=SRP_SEL_TOPK, window=0, tau=0, dev_mode=SRP_DEV_KV,
+                cand=None, cand_offsets=None) -> Select:
+    return Select(mode, float(ratio), int(window), int(tau), dev_mode, _ptr(cand), _ptr(cand_offsets))
+
+
+def srp_workspace_size(dims: Dims, batch: Batch, sel: Select) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().srp_workspace_size(ctypes.byref(dims), ctypes.byref(batch), ctypes.byref(sel),
+                                    ctypes.byref(n)))
+    return n.value
+
+
+def srp_fuse_layer(dims: Dims, batch: Batch, sel: Select, hidden, w_qkv, k_cache, v_cache,
+                   sel_idx, sel_offsets, attn_out, dev_out, workspace, workspace_bytes: int,
+                   stream=None) -> int:
+    return _check(lib().srp_fuse_layer(
+        ctypes.byref(dims), ctypes.byref(batch), ctypes.byref(sel), _ptr(hidden), _ptr(w_qkv),
+        _ptr(k_cache), _ptr(v_cache), _ptr(sel_idx), _ptr(sel_offsets), _ptr(attn_out),
+        _ptr(dev_out), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def srp_encode_kv(dims: Dims, n_rows: int, max_position: int, hidden, w_qkv, positions, k_out,
+                  v_out, stream=None) -> int:
+    return _check(lib().srp_encode_kv(ctypes.byref(dims), int(n_rows), int(max_position),
+                                      _ptr(hidden), _ptr(w_qkv), _ptr(positions), _ptr(k_out),
+                                      _ptr(v_out), _stream(stream)))
+
+
+def srp_rerotate_kv(dims: Dims, batch: Batch, k_cache, stream=None) -> int:
+    return _check(lib().srp_rerotate_kv(ctypes.byref(dims), ctypes.byref(batch), _ptr(k_cache),
+                                        _stream(stream)))
+
+
+def srp_residual_rmsnorm(dims: Dims, hidden, attn_out, sel_idx, sel_offsets, n_req: int,
+                         sel_capacity: int, eps: float = 1e-6, stream=None) -> int:
+    return _check(lib().srp_residual_rmsnorm(ctypes.byref(dims), _ptr(hidden), _ptr(attn_out),
+                                             _ptr(sel_idx), _ptr(sel_offsets), int(n_req),
+                                             int(sel_capacity), float(eps), _stream(stream)))
+
+
+def srp_validate_batch(batch: Batch, stream=None) -> int:
+    return _check(lib().srp_validate_batch(ctypes.byref(batch), _stream(stream)))
+
+
+def srp_version() -> str:
+    return lib().srp_version().decode()

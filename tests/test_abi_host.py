@@ -1,0 +1,104 @@
+"""Host-side checks of the C ABI: the library loads, exports every entry point the
+header declares, and rejects host-checkable bad arguments before touching a GPU.
+CPU only (no HIP call is reached on these paths)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from selective_recompute_prefill_amd import srp as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "srp.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:int|const char \*)\s*(srp_\w+)\s*\(", txt, re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) >= 8
+    L = S.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(S.EXPORTS)
+    assert "gfx950" in S.srp_version()
+
+
+def _dims(**kw):
+    d = dict(hidden=512, n_heads=8, n_kv_heads=2, head_dim=128, rope_base=1e4, dtype=S.SRP_BF16)
+    d.update(kw)
+    return S.Dims(**d)
+
+
+def _batch(**kw):
+    b = dict(n_req=1, n_chunks=1, total_rows=100, max_req_rows=100, max_position=100,
+             req_offsets=8, chunk_offsets=8, chunk_src_pos=8, positions=8)
+    b.update(kw)
+    return S.Batch(**b)
+
+
+@pytest.mark.parametrize("dims_kw,code", [
+    (dict(head_dim=96), S.SRP_E_UNSUPPORTED),
+    (dict(hidden=100), S.SRP_E_INVALID),
+    (dict(n_heads=6, n_kv_heads=4), S.SRP_E_INVALID),
+    (dict(n_heads=32, n_kv_heads=2), S.SRP_E_UNSUPPORTED),
+    (dict(dtype=7), S.SRP_E_INVALID),
+    (dict(rope_base=0.5), S.SRP_E_INVALID),
+])
+def test_bad_dims(dims_kw, code):
+    with pytest.raises(S.SrpError) as e:
+        S.srp_workspace_size(_dims(**dims_kw), _batch(), S.make_select(0.2))
+    assert e.value.code == code
+
+
+@pytest.mark.parametrize("sel,code", [
+    (dict(ratio=1.5), S.SRP_E_INVALID),
+    (dict(ratio=-0.1), S.SRP_E_INVALID),
+    (dict(ratio=float("nan")), S.SRP_E_INVALID),
+    (dict(ratio=0.2, window=8, tau=9), S.SRP_E_INVALID),
+    (dict(ratio=0.2, window=8, tau=0), S.SRP_E_INVALID),
+    (dict(ratio=0.2, window=8, tau=4, cand=8, cand_offsets=8), S.SRP_E_INVALID),
+    (dict(ratio=0.2, cand=8), S.SRP_E_INVALID),
+    (dict(ratio=0.2, mode=S.SRP_SEL_GIVEN), S.SRP_E_INVALID),
+    (dict(ratio=0.2, dev_mode=3), S.SRP_E_INVALID),
+])
+def test_bad_select(sel, code):
+    ratio = sel.pop("ratio")
+    with pytest.raises(S.SrpError) as e:
+        S.srp_workspace_size(_dims(), _batch(), S.make_select(ratio, **sel))
+    assert e.value.code == code
+    assert len(S.lib().srp_last_error()) > 0
+
+
+def test_bad_batch():
+    for kw in [dict(n_req=0), dict(total_rows=-1), dict(max_position=0), dict(req_offsets=None)]:
+        with pytest.raises(S.SrpError):
+            S.srp_workspace_size(_dims(), _batch(**kw), S.make_select(0.2))
+
+
+def test_workspace_too_small_is_rejected_before_launch():
+    d, b, s = _dims(), _batch(), S.make_select(0.2)
+    n = S.srp_workspace_size(d, b, s)
+    with pytest.raises(S.SrpError) as e:
+        S.srp_fuse_layer(d, b, s, 8, 8, 8, 8, 8, 8, 8, None, 8, n - 1, 0)
+    assert e.value.code == S.SRP_E_WORKSPACE
+
+
+def test_workspace_monotone():
+    s = S.make_select(0.2)
+    sizes = [S.srp_workspace_size(_dims(), _batch(total_rows=t, max_req_rows=t), s)
+             for t in (0, 1, 100, 1000, 10000)]
+    assert sizes == sorted(sizes)
+    assert S.srp_workspace_size(_dims(dtype=S.SRP_F32), _batch(), s) > \
+        S.srp_workspace_size(_dims(), _batch(), s)
+
+
+def test_struct_layouts_match_header():
+    # offsets the C compiler gives these structs on x86-64 (int32 then aligned double)
+    assert ctypes.sizeof(S.Dims) == 32 and S.Dims.rope_base.offset == 16
+    assert S.Batch.req_offsets.offset == 24 and ctypes.sizeof(S.Batch) == 56
+    assert S.Select.ratio.offset == 8 and S.Select.cand.offset == 32

@@ -1,0 +1,272 @@
+"""GPU parity of srp_fuse_layer and the other entry points against the fp64 oracle.
+
+Every case generates seeded inputs, lets the oracle encode the chunk caches, rounds
+them to the storage dtype, and feeds the same stored arrays to both sides. The
+selected set must match except for near-ties; K/V caches, deviations and attention
+rows must match within the dtype's tolerance (bf16: rel-L2 1e-2, max-abs 3e-2;
+fp32: 1e-5). Sizes here span several GEMM and attention tiles with ragged tails."""
+import copy
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import ref
+from selective_recompute_prefill_amd import inputs
+from selective_recompute_prefill_amd import srp as S
+from selective_recompute_prefill_amd.device import LayerCall, download, ints, upload
+
+from parity import assert_close, check_selection, csr_ok, oracle_caches, oracle_layer
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel_kw=None,
+             oracle_kw=None, check_group_s0=True, what=""):
+    """Run one layer on both sides and check every output."""
+    w = w or inputs.generate(spec)
+    lay = lay or w.layout
+    if kc_st is None:
+        kc_st, vc_st = oracle_caches(w)
+    hidden_st = w.hidden if hidden_st is None else hidden_st
+    wq_st = w.layers[0].w_qkv
+    sel_kw = dict(sel_kw or {})
+    sel_kw.setdefault("window", spec.window)
+    sel_kw.setdefault("tau", spec.tau)
+    ratio = sel_kw.pop("ratio", spec.ratio)
+    okw = dict(ratio=ratio, window=sel_kw["window"], tau=sel_kw["tau"])
+    okw.update(oracle_kw or {})
+    want = oracle_layer(spec, lay, hidden_st, wq_st, kc_st, vc_st, **okw)
+
+    _say(f"[gpu] {what or spec.name}: T={lay.total_rows} ratio={ratio} {sel_kw}")
+    call = LayerCall(spec, lay)
+    hid = upload(hidden_st, spec.dtype)
+    wq = upload(wq_st, spec.dtype)
+    kc = upload(kc_st, spec.dtype)
+    vc = upload(vc_st, spec.dtype)
+    call.fuse(call.select(ratio, **sel_kw), hid, wq, kc, vc)
+    torch.cuda.synchronize()
+    got = call.results()
+    k_out, v_out = download(kc), download(vc)
+
+    req, _ = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
+    csr_ok(got["sel_idx"], got["sel_offsets"], lay.req_offsets)
+    if sel_kw.get("window", 0) > 0 and check_group_s0:
+        # compare the top-k sets, then the grouping of the GPU's own top-k set
+        call0 = LayerCall(spec, lay)
+        kc0, vc0 = upload(kc_st, spec.dtype), upload(vc_st, spec.dtype)
+        kw0 = dict(sel_kw, window=0, tau=0)
+        call0.fuse(call0.select(ratio, **kw0), hid, wq, kc0, vc0)
+        torch.cuda.synchronize()
+        s0_gpu = call0.results()["sel_idx"]
+        ref0 = oracle_layer(spec, lay, hidden_st, wq_st, kc_st, vc_st, **dict(okw, window=0, tau=0))
+        check_selection(s0_gpu, ref0, req, what + " top-k")
+        _, src = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
+        expect = []
+        for r in range(lay.n_req):
+            rows = np.arange(lay.req_offsets[r], lay.req_offsets[r + 1])
+            seq = rows[src[rows] >= 0]
+            slot = {int(j): i for i, j in enumerate(seq)}
+            mine = [slot[int(j)] for j in s0_gpu if int(j) in slot]
+            kept = ref.group_windows(mine, len(seq), sel_kw["window"], sel_kw["tau"])
+            expect.append(np.union1d(seq[np.asarray(kept, np.int64)] if kept else [], rows[src[rows] < 0]))
+        expect = np.concatenate(expect).astype(np.int64) if expect else np.zeros(0, np.int64)
+        assert np.array_equal(got["sel_idx"], expect), what + ": grouping of the GPU top-k differs"
+    else:
+        check_selection(got["sel_idx"], want, req, what)
+    if not np.array_equal(got["sel_idx"], want["sel_idx"]):
+        want = oracle_layer(spec, lay, hidden_st, wq_st, kc_st, vc_st, sel_override=got["sel_idx"], **okw)
+    assert np.array_equal(got["sel_offsets"], want["sel_offsets"])
+
+    dt = spec.dtype
+    assert_close(ref.widen(k_out, dt), want["k_cache"], dt, what + " K cache")
+    assert_close(ref.widen(v_out, dt), want["v_cache"], dt, what + " V cache")
+    assert_close(ref.widen(got["attn_out"], dt), want["attn_out"], dt, what + " attention")
+    # deviations of scored rows (fp32 on the GPU)
+    scored = np.isfinite(want["dev"])
+    assert np.array_equal(np.isfinite(got["dev"][:lay.total_rows]), scored)
+    if scored.any():
+        rel = np.abs(got["dev"][scored] - want["dev"][scored]) / np.maximum(want["dev"][scored], 1e-30)
+        assert rel.max() < 1e-4, f"{what}: deviation rel err {rel.max():.2e}"
+    return got, want, call
+
+
+# --------------------------------------------------------------------------- #
+# small shapes (several tiles, ragged tails, two requests)
+# --------------------------------------------------------------------------- #
+
+def test_config0_tiny_fp32():
+    run_case(inputs.CONFIGS[0], what="config0")
+
+
+def test_mini_bf16_two_requests():
+    run_case(inputs.small_spec(), what="mini")
+
+
+def test_mini_fp32_d128():
+    run_case(inputs.small_spec(dtype="f32"), what="mini-f32")
+
+
+def test_mini_bf16_head_dim_64():
+    run_case(inputs.small_spec(head_dim=64, n_heads=8, n_kv_heads=4), what="mini-d64")
+
+
+def test_mini_bf16_gqa5():
+    run_case(inputs.small_spec(hidden=640, n_heads=5, n_kv_heads=1), what="mini-gqa5")
+
+
+def test_mini_grouping():
+    run_case(inputs.small_spec(window=8, tau=4, ratio=0.3), what="mini-grouping")
+
+
+def test_mini_v_only_deviation():
+    run_case(inputs.small_spec(), sel_kw=dict(dev_mode=S.SRP_DEV_V), oracle_kw=dict(dev_mode="v"),
+             what="mini-v")
+
+
+@pytest.mark.parametrize("ratio", [0.0, 1.0, 0.5])
+def test_mini_ratio_edges(ratio):
+    run_case(inputs.small_spec(), sel_kw=dict(ratio=ratio), what=f"mini-r{ratio}")
+
+
+def test_ratio_zero_without_query_tail_leaves_rerotated_cache():
+    spec = inputs.small_spec(n_query=0)
+    got, want, _ = run_case(spec, sel_kw=dict(ratio=0.0), what="r0-noquery")
+    assert len(got["sel_idx"]) == 0
+
+
+def test_exact_ties_take_lowest_rows():
+    # zero hidden rows and zero caches: every deviation is exactly 0
+    spec = inputs.small_spec(ratio=0.25)
+    w = inputs.generate(spec)
+    z = np.zeros_like(w.hidden)
+    kc = np.zeros((w.layout.total_rows, spec.n_kv_heads, spec.head_dim), np.uint16)
+    got, want, _ = run_case(spec, w=w, hidden_st=z, kc_st=kc, vc_st=kc.copy(), what="ties")
+    assert np.array_equal(got["sel_idx"], want["sel_idx"])
+
+
+def test_missing_chunk_and_negative_delta():
+    spec = inputs.small_spec()
+    w = inputs.generate(spec)
+    lay = copy.deepcopy(w.layout)
+    # chunk 1 of request 0 lost its cache (fresh rows in the middle); chunk 2 of
+    # request 1 was encoded far beyond its global position (negative delta)
+    lay.chunk_src_pos = lay.chunk_src_pos.copy()
+    lay.chunk_src_pos[1] = -1
+    lay.chunk_src_pos[6] = 1500
+    lay.max_position = 1500 + 300
+    w2 = copy.copy(w)
+    w2.layout = lay
+    w2.cache_row_of = w.cache_row_of.copy()
+    src = inputs.encode_positions(lay)
+    w2.cache_row_of[src < 0] = -1
+    kc, vc = oracle_caches(w2)
+    run_case(spec, w=w2, lay=lay, kc_st=kc, vc_st=vc, what="missing+negdelta")
+
+
+def test_candidate_list_topk_and_given():
+    spec = inputs.small_spec()
+    w = inputs.generate(spec)
+    kc, vc = oracle_caches(w)
+    lay = w.layout
+    rng = np.random.default_rng(5)
+    cand, off = [], [0]
+    for r in range(lay.n_req):
+        rows = np.arange(lay.req_offsets[r], lay.req_offsets[r + 1])
+        pick = np.sort(rng.choice(rows, len(rows) // 3, replace=False))
+        cand.append(pick)
+        off.append(off[-1] + len(pick))
+    cand = np.concatenate(cand)
+    for mode, omode in [(S.SRP_SEL_TOPK, "topk"), (S.SRP_SEL_GIVEN, "given")]:
+        c_t, o_t = ints(cand), ints(off)
+        run_case(spec, w=w, kc_st=kc, vc_st=vc,
+                 sel_kw=dict(ratio=0.15, mode=mode, cand=c_t, cand_offsets=o_t),
+                 oracle_kw=dict(mode=omode, cand=cand), what=f"cand-{omode}")
+
+
+def test_deterministic_bitwise():
+    spec = inputs.small_spec(window=8, tau=4)
+    w = inputs.generate(spec)
+    kc, vc = oracle_caches(w)
+    outs = []
+    for _ in range(2):
+        call = LayerCall(spec, w.layout)
+        k, v = upload(kc, spec.dtype), upload(vc, spec.dtype)
+        call.fuse(call.select(spec.ratio, window=8, tau=4), upload(w.hidden, spec.dtype),
+                  upload(w.layers[0].w_qkv, spec.dtype), k, v)
+        torch.cuda.synchronize()
+        res = call.results()
+        outs.append((res["sel_idx"], res["attn_out"], download(k), download(v), res["dev"]))
+    for a, b in zip(*outs):
+        assert np.array_equal(a, b, equal_nan=True) if a.dtype.kind == "f" else np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------- #
+# the other entry points
+# --------------------------------------------------------------------------- #
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_encode_kv(dtype):
+    spec = inputs.small_spec(dtype=dtype)
+    w = inputs.generate(spec)
+    lay = w.layout
+    src = inputs.encode_positions(lay)
+    rows = np.nonzero(src >= 0)[0]
+    wq = ref.widen(w.layers[0].w_qkv, dtype)
+    x = ref.widen(w.hidden, dtype)[rows]
+    k, v = ref.encode_kv(x, wq, src[rows], spec.n_heads, spec.n_kv_heads, spec.head_dim, spec.rope_base)
+    dims = S.make_dims(spec.hidden, spec.n_heads, spec.n_kv_heads, spec.head_dim, spec.rope_base,
+                       S.SRP_BF16 if dtype == "bf16" else S.SRP_F32)
+    _say(f"[gpu] encode_kv {dtype} rows={len(rows)}")
+    xd = upload(w.hidden[rows], dtype)
+    kd = torch.empty((len(rows), spec.n_kv_heads, spec.head_dim), dtype=xd.dtype, device="cuda")
+    vd = torch.empty_like(kd)
+    S.srp_encode_kv(dims, len(rows), lay.max_position, xd, upload(w.layers[0].w_qkv, dtype),
+                    ints(src[rows]), kd, vd)
+    torch.cuda.synchronize()
+    assert_close(ref.widen(download(kd), dtype), k, dtype, "encode K")
+    assert_close(ref.widen(download(vd), dtype), v, dtype, "encode V")
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_rerotate_kv(dtype):
+    spec = inputs.small_spec(dtype=dtype)
+    w = inputs.generate(spec)
+    kc, _ = oracle_caches(w)
+    lay = w.layout
+    _, src = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
+    want = ref.rerotate(ref.widen(kc, dtype), lay.positions.astype(np.int64), src, spec.rope_base)
+    call = LayerCall(spec, lay)
+    _say(f"[gpu] rerotate_kv {dtype}")
+    kd = upload(kc, dtype)
+    S.srp_rerotate_kv(call.dims, call.batch, kd)
+    torch.cuda.synchronize()
+    got = ref.widen(download(kd), dtype)
+    assert_close(got, want, dtype, "rerotate")
+    fresh = src < 0
+    assert np.array_equal(download(kd)[fresh], kc[fresh])
+
+
+def test_residual_rmsnorm():
+    spec = inputs.small_spec(hidden=1024, n_heads=8, n_kv_heads=2, head_dim=128)
+    w = inputs.generate(spec)
+    lay = w.layout
+    T = lay.total_rows
+    rng = np.random.default_rng(9)
+    sel = np.sort(rng.choice(T, 300, replace=False)).astype(np.int32)
+    attn = inputs.store(rng.standard_normal((300, spec.hidden)), "bf16")
+    x = ref.widen(w.hidden, "bf16")
+    want = x.copy()
+    want[sel] = ref.residual_rmsnorm(x[sel], ref.widen(attn, "bf16"))
+    call = LayerCall(spec, lay)
+    _say("[gpu] residual_rmsnorm")
+    hd = upload(w.hidden, "bf16")
+    S.srp_residual_rmsnorm(call.dims, hd, upload(attn, "bf16"), ints(sel), ints([0, 300]), 1, T)
+    torch.cuda.synchronize()
+    assert_close(ref.widen(download(hd), "bf16"), want, "bf16", "rmsnorm")
