@@ -1,0 +1,303 @@
+"""Benchmark of the selective-recompute prefill layer on one MI355X.
+
+One step = one srp_fuse_layer call over the whole batch (re-rotation, candidate
+K/V projection with deviation, top-k and grouping, scatter, Q projection of the
+selection, gathered-query attention); the 4-layer workload's step is its whole
+stack (4 layers and the 3 residual RMSNorm steps between them). Inputs are
+resident in HBM before timing starts; every timed step gets its own pristine copy
+of the chunk caches (the layer rewrites them in place), so nothing is restored
+inside the timed region. Stage times come from hipEvents the library records on
+its stream between launches.
+
+Prints one JSON line. Default workload: the 16K-token long-RAG layer (hidden 5120,
+40/8 heads, d 128, 32-row prefix + 32 x 512 chunks + 96 query rows, ratio 0.20,
+window-8 grouping with tau 4), the configuration the headline metric is quoted on
+(tokens fused per second per layer at 20% recompute, ms per layer at 16K).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3    # MI355X fp32 vector
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+
+WORKLOAD_NAMES = {
+    1: "llama3-8b-layer: hidden 4096, 32/8 heads, d 128, 6 x 512 chunks + 64 query rows = 3136 rows, ratio 0.15",
+    2: "14b-16k-grouped: hidden 5120, 40/8 heads, d 128, 32-row prefix + 32 x 512 chunks + 96 query rows = 16512 rows, ratio 0.20, window 8, tau 4",
+    3: "70b-4layer-gradual: hidden 8192, 64/8 heads, d 128, 8 x 512 chunks + 64 query rows = 4160 rows, 4 layers at ratios 0.30/0.15/0.15/0.15 with residual RMSNorm",
+    4: "8b-batch16x8k: 16 requests x 8192 rows (16 x 512 chunks, permuted per request), hidden 4096, 32/8 heads, d 128",
+}
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=20)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4])
+    p.add_argument("--ratio", type=float, default=None, help="override the workload's ratio")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--cpu-sample-chunks", type=int, default=16,
+                   help="chunks of the request the oracle is timed on")
+    return p.parse_args()
+
+
+def algorithmic_work(spec, lay, sel, ratio_rows):
+    """Per-stage algorithmic flops and bytes of one layer call (see the design notes):
+    bytes count what the method must move once, flops count the products it must
+    form; both use the actual selection."""
+    import numpy as np
+    e = 2 if spec.dtype == "bf16" else 4
+    H, kvd, qd = spec.hidden, spec.kvdim, spec.qdim
+    T = lay.total_rows
+    n_ctx = ratio_rows["n_ctx"]
+    n_rec = ratio_rows["n_rec"]  # rows projected to K/V (candidates + fresh)
+    n_sel = len(sel)
+    req_start = np.zeros(T, np.int64)
+    for r in range(lay.n_req):
+        req_start[lay.req_offsets[r]:lay.req_offsets[r + 1]] = lay.req_offsets[r]
+    pairs = int((sel - req_start[sel] + 1).sum()) if n_sel else 0
+    return {
+        "prepare": {"bytes": T * 4 * 3},
+        "kv_proj": {"flops": 2.0 * n_rec * H * 2 * kvd,
+                    # A rows, W_k/W_v, cached K read + K~ write, cached V read, fresh K/V write
+                    "bytes": e * (n_rec * H + 2 * kvd * H + 2 * n_ctx * kvd + n_ctx * kvd + 2 * n_rec * kvd)},
+        "select": {"bytes": n_rec * 2 * spec.n_kv_heads * 4 + n_rec * 4 * 4},
+        "scatter": {"bytes": e * 2 * n_sel * 2 * kvd},
+        "q_proj": {"flops": 2.0 * n_sel * H * qd, "bytes": e * (n_sel * H + qd * H + n_sel * qd)},
+        "attention": {"flops": 4.0 * spec.n_heads * spec.head_dim * pairs,
+                      "bytes": e * (n_sel * qd * 2 + 2 * n_ctx * kvd), "pairs": pairs},
+    }
+
+
+def cpu_baseline(spec, n_chunks_sample):
+    """Time the fp64 oracle on a bounded sample of the workload: the first
+    n_chunks_sample chunks of one request (with its prefix and query tail)."""
+    import numpy as np
+    from oracle import ref
+    from selective_recompute_prefill_amd import inputs
+    try:
+        from threadpoolctl import threadpool_info
+        info = threadpool_info()
+        threads = max((i.get("num_threads", 1) for i in info), default=1)
+        blas = ",".join(sorted({i.get("internal_api", "?") for i in info}))
+    except Exception:  # pragma: no cover
+        threads, blas = os.cpu_count(), "unknown"
+    n_ch = min(n_chunks_sample, len(spec.chunk_lens))
+    sub = spec.replace(chunk_lens=spec.chunk_lens[:n_ch], n_req=1, shared_chunks=False,
+                       n_layers=1, ratios=())
+    w = inputs.generate(sub)
+    lay = w.layout
+    src = inputs.encode_positions(lay)
+    cr = src >= 0
+    wq = ref.widen(w.layers[0].w_qkv, sub.dtype)
+    xe = w.encode_input(0)
+    kc = np.zeros((lay.total_rows, sub.n_kv_heads, sub.head_dim))
+    vc = np.zeros_like(kc)
+    kc[cr], vc[cr] = ref.encode_kv(xe[cr], wq, src[cr], sub.n_heads, sub.n_kv_heads,
+                                   sub.head_dim, sub.rope_base)
+    kc = ref.widen(inputs.store(kc, sub.dtype), sub.dtype)
+    vc = ref.widen(inputs.store(vc, sub.dtype), sub.dtype)
+    x = ref.widen(w.hidden, sub.dtype)
+    ratio = sub.layer_ratios()[0]
+    t0 = time.perf_counter()
+    ref.fuse_layer(hidden=x, w_qkv=wq, k_cache=kc, v_cache=vc, req_offsets=lay.req_offsets,
+                   chunk_offsets=lay.chunk_offsets, chunk_src_pos=lay.chunk_src_pos,
+                   positions=lay.positions, n_heads=sub.n_heads, n_kv=sub.n_kv_heads,
+                   head_dim=sub.head_dim, rope_base=sub.rope_base, ratio=ratio,
+                   window=sub.window, tau=sub.tau)
+    dt = time.perf_counter() - t0
+    n_ctx = int(cr.sum())
+    return {"value": n_ctx / dt, "unit": "context tokens/s per layer", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"one layer of the same shape on the first {n_ch} of {len(spec.chunk_lens)} chunks "
+                      f"({lay.total_rows} rows, {n_ctx} cached) timed once in fp64 numpy ({blas} BLAS); "
+                      f"attention cost per token grows with length, so this overstates the oracle's "
+                      f"rate at full length",
+            "seconds": dt}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
+              f"multi-GPU path", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    from selective_recompute_prefill_amd import inputs
+    from selective_recompute_prefill_amd import srp as S
+    from selective_recompute_prefill_amd.device import LayerCall, download, encode_cache, upload
+
+    S.lib()  # fail loudly if the library is not built
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    dev = "cuda"
+    spec = inputs.CONFIGS[args.workload]
+    if args.ratio is not None:
+        spec = spec.replace(ratio=args.ratio, ratios=())
+    print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)
+    w = inputs.generate(spec)
+    lay = w.layout
+    src = inputs.encode_positions(lay)
+    T = lay.total_rows
+    n_ctx = int((src >= 0).sum())
+    nl = spec.n_layers
+    ratios = spec.layer_ratios()
+
+    call = LayerCall(spec, lay, dev)
+    hidden0 = upload(w.hidden, spec.dtype, dev)
+    wqs = [upload(w.layers[l].w_qkv, spec.dtype, dev) for l in range(nl)]
+    # chunk caches encoded on the GPU (x + eps n at the encode positions)
+    print("[bench] encoding chunk caches", file=sys.stderr, flush=True)
+    caches = []
+    x_full = None  # float64 full-prefill hidden of the layer being encoded
+    x_dev = hidden0.clone()
+    for l in range(nl):
+        xe = upload(inputs.store(w.encode_input(l, x_full), spec.dtype), spec.dtype, dev)
+        caches.append(encode_cache(spec, lay, xe, wqs[l], src, dev))
+        del xe
+        if l + 1 < nl:
+            # the next layer's full-prefill hidden: this layer at ratio 1, then the
+            # residual RMSNorm, all in libsrp
+            kc, vc = caches[l][0].clone(), caches[l][1].clone()
+            call.fuse(call.select(1.0), x_dev, wqs[l], kc, vc, dev_out=False)
+            S.srp_residual_rmsnorm(call.dims, x_dev, call.attn_out, call.sel_idx, call.sel_offsets,
+                                   lay.n_req, T)
+            torch.cuda.synchronize()
+            x_full = _to_f64(download(x_dev), spec.dtype)
+            del kc, vc
+    del x_dev
+    torch.cuda.synchronize()
+
+    n_copies = args.steps + args.warmup
+    sel_kw = dict(window=spec.window, tau=spec.tau)
+    # pristine cache copies, one per step and layer
+    pristine = [[(c[0].clone(), c[1].clone()) for c in caches] for _ in range(n_copies)]
+    hiddens = [hidden0.clone() for _ in range(n_copies)] if nl > 1 else [hidden0]
+    del caches
+    torch.cuda.synchronize()
+
+    # buffers for chained layers (candidates = previous selection)
+    prev_idx = torch.empty_like(call.sel_idx)
+    prev_off = torch.empty_like(call.sel_offsets)
+
+    def step(i):
+        h = hiddens[i % len(hiddens)]
+        for l in range(nl):
+            kc, vc = pristine[i][l]
+            if l == 0:
+                sel = call.select(ratios[0], **sel_kw)
+            else:
+                prev_idx.copy_(call.sel_idx)
+                prev_off.copy_(call.sel_offsets)
+                sel = call.select(ratios[l], cand=prev_idx, cand_offsets=prev_off)
+            call.fuse(sel, h, wqs[l], kc, vc, dev_out=False)
+            if l + 1 < nl:
+                S.srp_residual_rmsnorm(call.dims, h, call.attn_out, call.sel_idx, call.sel_offsets,
+                                       lay.n_req, T)
+
+    for l in range(nl):
+        call.ensure_workspace(call.select(ratios[l], **(sel_kw if l == 0 else {})))
+    print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
+    for i in range(args.warmup):
+        step(args.steps + i)
+    torch.cuda.synchronize()
+
+    print(f"[bench] timing {args.steps} steps", file=sys.stderr, flush=True)
+    S.srp_profile_begin(args.steps * nl)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(i)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    stage_ms = S.srp_profile_end(args.steps * nl)
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    ms_per_layer = ms_per_step / nl
+    res = call.results()
+    sel = res["sel_idx"]
+
+    names = [S.srp_profile_stage_name(i) for i in range(S.SRP_N_STAGES)]
+    st = np.asarray(stage_ms, np.float64).reshape(args.steps, nl, S.SRP_N_STAGES)
+    # per-stage work of the first layer (the layer the metric is quoted on)
+    n_rec = T  # single-shot layer: every row is projected to K/V
+    work = algorithmic_work(spec, lay, sel if nl == 1 else _first_layer_sel(call, spec, lay, hidden0, wqs, pristine, sel_kw, ratios), {"n_ctx": n_ctx, "n_rec": n_rec})
+    stages = {}
+    peak_fl = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
+    for i, nm in enumerate(names):
+        ms = float(st[:, 0, i].mean())
+        wk = work[nm]
+        ent = {"ms": round(ms, 4)}
+        if "flops" in wk:
+            tf = wk["flops"] / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+            ent.update(flops=wk["flops"], tflops=round(tf, 1), frac_mfma=round(tf / peak_fl, 4))
+        if "bytes" in wk:
+            gbs = wk["bytes"] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+            ent.update(bytes=wk["bytes"], gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        stages[nm] = ent
+    # dominant kernel: the longest MFMA stage
+    dom = max(("kv_proj", "q_proj", "attention"), key=lambda n: stages[n]["ms"])
+    roof = {"kernel": {"kv_proj": "gemm_bf16_kernel<EPI_KV>", "q_proj": "gemm_bf16_kernel<EPI_Q>",
+                       "attention": "attn_bf16_kernel<128>"}[dom],
+            "bound": "mfma", "achieved": stages[dom]["tflops"], "peak": peak_fl, "unit": "TFLOP/s",
+            "frac": stages[dom]["frac_mfma"], "traffic": None,
+            "flops_per_launch": work[dom]["flops"], "avg_launch_ms": stages[dom]["ms"]}
+
+    value = n_ctx / (ms_per_layer * 1e-3)
+    out = {
+        "metric": "context tokens fused/s per layer at 20% recompute; ms/layer at 16K; % roofline",
+        "value": round(value, 1),
+        "unit": "context tokens/s per layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if spec.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": WORKLOAD_NAMES[args.workload] + (f" (ratio {args.ratio})" if args.ratio else ""),
+                   "global_batch": lay.n_req, "seq_len": int(lay.req_offsets[1]),
+                   "parallelism": "none (1 GPU)"},
+        "ms_per_layer": round(ms_per_layer, 4),
+        "n_selected": int(len(sel)),
+        "n_ctx": n_ctx,
+        "roofline": roof,
+        "stages": stages,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(spec, args.cpu_sample_chunks)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+def _to_f64(a, dtype):
+    import numpy as np
+    if dtype == "f32":
+        return a.astype(np.float64)
+    return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _first_layer_sel(call, spec, lay, hidden0, wqs, pristine, sel_kw, ratios):
+    """Selection of the stack's first layer (re-run once on a spare cache copy)."""
+    import torch
+    kc, vc = pristine[0][0][0].clone(), pristine[0][0][1].clone()
+    call.fuse(call.select(ratios[0], **sel_kw), hidden0, wqs[0], kc, vc, dev_out=False)
+    torch.cuda.synchronize()
+    return call.results()["sel_idx"]
+
+
+if __name__ == "__main__":
+    main()

@@ -173,6 +173,19 @@ int srp_residual_rmsnorm(const srp_dims *dims, void *hidden, const void *attn_ou
  * them to the host and synchronises). SRP_OK or SRP_E_BATCH with a message. */
 int srp_validate_batch(const srp_batch *batch, srp_stream_t stream);
 
+/* Stage timing (the pages report per-stage latency breakdowns of this path, e.g.
+ * the CacheClip paper's Table 6). After srp_profile_begin(max_calls), each of the
+ * next max_calls srp_fuse_layer calls records hipEvents on its stream between its
+ * SRP_N_STAGES launch stages (events only, the kernels are unchanged).
+ * srp_profile_end waits for those events and writes ms[c * SRP_N_STAGES + i], the
+ * GPU time of stage i of call c, for up to max_calls calls (*n_calls = number
+ * written). Stage names: srp_profile_stage_name(i). Process-wide; not meant for
+ * concurrent callers. */
+#define SRP_N_STAGES 6
+int srp_profile_begin(int32_t max_calls);
+int srp_profile_end(float *ms, int32_t max_calls, int32_t *n_calls);
+const char *srp_profile_stage_name(int32_t i);
+
 /* Message for the last failing call on this thread ("" if none). */
 const char *srp_last_error(void);
 

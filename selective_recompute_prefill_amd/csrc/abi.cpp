@@ -84,6 +84,33 @@ int get_table(int d, double base, int max_pos, RopeTable *out) {
 }
 
 // ------------------------------------------------------------------------- //
+// stage timing: hipEvents recorded on the caller's stream between the launch
+// stages of srp_fuse_layer, one row of events per call, up to a capacity
+// ------------------------------------------------------------------------- //
+constexpr int kStages = 6;
+const char *kStageNames[kStages] = {"prepare", "kv_proj", "select", "scatter", "q_proj", "attention"};
+struct Profile {
+  bool on = false;
+  int cap = 0, used = 0;
+  std::vector<hipEvent_t> ev;  // cap * (kStages + 1)
+};
+std::mutex g_pmu;
+Profile g_prof;
+
+// Records event `i` of the current call if profiling is on.
+struct StageMarks {
+  hipStream_t s;
+  hipEvent_t *row = nullptr;
+  explicit StageMarks(hipStream_t st) : s(st) {
+    std::lock_guard<std::mutex> lk(g_pmu);
+    if (g_prof.on && g_prof.used < g_prof.cap) row = &g_prof.ev[(size_t)g_prof.used++ * (kStages + 1)];
+  }
+  void mark(int i) {
+    if (row) (void)hipEventRecord(row[i], s);
+  }
+};
+
+// ------------------------------------------------------------------------- //
 // argument checks
 // ------------------------------------------------------------------------- //
 int check_dims(const srp_dims *d) {
@@ -190,6 +217,8 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   sa.dev_out = dev_out;
 
   // 1. row metadata; candidate list and the recomputed rows R when given
+  StageMarks marks(s);
+  marks.mark(0);
   SRP_HIP(launch_prepare(sa, w, s));
   // 2. positional recovery of cached rows outside R (inside R the projection
   //    epilogue rotates them next to the deviation)
@@ -218,12 +247,16 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   g.v_cache = v_cache;
   g.fresh = w.fresh_kv;
   g.dev_part = w.dev_part;
+  marks.mark(1);
   SRP_HIP(launch_gemm(g, s));
+  marks.mark(2);
   // 4. top-k / grouping per request, CSR offsets, attention tiles
   SRP_HIP(launch_select(sa, w, s));
   SRP_HIP(launch_finalize(sa, w, sel_offsets, s));
+  marks.mark(3);
   // 5. sel_idx and the scatter of fresh K/V into the cache
   SRP_HIP(launch_compact_scatter(sa, w, d.dtype, kvd, sel_idx, sel_offsets, k_cache, v_cache, s));
+  marks.mark(4);
   // 6. Q projection of the selected rows
   GemmArgs gq = g;
   gq.a_rows = sel_idx;
@@ -233,6 +266,7 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   gq.mode = EPI_Q;
   gq.q_out = w.q;
   SRP_HIP(launch_gemm(gq, s));
+  marks.mark(5);
   // 7. attention of the selected rows over the fused cache
   AttnArgs aa{};
   aa.dtype = d.dtype;
@@ -249,8 +283,43 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   aa.v_cache = v_cache;
   aa.out = attn_out;
   if (T > 0) SRP_HIP(launch_attention(aa, s));
+  marks.mark(6);
   return SRP_OK;
 }
+
+int srp_profile_begin(int32_t max_calls) {
+  g_err.clear();
+  if (max_calls < 1) return fail(SRP_E_INVALID, "max_calls must be >= 1");
+  std::lock_guard<std::mutex> lk(g_pmu);
+  const size_t need = (size_t)max_calls * (kStages + 1);
+  while (g_prof.ev.size() < need) {
+    hipEvent_t e;
+    SRP_HIP(hipEventCreate(&e));
+    g_prof.ev.push_back(e);
+  }
+  g_prof.cap = max_calls;
+  g_prof.used = 0;
+  g_prof.on = true;
+  return SRP_OK;
+}
+
+int srp_profile_end(float *ms, int32_t max_calls, int32_t *n_calls) {
+  g_err.clear();
+  std::lock_guard<std::mutex> lk(g_pmu);
+  if (!g_prof.on) return fail(SRP_E_INVALID, "profiling was not started");
+  g_prof.on = false;
+  const int n = g_prof.used < max_calls ? g_prof.used : max_calls;
+  if (n_calls) *n_calls = n;
+  for (int c = 0; c < n; ++c) {
+    hipEvent_t *row = &g_prof.ev[(size_t)c * (kStages + 1)];
+    SRP_HIP(hipEventSynchronize(row[kStages]));
+    for (int i = 0; i < kStages; ++i)
+      SRP_HIP(hipEventElapsedTime(&ms[(size_t)c * kStages + i], row[i], row[i + 1]));
+  }
+  return SRP_OK;
+}
+
+const char *srp_profile_stage_name(int32_t i) { return (i >= 0 && i < kStages) ? kStageNames[i] : ""; }
 
 int srp_encode_kv(const srp_dims *dims, int32_t n_rows, int32_t max_position, const void *hidden,
                   const void *w_qkv, const int32_t *positions, void *k_out, void *v_out,

@@ -18,7 +18,7 @@ constexpr int kBN = 128;
 // ------------------------------------------------------------------------- //
 // epilogue
 // ------------------------------------------------------------------------- //
-template <typename T, int BM>
+template <typename T, int BM, int MODE>
 __device__ __forceinline__ void epilogue(const float *Cs, int ldc, int m0, int n0, int M,
                                          const GemmArgs &g) {
   const int d = g.d, half = d >> 1;
@@ -38,8 +38,8 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, int m0, int n
     float part_sum = 0.f;
     int slot = -1;
     if (valid) {
-      const int row = (g.mode != EPI_ENC && g.a_rows) ? g.a_rows[m] : m;
-      if (g.mode == EPI_Q) {
+      const int row = (MODE != EPI_ENC && g.a_rows) ? g.a_rows[m] : m;
+      if (MODE == EPI_Q) {
         const int h = nu / d;
         rope4(a, b, g.rope, g.positions[row], i0);
         T *q = (T *)g.q_out + (size_t)m * g.nh * d + h * d;
@@ -49,7 +49,7 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, int m0, int n
         const int part = nu >= kvd;
         const int gh = (nu - part * kvd) / d;
         if (part == 0) rope4(a, b, g.rope, g.positions[row], i0);
-        if (g.mode == EPI_ENC) {
+        if (MODE == EPI_ENC) {
           T *o = (T *)(part ? g.v_cache : g.k_cache) + (size_t)m * kvd + gh * d;
           st4(o + i0, a);
           st4(o + half + i0, b);
@@ -80,7 +80,7 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, int m0, int n
         }
       }
     }
-    if (g.mode == EPI_KV) {
+    if (MODE == EPI_KV) {
       // fixed-order reduction over the head's tpu lanes (aligned groups)
       for (int o = 1; o < tpu; o <<= 1) part_sum += __shfl_xor(part_sum, o, 64);
       if (valid && t == 0) g.dev_part[(size_t)m * 2 * g.nkv + slot] = part_sum;
@@ -114,6 +114,7 @@ constexpr int kBM16 = 128, kBK16 = 64, kLDA16 = kBK16 + 8;  // 144-byte LDS rows
 constexpr int kStage16 = kBM16 * kLDA16;                    // elements per operand stage
 constexpr int kLDC = kBN + 4;
 
+template <int MODE>
 __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
   __shared__ __align__(16) uint16_t smem[4 * kStage16];  // A0 A1 B0 B1 (73,728 B)
   uint16_t *As = smem, *Bs = smem + 2 * kStage16;
@@ -211,7 +212,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
           Cs[row * kLDC + col] = acc[i][j][e];
         }
     __syncthreads();
-    epilogue<uint16_t, kBM16>(Cs, kLDC, m0, n0, M, g);
+    epilogue<uint16_t, kBM16, MODE>(Cs, kLDC, m0, n0, M, g);
     __syncthreads();
   }
 }
@@ -221,6 +222,7 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
 // ------------------------------------------------------------------------- //
 constexpr int kBM32 = 64, kBK32 = 16;
 
+template <int MODE>
 __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs g) {
   __shared__ __align__(16) float smem32[kBM32 * kLDC];  // 33,792 B; also holds A/B tiles
   float *As = smem32;                     // [BK][BM+4]
@@ -293,7 +295,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) Cs[(ty * 4 + i) * kLDC + tx + 16 * j] = acc[i][j];
     __syncthreads();
-    epilogue<float, kBM32>(Cs, kLDC, m0, n0, M, g);
+    epilogue<float, kBM32, MODE>(Cs, kLDC, m0, n0, M, g);
     __syncthreads();
   }
 }
@@ -305,10 +307,18 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
   // resident work-groups: 256 CUs x 2, rounded to a multiple of the 8 XCDs
   long grid = tiles < 512 ? tiles : 512;
   grid = (grid + 7) / 8 * 8;
-  if (g.dtype == SRP_BF16)
-    hipLaunchKernelGGL(gemm_bf16_kernel, dim3((unsigned)grid), dim3(256), 0, s, g);
-  else
-    hipLaunchKernelGGL(gemm_f32_kernel, dim3((unsigned)grid), dim3(256), 0, s, g);
+  const dim3 gr((unsigned)grid), bl(256);
+#define SRP_GEMM_LAUNCH(M)                                               \
+  if (g.dtype == SRP_BF16)                                               \
+    hipLaunchKernelGGL(gemm_bf16_kernel<M>, gr, bl, 0, s, g);            \
+  else                                                                   \
+    hipLaunchKernelGGL(gemm_f32_kernel<M>, gr, bl, 0, s, g);
+  switch (g.mode) {
+    case EPI_KV: SRP_GEMM_LAUNCH(EPI_KV); break;
+    case EPI_Q: SRP_GEMM_LAUNCH(EPI_Q); break;
+    default: SRP_GEMM_LAUNCH(EPI_ENC); break;
+  }
+#undef SRP_GEMM_LAUNCH
   return hipGetLastError();
 }
 

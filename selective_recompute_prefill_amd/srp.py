@@ -19,7 +19,9 @@ SRP_SEL_TOPK, SRP_SEL_GIVEN = 0, 1
 SRP_DEV_KV, SRP_DEV_V = 0, 1
 
 EXPORTS = ("srp_workspace_size", "srp_fuse_layer", "srp_encode_kv", "srp_rerotate_kv",
-           "srp_residual_rmsnorm", "srp_validate_batch", "srp_last_error", "srp_version")
+           "srp_residual_rmsnorm", "srp_validate_batch", "srp_profile_begin", "srp_profile_end",
+           "srp_profile_stage_name", "srp_last_error", "srp_version")
+SRP_N_STAGES = 6
 
 
 class SrpError(RuntimeError):
@@ -68,8 +70,13 @@ def lib() -> ctypes.CDLL:
         L.srp_rerotate_kv.argtypes = [P(Dims), P(Batch), vp, vp]
         L.srp_residual_rmsnorm.argtypes = [P(Dims), vp, vp, vp, vp, i32, i32, ctypes.c_float, vp]
         L.srp_validate_batch.argtypes = [P(Batch), vp]
+        L.srp_profile_begin.argtypes = [i32]
+        L.srp_profile_end.argtypes = [P(ctypes.c_float), i32, P(i32)]
+        L.srp_profile_stage_name.argtypes = [i32]
+        L.srp_profile_stage_name.restype = ctypes.c_char_p
         for f in ("srp_workspace_size", "srp_fuse_layer", "srp_encode_kv", "srp_rerotate_kv",
-                  "srp_residual_rmsnorm", "srp_validate_batch"):
+                  "srp_residual_rmsnorm", "srp_validate_batch", "srp_profile_begin",
+                  "srp_profile_end"):
             getattr(L, f).restype = ctypes.c_int
         L.srp_last_error.restype = ctypes.c_char_p
         L.srp_version.restype = ctypes.c_char_p
@@ -155,6 +162,22 @@ def srp_residual_rmsnorm(dims: Dims, hidden, attn_out, sel_idx, sel_offsets, n_r
 
 def srp_validate_batch(batch: Batch, stream=None) -> int:
     return _check(lib().srp_validate_batch(ctypes.byref(batch), _stream(stream)))
+
+
+def srp_profile_begin(max_calls: int) -> int:
+    return _check(lib().srp_profile_begin(int(max_calls)))
+
+
+def srp_profile_end(max_calls: int):
+    """Per-call stage times in ms: list of lists [call][stage]."""
+    buf = (ctypes.c_float * (max_calls * SRP_N_STAGES))()
+    n = ctypes.c_int32(0)
+    _check(lib().srp_profile_end(buf, int(max_calls), ctypes.byref(n)))
+    return [[buf[c * SRP_N_STAGES + i] for i in range(SRP_N_STAGES)] for c in range(n.value)]
+
+
+def srp_profile_stage_name(i: int) -> str:
+    return lib().srp_profile_stage_name(int(i)).decode()
 
 
 def srp_version() -> str:
