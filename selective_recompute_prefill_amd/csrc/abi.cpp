@@ -215,6 +215,7 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   sa.cand_offsets = sel->cand_offsets;
   sa.nkv = d.n_kv_heads;
   sa.dev_out = dev_out;
+  sa.tile_rows = attn_tile_rows(d.dtype, d.n_heads, d.n_kv_heads);
 
   // 1. row metadata; candidate list and the recomputed rows R when given
   StageMarks marks(s);
@@ -265,6 +266,8 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   gq.N = qd;
   gq.mode = EPI_Q;
   gq.q_out = w.q;
+  // bf16 attention works in base 2 on pre-scaled queries; the fp32 kernel scales itself
+  gq.q_scale = d.dtype == SRP_BF16 ? (float)(1.4426950408889634 / std::sqrt((double)d.head_dim)) : 1.0f;
   SRP_HIP(launch_gemm(gq, s));
   marks.mark(5);
   // 7. attention of the selected rows over the fused cache

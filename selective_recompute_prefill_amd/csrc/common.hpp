@@ -18,7 +18,8 @@ constexpr uint8_t kFreshF = 2; // fresh row: always recomputed and selected
 constexpr uint8_t kTop = 4;    // chosen by top-k
 constexpr uint8_t kSel = 8;    // in the final selection
 
-// Attention query tile (selected rows per work-group).
+// Smallest attention query tile (selected rows per work-group); tiles are a
+// multiple of it.
 constexpr int kQT = 32;
 
 // ------------------------------------------------------------------------- //

@@ -42,6 +42,8 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, int m0, int n
       if (MODE == EPI_Q) {
         const int h = nu / d;
         rope4(a, b, g.rope, g.positions[row], i0);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { a[k] *= g.q_scale; b[k] *= g.q_scale; }
         T *q = (T *)g.q_out + (size_t)m * g.nh * d + h * d;
         st4(q + i0, a);
         st4(q + half + i0, b);

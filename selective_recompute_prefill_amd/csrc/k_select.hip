@@ -2,12 +2,12 @@
 // by KV deviation with sliding-window grouping, CSR compaction, and the scatter of
 // the fresh K/V rows into the cache (gfx950).
 //
-// One work-group of 1024 threads owns a request during selection. Every pass walks
-// the request's entries in tiles of 1024 consecutive entries, so each thread owns
-// the same entry position in every pass and per-entry data it wrote earlier is its
-// own. The k-th largest squared deviation is found by an MSB-first radix select on
-// the fp32 bit patterns (order-preserving for non-negative floats); ties at the
-// threshold are taken in row order, so the result is deterministic.
+// Squared deviations are summed grid-wide; then one work-group of 1024 threads owns
+// a request: order-free passes (counts, histograms, marks) stride over its entries
+// so loads coalesce, and order-dependent scans run over pages of entry flags
+// staged in LDS, each thread walking a contiguous segment. The k-th largest squared deviation is found by an MSB-first
+// radix select on the fp32 bit patterns (order-preserving for non-negative floats);
+// ties at the threshold are taken in row order, so the result is deterministic.
 #include "kernels.hpp"
 
 namespace srp {
@@ -81,41 +81,57 @@ __global__ __launch_bounds__(1024) void r_write_kernel(SelectArgs a, Workspace w
 }
 
 // ------------------------------------------------------------------------- //
+// keys: squared deviation of every candidate entry (grid-wide, fixed-order sum of
+// the per-head partials), entry flags, and the optional deviation output
+// ------------------------------------------------------------------------- //
+__global__ __launch_bounds__(256) void keys_kernel(SelectArgs a, Workspace w) {
+  const int *roff = a.cand ? w.roff : a.req_offsets;
+  const int nR = roff[a.n_req];
+  const int P0 = a.dev_mode == SRP_DEV_V ? a.nkv : 0, P1 = 2 * a.nkv;
+  for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < nR; e += gridDim.x * blockDim.x) {
+    const int row = a.cand ? w.rlist[e] : e;
+    if (w.row_delta[row] == kFresh) {
+      w.eflag[e] = kFreshF;
+      continue;
+    }
+    const float *dp = w.dev_part + (size_t)e * 2 * a.nkv;
+    float s = 0.f;
+    for (int p = P0; p < P1; ++p) s += dp[p];
+    w.keys[e] = __float_as_uint(s);
+    w.eflag[e] = kCand;
+    if (a.dev_out) a.dev_out[row] = sqrtf(s);
+  }
+}
+
+// ------------------------------------------------------------------------- //
 // selection: one work-group per request
 // ------------------------------------------------------------------------- //
+// [lo, hi): the contiguous share of n items owned by this thread
+__device__ __forceinline__ void my_segment(int n, int &lo, int &hi) {
+  const int per = (n + (int)blockDim.x - 1) / (int)blockDim.x;
+  lo = min(n, (int)threadIdx.x * per);
+  hi = min(n, lo + per);
+}
+
+constexpr int kHistBins = 4096;
+constexpr int kPage = 32768;  // entries whose flags are staged in LDS at a time
+
 __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, Workspace w) {
   __shared__ int sh[17];
-  __shared__ int hist[256];
+  __shared__ int hist[kHistBins];
   __shared__ int digit_info[2];
-  const int r = blockIdx.x, tid = threadIdx.x;
+  __shared__ uint8_t pg[kPage];
+  const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int *roff = a.cand ? w.roff : a.req_offsets;
   const int e0 = roff[r], e1 = roff[r + 1];
   const int rq0 = a.req_offsets[r], rq1 = a.req_offsets[r + 1];
-  const int P0 = a.dev_mode == SRP_DEV_V ? a.nkv : 0, P1 = 2 * a.nkv;
 
-  // cached rows of the request (the N of the ratio)
-  int my_ctx = 0;
-  for (int j = rq0 + tid; j < rq1; j += 1024) my_ctx += w.row_delta[j] != kFresh;
+  // cached rows of the request (the N of the ratio) and its candidates; loops
+  // whose result does not depend on order stride over the entries (coalesced)
+  int my_ctx = 0, my_cand = 0;
+  for (int j = rq0 + tid; j < rq1; j += nt) my_ctx += w.row_delta[j] != kFresh;
+  for (int e = e0 + tid; e < e1; e += nt) my_cand += (w.eflag[e] & kCand) ? 1 : 0;
   const int n_ctx = block_sum(my_ctx, sh);
-
-  // entry flags and keys
-  int my_cand = 0;
-  for (int e = e0 + tid; e < e1; e += 1024) {
-    const int row = a.cand ? w.rlist[e] : e;
-    uint8_t fl;
-    if (w.row_delta[row] == kFresh) {
-      fl = kFreshF;
-    } else {
-      fl = kCand;
-      float s = 0.f;
-      const float *dp = w.dev_part + (size_t)e * 2 * a.nkv;
-      for (int p = P0; p < P1; ++p) s += dp[p];
-      w.keys[e] = __float_as_uint(s);
-      if (a.dev_out) a.dev_out[row] = sqrtf(s);
-      ++my_cand;
-    }
-    w.eflag[e] = fl;
-  }
   const int n_cand = block_sum(my_cand, sh);
 
   int k;
@@ -127,117 +143,131 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, Workspace w)
   }
 
   if (k >= n_cand) {
-    for (int e = e0 + tid; e < e1; e += 1024)
+    for (int e = e0 + tid; e < e1; e += nt)
       if (w.eflag[e] & kCand) w.eflag[e] |= kTop;
   } else if (k > 0) {
+    // radix select of the k-th largest key, digits of 12, 12 and 8 bits from
+    // the top (the first pass splits sign, exponent and 3 mantissa bits)
     uint32_t prefix = 0, pmask = 0;
     int need = k;
-    for (int pass = 0; pass < 4; ++pass) {
-      const int shift = 24 - 8 * pass;
-      if (tid < 256) hist[tid] = 0;
+    const int shifts[3] = {20, 8, 0}, widths[3] = {12, 12, 8};
+    for (int pass = 0; pass < 3; ++pass) {
+      const int shift = shifts[pass], nb = 1 << widths[pass];
+      const uint32_t dmask = (uint32_t)nb - 1u;
+      for (int b = tid; b < nb; b += nt) hist[b] = 0;
       __syncthreads();
-      for (int e = e0 + tid; e < e1; e += 1024) {
+      for (int e = e0 + tid; e < e1; e += nt) {
         if (!(w.eflag[e] & kCand)) continue;
         const uint32_t key = w.keys[e];
-        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & 255u], 1);
+        if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
       }
       __syncthreads();
-      if (tid < 64) {
-        // lane l owns digits 255-4l .. 252-4l (descending); find the digit where
-        // the count of keys at or above it first reaches `need`
-        int c[4], s4 = 0;
+      // thread t owns 4 digits in descending order: nb-1-4t .. nb-4-4t
+      int c[4], s4 = 0;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) { c[q] = hist[255 - 4 * tid - q]; s4 += c[q]; }
-        const int incl = wave_incl_scan(s4);
-        int above = incl - s4;
-        const bool mine = above < need && incl >= need;
-        if (mine) {
-          int dsel = 0, abv = above;
+      for (int q = 0; q < 4; ++q) {
+        const int dg = nb - 1 - 4 * tid - q;
+        c[q] = dg >= 0 ? hist[dg] : 0;
+        s4 += c[q];
+      }
+      int tot;
+      const int above = block_excl_scan(s4, sh, &tot);
+      if (above < need && above + s4 >= need) {
+        int abv = above, dsel = 0;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (abv + c[q] >= need) { dsel = 255 - 4 * tid - q; break; }
-            abv += c[q];
-          }
-          digit_info[0] = dsel;
-          digit_info[1] = abv;
+        for (int q = 0; q < 4; ++q) {
+          if (abv + c[q] >= need) { dsel = nb - 1 - 4 * tid - q; break; }
+          abv += c[q];
         }
+        digit_info[0] = dsel;
+        digit_info[1] = abv;
       }
       __syncthreads();
-      const uint32_t dsel = (uint32_t)digit_info[0];
       need -= digit_info[1];
-      prefix |= dsel << shift;
-      pmask |= 255u << shift;
+      prefix |= (uint32_t)digit_info[0] << shift;
+      pmask |= dmask << shift;
       __syncthreads();
     }
-    // prefix = the k-th largest key; take every larger key and the first `need`
-    // equal keys in entry (row) order
-    int eq_run = 0;
-    for (int base = e0; base < e1; base += 1024) {
-      const int e = base + tid;
-      bool gt = false, eq = false;
-      if (e < e1 && (w.eflag[e] & kCand)) {
-        const uint32_t key = w.keys[e];
-        gt = key > prefix;
-        eq = key == prefix;
+    // prefix = the k-th largest key: take every larger key and the first `need`
+    // keys equal to it in entry (row) order
+    int my_eq = 0;
+    for (int e = e0 + tid; e < e1; e += nt) {
+      if (!(w.eflag[e] & kCand)) continue;
+      const uint32_t key = w.keys[e];
+      if (key > prefix) w.eflag[e] |= kTop;
+      else if (key == prefix) ++my_eq;
+    }
+    const int eq_tot = block_sum(my_eq, sh);
+    if (eq_tot == need) {
+      for (int e = e0 + tid; e < e1; e += nt)
+        if ((w.eflag[e] & kCand) && w.keys[e] == prefix) w.eflag[e] |= kTop;
+    } else {
+      // several equal keys at the threshold: rank them in row order
+      int eq_run = 0;
+      for (int base = e0; base < e1; base += nt) {
+        const int e = base + tid;
+        const bool eq = e < e1 && (w.eflag[e] & kCand) && w.keys[e] == prefix;
+        int t;
+        const int rank = block_excl_scan(eq ? 1 : 0, sh, &t) + eq_run;
+        if (eq && rank < need) w.eflag[e] |= kTop;
+        eq_run += t;
       }
-      int eq_tot;
-      const int eqp = block_excl_scan(eq ? 1 : 0, sh, &eq_tot) + eq_run;
-      if (gt || (eq && eqp < need)) w.eflag[e] |= kTop;
-      eq_run += eq_tot;
     }
   }
   __threadfence_block();
   __syncthreads();
 
   if (a.window > 0) {
-    // the grouping sequence: the request's candidate rows in order
+    // the grouping sequence: the request's candidate rows in order; slot numbers
+    // and the inclusive count of top-k slots come from one ordered walk over pages
+    // of entry flags staged in LDS
     const int win = a.window;
-    int carry = 0;
-    for (int base = e0; base < e1; base += 1024) {
-      const int e = base + tid;
-      const uint8_t fl = e < e1 ? w.eflag[e] : 0;
-      const int c = (fl & kCand) ? 1 : 0;
-      int tot;
-      const int slot = block_excl_scan(c, sh, &tot) + carry;
-      if (c) {
-        w.seq_ent[e0 + slot] = e;
-        w.seq_flag[e0 + slot] = (fl & kTop) ? 1 : 0;
+    int carry_c = 0, carry_t = 0;
+    for (int pb = e0; pb < e1; pb += kPage) {
+      const int np = min(kPage, e1 - pb);
+      for (int i = tid; i < np; i += nt) pg[i] = w.eflag[pb + i];
+      __syncthreads();
+      int lo, hi;
+      my_segment(np, lo, hi);
+      int c = 0, t = 0;
+      for (int i = lo; i < hi; ++i) {
+        const uint8_t fl = pg[i];
+        if (fl & kCand) { ++c; t += (fl & kTop) ? 1 : 0; }
       }
-      carry += tot;
+      int ctot, ttot;
+      int cb = block_excl_scan(c, sh, &ctot);
+      int tb = block_excl_scan(t, sh, &ttot);
+      for (int i = lo; i < hi; ++i) {
+        const uint8_t fl = pg[i];
+        if (!(fl & kCand)) continue;
+        const int top = (fl & kTop) ? 1 : 0;
+        const int slot = carry_c + cb++;
+        tb += top;
+        w.seq_ent[e0 + slot] = pb + i;
+        w.seq_flag[e0 + slot] = (uint8_t)top;
+        w.seq_pre[e0 + slot] = carry_t + tb;
+      }
+      carry_c += ctot;
+      carry_t += ttot;
+      __syncthreads();
     }
-    const int n_seq = carry;
+    const int n_seq = carry_c;
     __threadfence_block();
     __syncthreads();
-    carry = 0;
-    for (int base = 0; base < n_seq; base += 1024) {
-      const int s = base + tid;
-      const int v = s < n_seq ? (w.seq_flag[e0 + s] & 1) : 0;
-      int tot;
-      const int p = block_excl_scan(v, sh, &tot) + carry;
-      if (s < n_seq) w.seq_pre[e0 + s] = p + v;  // inclusive count of top slots
-      carry += tot;
-    }
-    __threadfence_block();
-    __syncthreads();
-    for (int t = tid; t < n_seq; t += 1024) {
+    for (int t = tid; t < n_seq; t += nt) {
       const uint8_t f = w.seq_flag[e0 + t];
-      bool pass = false;
       if ((f & 1) && t + win <= n_seq) {
         const int cnt = w.seq_pre[e0 + t + win - 1] - (t > 0 ? w.seq_pre[e0 + t - 1] : 0);
-        pass = cnt >= a.tau;
+        if (cnt >= a.tau) w.seq_flag[e0 + t] = f | 2;
       }
-      if (pass) w.seq_flag[e0 + t] = f | 2;
     }
     __threadfence_block();
     __syncthreads();
-    for (int p = tid; p < n_seq; p += 1024) {
+    for (int p = tid; p < n_seq; p += nt) {
       bool kept = false;
       const int t0 = p - win + 1 > 0 ? p - win + 1 : 0;
       for (int t = t0; t <= p; ++t) kept |= (w.seq_flag[e0 + t] & 2) != 0;
-      if (kept) {
-        const int e = w.seq_ent[e0 + p];
-        w.eflag[e] |= kSel;
-      }
+      if (kept) w.eflag[w.seq_ent[e0 + p]] |= kSel;
     }
     __threadfence_block();
     __syncthreads();
@@ -246,17 +276,26 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, Workspace w)
   // compact the request's selection (fresh rows included) in row order
   const uint8_t want = a.window > 0 ? kSel : kTop;
   int carry = 0;
-  for (int base = e0; base < e1; base += 1024) {
-    const int e = base + tid;
-    const uint8_t fl = e < e1 ? w.eflag[e] : 0;
-    const int s = ((fl & kFreshF) || (fl & want)) ? 1 : 0;
+  for (int pb = e0; pb < e1; pb += kPage) {
+    const int np = min(kPage, e1 - pb);
+    for (int i = tid; i < np; i += nt) pg[i] = w.eflag[pb + i];
+    __syncthreads();
+    int lo, hi;
+    my_segment(np, lo, hi);
+    int c = 0;
+    for (int i = lo; i < hi; ++i) c += ((pg[i] & kFreshF) || (pg[i] & want)) ? 1 : 0;
     int tot;
-    const int p = block_excl_scan(s, sh, &tot) + carry;
-    if (s) {
-      w.tsel_row[e0 + p] = a.cand ? w.rlist[e] : e;
-      w.tsel_ent[e0 + p] = e;
+    int p = block_excl_scan(c, sh, &tot) + carry;
+    for (int i = lo; i < hi; ++i) {
+      if ((pg[i] & kFreshF) || (pg[i] & want)) {
+        const int e = pb + i;
+        w.tsel_row[e0 + p] = a.cand ? w.rlist[e] : e;
+        w.tsel_ent[e0 + p] = e;
+        ++p;
+      }
     }
     carry += tot;
+    __syncthreads();
   }
   if (tid == 0) w.sel_cnt[r] = carry;
 }
@@ -273,7 +312,7 @@ __global__ __launch_bounds__(1024) void finalize_kernel(SelectArgs a, Workspace 
   for (int base = 0; base < nr; base += 1024) {
     const int r = base + tid;
     const int c = r < nr ? w.sel_cnt[r] : 0;
-    const int nt = (c + kQT - 1) / kQT;
+    const int nt = (c + a.tile_rows - 1) / a.tile_rows;
     int tot, ttot;
     const int p = block_excl_scan(c, sh, &tot) + carry;
     const int tp = block_excl_scan(nt, sh, &ttot) + tcarry;
@@ -306,8 +345,9 @@ __global__ __launch_bounds__(1024) void finalize_kernel(SelectArgs a, Workspace 
       if (q < r && t > i) ++E;
     }
     const int c = w.sel_cnt[r];
-    w.tiles[3 * E + 0] = sel_offsets[r] + i * kQT;
-    w.tiles[3 * E + 1] = c - i * kQT < kQT ? c - i * kQT : kQT;
+    const int tr = a.tile_rows;
+    w.tiles[3 * E + 0] = sel_offsets[r] + i * tr;
+    w.tiles[3 * E + 1] = c - i * tr < tr ? c - i * tr : tr;
     w.tiles[3 * E + 2] = r;
   }
 }
@@ -369,6 +409,9 @@ hipError_t launch_prepare(const SelectArgs &a, const Workspace &w, hipStream_t s
 }
 
 hipError_t launch_select(const SelectArgs &a, const Workspace &w, hipStream_t s) {
+  int grid = (a.T + 255) / 256;
+  grid = grid < 2048 ? (grid > 0 ? grid : 1) : 2048;
+  hipLaunchKernelGGL(keys_kernel, dim3(grid), dim3(256), 0, s, a, w);
   hipLaunchKernelGGL(select_kernel, dim3(a.n_req), dim3(1024), 0, s, a, w);
   return hipGetLastError();
 }

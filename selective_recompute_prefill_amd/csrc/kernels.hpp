@@ -13,7 +13,7 @@ enum EpiMode { EPI_KV = 0, EPI_Q = 1, EPI_ENC = 2 };
 //           V heads. Fresh K/V go to `fresh` [m][2 kvdim]. For cached rows the
 //           cached K is rotated by the row's delta (written back in place) and the
 //           squared deviation of each head goes to dev_part [m][2 nkv].
-//  EPI_Q  : n are Q heads, roped; written to q_out [m][qdim].
+//  EPI_Q  : n are Q heads, roped and multiplied by q_scale; written to q_out [m][qdim].
 //  EPI_ENC: like EPI_KV's layout, K roped at positions[m]; K -> k_cache[m],
 //           V -> v_cache[m].
 struct GemmArgs {
@@ -35,6 +35,7 @@ struct GemmArgs {
   void *fresh;
   float *dev_part;
   void *q_out;
+  float q_scale;  // EPI_Q: factor applied to the roped queries
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 
@@ -47,6 +48,7 @@ struct SelectArgs {
   const int32_t *cand, *cand_offsets;
   int nkv;
   float *dev_out;
+  int tile_rows;  // selected rows per attention tile
 };
 // Row metadata (delta, request), dev_out prefill with NaN, candidate marking and
 // the R list (candidate rows plus fresh rows, per request) when cand is given.
@@ -67,7 +69,7 @@ hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *chun
 struct AttnArgs {
   int dtype;
   int nh, nkv, d;
-  const void *q;           // [n_sel][nh][d]
+  const void *q;           // [n_sel][nh][d]; bf16: pre-multiplied by log2(e)/sqrt(d)
   const int32_t *sel_idx;  // [n_sel]
   const int32_t *req_offsets;
   const int32_t *tiles;    // [3 * max_tiles]: first selected row, count, request
@@ -77,6 +79,8 @@ struct AttnArgs {
   void *out;               // [n_sel][nh][d]
 };
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
+// Selected rows per attention tile for this shape (a multiple of 32).
+int attn_tile_rows(int dtype, int nh, int nkv);
 
 hipError_t launch_residual_rmsnorm(int dtype, int H, void *hidden, const void *attn,
                                    const int32_t *sel_idx, const int32_t *total_dev,

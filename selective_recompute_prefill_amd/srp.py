@@ -11,7 +11,7 @@ import os
 from typing import Optional
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_PKG, "libsrp.so")
+LIB_PATH = os.environ.get("SRP_LIB", os.path.join(_PKG, "libsrp.so"))
 
 SRP_OK, SRP_E_INVALID, SRP_E_WORKSPACE, SRP_E_UNSUPPORTED, SRP_E_HIP, SRP_E_BATCH = 0, -1, -2, -3, -4, -5
 SRP_F32, SRP_BF16 = 0, 1
