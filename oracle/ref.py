@@ -219,7 +219,8 @@ def fuse_layer(*, hidden, w_qkv, k_cache, v_cache, req_offsets, chunk_offsets,
                chunk_src_pos, positions, n_heads, n_kv, head_dim, rope_base,
                ratio, mode: str = "topk", window: int = 0, tau: int = 0,
                dev_mode: str = "kv", cand: Optional[np.ndarray] = None,
-               sel_override: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+               sel_override: Optional[np.ndarray] = None,
+               attn_sample: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
     """One selective-recompute layer, all float64 (CacheBlend walkthrough,
     "Selective KV recompute" and "Implementation"; CacheClip paper 4.1-4.3).
 
@@ -307,9 +308,18 @@ def fuse_layer(*, hidden, w_qkv, k_cache, v_cache, req_offsets, chunk_offsets,
     v_out[sel] = v_new[sel]
 
     # 6. queries of the selected rows and their attention over the fused cache
-    q, _, _ = project(hidden[sel], w_qkv, n_heads, n_kv, d)
-    q = rope(q, pos[sel], rope_base)
-    attn = attention(q, sel, k_out, v_out, req, pos)
+    #    (attn_sample: positions into the selection whose rows are evaluated;
+    #    the others are left NaN -- a cost cut for large tests)
+    if attn_sample is None:
+        q, _, _ = project(hidden[sel], w_qkv, n_heads, n_kv, d)
+        q = rope(q, pos[sel], rope_base)
+        attn = attention(q, sel, k_out, v_out, req, pos)
+    else:
+        idx = np.asarray(attn_sample, np.int64)
+        q, _, _ = project(hidden[sel[idx]], w_qkv, n_heads, n_kv, d)
+        q = rope(q, pos[sel[idx]], rope_base)
+        attn = np.full((len(sel), n_heads, d), np.nan)
+        attn[idx] = attention(q, sel[idx], k_out, v_out, req, pos)
 
     return dict(sel_idx=sel, sel_offsets=sel_offsets, k_cache=k_out, v_cache=v_out,
                 attn_out=attn, dev=dev, s0=(np.concatenate(s0_parts) if s0_parts

@@ -8,38 +8,48 @@
 // (lanes l and l^32) and the rescale of O is per lane. The probabilities are
 // reused in registers as the B operand of the PV product, so V is staged in LDS
 // transposed. Causality is by row: positions rise strictly inside a request.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace srp {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// Waves per work-group: one per (query head of the group, 32-row query
-// sub-tile); groups with fewer than 4 heads take several sub-tiles so that at
-// least 4 waves share each K/V tile.
-__host__ __device__ constexpr int attn_subtiles(int G) { return G >= 4 ? 1 : (4 + G - 1) / G; }
+// Calls f(integral_constant<int, i>) for i = 0..N-1, so array indices inside f
+// are compile-time constants (register arrays stay in registers).
+template <int N, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (N > 0) {
+    static_for<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
+  }
+}
 
-#ifndef SRP_ATTN_KEYS
-#define SRP_ATTN_KEYS 64
-#endif
-#ifndef SRP_ATTN_OCC
-#define SRP_ATTN_OCC 2
-#endif
-constexpr int kBK = SRP_ATTN_KEYS;  // keys per LDS stage
+// Waves per work-group: one per (query head of the group, 32-row query
+// sub-tile); groups of fewer than 5 heads take several sub-tiles so that 6-8
+// waves (2 per SIMD) share each K/V tile.
+__host__ __device__ constexpr int attn_subtiles(int G) { return G >= 5 ? 1 : (G == 3 ? 2 : 8 / G); }
+
+constexpr int kBK = 64;  // keys per LDS stage
 
 template <int D, int W>
-__global__ __launch_bounds__(64 * W, (W == 5 || W == 6) ? SRP_ATTN_OCC : 2) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int KLD = D + 8;       // K tile row stride (elements)
-  constexpr int VLD = kBK + 8;     // V^T tile row stride
+__global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnArgs a) {
+  constexpr int KLD = D + 8;    // K tile row stride (elements, 16-byte padded rows)
+  constexpr int VLD = kBK + 8;  // V^T tile row stride
   constexpr int KSZ = kBK * KLD, VSZ = D * VLD;
   constexpr int NT = 64 * W;
   constexpr int KCH = kBK * (D / 8);        // 16-byte chunks of a K tile
   constexpr int VCH = (kBK / 2) * (D / 8);  // (key pair, 8-wide d chunk) items of a V tile
   constexpr int KIT = (KCH + NT - 1) / NT, VIT = (VCH + NT - 1) / NT;
   __shared__ __align__(16) uint16_t lds[2 * (KSZ + VSZ)];
+  __shared__ uint4 qlds[W * (D / 16) * 64];  // each lane's Q fragments, in fragment order
 
   const int n_tiles = *a.n_tiles;
   const int slot = blockIdx.x / a.nkv, g = blockIdx.x - slot * a.nkv;
@@ -51,165 +61,196 @@ __global__ __launch_bounds__(64 * W, (W == 5 || W == 6) ? SRP_ATTN_OCC : 2) void
   const int key_end = last_row + 1;
   const int nblk = (key_end - key_start + kBK - 1) / kBK;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
   const int hw = w % G, qs = w / G;
   const int h = g * G + hw;
   const int qi = lane & 31, gph = lane >> 5;
   const int qidx = qs * 32 + qi;
   const bool qvalid = qidx < nq;
   const int qrow = qvalid ? a.sel_idx[q0 + qidx] : last_row;
-  const size_t kvd = (size_t)a.nkv * D;
-  const uint16_t *K = (const uint16_t *)a.k_cache + g * D;
-  const uint16_t *V = (const uint16_t *)a.v_cache + g * D;
+  const int kvd = a.nkv * D;
+  const size_t row_bytes = (size_t)kvd * 2;
+  const char *Kg = (const char *)a.k_cache + (size_t)g * D * 2;
+  const char *Vg = (const char *)a.v_cache + (size_t)g * D * 2;
 
-  // register-staged loads of the next K/V tile (K and V in separate phases so
-  // only one of them is held in registers at a time)
-  uint4 rk[KIT], rv0[VIT], rv1[VIT];
-  auto kload = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < KIT; ++i) {
-      const int c = tid + NT * i;
-      const int key = c / (D / 8), dc = c - key * (D / 8);
-      const int krow = kb + key;
-      rk[i] = (c < KCH && krow < key_end)
-                  ? *reinterpret_cast<const uint4 *>(K + (size_t)krow * kvd + dc * 8)
-                  : make_uint4(0, 0, 0, 0);
-    }
-  };
-  auto kstore = [&](int st) {
-    uint16_t *Ks = lds + st * (KSZ + VSZ);
-#pragma unroll
-    for (int i = 0; i < KIT; ++i) {
-      const int c = tid + NT * i;
-      if (c < KCH) {
-        const int key = c / (D / 8), dc = c - key * (D / 8);
-        *reinterpret_cast<uint4 *>(Ks + key * KLD + dc * 8) = rk[i];
-      }
-    }
-  };
-  auto vload = [&](int kb) {
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int c = tid + NT * i;
-      const int kp = c % (kBK / 2), dc = c / (kBK / 2);
-      const int k0 = kb + 2 * kp;
-      const bool ok = c < VCH;
-      rv0[i] = (ok && k0 < key_end) ? *reinterpret_cast<const uint4 *>(V + (size_t)k0 * kvd + dc * 8)
-                                    : make_uint4(0, 0, 0, 0);
-      rv1[i] = (ok && k0 + 1 < key_end)
-                   ? *reinterpret_cast<const uint4 *>(V + (size_t)(k0 + 1) * kvd + dc * 8)
-                   : make_uint4(0, 0, 0, 0);
-    }
-  };
-  // V transposed: 8 key pairs of one 8-wide d chunk as 32-bit words
-  auto vstore = [&](int st) {
-    uint16_t *Vt = lds + st * (KSZ + VSZ) + KSZ;
-#pragma unroll
-    for (int i = 0; i < VIT; ++i) {
-      const int c = tid + NT * i;
-      if (c < VCH) {
-        const int kp = c % (kBK / 2), dc = c / (kBK / 2);
-        const uint32_t x0[4] = {rv0[i].x, rv0[i].y, rv0[i].z, rv0[i].w};
-        const uint32_t x1[4] = {rv1[i].x, rv1[i].y, rv1[i].z, rv1[i].w};
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          *reinterpret_cast<uint32_t *>(Vt + (dc * 8 + 2 * j) * VLD + 2 * kp) =
-              (x0[j] & 0xffffu) | (x1[j] << 16);
-          *reinterpret_cast<uint32_t *>(Vt + (dc * 8 + 2 * j + 1) * VLD + 2 * kp) =
-              (x0[j] >> 16) | (x1[j] & 0xffff0000u);
+  // Loader: thread chunk i covers K chunk c = tid + NT*i, i.e. key tid/(D/8) +
+  // i*NT/(D/8) at d chunk tid%(D/8), and V item c, i.e. key pair tid%32 at d chunk
+  // tid/32 + i*NT/32. NT is a multiple of both widths, so each offset is one
+  // per-thread constant plus a uniform step, and whether chunk i exists is uniform
+  // per wave (KCH, VCH and NT are multiples of 64).
+  constexpr int KSTEP = NT / (D / 8);  // keys per K chunk step
+  constexpr int VSTEP = NT / (kBK / 2);  // d chunks per V item step
+  const int kkey0 = tid / (D / 8), kdc = tid % (D / 8);
+  const int vkp = tid % (kBK / 2), vdc0 = tid / (kBK / 2);
+  const uint32_t koff0 = (uint32_t)(kkey0 * row_bytes + kdc * 16);
+  const uint32_t voff0 = (uint32_t)(2 * vkp * row_bytes + vdc0 * 16);
+  u32x4 rk[KIT], rv0[VIT], rv1[VIT];
+  auto load_next = [&](int kb) __attribute__((always_inline)) {
+    const char *kbase = Kg + (size_t)kb * row_bytes, *vbase = Vg + (size_t)kb * row_bytes;
+    if (kb + kBK <= key_end) {
+      static_for<KIT>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        if (w * 64 + NT * i < KCH)
+          rk[i] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)i * KSTEP * row_bytes + koff0);
+      });
+      static_for<VIT>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        if (w * 64 + NT * i < VCH) {
+          const char *p = vbase + (size_t)i * VSTEP * 16 + voff0;
+          rv0[i] = *reinterpret_cast<const u32x4 *>(p);
+          rv1[i] = *reinterpret_cast<const u32x4 *>(p + row_bytes);
         }
-      }
+      });
+    } else {
+      // last, partial tile: rows past key_end are clamped to the last valid row;
+      // every such key lies after every query of the tile and is masked
+      const int lastk = key_end - 1 - kb;
+      static_for<KIT>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        if (w * 64 + NT * i < KCH) {
+          const int key = min(kkey0 + i * KSTEP, lastk);
+          rk[i] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)key * row_bytes + kdc * 16);
+        }
+      });
+      static_for<VIT>([&](auto I) __attribute__((always_inline)) {
+        constexpr int i = decltype(I)::value;
+        if (w * 64 + NT * i < VCH) {
+          const char *p = vbase + (size_t)(vdc0 + i * VSTEP) * 16;
+          rv0[i] = *reinterpret_cast<const u32x4 *>(p + (size_t)min(2 * vkp, lastk) * row_bytes);
+          rv1[i] = *reinterpret_cast<const u32x4 *>(p + (size_t)min(2 * vkp + 1, lastk) * row_bytes);
+        }
+      });
     }
   };
+  auto store_next = [&](int st) __attribute__((always_inline)) {
+    uint16_t *Ks = lds + st * (KSZ + VSZ), *Vt = Ks + KSZ;
+    static_for<KIT>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if (w * 64 + NT * i < KCH)
+        *reinterpret_cast<u32x4 *>(Ks + (kkey0 + i * KSTEP) * KLD + kdc * 8) = rk[i];
+    });
+    // V transposed: word j of two keys -> d rows 2j (low halves), 2j+1 (high halves)
+    static_for<VIT>([&](auto I) __attribute__((always_inline)) {
+      constexpr int i = decltype(I)::value;
+      if (w * 64 + NT * i < VCH) {
+        uint16_t *vt = Vt + (vdc0 + i * VSTEP) * 8 * VLD + 2 * vkp;
+        const u32x4 a0 = rv0[i], a1 = rv1[i];
+        *reinterpret_cast<uint32_t *>(vt + 0 * VLD) = __builtin_amdgcn_perm(a1.x, a0.x, 0x05040100u);
+        *reinterpret_cast<uint32_t *>(vt + 1 * VLD) = __builtin_amdgcn_perm(a1.x, a0.x, 0x07060302u);
+        *reinterpret_cast<uint32_t *>(vt + 2 * VLD) = __builtin_amdgcn_perm(a1.y, a0.y, 0x05040100u);
+        *reinterpret_cast<uint32_t *>(vt + 3 * VLD) = __builtin_amdgcn_perm(a1.y, a0.y, 0x07060302u);
+        *reinterpret_cast<uint32_t *>(vt + 4 * VLD) = __builtin_amdgcn_perm(a1.z, a0.z, 0x05040100u);
+        *reinterpret_cast<uint32_t *>(vt + 5 * VLD) = __builtin_amdgcn_perm(a1.z, a0.z, 0x07060302u);
+        *reinterpret_cast<uint32_t *>(vt + 6 * VLD) = __builtin_amdgcn_perm(a1.w, a0.w, 0x05040100u);
+        *reinterpret_cast<uint32_t *>(vt + 7 * VLD) = __builtin_amdgcn_perm(a1.w, a0.w, 0x07060302u);
+      }
+    });
+  };
 
-  bf16x8 qf[D / 16];
+  // Q fragments (B operand of S^T = K Q^T): lane holds query qi, d range
+  // ks*16 + gph*8 .. +8; parked in LDS to keep registers for the accumulators
+  uint4 *qmine = qlds + w * (D / 16) * 64 + lane;
   {
     const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(q0 + qidx) * a.nh + h) * D + gph * 8;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      uint4 t = qvalid ? *reinterpret_cast<const uint4 *>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
-      qf[ks] = *reinterpret_cast<bf16x8 *>(&t);
-    }
+    for (int ks = 0; ks < D / 16; ++ks)
+      qmine[ks * 64] = qvalid ? *reinterpret_cast<const uint4 *>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
   }
   floatx16 acc[D / 32];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
-  // scores are already in base-2 units (queries carry log2(e)/sqrt(d)); m_ref is
-  // the reference max of the exponentials, raised only when a block's max exceeds
-  // it by more than 8, so probabilities stay below 2^8 and rescales are rare
-  float m_ref = -INFINITY, l = 0.f;
+  // Scores are in base-2 units (queries carry log2(e)/sqrt(d)). The score
+  // accumulators start at -m, so they come out of the MFMA already relative to
+  // the reference max m, which is raised only when a half-block's max exceeds
+  // it by more than 8: probabilities stay below 2^8 and rescales are rare.
+  float m = 0.f, l = 0.f;
+  bool first = true;
+  const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  kload(key_start);
-  vload(key_start);
-  kstore(0);
-  vstore(0);
+  load_next(key_start);
+  store_next(0);
   __syncthreads();
   for (int blk = 0; blk < nblk; ++blk) {
     const int kb = key_start + blk * kBK;
     const int st = blk & 1;
     const bool more = blk + 1 < nblk;
     const uint16_t *Ks = lds + st * (KSZ + VSZ), *Vt = Ks + KSZ;
-    const bool masked = kb + kBK - 1 > first_row;
-    if (kBK == 32 && more) {
-      kload(kb + kBK);
-      vload(kb + kBK);
+    if (more) load_next(kb + kBK);
+
+    // S^T[key][query] - m for both 32-key halves, two independent MFMA chains
+    floatx16 s[2];
+    const float c0 = first ? 0.f : -m;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { s[0][e] = c0; s[1][e] = c0; }
+#pragma unroll
+    for (int ks = 0; ks < D / 16; ++ks) {
+      uint4 qt = qmine[ks * 64];
+      const bf16x8 qf = *reinterpret_cast<bf16x8 *>(&qt);
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (hb * 32 + qi) * KLD + ks * 16 + gph * 8);
+        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, s[hb], 0, 0, 0);
+      }
     }
+    const bool masked = kb + kBK - 1 > first_row;
 #pragma unroll
-    for (int kb2 = 0; kb2 < kBK / 32; ++kb2) {
-      if (kBK == 64 && more) {
-        if (kb2 == 0) kload(kb + kBK);
-        else vload(kb + kBK);
-      }
-      // S^T[key][query] for 32 keys
-      floatx16 s;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) s[e] = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < D / 16; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (kb2 * 32 + qi) * KLD + ks * 16 + gph * 8);
-        s = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s, 0, 0, 0);
-      }
+    for (int hb = 0; hb < 2; ++hb) {
       if (masked) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
-          const int krow = kb + kb2 * 32 + (e >> 2) * 8 + gph * 4 + (e & 3);
-          if (krow > qrow) s[e] = -INFINITY;
+          const int krow = kb + hb * 32 + (e >> 2) * 8 + gph * 4 + (e & 3);
+          if (krow > qrow) s[hb][e] = -INFINITY;
         }
       }
       float mx = -INFINITY;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[hb][e]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const bool up = mx > m_ref + 8.f;
-      if (__any(up)) {
-        const float m_new = up ? mx : m_ref;
-        const float alpha = exp2f(m_ref - m_new);
-        m_ref = m_new;
-        l *= alpha;
+      if (first) {
+        // the first half-block sets the reference max (its first key is
+        // visible to every query, so mx is finite)
+        first = false;
+        m = mx;
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b)
+        for (int e = 0; e < 16; ++e) { s[0][e] -= mx; s[1][e] -= mx; }
+      } else {
+        const bool up = mx > 8.f;
+        if (__any(up)) {
+          const float dlt = up ? mx : 0.f;
+          const float alpha = __builtin_amdgcn_exp2f(-dlt);
+          m += dlt;
+          l *= alpha;
 #pragma unroll
-          for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+          for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            s[hb][e] -= dlt;
+            if (hb == 0) s[1][e] -= dlt;
+          }
+        }
       }
-      float rs = 0.f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const float p = exp2f(s[e] - m_ref);
-        s[e] = p;
-        rs += p;
-      }
-      l += rs + __shfl_xor(rs, 32, 64);
-
-      // O^T += V^T P^T, 16 keys per step; P^T element j of lane l is key
-      // 8*(j/4) + 4*(l/32) + j%4 of the step, matching the V^T fragment below
+      // probabilities in bf16 (the PV operand); the row sum uses the same
+      // rounded values
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         bf16x8 pf;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pf[j] = (__bf16)s[hf * 8 + j];
-        const int kbase = kb2 * 32 + hf * 16 + gph * 4;
+        for (int j = 0; j < 8; ++j) pf[j] = (__bf16)__builtin_amdgcn_exp2f(s[hb][hf * 8 + j]);
+        float rs = 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const bf16x2 pr = {pf[2 * j], pf[2 * j + 1]};
+          rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+        }
+        l += rs + __shfl_xor(rs, 32, 64);
+        // O^T += V^T P^T over 16 keys; P^T element j of lane l is key
+        // 8*(j/4) + 4*(l/32) + j%4 of the step, matching the V^T fragment
+        const int kbase = hb * 32 + hf * 16 + gph * 4;
 #pragma unroll
         for (int b = 0; b < D / 32; ++b) {
           const uint16_t *vr = Vt + (b * 32 + qi) * VLD + kbase;
@@ -220,15 +261,8 @@ __global__ __launch_bounds__(64 * W, (W == 5 || W == 6) ? SRP_ATTN_OCC : 2) void
           acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[b], 0, 0, 0);
         }
       }
-      if (kBK == 64 && more) {
-        if (kb2 == 0) kstore(st ^ 1);
-        else vstore(st ^ 1);
-      }
     }
-    if (kBK == 32 && more) {
-      kstore(st ^ 1);
-      vstore(st ^ 1);
-    }
+    if (more) store_next(st ^ 1);
     __syncthreads();
   }
 
@@ -239,10 +273,10 @@ __global__ __launch_bounds__(64 * W, (W == 5 || W == 6) ? SRP_ATTN_OCC : 2) void
     for (int b = 0; b < D / 32; ++b)
 #pragma unroll
       for (int e4 = 0; e4 < 4; ++e4) {
-        float v[4];
+        bf16x4 v;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = acc[b][e4 * 4 + i] * inv;
-        st4(op + b * 32 + e4 * 8 + gph * 4, v);
+        for (int i = 0; i < 4; ++i) v[i] = (__bf16)(acc[b][e4 * 4 + i] * inv);
+        *reinterpret_cast<bf16x4 *>(op + b * 32 + e4 * 8 + gph * 4) = v;
       }
   }
 }
