@@ -257,6 +257,8 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   marks.mark(3);
   // 5. sel_idx and the scatter of fresh K/V into the cache
   SRP_HIP(launch_compact_scatter(sa, w, d.dtype, kvd, sel_idx, sel_offsets, k_cache, v_cache, s));
+  if (d.dtype == SRP_BF16 && T > 0)
+    SRP_HIP(launch_v_transpose(T, d.n_kv_heads, d.head_dim, v_cache, w.vt, vt_stride(T), s));
   marks.mark(4);
   // 6. Q projection of the selected rows
   GemmArgs gq = g;
@@ -284,6 +286,9 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   aa.max_tiles = max_attn_tiles(T, b.n_req);
   aa.k_cache = k_cache;
   aa.v_cache = v_cache;
+  aa.vt = w.vt;
+  aa.vt_stride = vt_stride(T);
+  aa.total_rows = T;
   aa.out = attn_out;
   if (T > 0) SRP_HIP(launch_attention(aa, s));
   marks.mark(6);

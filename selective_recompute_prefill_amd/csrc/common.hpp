@@ -164,6 +164,7 @@ struct Workspace {
   int32_t *sel_cnt;    // [n_req]
   int32_t *sel_ent;    // [T] compact: R entry of each selected row
   void *q;             // [T][qdim] roped queries of the selected rows
+  void *vt;            // bf16: [nkv][d][vt_stride] fused V transposed for attention
   int32_t *tiles;      // [3 * max_tiles] attention tiles (first sel, count, req)
   int32_t *ctr;        // [16] device counters (see kCtr*)
   size_t bytes;
@@ -176,6 +177,9 @@ inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline int blocks_per_req(int max_req_rows) { return (max_req_rows + 1023) / 1024 > 0 ? (max_req_rows + 1023) / 1024 : 1; }
 inline int max_attn_tiles(int T, int n_req) { return T / kQT + n_req + 1; }
+// Row stride of the transposed V copy: T rounded up to 64 plus one zeroed tile, so
+// a key tile that starts inside the batch never reads past the copy.
+inline int vt_stride(int T) { return (T + 63) / 64 * 64 + 64; }
 
 // Lays the workspace out from `base` (nullptr: just measure).
 inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base) {
@@ -211,6 +215,7 @@ inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base) {
   w.sel_cnt = (int32_t *)take(nr * 4);
   w.sel_ent = (int32_t *)take(T * 4);
   w.q = take(T * qd * es);
+  w.vt = d.dtype == SRP_BF16 ? take((size_t)d.n_kv_heads * d.head_dim * vt_stride(b.total_rows) * 2) : nullptr;
   w.tiles = (int32_t *)take((size_t)3 * max_attn_tiles((int)T, (int)nr) * 4);
   w.ctr = (int32_t *)take(16 * 4);
   w.bytes = off;

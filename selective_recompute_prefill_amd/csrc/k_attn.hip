@@ -37,19 +37,58 @@ __device__ __forceinline__ void static_for(F &&f) {
 // waves (2 per SIMD) share each K/V tile.
 __host__ __device__ constexpr int attn_subtiles(int G) { return G >= 5 ? 1 : (G == 3 ? 2 : 8 / G); }
 
-constexpr int kBK = 64;  // keys per LDS stage
+constexpr int kBK = 64;      // keys per LDS stage
+constexpr int kStages = 3;   // LDS ring depth: tiles are fetched two blocks ahead (slots st0..st2)
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One wave-wide direct-to-LDS copy: lane l's 16 bytes at src land at dst + 16 l
+// (dst wave-uniform). Issued as inline asm so the compiler inserts no waits for
+// it; the ring below waits for its copies explicitly (vmcnt) before a barrier.
+// M0 is written here and used nowhere else by these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *src, char *dst) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void *)dst;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds_addr)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt with only the vector-memory counter constrained to <= n.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 
 template <int D, int W>
-__global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnArgs a) {
-  constexpr int KLD = D + 8;    // K tile row stride (elements, 16-byte padded rows)
-  constexpr int VLD = kBK + 8;  // V^T tile row stride
-  constexpr int KSZ = kBK * KLD, VSZ = D * VLD;
-  constexpr int NT = 64 * W;
-  constexpr int KCH = kBK * (D / 8);        // 16-byte chunks of a K tile
-  constexpr int VCH = (kBK / 2) * (D / 8);  // (key pair, 8-wide d chunk) items of a V tile
-  constexpr int KIT = (KCH + NT - 1) / NT, VIT = (VCH + NT - 1) / NT;
-  __shared__ __align__(16) uint16_t lds[2 * (KSZ + VSZ)];
-  __shared__ uint4 qlds[W * (D / 16) * 64];  // each lane's Q fragments, in fragment order
+__global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(AttnArgs a) {
+  static_assert(W >= 4, "four loader waves");
+  // K tile: 64 rows of D bf16 (D*2 bytes), 16-byte chunks XOR-swizzled by row.
+  // V^T tile: D rows of 64 keys (128 bytes), chunks XOR-swizzled by row.
+  constexpr int KT = kBK * D * 2, VT = D * kBK * 2, STAGE = KT + VT;
+  constexpr int KCH = D / 8;              // chunks per K row
+  constexpr int KROWS = 64 / KCH;         // K rows per wave copy
+  constexpr int KJ = kBK / KROWS / 4;     // K copies per loader wave per tile
+  constexpr int VJ = D / 8 / 4;           // V^T copies per loader wave per tile (8 rows each)
+  constexpr int LOADS = KJ + VJ;
+  // three ring slots as separate LDS objects: every access below names its slot
+  // at compile time, so a read of one slot never waits on copies into another
+  __shared__ __align__(16) char st0[STAGE];
+  __shared__ __align__(16) char st1[STAGE];
+  __shared__ __align__(16) char st2[STAGE];
+  __shared__ u32x4 qlds[W * (D / 16) * 64];  // each lane's Q fragments, in fragment order
+  auto slot_ptr = [&](auto I) __attribute__((always_inline)) -> char * {
+    if constexpr (decltype(I)::value == 0) return st0;
+    else if constexpr (decltype(I)::value == 1) return st1;
+    else return st2;
+  };
 
   const int n_tiles = *a.n_tiles;
   const int slot = blockIdx.x / a.nkv, g = blockIdx.x - slot * a.nkv;
@@ -69,93 +108,51 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnArgs a) {
   const int qidx = qs * 32 + qi;
   const bool qvalid = qidx < nq;
   const int qrow = qvalid ? a.sel_idx[q0 + qidx] : last_row;
-  const int kvd = a.nkv * D;
-  const size_t row_bytes = (size_t)kvd * 2;
+  const size_t row_bytes = (size_t)a.nkv * D * 2;
   const char *Kg = (const char *)a.k_cache + (size_t)g * D * 2;
-  const char *Vg = (const char *)a.v_cache + (size_t)g * D * 2;
+  const char *Vg = (const char *)a.vt + (size_t)g * D * a.vt_stride * 2;
+  const size_t vrow_bytes = (size_t)a.vt_stride * 2;
 
-  // Loader: thread chunk i covers K chunk c = tid + NT*i, i.e. key tid/(D/8) +
-  // i*NT/(D/8) at d chunk tid%(D/8), and V item c, i.e. key pair tid%32 at d chunk
-  // tid/32 + i*NT/32. NT is a multiple of both widths, so each offset is one
-  // per-thread constant plus a uniform step, and whether chunk i exists is uniform
-  // per wave (KCH, VCH and NT are multiples of 64).
-  constexpr int KSTEP = NT / (D / 8);  // keys per K chunk step
-  constexpr int VSTEP = NT / (kBK / 2);  // d chunks per V item step
-  const int kkey0 = tid / (D / 8), kdc = tid % (D / 8);
-  const int vkp = tid % (kBK / 2), vdc0 = tid / (kBK / 2);
-  const uint32_t koff0 = (uint32_t)(kkey0 * row_bytes + kdc * 16);
-  const uint32_t voff0 = (uint32_t)(2 * vkp * row_bytes + vdc0 * 16);
-  u32x4 rk[KIT], rv0[VIT], rv1[VIT];
-  auto load_next = [&](int kb) __attribute__((always_inline)) {
-    const char *kbase = Kg + (size_t)kb * row_bytes, *vbase = Vg + (size_t)kb * row_bytes;
-    if (kb + kBK <= key_end) {
-      static_for<KIT>([&](auto I) __attribute__((always_inline)) {
-        constexpr int i = decltype(I)::value;
-        if (w * 64 + NT * i < KCH)
-          rk[i] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)i * KSTEP * row_bytes + koff0);
-      });
-      static_for<VIT>([&](auto I) __attribute__((always_inline)) {
-        constexpr int i = decltype(I)::value;
-        if (w * 64 + NT * i < VCH) {
-          const char *p = vbase + (size_t)i * VSTEP * 16 + voff0;
-          rv0[i] = *reinterpret_cast<const u32x4 *>(p);
-          rv1[i] = *reinterpret_cast<const u32x4 *>(p + row_bytes);
+  // Loader waves 0-3 copy K rows KROWS*i.. (i = w + 4j) and V^T rows 8i.. per tile;
+  // each lane's source offset inside a copy is a constant (the swizzle term only
+  // depends on the lane for these row groups).
+  const int k_lrow = lane / KCH, k_logical = (lane % KCH) ^ ((KROWS * w + k_lrow) & (KCH - 1));
+  const uint32_t k_lane_off = (uint32_t)(k_lrow * row_bytes + k_logical * 16);
+  const int v_lrow = lane >> 3, v_logical = (lane & 7) ^ (v_lrow & 7);
+  const uint32_t v_lane_off = (uint32_t)(v_lrow * vrow_bytes + v_logical * 16);
+  auto issue = [&](auto SLOT, int blk) __attribute__((always_inline)) {
+    const int kb = key_start + blk * kBK;
+    char *st = slot_ptr(SLOT);
+    if (w < 4) {
+      const bool partial = kb + kBK > key_end;
+      static_for<KJ>([&](auto J) __attribute__((always_inline)) {
+        const int i = w + 4 * decltype(J)::value;
+        const char *src;
+        if (!partial) {
+          src = Kg + (size_t)(kb + KROWS * i) * row_bytes + k_lane_off;
+        } else {
+          // rows past key_end are clamped to the last valid row; such keys come
+          // after every query of the tile and are masked
+          const int row = min(kb + KROWS * i + k_lrow, key_end - 1);
+          src = Kg + (size_t)row * row_bytes + k_logical * 16;
         }
+        dma16(src, st + i * 1024);
       });
-    } else {
-      // last, partial tile: rows past key_end are clamped to the last valid row;
-      // every such key lies after every query of the tile and is masked
-      const int lastk = key_end - 1 - kb;
-      static_for<KIT>([&](auto I) __attribute__((always_inline)) {
-        constexpr int i = decltype(I)::value;
-        if (w * 64 + NT * i < KCH) {
-          const int key = min(kkey0 + i * KSTEP, lastk);
-          rk[i] = *reinterpret_cast<const u32x4 *>(kbase + (size_t)key * row_bytes + kdc * 16);
-        }
-      });
-      static_for<VIT>([&](auto I) __attribute__((always_inline)) {
-        constexpr int i = decltype(I)::value;
-        if (w * 64 + NT * i < VCH) {
-          const char *p = vbase + (size_t)(vdc0 + i * VSTEP) * 16;
-          rv0[i] = *reinterpret_cast<const u32x4 *>(p + (size_t)min(2 * vkp, lastk) * row_bytes);
-          rv1[i] = *reinterpret_cast<const u32x4 *>(p + (size_t)min(2 * vkp + 1, lastk) * row_bytes);
-        }
+      static_for<VJ>([&](auto J) __attribute__((always_inline)) {
+        const int i = w + 4 * decltype(J)::value;
+        dma16(Vg + (size_t)(8 * i) * vrow_bytes + (size_t)kb * 2 + v_lane_off, st + KT + i * 1024);
       });
     }
-  };
-  auto store_next = [&](int st) __attribute__((always_inline)) {
-    uint16_t *Ks = lds + st * (KSZ + VSZ), *Vt = Ks + KSZ;
-    static_for<KIT>([&](auto I) __attribute__((always_inline)) {
-      constexpr int i = decltype(I)::value;
-      if (w * 64 + NT * i < KCH)
-        *reinterpret_cast<u32x4 *>(Ks + (kkey0 + i * KSTEP) * KLD + kdc * 8) = rk[i];
-    });
-    // V transposed: word j of two keys -> d rows 2j (low halves), 2j+1 (high halves)
-    static_for<VIT>([&](auto I) __attribute__((always_inline)) {
-      constexpr int i = decltype(I)::value;
-      if (w * 64 + NT * i < VCH) {
-        uint16_t *vt = Vt + (vdc0 + i * VSTEP) * 8 * VLD + 2 * vkp;
-        const u32x4 a0 = rv0[i], a1 = rv1[i];
-        *reinterpret_cast<uint32_t *>(vt + 0 * VLD) = __builtin_amdgcn_perm(a1.x, a0.x, 0x05040100u);
-        *reinterpret_cast<uint32_t *>(vt + 1 * VLD) = __builtin_amdgcn_perm(a1.x, a0.x, 0x07060302u);
-        *reinterpret_cast<uint32_t *>(vt + 2 * VLD) = __builtin_amdgcn_perm(a1.y, a0.y, 0x05040100u);
-        *reinterpret_cast<uint32_t *>(vt + 3 * VLD) = __builtin_amdgcn_perm(a1.y, a0.y, 0x07060302u);
-        *reinterpret_cast<uint32_t *>(vt + 4 * VLD) = __builtin_amdgcn_perm(a1.z, a0.z, 0x05040100u);
-        *reinterpret_cast<uint32_t *>(vt + 5 * VLD) = __builtin_amdgcn_perm(a1.z, a0.z, 0x07060302u);
-        *reinterpret_cast<uint32_t *>(vt + 6 * VLD) = __builtin_amdgcn_perm(a1.w, a0.w, 0x05040100u);
-        *reinterpret_cast<uint32_t *>(vt + 7 * VLD) = __builtin_amdgcn_perm(a1.w, a0.w, 0x07060302u);
-      }
-    });
   };
 
   // Q fragments (B operand of S^T = K Q^T): lane holds query qi, d range
   // ks*16 + gph*8 .. +8; parked in LDS to keep registers for the accumulators
-  uint4 *qmine = qlds + w * (D / 16) * 64 + lane;
+  u32x4 *qmine = qlds + w * (D / 16) * 64 + lane;
   {
     const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(q0 + qidx) * a.nh + h) * D + gph * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      qmine[ks * 64] = qvalid ? *reinterpret_cast<const uint4 *>(qp + ks * 16) : make_uint4(0, 0, 0, 0);
+      qmine[ks * 64] = qvalid ? *reinterpret_cast<const u32x4 *>(qp + ks * 16) : u32x4{0, 0, 0, 0};
   }
   floatx16 acc[D / 32];
 #pragma unroll
@@ -170,15 +167,25 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnArgs a) {
   bool first = true;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  load_next(key_start);
-  store_next(0);
-  __syncthreads();
-  for (int blk = 0; blk < nblk; ++blk) {
+  __syncthreads();  // Q fragments visible before any copy is in flight
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  issue(I0{}, 0);
+  if (nblk > 1) issue(I1{}, 1);
+  auto step = [&](auto SLOT, int blk) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    // this tile's copies are done once at most the next tile's are outstanding;
+    // every loader wave waits for its own copies, then the raw barrier (no
+    // full memory fence, which would drain the prefetches) publishes the slot
+    if (blk + 1 < nblk) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+    // the slot of tile blk+2 was last read in iteration blk-1, which every wave
+    // finished before the barrier above
+    if (blk + 2 < nblk) issue(std::integral_constant<int, (sl + 2) % 3>{}, blk + 2);
     const int kb = key_start + blk * kBK;
-    const int st = blk & 1;
-    const bool more = blk + 1 < nblk;
-    const uint16_t *Ks = lds + st * (KSZ + VSZ), *Vt = Ks + KSZ;
-    if (more) load_next(kb + kBK);
+    const char *Ks = slot_ptr(SLOT), *Vs = Ks + KT;
 
     // S^T[key][query] - m for both 32-key halves, two independent MFMA chains
     floatx16 s[2];
@@ -187,11 +194,12 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnArgs a) {
     for (int e = 0; e < 16; ++e) { s[0][e] = c0; s[1][e] = c0; }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      uint4 qt = qmine[ks * 64];
-      const bf16x8 qf = *reinterpret_cast<bf16x8 *>(&qt);
+      const bf16x8 qf = __builtin_bit_cast(bf16x8, qmine[ks * 64]);
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + (hb * 32 + qi) * KLD + ks * 16 + gph * 8);
+        const int row = hb * 32 + qi;
+        const int phys = (2 * ks + gph) ^ (row & (KCH - 1));
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + row * (D * 2) + phys * 16);
         s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, s[hb], 0, 0, 0);
       }
     }
@@ -249,21 +257,25 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnArgs a) {
         }
         l += rs + __shfl_xor(rs, 32, 64);
         // O^T += V^T P^T over 16 keys; P^T element j of lane l is key
-        // 8*(j/4) + 4*(l/32) + j%4 of the step, matching the V^T fragment
-        const int kbase = hb * 32 + hf * 16 + gph * 4;
+        // 8*(j/4) + 4*(l/32) + j%4 of the step, i.e. 4 keys in 16-byte chunk c
+        // and 4 in chunk c+1, at byte 8*(l/32) of each
+        const int c = hb * 4 + hf * 2;
 #pragma unroll
         for (int b = 0; b < D / 32; ++b) {
-          const uint16_t *vr = Vt + (b * 32 + qi) * VLD + kbase;
-          uint2 lo = *reinterpret_cast<const uint2 *>(vr);
-          uint2 hi = *reinterpret_cast<const uint2 *>(vr + 8);
-          uint4 vv = make_uint4(lo.x, lo.y, hi.x, hi.y);
-          const bf16x8 vf = *reinterpret_cast<bf16x8 *>(&vv);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[b], 0, 0, 0);
+          const int drow = b * 32 + qi;
+          const char *vr = Vs + drow * 128 + gph * 8;
+          const uint2 lo = *reinterpret_cast<const uint2 *>(vr + ((c ^ (drow & 7)) * 16));
+          const uint2 hi = *reinterpret_cast<const uint2 *>(vr + (((c + 1) ^ (drow & 7)) * 16));
+          const u32x4 vv = {lo.x, lo.y, hi.x, hi.y};
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[b], 0, 0, 0);
         }
       }
     }
-    if (more) store_next(st ^ 1);
-    __syncthreads();
+  };
+  for (int b0 = 0; b0 < nblk; b0 += 3) {
+    step(I0{}, b0);
+    if (b0 + 1 < nblk) step(I1{}, b0 + 1);
+    if (b0 + 2 < nblk) step(I2{}, b0 + 2);
   }
 
   if (qvalid) {
@@ -279,6 +291,41 @@ __global__ __launch_bounds__(64 * W, 2) void attn_bf16_kernel(AttnArgs a) {
         *reinterpret_cast<bf16x4 *>(op + b * 32 + e4 * 8 + gph * 4) = v;
       }
   }
+}
+
+// V transposed for the attention's DMA loads: block (64-row tile, KV head).
+__global__ __launch_bounds__(256) void v_transpose_kernel(int T, int D, int nkv, const uint16_t *v,
+                                                         uint16_t *vt, int vts) {
+  __shared__ uint16_t tile[128][64 + 2];
+  const int r0 = blockIdx.x * 64, g = blockIdx.y, tid = threadIdx.x;
+  const int kvd = nkv * D, dch = D / 8;
+  for (int c = tid; c < 64 * dch; c += 256) {
+    const int key = c / dch, dc = c - key * dch;
+    const int row = r0 + key;
+    u32x4 x = {0, 0, 0, 0};
+    if (row < T) x = *reinterpret_cast<const u32x4 *>(v + (size_t)row * kvd + g * D + dc * 8);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[dc * 8 + 2 * i][key] = (uint16_t)(x[i] & 0xffffu);
+      tile[dc * 8 + 2 * i + 1][key] = (uint16_t)(x[i] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < D * 8; c += 256) {
+    const int dd = c >> 3, kc = c & 7;
+    u32x4 y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      y[i] = (uint32_t)tile[dd][kc * 8 + 2 * i] | ((uint32_t)tile[dd][kc * 8 + 2 * i + 1] << 16);
+    *reinterpret_cast<u32x4 *>(vt + ((size_t)g * D + dd) * vts + r0 + kc * 8) = y;
+  }
+}
+
+hipError_t launch_v_transpose(int T, int nkv, int d, const void *v_cache, void *vt, int vt_stride,
+                              hipStream_t s) {
+  hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)(vt_stride / 64), (unsigned)nkv), dim3(256),
+                     0, s, T, d, nkv, (const uint16_t *)v_cache, (uint16_t *)vt, vt_stride);
+  return hipGetLastError();
 }
 
 // fp32 variant: one wave per head, one query at a time, one key per lane.

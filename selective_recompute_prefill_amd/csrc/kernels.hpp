@@ -76,9 +76,15 @@ struct AttnArgs {
   const int32_t *n_tiles;  // device
   int max_tiles;
   const void *k_cache, *v_cache;
+  const void *vt;          // bf16: V transposed, [nkv][d][vt_stride]
+  int vt_stride;
+  int total_rows;
   void *out;               // [n_sel][nh][d]
 };
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
+// bf16: vt[g][i][j] = v_cache[j][g][i] for j < T, zero for T <= j < vt_stride.
+hipError_t launch_v_transpose(int T, int nkv, int d, const void *v_cache, void *vt, int vt_stride,
+                              hipStream_t s);
 // Selected rows per attention tile for this shape (a multiple of 32).
 int attn_tile_rows(int dtype, int nh, int nkv);
 
