@@ -143,6 +143,36 @@ __device__ __forceinline__ void rope4(float a[4], float b[4], const RopeTable &t
 }
 
 // ------------------------------------------------------------------------- //
+// direct-to-LDS copies (gfx950 global_load_lds_dwordx4)
+// ------------------------------------------------------------------------- //
+typedef __attribute__((address_space(3))) void lds_void;
+
+// One wave-wide direct-to-LDS copy: lane l's 16 bytes at src land at dst + 16 l
+// (dst wave-uniform). Issued as inline asm so the compiler inserts no waits for
+// it; the ring below waits for its copies explicitly (vmcnt) before a barrier.
+// M0 is written here and used nowhere else by these kernels.
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"
+__device__ __forceinline__ void dma16(const void *src, char *dst) {
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void *)dst;
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off"
+      :
+      : "v"(src), "s"(lds_addr)
+      : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
+// s_waitcnt with only the vector-memory counter constrained to <= n.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+// ------------------------------------------------------------------------- //
 // workspace carve-up
 // ------------------------------------------------------------------------- //
 struct Workspace {

@@ -110,26 +110,38 @@ struct TileIter {
 
 // ------------------------------------------------------------------------- //
 // bf16 MFMA kernel: 128x128 tile, BK 64, 4 waves (2x2), wave tile 64x64 made of
-// 2x2 blocks of 32x32x16 MFMA.
+// 2x2 blocks of 32x32x16 MFMA. Operand tiles stream into an LDS ring with
+// direct-to-LDS copies (no staging registers): copy i of a tile moves rows
+// 8i..8i+7 (128 bytes each); 16-byte chunks are XOR-swizzled by row so the
+// fragment reads of 32 consecutive rows spread over all banks.
 // ------------------------------------------------------------------------- //
-constexpr int kBM16 = 128, kBK16 = 64, kLDA16 = kBK16 + 8;  // 144-byte LDS rows
-constexpr int kStage16 = kBM16 * kLDA16;                    // elements per operand stage
+#ifndef SRP_GEMM_STAGES
+#define SRP_GEMM_STAGES 2
+#endif
+constexpr int kBM16 = 128, kBK16 = 64;
+constexpr int kGStages = SRP_GEMM_STAGES;
+constexpr int kGTile = kBM16 * kBK16 * 2;  // bytes of one operand tile (16 KB)
+constexpr int kGStage = 2 * kGTile;         // A tile then B tile
 constexpr int kLDC = kBN + 4;
+constexpr int kGSmem = kGStages * kGStage > kBM16 * kLDC * 4 ? kGStages * kGStage : kBM16 * kLDC * 4;
 
 template <int MODE>
-__global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __align__(16) uint16_t smem[4 * kStage16];  // A0 A1 B0 B1 (73,728 B)
-  uint16_t *As = smem, *Bs = smem + 2 * kStage16;
-  float *Cs = reinterpret_cast<float *>(smem);           // 128 x 132 fp32 (67,584 B)
+__global__ __launch_bounds__(256, kGStages >= 3 ? 1 : 2) void gemm_bf16_kernel(GemmArgs g) {
+  __shared__ __align__(16) char smem[kGSmem];
+  float *Cs = reinterpret_cast<float *>(smem);  // epilogue staging, 128 x 132 fp32
 
   const int M = g.M_dev ? *g.M_dev : g.M_host;
   const int K = g.K, N = g.N;
   const int mt_n = (M + kBM16 - 1) / kBM16, nt_n = (N + kBN - 1) / kBN;
   const TileIter ti(mt_n * nt_n);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w >> 1, wn = w & 1;
-  const uint16_t *A = (const uint16_t *)g.A, *B = (const uint16_t *)g.B;
+  const char *A = (const char *)g.A, *B = (const char *)g.B;
   const int KT = K / kBK16;
+  const size_t rowb = (size_t)K * 2;
+  // copy layout: lane covers row 8i + lrow, physical chunk lane%8 <- logical chunk lchunk
+  const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lrow & 7);
 
   for (int lt = ti.loc;; lt += ti.per_x) {
     const int tile = ti.tile(lt);
@@ -137,34 +149,24 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
     const int mt = tile / nt_n, nt = tile - mt * nt_n;
     const int m0 = mt * kBM16, n0 = nt * kBN;
 
-    // per-thread global source rows for its 4 A and 4 B chunks (16 B each)
-    const uint16_t *pa[4], *pb[4];
-    int lds_off[4];
+    // wave w copies A rows and B rows of copies i = w + 4j; rows past M or N
+    // read a valid row (their results are never stored)
+    const char *pa[4], *pb[4];
+    const int row0 = g.a_rows ? g.a_rows[m0] : m0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, kc = c & 7;
+    for (int j = 0; j < 4; ++j) {
+      const int r = 8 * (w + 4 * j) + lrow;
       const int m = m0 + r, n = n0 + r;
-      pa[i] = nullptr;
-      if (m < M) {
-        const int row = g.a_rows ? g.a_rows[m] : m;
-        pa[i] = A + (size_t)row * K + kc * 8;
-      }
-      pb[i] = n < N ? B + (size_t)n * K + kc * 8 : nullptr;
-      lds_off[i] = r * kLDA16 + kc * 8;
+      const int row = m < M ? (g.a_rows ? g.a_rows[m] : m) : row0;
+      pa[j] = A + (size_t)row * rowb + lchunk * 16;
+      pb[j] = B + (size_t)(n < N ? n : N - 1) * rowb + lchunk * 16;
     }
-    uint4 ra[4], rb[4];
-    auto gload = [&](int kt) {
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+      char *st = smem + (kt % kGStages) * kGStage;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        ra[i] = pa[i] ? *reinterpret_cast<const uint4 *>(pa[i] + kt * kBK16) : make_uint4(0, 0, 0, 0);
-        rb[i] = pb[i] ? *reinterpret_cast<const uint4 *>(pb[i] + kt * kBK16) : make_uint4(0, 0, 0, 0);
-      }
-    };
-    auto sstore = [&](int st) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        *reinterpret_cast<uint4 *>(As + st * kStage16 + lds_off[i]) = ra[i];
-        *reinterpret_cast<uint4 *>(Bs + st * kStage16 + lds_off[i]) = rb[i];
+      for (int j = 0; j < 4; ++j) {
+        dma16(pa[j] + (size_t)kt * 128, st + (w + 4 * j) * 1024);
+        dma16(pb[j] + (size_t)kt * 128, st + kGTile + (w + 4 * j) * 1024);
       }
     };
 
@@ -176,32 +178,42 @@ __global__ __launch_bounds__(256, 2) void gemm_bf16_kernel(GemmArgs g) {
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
 
-    gload(0);
-    sstore(0);
-    __syncthreads();
-    const int fr = lane & 31, fk = (lane >> 5) * 8;
+#pragma unroll
+    for (int p = 0; p < kGStages - 1; ++p)
+      if (p < KT) issue(p);
+    const int fr = lane & 31, fk = lane >> 5;
     for (int kt = 0; kt < KT; ++kt) {
-      const int st = kt & 1;
-      if (kt + 1 < KT) gload(kt + 1);
-      const uint16_t *as = As + st * kStage16, *bs = Bs + st * kStage16;
+      // this tile's copies are done once at most the later prefetched tiles'
+      // copies (8 per tile per wave) are outstanding
+      const int later = min(KT - 1 - kt, kGStages - 2);
+      if (later >= 2) wait_vmcnt<16>();
+      else if (later == 1) wait_vmcnt<8>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      // the slot of tile kt+S-1 was last read in iteration kt-1
+      if (kt + kGStages - 1 < KT) issue(kt + kGStages - 1);
+      const char *as = smem + (kt % kGStages) * kGStage, *bs = as + kGTile;
 #pragma unroll
       for (int ks = 0; ks < kBK16 / 16; ++ks) {
         bf16x8 af[2], bfr[2];
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          af[i] = *reinterpret_cast<const bf16x8 *>(as + (wm * 64 + i * 32 + fr) * kLDA16 + ks * 16 + fk);
+        for (int i = 0; i < 2; ++i) {
+          const int r = wm * 64 + i * 32 + fr;
+          af[i] = *reinterpret_cast<const bf16x8 *>(as + r * 128 + (((2 * ks + fk) ^ (r & 7)) * 16));
+        }
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + (wn * 64 + j * 32 + fr) * kLDA16 + ks * 16 + fk);
+        for (int j = 0; j < 2; ++j) {
+          const int r = wn * 64 + j * 32 + fr;
+          bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + r * 128 + (((2 * ks + fk) ^ (r & 7)) * 16));
+        }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
 #pragma unroll
           for (int j = 0; j < 2; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
       }
-      if (kt + 1 < KT) sstore(st ^ 1);
-      __syncthreads();
     }
+    __syncthreads();  // every wave is done with the ring before it becomes Cs
     // stage the accumulators: D[row][col], row = 8*(e/4) + 4*(lane/32) + e%4
 #pragma unroll
     for (int i = 0; i < 2; ++i)
@@ -306,8 +318,9 @@ hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
   const int bm = g.dtype == SRP_BF16 ? kBM16 : kBM32;
   const long tiles = (long)((g.M_cap + bm - 1) / bm) * ((g.N + kBN - 1) / kBN);
   if (tiles <= 0) return hipSuccess;
-  // resident work-groups: 256 CUs x 2, rounded to a multiple of the 8 XCDs
-  long grid = tiles < 512 ? tiles : 512;
+  // resident work-groups (256 CUs x work-groups per CU), a multiple of the 8 XCDs
+  const long resident = g.dtype == SRP_BF16 ? 256L * (kGStages >= 3 ? 1 : 2) : 512L;
+  long grid = tiles < resident ? tiles : resident;
   grid = (grid + 7) / 8 * 8;
   const dim3 gr((unsigned)grid), bl(256);
 #define SRP_GEMM_LAUNCH(M)                                               \
