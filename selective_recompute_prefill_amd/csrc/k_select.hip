@@ -301,6 +301,187 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, Workspace w)
 }
 
 // ------------------------------------------------------------------------- //
+// selection with the request resident in LDS (requests of up to kLdsEntries
+// entries): keys and flags are loaded once; after marking, the key storage holds
+// the grouping sequence as 16-bit entry offsets and prefix counts
+// ------------------------------------------------------------------------- //
+constexpr int kLdsEntries = 22528;
+
+__device__ __forceinline__ int radix_digit_pass(const uint32_t *keys, const uint8_t *fl, int n,
+                                                uint32_t prefix, uint32_t pmask, int shift, int nb,
+                                                int need, int *hist, int *sh, int *digit_info,
+                                                int *above_out) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const uint32_t dmask = (uint32_t)nb - 1u;
+  for (int b = tid; b < nb; b += nt) hist[b] = 0;
+  __syncthreads();
+  for (int i = tid; i < n; i += nt) {
+    if (!(fl[i] & kCand)) continue;
+    const uint32_t key = keys[i];
+    if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
+  }
+  __syncthreads();
+  int c[4], s4 = 0;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int dg = nb - 1 - 4 * tid - q;
+    c[q] = dg >= 0 ? hist[dg] : 0;
+    s4 += c[q];
+  }
+  int tot;
+  const int above = block_excl_scan(s4, sh, &tot);
+  if (above < need && above + s4 >= need) {
+    int abv = above, dsel = 0;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (abv + c[q] >= need) { dsel = nb - 1 - 4 * tid - q; break; }
+      abv += c[q];
+    }
+    digit_info[0] = dsel;
+    digit_info[1] = abv;
+  }
+  __syncthreads();
+  *above_out = digit_info[1];
+  const int d = digit_info[0];
+  __syncthreads();
+  return d;
+}
+
+__global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspace w) {
+  __shared__ int sh[17];
+  __shared__ int hist[kHistBins];
+  __shared__ int digit_info[2];
+  __shared__ uint32_t keys_s[kLdsEntries];  // later: seq_ent (u16) | seq_pre (u16)
+  __shared__ uint8_t fl_s[kLdsEntries];
+  __shared__ uint8_t sq_s[kLdsEntries];      // grouping: bit 0 top-k slot, bit 1 passing window
+  const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int *roff = a.cand ? w.roff : a.req_offsets;
+  const int e0 = roff[r], e1 = roff[r + 1], n = e1 - e0;
+
+  int my_cand = 0;
+  for (int i = tid; i < n; i += nt) {
+    const uint8_t f = w.eflag[e0 + i];
+    fl_s[i] = f;
+    keys_s[i] = (f & kCand) ? w.keys[e0 + i] : 0u;
+    my_cand += (f & kCand) ? 1 : 0;
+  }
+  int my_ctx = 0;
+  if (a.cand) {
+    for (int j = a.req_offsets[r] + tid; j < a.req_offsets[r + 1]; j += nt) my_ctx += w.row_delta[j] != kFresh;
+  } else {
+    my_ctx = my_cand;  // every cached row of the request is a candidate
+  }
+  const int n_cand = block_sum(my_cand, sh);
+  const int n_ctx = block_sum(my_ctx, sh);
+
+  int k;
+  if (a.mode == SRP_SEL_GIVEN) {
+    k = n_cand;
+  } else {
+    const double kd = floor(a.ratio * (double)n_ctx + 0.5);
+    k = kd < (double)n_cand ? (int)kd : n_cand;
+  }
+  if (k >= n_cand) {
+    for (int i = tid; i < n; i += nt)
+      if (fl_s[i] & kCand) fl_s[i] |= kTop;
+  } else if (k > 0) {
+    uint32_t prefix = 0, pmask = 0;
+    int need = k;
+    const int shifts[3] = {20, 8, 0}, widths[3] = {12, 12, 8};
+    for (int pass = 0; pass < 3; ++pass) {
+      int above;
+      const int d = radix_digit_pass(keys_s, fl_s, n, prefix, pmask, shifts[pass], 1 << widths[pass],
+                                     need, hist, sh, digit_info, &above);
+      need -= above;
+      prefix |= (uint32_t)d << shifts[pass];
+      pmask |= ((1u << widths[pass]) - 1u) << shifts[pass];
+    }
+    int my_eq = 0;
+    for (int i = tid; i < n; i += nt) {
+      if (!(fl_s[i] & kCand)) continue;
+      if (keys_s[i] > prefix) fl_s[i] |= kTop;
+      else if (keys_s[i] == prefix) ++my_eq;
+    }
+    const int eq_tot = block_sum(my_eq, sh);
+    if (eq_tot == need) {
+      for (int i = tid; i < n; i += nt)
+        if ((fl_s[i] & kCand) && keys_s[i] == prefix) fl_s[i] |= kTop;
+    } else {
+      // several equal keys at the threshold: the first `need` in row order
+      int lo, hi;
+      my_segment(n, lo, hi);
+      int c = 0;
+      for (int i = lo; i < hi; ++i) c += ((fl_s[i] & kCand) && keys_s[i] == prefix) ? 1 : 0;
+      int t;
+      int rank = block_excl_scan(c, sh, &t);
+      for (int i = lo; i < hi; ++i)
+        if ((fl_s[i] & kCand) && keys_s[i] == prefix) {
+          if (rank < need) fl_s[i] |= kTop;
+          ++rank;
+        }
+    }
+  }
+  __syncthreads();
+
+  if (a.window > 0) {
+    const int win = a.window;
+    uint16_t *seq_ent = reinterpret_cast<uint16_t *>(keys_s);   // [n] slot -> entry offset
+    uint16_t *seq_pre = seq_ent + kLdsEntries;                  // [n] inclusive top count
+    int lo, hi;
+    my_segment(n, lo, hi);
+    int c = 0, tp = 0;
+    for (int i = lo; i < hi; ++i)
+      if (fl_s[i] & kCand) { ++c; tp += (fl_s[i] & kTop) ? 1 : 0; }
+    int n_seq, n_top;
+    int slot = block_excl_scan(c, sh, &n_seq);
+    int run = block_excl_scan(tp, sh, &n_top);
+    for (int i = lo; i < hi; ++i) {
+      const uint8_t f = fl_s[i];
+      if (!(f & kCand)) continue;
+      const int top = (f & kTop) ? 1 : 0;
+      run += top;
+      seq_ent[slot] = (uint16_t)i;
+      seq_pre[slot] = (uint16_t)run;
+      sq_s[slot] = (uint8_t)top;
+      ++slot;
+    }
+    __syncthreads();
+    for (int t = tid; t < n_seq; t += nt) {
+      if ((sq_s[t] & 1) && t + win <= n_seq) {
+        const int cnt = (int)seq_pre[t + win - 1] - (t > 0 ? (int)seq_pre[t - 1] : 0);
+        if (cnt >= a.tau) sq_s[t] |= 2;
+      }
+    }
+    __syncthreads();
+    for (int p = tid; p < n_seq; p += nt) {
+      bool kept = false;
+      const int t0 = p - win + 1 > 0 ? p - win + 1 : 0;
+      for (int t = t0; t <= p; ++t) kept |= (sq_s[t] & 2) != 0;
+      if (kept) fl_s[seq_ent[p]] |= kSel;
+    }
+    __syncthreads();
+  }
+
+  // compact the request's selection (fresh rows included) in row order
+  const uint8_t want = a.window > 0 ? kSel : kTop;
+  int lo, hi;
+  my_segment(n, lo, hi);
+  int c = 0;
+  for (int i = lo; i < hi; ++i) c += ((fl_s[i] & kFreshF) || (fl_s[i] & want)) ? 1 : 0;
+  int total;
+  int p = block_excl_scan(c, sh, &total);
+  for (int i = lo; i < hi; ++i) {
+    if ((fl_s[i] & kFreshF) || (fl_s[i] & want)) {
+      const int e = e0 + i;
+      w.tsel_row[e0 + p] = a.cand ? w.rlist[e] : e;
+      w.tsel_ent[e0 + p] = e;
+      ++p;
+    }
+  }
+  if (tid == 0) w.sel_cnt[r] = total;
+}
+
+// ------------------------------------------------------------------------- //
 // finalize: CSR offsets and the attention tile list (longest first)
 // ------------------------------------------------------------------------- //
 __global__ __launch_bounds__(1024) void finalize_kernel(SelectArgs a, Workspace w, int32_t *sel_offsets) {
@@ -412,6 +593,10 @@ hipError_t launch_select(const SelectArgs &a, const Workspace &w, hipStream_t s)
   int grid = (a.T + 255) / 256;
   grid = grid < 2048 ? (grid > 0 ? grid : 1) : 2048;
   hipLaunchKernelGGL(keys_kernel, dim3(grid), dim3(256), 0, s, a, w);
+  if (a.max_req_rows <= kLdsEntries) {
+    hipLaunchKernelGGL(select_lds_kernel, dim3(a.n_req), dim3(1024), 0, s, a, w);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(select_kernel, dim3(a.n_req), dim3(1024), 0, s, a, w);
   return hipGetLastError();
 }
