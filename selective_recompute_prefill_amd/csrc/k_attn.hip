@@ -1,13 +1,17 @@
 // Gathered-query causal GQA flash attention over the fused cache (gfx950).
 //
-// Work-group = (tile of up to 32 selected rows of one request, KV head g); one
-// wave per query head of the group, so each K/V tile staged in LDS serves all
-// nh/nkv heads that read it. The bf16 kernel computes S^T = K Q^T and
-// O^T = V^T P^T with v_mfma_f32_32x32x16_bf16: in that orientation a lane holds
-// one query's column, so the online-softmax max/sum need only one cross-lane step
-// (lanes l and l^32) and the rescale of O is per lane. The probabilities are
-// reused in registers as the B operand of the PV product, so V is staged in LDS
-// transposed. Causality is by row: positions rise strictly inside a request.
+// bf16: a work-group is (tile of selected rows of one request, KV head g) and
+// eight waves, two per SIMD. Its 256 MFMA columns are (query, head) pairs of the
+// group, query-major: column c is query c / G, head c % G, so every K/V tile
+// staged in LDS serves all G heads that read it and the waves stay balanced for
+// any G <= 8 (G = 5 packs 51 queries x 5 heads). Each wave computes, for its 32
+// columns, S^T = K Q^T and O^T = V^T P^T with v_mfma_f32_32x32x16_bf16: a lane
+// holds one column, so the online-softmax max needs one exchange between lanes
+// l and l+32 and the rescale of O is per lane. The probabilities are reused in
+// registers as the B operand of the PV product; V is staged in LDS transposed,
+// with the keys of every 16-key group stored in the order that operand reads
+// them, so each V fragment is one 16-byte LDS read. Causality is by row:
+// positions rise strictly inside a request.
 #include <type_traits>
 
 #include "kernels.hpp"
@@ -20,8 +24,6 @@ typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-constexpr float kLog2e = 1.4426950408889634f;
-
 // Calls f(integral_constant<int, i>) for i = 0..N-1, so array indices inside f
 // are compile-time constants (register arrays stay in registers).
 template <int N, typename F>
@@ -32,31 +34,36 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-// Waves per work-group: one per (query head of the group, 32-row query
-// sub-tile); groups of fewer than 5 heads take several sub-tiles so that 6-8
-// waves (2 per SIMD) share each K/V tile.
-__host__ __device__ constexpr int attn_subtiles(int G) { return G >= 5 ? 1 : (G == 3 ? 2 : 8 / G); }
+constexpr int kBK = 64;          // keys per LDS stage
+constexpr int kAW = 8;           // waves per work-group (two per SIMD)
+constexpr int kACols = 32 * kAW; // (query, head) columns per work-group
 
-constexpr int kBK = 64;      // keys per LDS stage
-constexpr int kStages = 3;   // LDS ring depth: tiles are fetched two blocks ahead (slots st0..st2)
+// max of x over lanes l and l^32 (v_permlane32_swap: no LDS round trip)
+__device__ __forceinline__ float pair_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __builtin_fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
-template <int D, int W>
-__global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(AttnArgs a) {
-  static_assert(W >= 4, "four loader waves");
+template <int D>
+__global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   // K tile: 64 rows of D bf16 (D*2 bytes), 16-byte chunks XOR-swizzled by row.
   // V^T tile: D rows of 64 keys (128 bytes), chunks XOR-swizzled by row.
   constexpr int KT = kBK * D * 2, VT = D * kBK * 2, STAGE = KT + VT;
-  constexpr int KCH = D / 8;              // chunks per K row
-  constexpr int KROWS = 64 / KCH;         // K rows per wave copy
-  constexpr int KJ = kBK / KROWS / 4;     // K copies per loader wave per tile
-  constexpr int VJ = D / 8 / 4;           // V^T copies per loader wave per tile (8 rows each)
+  constexpr int KCH = D / 8;               // chunks per K row
+  constexpr int KROWS = 64 / KCH;          // K rows per wave copy
+  constexpr int KJ = kBK / KROWS / kAW;    // K copies per wave per tile
+  constexpr int VJ = D / 8 / kAW;          // V^T copies per wave per tile (8 rows each)
   constexpr int LOADS = KJ + VJ;
+  static_assert(KJ >= 1 && VJ >= 1, "every wave copies K and V^T rows");
   // three ring slots as separate LDS objects: every access below names its slot
   // at compile time, so a read of one slot never waits on copies into another
   __shared__ __align__(16) char st0[STAGE];
   __shared__ __align__(16) char st1[STAGE];
   __shared__ __align__(16) char st2[STAGE];
-  __shared__ u32x4 qlds[W * (D / 16) * 64];  // each lane's Q fragments, in fragment order
   auto slot_ptr = [&](auto I) __attribute__((always_inline)) -> char * {
     if constexpr (decltype(I)::value == 0) return st0;
     else if constexpr (decltype(I)::value == 1) return st1;
@@ -68,64 +75,72 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(AttnArgs a) {
   if (slot >= n_tiles) return;
   const int G = a.nh / a.nkv;
   const int q0 = a.tiles[3 * slot], nq = a.tiles[3 * slot + 1], r = a.tiles[3 * slot + 2];
+  // key tiles are aligned to 64 rows (the V^T key order repeats every 16 rows
+  // and the copies stay 128-byte aligned); rows of the first tile before the
+  // request's first row are masked
   const int key_start = a.req_offsets[r];
-  const int first_row = a.sel_idx[q0], last_row = a.sel_idx[q0 + nq - 1];
+  const int key_base = key_start & ~(kBK - 1);
+  const int last_row = a.sel_idx[q0 + nq - 1];
   const int key_end = last_row + 1;
-  const int nblk = (key_end - key_start + kBK - 1) / kBK;
+  const int nblk = (key_end - key_base + kBK - 1) / kBK;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
-  const int hw = w % G, qs = w / G;
-  const int h = g * G + hw;
   const int qi = lane & 31, gph = lane >> 5;
-  const int qidx = qs * 32 + qi;
-  const bool qvalid = qidx < nq;
-  const int qrow = qvalid ? a.sel_idx[q0 + qidx] : last_row;
+  const int col = 32 * w + qi;
+  const int qq = col / G, hh = col - qq * G;
+  const bool cvalid = qq < nq;
+  const int qrow = a.sel_idx[q0 + (cvalid ? qq : nq - 1)];
+  // the wave's first and last query rows (uniform); a wave with no query
+  // columns computes nothing but still copies tiles and meets the barriers
+  const int wq_lo = (32 * w) / G, wq_hi = min(nq - 1, (32 * w + 31) / G);
+  const bool wactive = wq_lo < nq;
+  const int w_first = wactive ? a.sel_idx[q0 + wq_lo] : key_end;
+  const int w_last = wactive ? a.sel_idx[q0 + wq_hi] : key_start - 1;
   const size_t row_bytes = (size_t)a.nkv * D * 2;
   const char *Kg = (const char *)a.k_cache + (size_t)g * D * 2;
   const char *Vg = (const char *)a.vt + (size_t)g * D * a.vt_stride * 2;
   const size_t vrow_bytes = (size_t)a.vt_stride * 2;
 
-  // Loader waves 0-3 copy K rows KROWS*i.. (i = w + 4j) and V^T rows 8i.. per tile;
-  // each lane's source offset inside a copy is a constant (the swizzle term only
+  // Wave w copies K rows KROWS*i.. (i = w + 8j) and V^T rows 8i.. per tile; each
+  // lane's source offset inside a copy is a constant (the swizzle term only
   // depends on the lane for these row groups).
   const int k_lrow = lane / KCH, k_logical = (lane % KCH) ^ ((KROWS * w + k_lrow) & (KCH - 1));
   const uint32_t k_lane_off = (uint32_t)(k_lrow * row_bytes + k_logical * 16);
   const int v_lrow = lane >> 3, v_logical = (lane & 7) ^ (v_lrow & 7);
   const uint32_t v_lane_off = (uint32_t)(v_lrow * vrow_bytes + v_logical * 16);
   auto issue = [&](auto SLOT, int blk) __attribute__((always_inline)) {
-    const int kb = key_start + blk * kBK;
+    const int kb = key_base + blk * kBK;
     char *st = slot_ptr(SLOT);
-    if (w < 4) {
-      const bool partial = kb + kBK > key_end;
-      static_for<KJ>([&](auto J) __attribute__((always_inline)) {
-        const int i = w + 4 * decltype(J)::value;
-        const char *src;
-        if (!partial) {
-          src = Kg + (size_t)(kb + KROWS * i) * row_bytes + k_lane_off;
-        } else {
-          // rows past key_end are clamped to the last valid row; such keys come
-          // after every query of the tile and are masked
-          const int row = min(kb + KROWS * i + k_lrow, key_end - 1);
-          src = Kg + (size_t)row * row_bytes + k_logical * 16;
-        }
-        dma16(src, st + i * 1024);
-      });
-      static_for<VJ>([&](auto J) __attribute__((always_inline)) {
-        const int i = w + 4 * decltype(J)::value;
-        dma16(Vg + (size_t)(8 * i) * vrow_bytes + (size_t)kb * 2 + v_lane_off, st + KT + i * 1024);
-      });
-    }
+    const bool partial = kb + kBK > key_end;
+    static_for<KJ>([&](auto J) __attribute__((always_inline)) {
+      const int i = w + kAW * decltype(J)::value;
+      const char *src;
+      if (!partial) {
+        src = Kg + (size_t)(kb + KROWS * i) * row_bytes + k_lane_off;
+      } else {
+        // rows past key_end are clamped to the last valid row; such keys come
+        // after every query of the tile and are masked
+        const int row = min(kb + KROWS * i + k_lrow, key_end - 1);
+        src = Kg + (size_t)row * row_bytes + k_logical * 16;
+      }
+      dma16(src, st + i * 1024);
+    });
+    static_for<VJ>([&](auto J) __attribute__((always_inline)) {
+      const int i = w + kAW * decltype(J)::value;
+      dma16(Vg + (size_t)(8 * i) * vrow_bytes + (size_t)kb * 2 + v_lane_off, st + KT + i * 1024);
+    });
   };
 
-  // Q fragments (B operand of S^T = K Q^T): lane holds query qi, d range
-  // ks*16 + gph*8 .. +8; parked in LDS to keep registers for the accumulators
-  u32x4 *qmine = qlds + w * (D / 16) * 64 + lane;
+  // Q fragments (B operand of S^T = K Q^T): lane holds its column's query row,
+  // d range ks*16 + gph*8 .. +8, in registers for the whole tile
+  u32x4 qf[D / 16];
   {
-    const uint16_t *qp = (const uint16_t *)a.q + ((size_t)(q0 + qidx) * a.nh + h) * D + gph * 8;
+    const uint16_t *qp =
+        (const uint16_t *)a.q + ((size_t)(q0 + (cvalid ? qq : 0)) * a.nh + g * G + hh) * D + gph * 8;
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks)
-      qmine[ks * 64] = qvalid ? *reinterpret_cast<const u32x4 *>(qp + ks * 16) : u32x4{0, 0, 0, 0};
+      qf[ks] = cvalid ? *reinterpret_cast<const u32x4 *>(qp + ks * 16) : u32x4{0, 0, 0, 0};
   }
   floatx16 acc[D / 32];
 #pragma unroll
@@ -134,13 +149,22 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(AttnArgs a) {
     for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
   // Scores are in base-2 units (queries carry log2(e)/sqrt(d)). The score
   // accumulators start at -m, so they come out of the MFMA already relative to
-  // the reference max m, which is raised only when a half-block's max exceeds
-  // it by more than 8: probabilities stay below 2^8 and rescales are rare.
+  // the reference max m, which is raised only when a tile's max exceeds it by
+  // more than 8: probabilities stay below 2^8 and rescales are rare.
+  // l is this lane's share of the row sum (its keys of each 16-key step); the
+  // two lanes of a column are added at the end.
   float m = 0.f, l = 0.f;
   bool first = true;
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
 
-  __syncthreads();  // Q fragments visible before any copy is in flight
+  // per-lane LDS byte offsets of the K and V^T fragments inside a slot
+  uint32_t koff[D / 16];
+#pragma unroll
+  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = qi * (D * 2) + (((2 * ks + gph) ^ (qi & (KCH - 1))) * 16);
+  uint32_t voff[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) voff[c] = KT + qi * 128 + (((2 * c + gph) ^ (qi & 7)) * 16);
+
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -149,98 +173,89 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(AttnArgs a) {
   auto step = [&](auto SLOT, int blk) __attribute__((always_inline)) {
     constexpr int sl = decltype(SLOT)::value;
     // this tile's copies are done once at most the next tile's are outstanding;
-    // every loader wave waits for its own copies, then the raw barrier (no
-    // full memory fence, which would drain the prefetches) publishes the slot
+    // every wave waits for its own copies, then the raw barrier (no full memory
+    // fence, which would drain the prefetches) publishes the slot
     if (blk + 1 < nblk) wait_vmcnt<LOADS>();
     else wait_vmcnt<0>();
     __builtin_amdgcn_s_barrier();
     // the slot of tile blk+2 was last read in iteration blk-1, which every wave
     // finished before the barrier above
     if (blk + 2 < nblk) issue(std::integral_constant<int, (sl + 2) % 3>{}, blk + 2);
-    const int kb = key_start + blk * kBK;
-    const char *Ks = slot_ptr(SLOT), *Vs = Ks + KT;
+    const int kb = key_base + blk * kBK;
+    if (kb > w_last) return;  // every key of the tile is after the wave's queries
+    const char *St = slot_ptr(SLOT);
 
-    // S^T[key][query] - m for both 32-key halves, two independent MFMA chains
+    // S^T[key][column] - m for both 32-key halves, two independent MFMA chains
     floatx16 s[2];
     const float c0 = first ? 0.f : -m;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { s[0][e] = c0; s[1][e] = c0; }
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
-      const bf16x8 qf = __builtin_bit_cast(bf16x8, qmine[ks * 64]);
+      const bf16x8 q8 = __builtin_bit_cast(bf16x8, qf[ks]);
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb) {
-        const int row = hb * 32 + qi;
-        const int phys = (2 * ks + gph) ^ (row & (KCH - 1));
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(Ks + row * (D * 2) + phys * 16);
-        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf, s[hb], 0, 0, 0);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(St + koff[ks] + hb * 32 * (D * 2));
+        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q8, s[hb], 0, 0, 0);
       }
     }
-    const bool masked = kb + kBK - 1 > first_row;
+    if (kb < key_start || kb + kBK - 1 > w_first) {
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      if (masked) {
+      for (int hb = 0; hb < 2; ++hb)
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
           const int krow = kb + hb * 32 + (e >> 2) * 8 + gph * 4 + (e & 3);
-          if (krow > qrow) s[hb][e] = -INFINITY;
+          if (krow > qrow || krow < key_start) s[hb][e] = -INFINITY;
         }
+    }
+    float mx = __builtin_fmaxf(__builtin_fmaxf(s[0][0], s[0][1]), s[0][2]);
+#pragma unroll
+    for (int e = 3; e < 31; e += 2)
+      mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[e >> 4][e & 15]), s[(e + 1) >> 4][(e + 1) & 15]);
+    mx = pair_max(__builtin_fmaxf(mx, s[1][15]));
+    if (first) {
+      // the first tile sets the reference max (it holds the request's first
+      // row, which every query sees, so mx is finite)
+      first = false;
+      m = mx;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) { s[0][e] -= mx; s[1][e] -= mx; }
+    } else {
+      const bool up = mx > 8.f;
+      if (__any(up)) {
+        const float dlt = up ? mx : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-dlt);
+        m += dlt;
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { s[0][e] -= dlt; s[1][e] -= dlt; }
       }
-      float mx = -INFINITY;
+    }
 #pragma unroll
-      for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[hb][e]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      if (first) {
-        // the first half-block sets the reference max (its first key is
-        // visible to every query, so mx is finite)
-        first = false;
-        m = mx;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) { s[0][e] -= mx; s[1][e] -= mx; }
-      } else {
-        const bool up = mx > 8.f;
-        if (__any(up)) {
-          const float dlt = up ? mx : 0.f;
-          const float alpha = __builtin_amdgcn_exp2f(-dlt);
-          m += dlt;
-          l *= alpha;
-#pragma unroll
-          for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) {
-            s[hb][e] -= dlt;
-            if (hb == 0) s[1][e] -= dlt;
-          }
-        }
-      }
+    for (int hb = 0; hb < 2; ++hb) {
       // probabilities in bf16 (the PV operand); the row sum uses the same
-      // rounded values
+      // rounded values. Elements 8hf..8hf+7 of the half are keys
+      // 16c + 8(j/4) + 4(l/32) + j%4 of k-step c = 2hb + hf: the order in which
+      // the V^T copy stores each 16-key group
 #pragma unroll
       for (int hf = 0; hf < 2; ++hf) {
         bf16x8 pf;
 #pragma unroll
         for (int j = 0; j < 8; ++j) pf[j] = (__bf16)__builtin_amdgcn_exp2f(s[hb][hf * 8 + j]);
-        float rs = 0.f;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const bf16x2 pr = {pf[2 * j], pf[2 * j + 1]};
-          rs = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, rs, false);
+          l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
         }
-        l += rs + __shfl_xor(rs, 32, 64);
-        // O^T += V^T P^T over 16 keys; P^T element j of lane l is key
-        // 8*(j/4) + 4*(l/32) + j%4 of the step, i.e. 4 keys in 16-byte chunk c
-        // and 4 in chunk c+1, at byte 8*(l/32) of each
-        const int c = hb * 4 + hf * 2;
+        const int c = hb * 2 + hf;
 #pragma unroll
         for (int b = 0; b < D / 32; ++b) {
-          const int drow = b * 32 + qi;
-          const char *vr = Vs + drow * 128 + gph * 8;
-          const uint2 lo = *reinterpret_cast<const uint2 *>(vr + ((c ^ (drow & 7)) * 16));
-          const uint2 hi = *reinterpret_cast<const uint2 *>(vr + (((c + 1) ^ (drow & 7)) * 16));
-          const u32x4 vv = {lo.x, lo.y, hi.x, hi.y};
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf, acc[b], 0, 0, 0);
+          const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(St + voff[c] + b * 32 * 128);
+          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[b], 0, 0, 0);
         }
       }
     }
@@ -251,9 +266,10 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(AttnArgs a) {
     if (b0 + 2 < nblk) step(I2{}, b0 + 2);
   }
 
-  if (qvalid) {
-    const float inv = 1.f / l;
-    uint16_t *op = (uint16_t *)a.out + ((size_t)(q0 + qidx) * a.nh + h) * D;
+  const float lt = pair_sum(l);
+  if (cvalid) {
+    const float inv = 1.f / lt;
+    uint16_t *op = (uint16_t *)a.out + ((size_t)(q0 + qq) * a.nh + g * G + hh) * D;
 #pragma unroll
     for (int b = 0; b < D / 32; ++b)
 #pragma unroll
@@ -267,6 +283,8 @@ __global__ __launch_bounds__(64 * W, 1) void attn_bf16_kernel(AttnArgs a) {
 }
 
 // V transposed for the attention's DMA loads: block (64-row tile, KV head).
+// Inside every 16-key group the keys are stored in the order 0-3, 8-11, 4-7,
+// 12-15 (the PV operand's lane order); keys at or past T are zero.
 __global__ __launch_bounds__(256) void v_transpose_kernel(int T, int D, int nkv, const uint16_t *v,
                                                          uint16_t *vt, int vts) {
   __shared__ uint16_t tile[128][64 + 2];
@@ -277,10 +295,12 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(int T, int D, int nkv,
     const int row = r0 + key;
     u32x4 x = {0, 0, 0, 0};
     if (row < T) x = *reinterpret_cast<const u32x4 *>(v + (size_t)row * kvd + g * D + dc * 8);
+    // stored position of this key: swap bits 2 and 3 of its index
+    const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      tile[dc * 8 + 2 * i][key] = (uint16_t)(x[i] & 0xffffu);
-      tile[dc * 8 + 2 * i + 1][key] = (uint16_t)(x[i] >> 16);
+      tile[dc * 8 + 2 * i][pos] = (uint16_t)(x[i] & 0xffffu);
+      tile[dc * 8 + 2 * i + 1][pos] = (uint16_t)(x[i] >> 16);
     }
   }
   __syncthreads();
@@ -358,27 +378,15 @@ __global__ __launch_bounds__(512) void attn_f32_kernel(AttnArgs a) {
 }
 
 int attn_tile_rows(int dtype, int nh, int nkv) {
-  return dtype == SRP_BF16 ? 32 * attn_subtiles(nh / nkv) : 32;
-}
-
-template <int D>
-static void launch_bf16(const AttnArgs &a, int W, dim3 grid, hipStream_t s) {
-  switch (W) {
-    case 4: hipLaunchKernelGGL((attn_bf16_kernel<D, 4>), grid, dim3(256), 0, s, a); break;
-    case 5: hipLaunchKernelGGL((attn_bf16_kernel<D, 5>), grid, dim3(320), 0, s, a); break;
-    case 6: hipLaunchKernelGGL((attn_bf16_kernel<D, 6>), grid, dim3(384), 0, s, a); break;
-    case 7: hipLaunchKernelGGL((attn_bf16_kernel<D, 7>), grid, dim3(448), 0, s, a); break;
-    default: hipLaunchKernelGGL((attn_bf16_kernel<D, 8>), grid, dim3(512), 0, s, a); break;
-  }
+  return dtype == SRP_BF16 ? kACols / (nh / nkv) : 32;
 }
 
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s) {
   const int G = a.nh / a.nkv;
   const dim3 grid((unsigned)(a.max_tiles * a.nkv));
   if (a.dtype == SRP_BF16) {
-    const int W = G * attn_subtiles(G);
-    if (a.d == 128) launch_bf16<128>(a, W, grid, s);
-    else launch_bf16<64>(a, W, grid, s);
+    if (a.d == 128) hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(64 * kAW), 0, s, a);
+    else hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(64 * kAW), 0, s, a);
   } else {
     const dim3 block((unsigned)(64 * G));
     if (a.d == 128) hipLaunchKernelGGL(attn_f32_kernel<128>, grid, block, 0, s, a);
