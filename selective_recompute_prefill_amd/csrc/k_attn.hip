@@ -50,8 +50,11 @@ __device__ __forceinline__ float pair_sum(float x) {
 
 template <int D>
 __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
-  // K tile: 64 rows of D bf16 (D*2 bytes), 16-byte chunks XOR-swizzled by row.
-  // V^T tile: D rows of 64 keys (128 bytes), chunks XOR-swizzled by row.
+  // K tile: 64 rows of D bf16 (D*2 bytes), 16-byte chunk c of row r stored at
+  // c ^ (r % KCH). V^T tile: D rows of 64 keys (128 bytes), chunk c of row r
+  // stored at c ^ ((r / 2) % 8). A 16-byte LDS read serves 16 lanes (64 banks)
+  // per cycle; the fragment reads put 16 consecutive rows in those lanes, and
+  // both layouts give them 16 different bank groups.
   constexpr int KT = kBK * D * 2, VT = D * kBK * 2, STAGE = KT + VT;
   constexpr int KCH = D / 8;               // chunks per K row
   constexpr int KROWS = 64 / KCH;          // K rows per wave copy
@@ -91,8 +94,9 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   const int qq = col / G, hh = col - qq * G;
   const bool cvalid = qq < nq;
   const int qrow = a.sel_idx[q0 + (cvalid ? qq : nq - 1)];
-  // the wave's first and last query rows (uniform); a wave with no query
-  // columns computes nothing but still copies tiles and meets the barriers
+  // the wave's first and last query rows (uniform): tiles that end after the
+  // first are masked, tiles that start after the last are skipped. A wave with
+  // no query columns skips every tile but still copies and meets the barriers.
   const int wq_lo = (32 * w) / G, wq_hi = min(nq - 1, (32 * w + 31) / G);
   const bool wactive = wq_lo < nq;
   const int w_first = wactive ? a.sel_idx[q0 + wq_lo] : key_end;
@@ -107,7 +111,7 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   // depends on the lane for these row groups).
   const int k_lrow = lane / KCH, k_logical = (lane % KCH) ^ ((KROWS * w + k_lrow) & (KCH - 1));
   const uint32_t k_lane_off = (uint32_t)(k_lrow * row_bytes + k_logical * 16);
-  const int v_lrow = lane >> 3, v_logical = (lane & 7) ^ (v_lrow & 7);
+  const int v_lrow = lane >> 3, v_logical = (lane & 7) ^ (((8 * w + v_lrow) >> 1) & 7);
   const uint32_t v_lane_off = (uint32_t)(v_lrow * vrow_bytes + v_logical * 16);
   auto issue = [&](auto SLOT, int blk) __attribute__((always_inline)) {
     const int kb = key_base + blk * kBK;
@@ -142,6 +146,10 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
     for (int ks = 0; ks < D / 16; ++ks)
       qf[ks] = cvalid ? *reinterpret_cast<const u32x4 *>(qp + ks * 16) : u32x4{0, 0, 0, 0};
   }
+  // the Q loads complete before the first tile copy is issued: the copies are
+  // invisible to the compiler's wait counting, which would otherwise wait for
+  // every outstanding load (the whole prefetch ring) at each use of Q
+  wait_vmcnt<0>();
   floatx16 acc[D / 32];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
@@ -163,30 +171,25 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   for (int ks = 0; ks < D / 16; ++ks) koff[ks] = qi * (D * 2) + (((2 * ks + gph) ^ (qi & (KCH - 1))) * 16);
   uint32_t voff[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) voff[c] = KT + qi * 128 + (((2 * c + gph) ^ (qi & 7)) * 16);
+  for (int c = 0; c < 4; ++c) voff[c] = KT + qi * 128 + (((2 * c + gph) ^ ((qi >> 1) & 7)) * 16);
 
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
-  issue(I0{}, 0);
-  if (nblk > 1) issue(I1{}, 1);
-  auto step = [&](auto SLOT, int blk) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SLOT)::value;
-    // this tile's copies are done once at most the next tile's are outstanding;
-    // every wave waits for its own copies, then the raw barrier (no full memory
-    // fence, which would drain the prefetches) publishes the slot
-    if (blk + 1 < nblk) wait_vmcnt<LOADS>();
-    else wait_vmcnt<0>();
-    __builtin_amdgcn_s_barrier();
-    // the slot of tile blk+2 was last read in iteration blk-1, which every wave
-    // finished before the barrier above
-    if (blk + 2 < nblk) issue(std::integral_constant<int, (sl + 2) % 3>{}, blk + 2);
+  // Ping-pong schedule in half-steps: waves 0-3 run phase 1 of tile j (S^T,
+  // mask, max, rescale: MFMA-bound) while waves 4-7 run phase 2 of tile j-1
+  // (exp, row sums, PV: exp-heavy), then they swap, so the two waves sharing a
+  // SIMD keep its matrix and vector units busy together. Every half-step ends
+  // in a barrier; the copy of tile j+2 starts after the barrier that ends
+  // half-step 2j, when slot (j+2)%3 = (j-1)%3 has been read for the last time
+  // (by waves 4-7, phase 2 of tile j-1), and is waited for at the end of
+  // half-step 2j+3, just before waves 0-3 start on it.
+  floatx16 s[2];
+  auto phase1 = [&](auto SLOT, int blk) __attribute__((always_inline)) {
     const int kb = key_base + blk * kBK;
-    if (kb > w_last) return;  // every key of the tile is after the wave's queries
+    if (kb > w_last) return;
     const char *St = slot_ptr(SLOT);
-
     // S^T[key][column] - m for both 32-key halves, two independent MFMA chains
-    floatx16 s[2];
     const float c0 = first ? 0.f : -m;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { s[0][e] = c0; s[1][e] = c0; }
@@ -235,6 +238,10 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
         for (int e = 0; e < 16; ++e) { s[0][e] -= dlt; s[1][e] -= dlt; }
       }
     }
+  };
+  auto phase2 = [&](auto SLOT, int blk) __attribute__((always_inline)) {
+    if (key_base + blk * kBK > w_last) return;
+    const char *St = slot_ptr(SLOT);
 #pragma unroll
     for (int hb = 0; hb < 2; ++hb) {
       // probabilities in bf16 (the PV operand); the row sum uses the same
@@ -260,11 +267,58 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
       }
     }
   };
-  for (int b0 = 0; b0 < nblk; b0 += 3) {
-    step(I0{}, b0);
-    if (b0 + 1 < nblk) step(I1{}, b0 + 1);
-    if (b0 + 2 < nblk) step(I2{}, b0 + 2);
+  // end of half-step h (h = -1: the prologue)
+  auto sync = [&](int h) __attribute__((always_inline)) {
+    if (h & 1) {
+      // the next half-step starts tile (h+1)/2: its copies must be complete;
+      // those of the tile after it may still be in flight
+      if ((h + 1) / 2 + 1 < nblk) wait_vmcnt<LOADS>();
+      else wait_vmcnt<0>();
+    }
+    __builtin_amdgcn_s_barrier();
+  };
+  auto issue_after = [&](auto SLOT, int h) __attribute__((always_inline)) {
+    // after the barrier ending even half-step h = 2j: copy tile j+2
+    if (h / 2 + 2 < nblk) issue(SLOT, h / 2 + 2);
+  };
+
+  issue(I0{}, 0);
+  if (nblk > 1) issue(I1{}, 1);
+  sync(-1);
+  const bool lead = w < kAW / 2;
+  if (!lead) {
+    sync(0);
+    issue_after(I2{}, 0);
   }
+  // tile j uses slot j % 3; the loop is unrolled by three so slots are
+  // constants. Both groups run the same phase code; only the barrier
+  // bookkeeping between phases depends on the group (waves 0-3 end half-steps
+  // 2j and 2j+1 around tile j, waves 4-7 end 2j+1 and 2j+2).
+  auto tile = [&](auto SLOT, int j) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    using NEXT2 = std::integral_constant<int, (sl + 2) % 3>;
+    using NEXT3 = std::integral_constant<int, (sl + 3) % 3>;
+    phase1(SLOT, j);
+    if (lead) {
+      sync(2 * j);
+      issue_after(NEXT2{}, 2 * j);
+    } else {
+      sync(2 * j + 1);
+    }
+    phase2(SLOT, j);
+    if (lead) {
+      sync(2 * j + 1);
+    } else {
+      sync(2 * j + 2);
+      issue_after(NEXT3{}, 2 * j + 2);
+    }
+  };
+  for (int j0 = 0; j0 < nblk; j0 += 3) {
+    tile(I0{}, j0);
+    if (j0 + 1 < nblk) tile(I1{}, j0 + 1);
+    if (j0 + 2 < nblk) tile(I2{}, j0 + 2);
+  }
+  if (lead) sync(2 * nblk);
 
   const float lt = pair_sum(l);
   if (cvalid) {

@@ -112,8 +112,10 @@ struct TileIter {
 // bf16 MFMA kernel: 128x128 tile, BK 64, 4 waves (2x2), wave tile 64x64 made of
 // 2x2 blocks of 32x32x16 MFMA. Operand tiles stream into an LDS ring with
 // direct-to-LDS copies (no staging registers): copy i of a tile moves rows
-// 8i..8i+7 (128 bytes each); 16-byte chunks are XOR-swizzled by row so the
-// fragment reads of 32 consecutive rows spread over all banks.
+// 8i..8i+7 (128 bytes each). Chunk c of row r is stored at c ^ ((r / 2) % 8):
+// a 16-byte LDS read serves 16 lanes (64 banks) per cycle, and the fragment
+// reads put 16 consecutive rows in those lanes, which this layout spreads over
+// 16 different bank groups.
 // ------------------------------------------------------------------------- //
 #ifndef SRP_GEMM_STAGES
 #define SRP_GEMM_STAGES 2
@@ -140,8 +142,10 @@ __global__ __launch_bounds__(256, kGStages >= 3 ? 1 : 2) void gemm_bf16_kernel(G
   const char *A = (const char *)g.A, *B = (const char *)g.B;
   const int KT = K / kBK16;
   const size_t rowb = (size_t)K * 2;
-  // copy layout: lane covers row 8i + lrow, physical chunk lane%8 <- logical chunk lchunk
-  const int lrow = lane >> 3, lchunk = (lane & 7) ^ (lrow & 7);
+  // copy layout: lane covers row 8i + lrow, physical chunk lane%8 <- logical
+  // chunk lchunk; for the rows i = w + 4j of this wave the swizzle term is a
+  // per-lane constant
+  const int lrow = lane >> 3, lchunk = (lane & 7) ^ (((8 * w + lrow) >> 1) & 7);
 
   for (int lt = ti.loc;; lt += ti.per_x) {
     const int tile = ti.tile(lt);
@@ -199,12 +203,12 @@ __global__ __launch_bounds__(256, kGStages >= 3 ? 1 : 2) void gemm_bf16_kernel(G
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
           const int r = wm * 64 + i * 32 + fr;
-          af[i] = *reinterpret_cast<const bf16x8 *>(as + r * 128 + (((2 * ks + fk) ^ (r & 7)) * 16));
+          af[i] = *reinterpret_cast<const bf16x8 *>(as + r * 128 + (((2 * ks + fk) ^ ((r >> 1) & 7)) * 16));
         }
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
           const int r = wn * 64 + j * 32 + fr;
-          bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + r * 128 + (((2 * ks + fk) ^ (r & 7)) * 16));
+          bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + r * 128 + (((2 * ks + fk) ^ ((r >> 1) & 7)) * 16));
         }
 #pragma unroll
         for (int i = 0; i < 2; ++i)
