@@ -45,8 +45,18 @@ def parse():
     p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4])
     p.add_argument("--ratio", type=float, default=None, help="override the workload's ratio")
     p.add_argument("--no-cpu-baseline", action="store_true")
-    p.add_argument("--cpu-sample-chunks", type=int, default=16,
-                   help="chunks of the request the oracle is timed on")
+    p.add_argument("--cpu-sample-chunks", type=int, default=0,
+                   help="chunks of the request the oracle is timed on (0: all of them)")
+    p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                   help="only run a plain device-to-device copy of MIB MiB five times (the "
+                        "reference for scaling the HBM byte counters) and exit")
+    p.add_argument("--summarize-trace", metavar="STATS_CSV",
+                   help="print a markdown table of a rocprofv3 --stats kernel CSV and exit")
+    p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
+                   help="print the per-launch HBM traffic summary from four rocprofv3 --pmc "
+                        "counter CSVs (kernel FETCH_SIZE, kernel WRITE_SIZE, copy FETCH_SIZE, "
+                        "copy WRITE_SIZE; the copy runs use --copy-calibration) and exit")
+    p.add_argument("--copy-mib", type=int, default=1024, help="size the copy runs used")
     return p.parse_args()
 
 
@@ -78,6 +88,121 @@ def algorithmic_work(spec, lay, sel, ratio_rows):
     }
 
 
+# Kernels whose HBM traffic is reported, with the sources their code comes from:
+# a recorded traffic figure is used only while these files are unchanged.
+TRAFFIC_KERNELS = {
+    "attn_bf16_kernel<128>": ("attn_bf16_kernel<128>", ["k_attn.hip", "kernels.hpp", "common.hpp"]),
+    "gemm_bf16_kernel<EPI_KV>": ("gemm_bf16_kernel<0>", ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
+    "gemm_bf16_kernel<EPI_Q>": ("gemm_bf16_kernel<1>", ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
+}
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_14b_16k_grouped.md")
+
+
+def source_hash(files):
+    import hashlib
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "selective_recompute_prefill_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def recorded_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the recorded counter runs, or None
+    when there is no record or the kernel's sources changed since."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+    except (OSError, IndexError, ValueError):
+        return None
+    ent = rec.get("kernels", {}).get(kernel)
+    if not ent or ent.get("source_hash") != source_hash(TRAFFIC_KERNELS[kernel][1]):
+        return None
+    return ent["bytes_per_launch"]
+
+
+def _pmc_rows(path):
+    import csv
+    if os.path.isdir(path):
+        cands = [os.path.join(dp, f) for dp, _, fs in os.walk(path) for f in fs
+                 if f.endswith("counter_collection.csv")]
+        path = sorted(cands)[0]
+    with open(path) as fh:
+        return list(csv.DictReader(fh))
+
+
+def _per_dispatch(rows, counter):
+    """{dispatch id: (kernel name, summed counter value)} for one counter."""
+    out = {}
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        d = int(r["Dispatch_Id"])
+        name, v = out.get(d, (r["Kernel_Name"], 0.0))
+        out[d] = (name, v + float(r["Counter_Value"]))
+    return out
+
+
+def summarize_pmc(fetch, write, cfetch, cwrite, copy_mib):
+    """Markdown + JSON record of HBM traffic per launch: the kernels' FETCH_SIZE
+    and WRITE_SIZE (KiB per dispatch, averaged over their dispatches), each scaled
+    by true bytes / counter bytes of the plain copy."""
+    import numpy as np
+    true_kib = copy_mib * 1024.0
+
+    def copy_factor(path, counter):
+        d = _per_dispatch(_pmc_rows(path), counter)
+        vals = [v for n, v in d.values() if "copy" in n.lower()]
+        return true_kib / float(np.median(vals)), float(np.median(vals))
+
+    f_fac, f_raw = copy_factor(cfetch, "FETCH_SIZE")
+    w_fac, w_raw = copy_factor(cwrite, "WRITE_SIZE")
+    fd, wd = _per_dispatch(_pmc_rows(fetch), "FETCH_SIZE"), _per_dispatch(_pmc_rows(write), "WRITE_SIZE")
+    rec = {"copy_mib": copy_mib, "copy_fetch_kib": f_raw, "copy_write_kib": w_raw,
+           "fetch_factor": f_fac, "write_factor": w_fac, "kernels": {}}
+    lines = ["| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch (scaled) |",
+             "|---|---|---|---|---|"]
+    for label, (match, files) in TRAFFIC_KERNELS.items():
+        fv = [v for n, v in fd.values() if match in n]
+        wv = [v for n, v in wd.values() if match in n]
+        if not fv or not wv:
+            continue
+        f_kib, w_kib = float(np.mean(fv)), float(np.mean(wv))
+        total = (f_kib * f_fac + w_kib * w_fac) * 1024.0
+        rec["kernels"][label] = {"fetch_kib": f_kib, "write_kib": w_kib, "launches": len(fv),
+                                 "bytes_per_launch": total, "source_hash": source_hash(files)}
+        lines.append(f"| {label} | {len(fv)} | {f_kib:.0f} | {w_kib:.0f} | {total:.4g} |")
+    head = [f"Copy calibration: a {copy_mib} MiB device-to-device copy reads FETCH_SIZE "
+            f"{f_raw:.0f} KiB and WRITE_SIZE {w_raw:.0f} KiB for {true_kib:.0f} KiB each way: "
+            f"factors {f_fac:.4f} (fetch) and {w_fac:.4f} (write).", ""]
+    return "\n".join(head + lines + ["", "```json", json.dumps(rec, indent=1), "```", ""])
+
+
+def summarize_trace(stats_csv):
+    import csv
+    with open(stats_csv) as fh:
+        rows = list(csv.DictReader(fh))
+    lines = ["| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows[:16]:
+        nm = r["Name"] if len(r["Name"]) < 70 else r["Name"][:67] + "..."
+        lines.append(f"| {nm} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
+                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
+                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
+    return "\n".join(lines) + "\n"
+
+
+def copy_calibration(mib):
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.empty(n, dtype=torch.float32, device="cuda").fill_(1.0)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_mib": mib, "repeats": 5}), flush=True)
+
+
 def cpu_baseline(spec, n_chunks_sample):
     """Time the fp64 oracle on a bounded sample of the workload: the first
     n_chunks_sample chunks of one request (with its prefix and query tail)."""
@@ -91,7 +216,7 @@ def cpu_baseline(spec, n_chunks_sample):
         blas = ",".join(sorted({i.get("internal_api", "?") for i in info}))
     except Exception:  # pragma: no cover
         threads, blas = os.cpu_count(), "unknown"
-    n_ch = min(n_chunks_sample, len(spec.chunk_lens))
+    n_ch = min(n_chunks_sample or len(spec.chunk_lens), len(spec.chunk_lens))
     sub = spec.replace(chunk_lens=spec.chunk_lens[:n_ch], n_req=1, shared_chunks=False,
                        n_layers=1, ratios=())
     w = inputs.generate(sub)
@@ -118,15 +243,22 @@ def cpu_baseline(spec, n_chunks_sample):
     n_ctx = int(cr.sum())
     return {"value": n_ctx / dt, "unit": "context tokens/s per layer", "cores": int(threads),
             "kind": "oracle",
-            "sample": f"one layer of the same shape on the first {n_ch} of {len(spec.chunk_lens)} chunks "
-                      f"({lay.total_rows} rows, {n_ctx} cached) timed once in fp64 numpy ({blas} BLAS); "
-                      f"attention cost per token grows with length, so this overstates the oracle's "
-                      f"rate at full length",
+            "sample": (f"one layer of the same shape on the first {n_ch} of {len(spec.chunk_lens)} chunks "
+                       f"({lay.total_rows} rows, {n_ctx} cached) timed once in fp64 numpy ({blas} BLAS)"
+                       + ("; attention cost per token grows with length, so this overstates the "
+                          "oracle's rate at full length" if n_ch < len(spec.chunk_lens) else
+                          " (one request of the workload, timed once)")),
             "seconds": dt}
 
 
 def main():
     args = parse()
+    if args.summarize_trace:
+        print(summarize_trace(args.summarize_trace), end="")
+        return
+    if args.summarize_pmc:
+        print(summarize_pmc(*args.summarize_pmc, args.copy_mib), end="")
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
               f"multi-GPU path", file=sys.stderr)
@@ -138,8 +270,11 @@ def main():
     from selective_recompute_prefill_amd import srp as S
     from selective_recompute_prefill_amd.device import LayerCall, download, encode_cache, upload
 
-    S.lib()  # fail loudly if the library is not built
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
+    S.lib()  # fail loudly if the library is not built
     dev = "cuda"
     spec = inputs.CONFIGS[args.workload]
     if args.ratio is not None:
@@ -251,6 +386,10 @@ def main():
             "bound": "mfma", "achieved": stages[dom]["tflops"], "peak": peak_fl, "unit": "TFLOP/s",
             "frac": stages[dom]["frac_mfma"], "traffic": None,
             "flops_per_launch": work[dom]["flops"], "avg_launch_ms": stages[dom]["ms"]}
+
+    if args.workload == 2 and args.ratio is None:
+        # HBM bytes per launch from the recorded counter runs of this workload
+        roof["traffic"] = recorded_traffic(roof["kernel"])
 
     value = n_ctx / (ms_per_layer * 1e-3)
     out = {
