@@ -248,6 +248,8 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   g.v_cache = v_cache;
   g.fresh = w.fresh_kv;
   g.dev_part = w.dev_part;
+  g.part = w.gemm_part;
+  g.part_cap = w.gemm_part ? kGemmParts : 0;
   marks.mark(1);
   SRP_HIP(launch_gemm(g, s));
   marks.mark(2);

@@ -197,8 +197,12 @@ struct Workspace {
   void *vt;            // bf16: [nkv][d][vt_stride] fused V transposed for attention
   int32_t *tiles;      // [3 * max_tiles] attention tiles (first sel, count, req)
   int32_t *ctr;        // [16] device counters (see kCtr*)
+  float *gemm_part;    // bf16: [kGemmParts][kGemmPartFloats] split-K partial tiles
   size_t bytes;
 };
+// split-K partial tiles of the projection GEMMs' last round
+constexpr int kGemmParts = 128;
+constexpr size_t kGemmPartFloats = 256 * 256;
 constexpr int kCtrTotalSel = 0;
 constexpr int kCtrTiles = 1;
 constexpr int kCtrREntries = 2;
@@ -248,6 +252,7 @@ inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base) {
   w.vt = d.dtype == SRP_BF16 ? take((size_t)d.n_kv_heads * d.head_dim * vt_stride(b.total_rows) * 2) : nullptr;
   w.tiles = (int32_t *)take((size_t)3 * max_attn_tiles((int)T, (int)nr) * 4);
   w.ctr = (int32_t *)take(16 * 4);
+  w.gemm_part = d.dtype == SRP_BF16 ? (float *)take((size_t)kGemmParts * kGemmPartFloats * 4) : nullptr;
   w.bytes = off;
   return w;
 }

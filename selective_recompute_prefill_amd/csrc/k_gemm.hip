@@ -14,78 +14,147 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
 constexpr int kBN = 128;
+constexpr int kLDC = kBN + 4;  // fp32 kernel staging stride
 
 // ------------------------------------------------------------------------- //
 // epilogue
 // ------------------------------------------------------------------------- //
-template <typename T, int BM, int MODE>
-__device__ __forceinline__ void epilogue(const float *Cs, int ldc, int m0, int n0, int M,
-                                         const GemmArgs &g) {
-  const int d = g.d, half = d >> 1;
-  const int tpu = d >> 3;          // threads per head unit (4 pairs each)
-  const int kvd = g.nkv * d;
-  for (int it = threadIdx.x; it < BM * 16; it += blockDim.x) {
-    const int r = it >> 4, qq = it & 15;
-    const int u = qq / tpu, t = qq - u * tpu;
+// Per-row metadata of a tile (token row, position, position delta), loaded
+// once per tile so the epilogue's global loads do not wait on each other.
+struct EpiRow {
+  int row, pos, delta;
+};
+
+template <int MODE, int ROWS>
+__device__ __forceinline__ void load_row_meta(EpiRow *meta, int m0, int M, const GemmArgs &g) {
+  for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
     const int m = m0 + r;
-    const int nu = n0 + u * d;
-    const bool valid = (m < M) && (nu < g.N);
-    const int i0 = t * 4;
-    float a[4], b[4];
-    const float *src = Cs + r * ldc + u * d;
+    EpiRow e{-1, 0, kFresh};
+    if (m < M) {
+      e.row = (MODE != EPI_ENC && g.a_rows) ? g.a_rows[m] : m;
+      e.pos = g.positions[e.row];
+      if (MODE == EPI_KV) e.delta = g.row_delta[e.row];
+    }
+    meta[r] = e;
+  }
+}
+
+__device__ __forceinline__ void rope_coef(const RopeTable &t, int p, int i0, float c[4], float s[4]) {
+  int ap = p < 0 ? -p : p;
+  ap = ap < t.max_pos ? ap : t.max_pos - 1;  // never read past the table
+  ld4(t.cos_t + (size_t)ap * t.half + i0, c);
+  ld4(t.sin_t + (size_t)ap * t.half + i0, s);
+  if (p < 0) {
 #pragma unroll
-    for (int k = 0; k < 4; ++k) { a[k] = src[i0 + k]; b[k] = src[half + i0 + k]; }
-    float part_sum = 0.f;
-    int slot = -1;
-    if (valid) {
-      const int row = (MODE != EPI_ENC && g.a_rows) ? g.a_rows[m] : m;
-      if (MODE == EPI_Q) {
-        const int h = nu / d;
-        rope4(a, b, g.rope, g.positions[row], i0);
+    for (int k = 0; k < 4; ++k) s[k] = -s[k];
+  }
+}
+
+__device__ __forceinline__ void rotate4(float a[4], float b[4], const float c[4], const float s[4]) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) { a[k] *= g.q_scale; b[k] *= g.q_scale; }
-        T *q = (T *)g.q_out + (size_t)m * g.nh * d + h * d;
-        st4(q + i0, a);
-        st4(q + half + i0, b);
-      } else {
-        const int part = nu >= kvd;
+  for (int k = 0; k < 4; ++k) {
+    const float x = a[k], y = b[k];
+    a[k] = x * c[k] - y * s[k];
+    b[k] = y * c[k] + x * s[k];
+  }
+}
+
+// Works through ROWS staged rows x 128 columns (Cs[r * ldc + c], fp32; block
+// row r is tile row m_base + r, its metadata meta[r]) with NT threads: item =
+// (row, head unit, 4 rotation pairs). Items go in batches of B whose global
+// loads (rotation coefficients, cached K/V) are all issued before any of the
+// batch's stores.
+template <typename T, int ROWS, int MODE, int NT, int B>
+__device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow *meta, int m_base,
+                                         int n0, const GemmArgs &g) {
+  constexpr int ITEMS = ROWS * 16 / NT;
+  static_assert(ROWS * 16 % NT == 0 && ITEMS % B == 0, "items split evenly");
+  const int d = g.d, half = d >> 1;
+  const int tpu = d >> 3;  // threads per head unit (4 pairs each)
+  const int kvd = g.nkv * d;
+#pragma unroll 1
+  for (int kb = 0; kb < ITEMS; kb += B) {
+    float c1[B][4], s1[B][4], c2[B][4], s2[B][4], ca[B][4], cb[B][4];
+    // loads of the batch
+#pragma unroll
+    for (int j = 0; j < B; ++j) {
+      const int it = threadIdx.x + (kb + j) * NT;
+      const int r = it >> 4, qq = it & 15;
+      const int u = qq / tpu, t = qq - u * tpu;
+      const int nu = n0 + u * d, i0 = t * 4;
+      const EpiRow e = meta[r];
+      const bool valid = e.row >= 0 && nu < g.N;
+      const int part = MODE == EPI_Q ? 0 : (nu >= kvd);
+      if (valid && part == 0) rope_coef(g.rope, e.pos, i0, c1[j], s1[j]);
+      if (MODE == EPI_KV && valid && e.delta != kFresh) {
         const int gh = (nu - part * kvd) / d;
-        if (part == 0) rope4(a, b, g.rope, g.positions[row], i0);
-        if (MODE == EPI_ENC) {
-          T *o = (T *)(part ? g.v_cache : g.k_cache) + (size_t)m * kvd + gh * d;
-          st4(o + i0, a);
-          st4(o + half + i0, b);
-        } else {
-          T *f = (T *)g.fresh + (size_t)m * 2 * kvd + part * kvd + gh * d;
-          st4(f + i0, a);
-          st4(f + half + i0, b);
-          const int delta = g.row_delta[row];
-          slot = part * g.nkv + gh;
-          if (delta != kFresh) {
-            T *c = (T *)(part ? g.v_cache : g.k_cache) + (size_t)row * kvd + gh * d;
-            float ca[4], cb[4];
-            ld4(c + i0, ca);
-            ld4(c + half + i0, cb);
-            if (part == 0) {
-              // positional recovery of the cached key, kept in fp32 for the
-              // deviation and written back to the cache
-              rope4(ca, cb, g.rope, delta, i0);
-              st4(c + i0, ca);
-              st4(c + half + i0, cb);
-            }
+        const T *c = (const T *)(part ? g.v_cache : g.k_cache) + (size_t)e.row * kvd + gh * d;
+        ld4(c + i0, ca[j]);
+        ld4(c + half + i0, cb[j]);
+        if (part == 0) rope_coef(g.rope, e.delta, i0, c2[j], s2[j]);
+      }
+    }
+    // compute and store
 #pragma unroll
-            for (int k = 0; k < 4; ++k) {
-              float x = a[k] - ca[k], y = b[k] - cb[k];
-              part_sum += x * x + y * y;
+    for (int j = 0; j < B; ++j) {
+      const int it = threadIdx.x + (kb + j) * NT;
+      const int r = it >> 4, qq = it & 15;
+      const int u = qq / tpu, t = qq - u * tpu;
+      const int nu = n0 + u * d, i0 = t * 4;
+      const int m = m_base + r;
+      const EpiRow e = meta[r];
+      const bool valid = e.row >= 0 && nu < g.N;
+      float a[4], b[4];
+      const float *src = Cs + r * ldc + u * d;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { a[k] = src[i0 + k]; b[k] = src[half + i0 + k]; }
+      float part_sum = 0.f;
+      int slot = -1;
+      if (valid) {
+        if (MODE == EPI_Q) {
+          const int h = nu / d;
+          rotate4(a, b, c1[j], s1[j]);
+#pragma unroll
+          for (int k = 0; k < 4; ++k) { a[k] *= g.q_scale; b[k] *= g.q_scale; }
+          T *q = (T *)g.q_out + (size_t)m * g.nh * d + h * d;
+          st4(q + i0, a);
+          st4(q + half + i0, b);
+        } else {
+          const int part = nu >= kvd;
+          const int gh = (nu - part * kvd) / d;
+          if (part == 0) rotate4(a, b, c1[j], s1[j]);
+          if (MODE == EPI_ENC) {
+            T *o = (T *)(part ? g.v_cache : g.k_cache) + (size_t)m * kvd + gh * d;
+            st4(o + i0, a);
+            st4(o + half + i0, b);
+          } else {
+            T *f = (T *)g.fresh + (size_t)m * 2 * kvd + part * kvd + gh * d;
+            st4(f + i0, a);
+            st4(f + half + i0, b);
+            slot = part * g.nkv + gh;
+            if (e.delta != kFresh) {
+              if (part == 0) {
+                // positional recovery of the cached key, kept in fp32 for the
+                // deviation and written back to the cache
+                rotate4(ca[j], cb[j], c2[j], s2[j]);
+                T *c = (T *)g.k_cache + (size_t)e.row * kvd + gh * d;
+                st4(c + i0, ca[j]);
+                st4(c + half + i0, cb[j]);
+              }
+#pragma unroll
+              for (int k = 0; k < 4; ++k) {
+                const float x = a[k] - ca[j][k], y = b[k] - cb[j][k];
+                part_sum += x * x + y * y;
+              }
             }
           }
         }
       }
-    }
-    if (MODE == EPI_KV) {
-      // fixed-order reduction over the head's tpu lanes (aligned groups)
-      for (int o = 1; o < tpu; o <<= 1) part_sum += __shfl_xor(part_sum, o, 64);
-      if (valid && t == 0) g.dev_part[(size_t)m * 2 * g.nkv + slot] = part_sum;
+      if (MODE == EPI_KV) {
+        // fixed-order reduction over the head's tpu lanes (aligned groups)
+        for (int o = 1; o < tpu; o <<= 1) part_sum += __shfl_xor(part_sum, o, 64);
+        if (valid && t == 0) g.dev_part[(size_t)m * 2 * g.nkv + slot] = part_sum;
+      }
     }
   }
 }
@@ -109,131 +178,246 @@ struct TileIter {
 };
 
 // ------------------------------------------------------------------------- //
-// bf16 MFMA kernel: 128x128 tile, BK 64, 4 waves (2x2), wave tile 64x64 made of
-// 2x2 blocks of 32x32x16 MFMA. Operand tiles stream into an LDS ring with
-// direct-to-LDS copies (no staging registers): copy i of a tile moves rows
-// 8i..8i+7 (128 bytes each). Chunk c of row r is stored at c ^ ((r / 2) % 8):
-// a 16-byte LDS read serves 16 lanes (64 banks) per cycle, and the fragment
-// reads put 16 consecutive rows in those lanes, which this layout spreads over
-// 16 different bank groups.
+// bf16 MFMA kernel: BM x BN tile, WM x WN waves, each wave owning a
+// (BM/WM) x (BN/WN) block of 32x32x16 MFMA tiles. Operand tiles of depth 32
+// (64-byte rows) stream into an S-slot LDS ring with direct-to-LDS copies (no
+// staging registers); copy q of a tile moves rows 16q..16q+15. Chunk c of row r
+// is stored at c ^ ((r / 4) % 4): a 16-byte LDS read serves 16 lanes (64 banks)
+// per cycle and the fragment reads put 16 consecutive rows in those lanes,
+// which this layout spreads over 16 different bank groups.
 // ------------------------------------------------------------------------- //
-#ifndef SRP_GEMM_STAGES
-#define SRP_GEMM_STAGES 2
-#endif
-constexpr int kBM16 = 128, kBK16 = 64;
-constexpr int kGStages = SRP_GEMM_STAGES;
-constexpr int kGTile = kBM16 * kBK16 * 2;  // bytes of one operand tile (16 KB)
-constexpr int kGStage = 2 * kGTile;         // A tile then B tile
-constexpr int kLDC = kBN + 4;
-constexpr int kGSmem = kGStages * kGStage > kBM16 * kLDC * 4 ? kGStages * kGStage : kBM16 * kLDC * 4;
+constexpr int kGBK = 32;
 
-template <int MODE>
-__global__ __launch_bounds__(256, kGStages >= 3 ? 1 : 2) void gemm_bf16_kernel(GemmArgs g) {
-  __shared__ __align__(16) char smem[kGSmem];
-  float *Cs = reinterpret_cast<float *>(smem);  // epilogue staging, 128 x 132 fp32
+template <int BM_, int BN_, int WM_, int WN_, int S_>
+struct GemmCfg {
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
+  static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
+  static constexpr int MI = TM / 32, NI = TN / 32;
+  static constexpr int ATILE = BM * kGBK * 2, STAGE = (BM + BN) * kGBK * 2;
+  static constexpr int ACOPY = BM / 16, COPIES = (BM + BN) / 16;
+  static constexpr int CPW = COPIES / WAVES;  // copies per wave per tile
+  static constexpr int EROWS = TM;            // rows staged per epilogue pass (one wave row)
+  static constexpr int LDC = BN + 4;
+  static constexpr int RING = S * STAGE, CS = EROWS * LDC * 4;
+  static constexpr int SMEM = RING > CS ? RING : CS;
+  static constexpr int PER_CU = THREADS >= 512 ? 1 : 2;  // resident work-groups per CU
+  // epilogue load batch (items per thread): the other wave row's accumulators
+  // are still live while the first row is finished, which leaves room for one
+  static constexpr int EPI_B = 1;
+  static_assert(COPIES % WAVES == 0 && ACOPY % WAVES == 0, "copies split evenly, A before B");
+  static_assert(BN % kBN == 0, "the epilogue works on 128-column blocks");
+};
+
+// Work split: the full rounds of tiles (floor(T / P) per work-group) run whole;
+// the R tiles of the last, partial round are split along K into s pieces each
+// (s <= P / R), whose fp32 partial tiles a second kernel adds up and finishes
+// with the epilogue. Both kernels derive the plan from the same numbers.
+constexpr int kMaxSplit = 8;
+struct SplitPlan {
+  int tiles, full, tail, split;  // T, tiles run whole, tail tiles, pieces per tail tile
+};
+__device__ __forceinline__ SplitPlan split_plan(int tiles, int grid, int part_cap) {
+  SplitPlan sp{tiles, tiles, 0, 1};
+  const int tail = tiles % grid;
+  if (tail == 0 || part_cap <= 0) return sp;
+  int s = grid / tail;
+  s = s < kMaxSplit ? s : kMaxSplit;
+  s = s < part_cap / tail ? s : part_cap / tail;
+  if (s < 2) return sp;
+  sp.full = tiles - tail;
+  sp.tail = tail;
+  sp.split = s;
+  return sp;
+}
+
+template <int MODE, typename C>
+__global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmArgs g) {
+  static_assert(C::BM * C::BN <= kGemmPartFloats, "partial tiles fit their slots");
+  __shared__ __align__(16) char smem[C::SMEM];
+  __shared__ EpiRow meta[C::BM];
+  float *Cs = reinterpret_cast<float *>(smem);  // epilogue staging, EROWS x LDC fp32
 
   const int M = g.M_dev ? *g.M_dev : g.M_host;
   const int K = g.K, N = g.N;
-  const int mt_n = (M + kBM16 - 1) / kBM16, nt_n = (N + kBN - 1) / kBN;
-  const TileIter ti(mt_n * nt_n);
+  const int mt_n = (M + C::BM - 1) / C::BM, nt_n = (N + C::BN - 1) / C::BN;
+  const SplitPlan sp = split_plan(mt_n * nt_n, gridDim.x, g.part_cap);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm = w >> 1, wn = w & 1;
+  const int wm = w / C::WN, wn = w - wm * C::WN;
   const char *A = (const char *)g.A, *B = (const char *)g.B;
-  const int KT = K / kBK16;
+  const int KT = K / kGBK;
   const size_t rowb = (size_t)K * 2;
-  // copy layout: lane covers row 8i + lrow, physical chunk lane%8 <- logical
-  // chunk lchunk; for the rows i = w + 4j of this wave the swizzle term is a
-  // per-lane constant
-  const int lrow = lane >> 3, lchunk = (lane & 7) ^ (((8 * w + lrow) >> 1) & 7);
+  // copy layout: lane covers row 16q + lrow and physical chunk lane % 4, which
+  // holds logical chunk lchunk (the swizzle term depends on the lane only)
+  const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  // fragment reads: lane holds row (lane % 32) of a 32-row block and k-values
+  // 8 * (lane / 32) .. +8 of each 16-deep step
+  const int fr = lane & 31, fk = lane >> 5;
+  const uint32_t fswz = (fr >> 2) & 3;
+  floatx16 acc[C::MI][C::NI];
 
+  // acc = A[m0.., k0*32 ..] * B[n0.., ..]^T over nk k-tiles; `pre` runs once the
+  // first copies are in flight
+  auto mainloop = [&](int m0, int n0, int k0, int nk, auto pre) __attribute__((always_inline)) {
+    // wave w moves copies q = w + WAVES*j; A copies come first. Rows past M or
+    // N read a valid row (their results are never stored).
+    const char *src[C::CPW];
+    const int row0 = g.a_rows ? g.a_rows[m0] : m0;
+#pragma unroll
+    for (int j = 0; j < C::CPW; ++j) {
+      const int q = w + C::WAVES * j;
+      if (q < C::ACOPY) {
+        const int m = m0 + 16 * q + lrow;
+        const int row = m < M ? (g.a_rows ? g.a_rows[m] : m) : row0;
+        src[j] = A + (size_t)row * rowb + (size_t)k0 * (kGBK * 2) + lchunk * 16;
+      } else {
+        const int n = n0 + 16 * (q - C::ACOPY) + lrow;
+        src[j] = B + (size_t)(n < N ? n : N - 1) * rowb + (size_t)k0 * (kGBK * 2) + lchunk * 16;
+      }
+    }
+    auto issue = [&](int kt) __attribute__((always_inline)) {
+      char *st = smem + (kt % C::S) * C::STAGE;
+#pragma unroll
+      for (int j = 0; j < C::CPW; ++j) dma16(src[j] + (size_t)kt * (kGBK * 2), st + (w + C::WAVES * j) * 1024);
+    };
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+#pragma unroll
+    for (int p = 0; p < C::S - 1; ++p)
+      if (p < nk) issue(p);
+    pre();
+    for (int kt = 0; kt < nk; ++kt) {
+      // this tile's copies are done once at most those of the later tiles
+      // already in flight are outstanding
+      const int later = min(nk - 1 - kt, C::S - 2);
+      if (later >= 3) wait_vmcnt<3 * C::CPW>();
+      else if (later == 2) wait_vmcnt<2 * C::CPW>();
+      else if (later == 1) wait_vmcnt<C::CPW>();
+      else wait_vmcnt<0>();
+      __builtin_amdgcn_s_barrier();
+      // the slot of tile kt+S-1 was last read in iteration kt-1
+      if (kt + C::S - 1 < nk) issue(kt + C::S - 1);
+      const char *as = smem + (kt % C::S) * C::STAGE, *bs = as + C::ATILE;
+#pragma unroll
+      for (int ks = 0; ks < kGBK / 16; ++ks) {
+        const uint32_t off = fr * (kGBK * 2) + (((2 * ks + fk) ^ fswz) * 16);
+        bf16x8 af[C::MI], bfr[C::NI];
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+          af[i] = *reinterpret_cast<const bf16x8 *>(as + (wm * C::TM + i * 32) * (kGBK * 2) + off);
+#pragma unroll
+        for (int j = 0; j < C::NI; ++j)
+          bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + (wn * C::TN + j * 32) * (kGBK * 2) + off);
+#pragma unroll
+        for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+          for (int j = 0; j < C::NI; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  };
+
+  // 1. one K-piece of a tail tile: fp32 partial tile to its slot
+  if (sp.split > 1 && (int)blockIdx.x < sp.tail * sp.split) {
+    const int piece = blockIdx.x;
+    const int tile = sp.full + piece / sp.split, j = piece - (piece / sp.split) * sp.split;
+    const int mt = tile / nt_n, nt = tile - mt * nt_n;
+    const int k0 = (int)((long)KT * j / sp.split), k1 = (int)((long)KT * (j + 1) / sp.split);
+    mainloop(mt * C::BM, nt * C::BN, k0, k1 - k0, [] {});
+    float *dst = g.part + (size_t)piece * kGemmPartFloats;
+#pragma unroll
+    for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+      for (int jj = 0; jj < C::NI; ++jj)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int row = wm * C::TM + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+          const int col = wn * C::TN + jj * 32 + (lane & 31);
+          dst[row * C::BN + col] = acc[i][jj][e];
+        }
+    __syncthreads();  // the ring is free before the next tile's copies
+  }
+
+  // 2. whole tiles: each XCD walks a contiguous range of row-major tiles
+  const TileIter ti(sp.full);
   for (int lt = ti.loc;; lt += ti.per_x) {
     const int tile = ti.tile(lt);
     if (tile < 0) break;
     const int mt = tile / nt_n, nt = tile - mt * nt_n;
-    const int m0 = mt * kBM16, n0 = nt * kBN;
-
-    // wave w copies A rows and B rows of copies i = w + 4j; rows past M or N
-    // read a valid row (their results are never stored)
-    const char *pa[4], *pb[4];
-    const int row0 = g.a_rows ? g.a_rows[m0] : m0;
+    const int m0 = mt * C::BM, n0 = nt * C::BN;
+    // the epilogue's row metadata loads while the first copies are in flight
+    mainloop(m0, n0, 0, KT, [&] { load_row_meta<MODE, C::BM>(meta, m0, M, g); });
+    // the epilogue runs once per wave row: the waves of row p stage their
+    // accumulators (D[row][col], row = 8*(e/4) + 4*(lane/32) + e%4), then every
+    // wave works through the staged rows one 128-column block at a time
+#pragma unroll 1
+    for (int p = 0; p < C::WM; ++p) {
+      __syncthreads();  // the ring (or the previous pass) is no longer read
+      if (wm == p) {
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int r = 8 * (w + 4 * j) + lrow;
-      const int m = m0 + r, n = n0 + r;
-      const int row = m < M ? (g.a_rows ? g.a_rows[m] : m) : row0;
-      pa[j] = A + (size_t)row * rowb + lchunk * 16;
-      pb[j] = B + (size_t)(n < N ? n : N - 1) * rowb + lchunk * 16;
-    }
-    auto issue = [&](int kt) __attribute__((always_inline)) {
-      char *st = smem + (kt % kGStages) * kGStage;
+        for (int i = 0; i < C::MI; ++i)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        dma16(pa[j] + (size_t)kt * 128, st + (w + 4 * j) * 1024);
-        dma16(pb[j] + (size_t)kt * 128, st + kGTile + (w + 4 * j) * 1024);
+          for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int row = i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+              const int col = wn * C::TN + j * 32 + (lane & 31);
+              Cs[row * C::LDC + col] = acc[i][j][e];
+            }
       }
-    };
-
-    floatx16 acc[2][2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
-
-#pragma unroll
-    for (int p = 0; p < kGStages - 1; ++p)
-      if (p < KT) issue(p);
-    const int fr = lane & 31, fk = lane >> 5;
-    for (int kt = 0; kt < KT; ++kt) {
-      // this tile's copies are done once at most the later prefetched tiles'
-      // copies (8 per tile per wave) are outstanding
-      const int later = min(KT - 1 - kt, kGStages - 2);
-      if (later >= 2) wait_vmcnt<16>();
-      else if (later == 1) wait_vmcnt<8>();
-      else wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      // the slot of tile kt+S-1 was last read in iteration kt-1
-      if (kt + kGStages - 1 < KT) issue(kt + kGStages - 1);
-      const char *as = smem + (kt % kGStages) * kGStage, *bs = as + kGTile;
-#pragma unroll
-      for (int ks = 0; ks < kBK16 / 16; ++ks) {
-        bf16x8 af[2], bfr[2];
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int r = wm * 64 + i * 32 + fr;
-          af[i] = *reinterpret_cast<const bf16x8 *>(as + r * 128 + (((2 * ks + fk) ^ ((r >> 1) & 7)) * 16));
-        }
-#pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          const int r = wn * 64 + j * 32 + fr;
-          bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + r * 128 + (((2 * ks + fk) ^ ((r >> 1) & 7)) * 16));
-        }
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
-      }
+      __syncthreads();
+#pragma unroll 1
+      for (int cb = 0; cb < C::BN / kBN; ++cb)
+        epilogue<uint16_t, C::EROWS, MODE, C::THREADS, C::EPI_B>(Cs + cb * kBN, C::LDC, meta + p * C::TM,
+                                                                m0 + p * C::TM, n0 + cb * kBN, g);
     }
-    __syncthreads();  // every wave is done with the ring before it becomes Cs
-    // stage the accumulators: D[row][col], row = 8*(e/4) + 4*(lane/32) + e%4
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = wm * 64 + i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
-          const int col = wn * 64 + j * 32 + (lane & 31);
-          Cs[row * kLDC + col] = acc[i][j][e];
-        }
-    __syncthreads();
-    epilogue<uint16_t, kBM16, MODE>(Cs, kLDC, m0, n0, M, g);
     __syncthreads();
   }
 }
+
+// Finishes the split tail tiles: work-group = (tail tile, 32-row block); adds
+// the tile's K-piece partials and runs the epilogue on them.
+constexpr int kFixRows = 32;
+template <int MODE, typename C>
+__global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
+  constexpr int LDC = C::BN + 4;
+  __shared__ __align__(16) float Cs[kFixRows * LDC];
+  __shared__ EpiRow meta[kFixRows];
+  const int M = g.M_dev ? *g.M_dev : g.M_host;
+  const int mt_n = (M + C::BM - 1) / C::BM, nt_n = (g.N + C::BN - 1) / C::BN;
+  const SplitPlan sp = split_plan(mt_n * nt_n, g.grid_main, g.part_cap);
+  constexpr int RB = C::BM / kFixRows;
+  const int ti = blockIdx.x / RB, rb = blockIdx.x - ti * RB;
+  if (sp.split < 2 || ti >= sp.tail) return;
+  const int tile = sp.full + ti;
+  const int mt = tile / nt_n, nt = tile - mt * nt_n;
+  const int m0 = mt * C::BM + rb * kFixRows, n0 = nt * C::BN;
+  if (m0 >= M) return;
+  load_row_meta<MODE, kFixRows>(meta, m0, M, g);
+  // sum of the pieces, 4 columns per thread and step
+  for (int idx = threadIdx.x; idx < kFixRows * C::BN / 4; idx += 256) {
+    const int r = idx / (C::BN / 4), c4 = (idx - r * (C::BN / 4)) * 4;
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < sp.split; ++j) {
+      const float4 v = *reinterpret_cast<const float4 *>(
+          g.part + (size_t)(ti * sp.split + j) * kGemmPartFloats + (size_t)(rb * kFixRows + r) * C::BN + c4);
+      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+    }
+    *reinterpret_cast<float4 *>(Cs + r * LDC + c4) = acc;
+  }
+  __syncthreads();
+#pragma unroll 1
+  for (int cb = 0; cb < C::BN / kBN; ++cb)
+    epilogue<uint16_t, kFixRows, MODE, 256, 2>(Cs + cb * kBN, LDC, meta, m0, n0 + cb * kBN, g);
+}
+
+// 256x256 tiles, 8 waves of 128x64, four ring slots (128 KB), one work-group per CU
+using GemmBig = GemmCfg<256, 256, 2, 4, 4>;
 
 // ------------------------------------------------------------------------- //
 // fp32 kernel: 64x128 tile, BK 16, each thread 4 rows x 8 columns.
@@ -243,6 +427,7 @@ constexpr int kBM32 = 64, kBK32 = 16;
 template <int MODE>
 __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs g) {
   __shared__ __align__(16) float smem32[kBM32 * kLDC];  // 33,792 B; also holds A/B tiles
+  __shared__ EpiRow meta32[kBM32];
   float *As = smem32;                     // [BK][BM+4]
   float *Bs = smem32 + kBK32 * (kBM32 + 4);  // [BK][BN+4]
   float *Cs = smem32;
@@ -258,6 +443,7 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs g) {
     if (tile < 0) break;
     const int mt = tile / nt_n, nt = tile - mt * nt_n;
     const int m0 = mt * kBM32, n0 = nt * kBN;
+    load_row_meta<MODE, kBM32>(meta32, m0, M, g);
     float acc[4][8];
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -313,25 +499,36 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs g) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) Cs[(ty * 4 + i) * kLDC + tx + 16 * j] = acc[i][j];
     __syncthreads();
-    epilogue<float, kBM32, MODE>(Cs, kLDC, m0, n0, M, g);
+    epilogue<float, kBM32, MODE, 256, 4>(Cs, kLDC, meta32, m0, n0, g);
     __syncthreads();
   }
 }
 
-hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
-  const int bm = g.dtype == SRP_BF16 ? kBM16 : kBM32;
-  const long tiles = (long)((g.M_cap + bm - 1) / bm) * ((g.N + kBN - 1) / kBN);
+hipError_t launch_gemm(const GemmArgs &g0, hipStream_t s) {
+  using C = GemmBig;
+  GemmArgs g = g0;
+  const bool bf = g.dtype == SRP_BF16;
+  const int bm = bf ? C::BM : kBM32, bn = bf ? C::BN : kBN;
+  const long tiles = (long)((g.M_cap + bm - 1) / bm) * ((g.N + bn - 1) / bn);
   if (tiles <= 0) return hipSuccess;
   // resident work-groups (256 CUs x work-groups per CU), a multiple of the 8 XCDs
-  const long resident = g.dtype == SRP_BF16 ? 256L * (kGStages >= 3 ? 1 : 2) : 512L;
+  const long resident = bf ? 256L * C::PER_CU : 512L;
   long grid = tiles < resident ? tiles : resident;
   grid = (grid + 7) / 8 * 8;
-  const dim3 gr((unsigned)grid), bl(256);
-#define SRP_GEMM_LAUNCH(M)                                               \
-  if (g.dtype == SRP_BF16)                                               \
-    hipLaunchKernelGGL(gemm_bf16_kernel<M>, gr, bl, 0, s, g);            \
-  else                                                                   \
-    hipLaunchKernelGGL(gemm_f32_kernel<M>, gr, bl, 0, s, g);
+  g.grid_main = (int)grid;
+  if (!bf || !g.part) g.part_cap = 0;
+  const dim3 gr((unsigned)grid), bl(bf ? C::THREADS : 256);
+  // fix-up grid: every tail tile a split can produce (at most part_cap / 2)
+  const long fix_tiles = g.part_cap / 2 < tiles ? g.part_cap / 2 : tiles;
+  const dim3 fgr((unsigned)(fix_tiles > 0 ? fix_tiles * (C::BM / kFixRows) : 1));
+#define SRP_GEMM_LAUNCH(M)                                                     \
+  if (bf) {                                                                    \
+    hipLaunchKernelGGL((gemm_bf16_kernel<M, C>), gr, bl, 0, s, g);             \
+    if (fix_tiles > 0)                                                         \
+      hipLaunchKernelGGL((gemm_fixup_kernel<M, C>), fgr, dim3(256), 0, s, g);  \
+  } else {                                                                     \
+    hipLaunchKernelGGL(gemm_f32_kernel<M>, gr, bl, 0, s, g);                   \
+  }
   switch (g.mode) {
     case EPI_KV: SRP_GEMM_LAUNCH(EPI_KV); break;
     case EPI_Q: SRP_GEMM_LAUNCH(EPI_Q); break;

@@ -36,6 +36,9 @@ struct GemmArgs {
   float *dev_part;
   void *q_out;
   float q_scale;  // EPI_Q: factor applied to the roped queries
+  float *part;    // bf16: fp32 partial tiles of split tail tiles (kGemmPartFloats each), or NULL
+  int part_cap;   // partial-tile slots at `part`
+  int grid_main;  // set by launch_gemm: work-groups of the main kernel
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 

@@ -93,8 +93,13 @@ def test_workspace_monotone():
     sizes = [S.srp_workspace_size(_dims(), _batch(total_rows=t, max_req_rows=t), s)
              for t in (0, 1, 100, 1000, 10000)]
     assert sizes == sorted(sizes)
-    assert S.srp_workspace_size(_dims(dtype=S.SRP_F32), _batch(), s) > \
-        S.srp_workspace_size(_dims(), _batch(), s)
+    # the per-row part scales with the element size (bf16 adds a fixed block of
+    # split-K partial tiles)
+    def growth(dt):
+        dd = _dims(dtype=dt)
+        return (S.srp_workspace_size(dd, _batch(total_rows=10000, max_req_rows=10000), s)
+                - S.srp_workspace_size(dd, _batch(total_rows=1000, max_req_rows=1000), s))
+    assert growth(S.SRP_F32) > growth(S.SRP_BF16)
 
 
 def test_struct_layouts_match_header():
