@@ -179,23 +179,28 @@ struct TileIter {
 
 // ------------------------------------------------------------------------- //
 // bf16 MFMA kernel: BM x BN tile, WM x WN waves, each wave owning a
-// (BM/WM) x (BN/WN) block of 32x32x16 MFMA tiles. Operand tiles of depth 32
-// (64-byte rows) stream into an S-slot LDS ring with direct-to-LDS copies (no
-// staging registers); copy q of a tile moves rows 16q..16q+15. Chunk c of row r
-// is stored at c ^ ((r / 4) % 4): a 16-byte LDS read serves 16 lanes (64 banks)
-// per cycle and the fragment reads put 16 consecutive rows in those lanes,
-// which this layout spreads over 16 different bank groups.
+// (BM/WM) x (BN/WN) block of 32x32x16 MFMA tiles. Operand tiles of depth BK
+// stream into an S-slot LDS ring with direct-to-LDS copies (no staging
+// registers); each copy moves 1 KB, i.e. 1024 / (2 BK) whole row segments.
+// Row segments of at least 128 bytes (BK >= 64) keep the copies at full rate;
+// 64-byte segments (half cache lines) run at a third of it. With CH = BK / 8
+// chunks of 16 bytes per row, chunk c of row r is stored at
+// c ^ ((r / (16 / CH)) % CH): a 16-byte LDS read serves 16 lanes (64 banks) per
+// cycle, the fragment reads put 16 consecutive rows in those lanes, and this
+// layout gives them 16 different bank groups.
 // ------------------------------------------------------------------------- //
-constexpr int kGBK = 32;
 
-template <int BM_, int BN_, int WM_, int WN_, int S_>
+template <int BM_, int BN_, int WM_, int WN_, int S_, int BK_>
 struct GemmCfg {
-  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_;
+  static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_, S = S_, BK = BK_;
+  static constexpr int CH = BK / 8;    // 16-byte chunks per operand row
+  static constexpr int RPC = 64 / CH;  // rows per 1 KB copy
+  static constexpr int SWZ = 16 / CH;  // consecutive rows sharing a swizzle value
   static constexpr int WAVES = WM * WN, THREADS = 64 * WAVES;
   static constexpr int TM = BM / WM, TN = BN / WN;  // wave tile
   static constexpr int MI = TM / 32, NI = TN / 32;
-  static constexpr int ATILE = BM * kGBK * 2, STAGE = (BM + BN) * kGBK * 2;
-  static constexpr int ACOPY = BM / 16, COPIES = (BM + BN) / 16;
+  static constexpr int ATILE = BM * BK * 2, STAGE = (BM + BN) * BK * 2;
+  static constexpr int ACOPY = BM / RPC, COPIES = (BM + BN) / RPC;
   static constexpr int CPW = COPIES / WAVES;  // copies per wave per tile
   static constexpr int EROWS = TM;            // rows staged per epilogue pass (one wave row)
   static constexpr int LDC = BN + 4;
@@ -246,15 +251,17 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / C::WN, wn = w - wm * C::WN;
   const char *A = (const char *)g.A, *B = (const char *)g.B;
-  const int KT = K / kGBK;
+  const int KT = K / C::BK;
   const size_t rowb = (size_t)K * 2;
-  // copy layout: lane covers row 16q + lrow and physical chunk lane % 4, which
-  // holds logical chunk lchunk (the swizzle term depends on the lane only)
-  const int lrow = lane >> 2, lchunk = (lane & 3) ^ ((lrow >> 2) & 3);
+  // copy layout: lane covers row RPC*q + lrow and physical chunk lane % CH,
+  // which holds logical chunk lchunk. This wave's copies are q = w + WAVES*j,
+  // and the swizzle term of their rows depends on q only through w.
+  const int lrow = lane / C::CH;
+  const int lchunk = (lane % C::CH) ^ (((C::RPC * w + lrow) / C::SWZ) % C::CH);
   // fragment reads: lane holds row (lane % 32) of a 32-row block and k-values
   // 8 * (lane / 32) .. +8 of each 16-deep step
   const int fr = lane & 31, fk = lane >> 5;
-  const uint32_t fswz = (fr >> 2) & 3;
+  const uint32_t fswz = (fr / C::SWZ) % C::CH;
   floatx16 acc[C::MI][C::NI];
 
   // acc = A[m0.., k0*32 ..] * B[n0.., ..]^T over nk k-tiles; `pre` runs once the
@@ -268,18 +275,18 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
     for (int j = 0; j < C::CPW; ++j) {
       const int q = w + C::WAVES * j;
       if (q < C::ACOPY) {
-        const int m = m0 + 16 * q + lrow;
+        const int m = m0 + C::RPC * q + lrow;
         const int row = m < M ? (g.a_rows ? g.a_rows[m] : m) : row0;
-        src[j] = A + (size_t)row * rowb + (size_t)k0 * (kGBK * 2) + lchunk * 16;
+        src[j] = A + (size_t)row * rowb + (size_t)k0 * (C::BK * 2) + lchunk * 16;
       } else {
-        const int n = n0 + 16 * (q - C::ACOPY) + lrow;
-        src[j] = B + (size_t)(n < N ? n : N - 1) * rowb + (size_t)k0 * (kGBK * 2) + lchunk * 16;
+        const int n = n0 + C::RPC * (q - C::ACOPY) + lrow;
+        src[j] = B + (size_t)(n < N ? n : N - 1) * rowb + (size_t)k0 * (C::BK * 2) + lchunk * 16;
       }
     }
     auto issue = [&](int kt) __attribute__((always_inline)) {
       char *st = smem + (kt % C::S) * C::STAGE;
 #pragma unroll
-      for (int j = 0; j < C::CPW; ++j) dma16(src[j] + (size_t)kt * (kGBK * 2), st + (w + C::WAVES * j) * 1024);
+      for (int j = 0; j < C::CPW; ++j) dma16(src[j] + (size_t)kt * (C::BK * 2), st + (w + C::WAVES * j) * 1024);
     };
 #pragma unroll
     for (int i = 0; i < C::MI; ++i)
@@ -304,15 +311,15 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
       if (kt + C::S - 1 < nk) issue(kt + C::S - 1);
       const char *as = smem + (kt % C::S) * C::STAGE, *bs = as + C::ATILE;
 #pragma unroll
-      for (int ks = 0; ks < kGBK / 16; ++ks) {
-        const uint32_t off = fr * (kGBK * 2) + (((2 * ks + fk) ^ fswz) * 16);
+      for (int ks = 0; ks < C::BK / 16; ++ks) {
+        const uint32_t off = fr * (C::BK * 2) + (((2 * ks + fk) ^ fswz) * 16);
         bf16x8 af[C::MI], bfr[C::NI];
 #pragma unroll
         for (int i = 0; i < C::MI; ++i)
-          af[i] = *reinterpret_cast<const bf16x8 *>(as + (wm * C::TM + i * 32) * (kGBK * 2) + off);
+          af[i] = *reinterpret_cast<const bf16x8 *>(as + (wm * C::TM + i * 32) * (C::BK * 2) + off);
 #pragma unroll
         for (int j = 0; j < C::NI; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + (wn * C::TN + j * 32) * (kGBK * 2) + off);
+          bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + (wn * C::TN + j * 32) * (C::BK * 2) + off);
 #pragma unroll
         for (int i = 0; i < C::MI; ++i)
 #pragma unroll
@@ -416,8 +423,9 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
     epilogue<uint16_t, kFixRows, MODE, 256, 2>(Cs + cb * kBN, LDC, meta, m0, n0 + cb * kBN, g);
 }
 
-// 256x256 tiles, 8 waves of 128x64, four ring slots (128 KB), one work-group per CU
-using GemmBig = GemmCfg<256, 256, 2, 4, 4>;
+// 256x256 tiles, 8 waves of 128x64, two 64-deep ring slots (128 KB), one
+// work-group per CU
+using GemmBig = GemmCfg<256, 256, 2, 4, 2, 64>;
 
 // ------------------------------------------------------------------------- //
 // fp32 kernel: 64x128 tile, BK 16, each thread 4 rows x 8 columns.
