@@ -68,13 +68,16 @@ __device__ __forceinline__ void st4(uint16_t *p, const float v[4]) {
 // ------------------------------------------------------------------------- //
 // wave / block primitives (wave64)
 // ------------------------------------------------------------------------- //
+// Inclusive scan over the wave with DPP lane shifts (no LDS round trips):
+// row_shr 1/2/4/8 scan each row of 16 lanes, row_bcast 15/31 carry the row
+// totals into the rows above.
 __device__ __forceinline__ int wave_incl_scan(int v) {
-  const int lane = threadIdx.x & 63;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int t = __shfl_up(v, o, 64);
-    if (lane >= o) v += t;
-  }
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);  // row_bcast:15 -> rows 1, 3
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);  // row_bcast:31 -> rows 2, 3
   return v;
 }
 
@@ -82,16 +85,18 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
 // `sh` needs 17 ints of LDS. Returns the exclusive prefix; *total = block sum.
 __device__ __forceinline__ int block_excl_scan(int v, int *sh, int *total) {
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  int inc = wave_incl_scan(v);
+  const int inc = wave_incl_scan(v);
   if (lane == 63) sh[wid] = inc;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int run = 0;
-    for (int w = 0; w < nw; ++w) { int t = sh[w]; sh[w] = run; run += t; }
-    sh[16] = run;
+  if (wid == 0) {
+    // wave 0 scans the wave totals
+    const int t = lane < nw ? sh[lane] : 0;
+    const int ti = wave_incl_scan(t);
+    if (lane < nw) sh[lane] = ti - t;
+    if (lane == 63) sh[16] = ti;
   }
   __syncthreads();
-  int res = sh[wid] + inc - v;
+  const int res = sh[wid] + inc - v;
   *total = sh[16];
   __syncthreads();
   return res;

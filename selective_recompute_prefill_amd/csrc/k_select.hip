@@ -354,16 +354,31 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
   __shared__ uint32_t keys_s[kLdsEntries];  // later: seq_ent (u16) | seq_pre (u16)
   __shared__ uint8_t fl_s[kLdsEntries];
   __shared__ uint8_t sq_s[kLdsEntries];      // grouping: bit 0 top-k slot, bit 1 passing window
+  __shared__ int sh_max[1024];               // grouping: max-scan of passing starts
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int *roff = a.cand ? w.roff : a.req_offsets;
   const int e0 = roff[r], e1 = roff[r + 1], n = e1 - e0;
 
   int my_cand = 0;
-  for (int i = tid; i < n; i += nt) {
-    const uint8_t f = w.eflag[e0 + i];
-    fl_s[i] = f;
-    keys_s[i] = (f & kCand) ? w.keys[e0 + i] : 0u;
-    my_cand += (f & kCand) ? 1 : 0;
+  for (int i = tid; i < n; i += 4 * nt) {
+    // four independent loads of flags and keys per thread before any store
+    uint8_t f[4];
+    uint32_t k4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = i + u * nt;
+      f[u] = j < n ? w.eflag[e0 + j] : 0;
+      k4[u] = j < n ? w.keys[e0 + j] : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = i + u * nt;
+      if (j < n) {
+        fl_s[j] = f[u];
+        keys_s[j] = (f[u] & kCand) ? k4[u] : 0u;
+        my_cand += (f[u] & kCand) ? 1 : 0;
+      }
+    }
   }
   int my_ctx = 0;
   if (a.cand) {
@@ -453,11 +468,27 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
       }
     }
     __syncthreads();
-    for (int p = tid; p < n_seq; p += nt) {
-      bool kept = false;
-      const int t0 = p - win + 1 > 0 ? p - win + 1 : 0;
-      for (int t = t0; t <= p; ++t) kept |= (sq_s[t] & 2) != 0;
-      if (kept) fl_s[seq_ent[p]] |= kSel;
+    // a slot is kept when the latest passing window start at or before it lies
+    // within the window: a max-scan of passing starts over contiguous segments
+    {
+      int lo2, hi2;
+      my_segment(n_seq, lo2, hi2);
+      int last = -1;
+      for (int t = lo2; t < hi2; ++t) last = (sq_s[t] & 2) ? t : last;
+      // latest passing start before this segment: max over earlier segments
+      sh_max[tid] = last;
+      __syncthreads();
+      for (int o = 1; o < nt; o <<= 1) {
+        const int v = tid >= o ? sh_max[tid - o] : -1;
+        __syncthreads();
+        if (v > sh_max[tid]) sh_max[tid] = v;
+        __syncthreads();
+      }
+      int run = tid > 0 ? sh_max[tid - 1] : -1;
+      for (int t = lo2; t < hi2; ++t) {
+        if (sq_s[t] & 2) run = t;
+        if (run >= 0 && run > t - win) fl_s[seq_ent[t]] |= kSel;
+      }
     }
     __syncthreads();
   }
