@@ -406,16 +406,36 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   const int m0 = mt * C::BM + rb * kFixRows, n0 = nt * C::BN;
   if (m0 >= M) return;
   load_row_meta<MODE, kFixRows>(meta, m0, M, g);
-  // sum of the pieces, 4 columns per thread and step
-  for (int idx = threadIdx.x; idx < kFixRows * C::BN / 4; idx += 256) {
-    const int r = idx / (C::BN / 4), c4 = (idx - r * (C::BN / 4)) * 4;
-    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < sp.split; ++j) {
-      const float4 v = *reinterpret_cast<const float4 *>(
-          g.part + (size_t)(ti * sp.split + j) * kGemmPartFloats + (size_t)(rb * kFixRows + r) * C::BN + c4);
-      acc.x += v.x; acc.y += v.y; acc.z += v.z; acc.w += v.w;
+  // sum of the pieces, 4 columns per thread and step. The loads of all
+  // kMaxSplit slots (unused ones clamped to a valid slot and weighted 0) and of
+  // two column groups are issued together, so the sum waits for one round trip.
+  constexpr int PER = kFixRows * C::BN / 4 / 256;
+  static_assert(PER % 2 == 0, "column groups in pairs");
+  for (int u0 = 0; u0 < PER; u0 += 2) {
+    float4 v[kMaxSplit][2];
+#pragma unroll
+    for (int j = 0; j < kMaxSplit; ++j) {
+      const int jj = j < sp.split ? j : sp.split - 1;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = threadIdx.x + (u0 + u) * 256;
+        const int r = idx / (C::BN / 4), c4 = (idx - r * (C::BN / 4)) * 4;
+        v[j][u] = *reinterpret_cast<const float4 *>(
+            g.part + (size_t)(ti * sp.split + jj) * kGemmPartFloats + (size_t)(rb * kFixRows + r) * C::BN + c4);
+      }
     }
-    *reinterpret_cast<float4 *>(Cs + r * LDC + c4) = acc;
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < kMaxSplit; ++j) {
+        const float wj = j < sp.split ? 1.f : 0.f;
+        acc.x += wj * v[j][u].x; acc.y += wj * v[j][u].y; acc.z += wj * v[j][u].z; acc.w += wj * v[j][u].w;
+      }
+      const int idx = threadIdx.x + (u0 + u) * 256;
+      const int r = idx / (C::BN / 4), c4 = (idx - r * (C::BN / 4)) * 4;
+      *reinterpret_cast<float4 *>(Cs + r * LDC + c4) = acc;
+    }
   }
   __syncthreads();
 #pragma unroll 1
