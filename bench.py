@@ -50,8 +50,12 @@ def parse():
     p.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                    help="only run a plain device-to-device copy of MIB MiB five times (the "
                         "reference for scaling the HBM byte counters) and exit")
-    p.add_argument("--summarize-trace", metavar="STATS_CSV",
-                   help="print a markdown table of a rocprofv3 --stats kernel CSV and exit")
+    p.add_argument("--summarize-trace", metavar="CSV",
+                   help="print a markdown table of a rocprofv3 kernel CSV (--stats summary, or the "
+                        "per-dispatch kernel trace, see --trace-skip) and exit")
+    p.add_argument("--trace-skip", type=int, default=0,
+                   help="with a per-dispatch kernel trace: leave out each kernel's first N "
+                        "dispatches (the warm-up calls)")
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
                    help="print the per-launch HBM traffic summary from four rocprofv3 --pmc "
                         "counter CSVs (kernel FETCH_SIZE, kernel WRITE_SIZE, copy FETCH_SIZE, "
@@ -92,8 +96,8 @@ def algorithmic_work(spec, lay, sel, ratio_rows):
 # a recorded traffic figure is used only while these files are unchanged.
 TRAFFIC_KERNELS = {
     "attn_bf16_kernel<128>": ("attn_bf16_kernel<128>", ["k_attn.hip", "kernels.hpp", "common.hpp"]),
-    "gemm_bf16_kernel<EPI_KV>": ("gemm_bf16_kernel<0>", ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
-    "gemm_bf16_kernel<EPI_Q>": ("gemm_bf16_kernel<1>", ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
+    "gemm_bf16_kernel<EPI_KV>": ("gemm_bf16_kernel<0,", ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
+    "gemm_bf16_kernel<EPI_Q>": ("gemm_bf16_kernel<1,", ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
 }
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_14b_16k_grouped.md")
 
@@ -178,10 +182,24 @@ def summarize_pmc(fetch, write, cfetch, cwrite, copy_mib):
     return "\n".join(head + lines + ["", "```json", json.dumps(rec, indent=1), "```", ""])
 
 
-def summarize_trace(stats_csv):
+def summarize_trace(stats_csv, skip=0):
     import csv
     with open(stats_csv) as fh:
         rows = list(csv.DictReader(fh))
+    if rows and "Start_Timestamp" in rows[0]:
+        # per-dispatch trace: aggregate per kernel, without its first `skip` calls
+        per = {}
+        for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
+            per.setdefault(r["Kernel_Name"], []).append(
+                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+        agg = []
+        for name, d in per.items():
+            d = d[skip:] if len(d) > skip else d
+            agg.append((name, len(d), sum(d), min(d), max(d)))
+        total = sum(a[2] for a in agg) or 1
+        rows = [{"Name": n, "Calls": c, "TotalDurationNs": t, "AverageNs": t / c, "MinNs": mn,
+                 "MaxNs": mx, "Percentage": 100.0 * t / total}
+                for n, c, t, mn, mx in sorted(agg, key=lambda a: -a[2])]
     lines = ["| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
     for r in rows[:16]:
         nm = r["Name"] if len(r["Name"]) < 70 else r["Name"][:67] + "..."
@@ -254,7 +272,7 @@ def cpu_baseline(spec, n_chunks_sample):
 def main():
     args = parse()
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace), end="")
+        print(summarize_trace(args.summarize_trace, args.trace_skip), end="")
         return
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc, args.copy_mib), end="")
