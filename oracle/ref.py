@@ -21,7 +21,9 @@ Where the pages are silent, garbled or disagree, the reading taken is stated at 
 function and listed, with every other reading, in the design notes of the repo.
 
 Parity status: every function is pinned by the CPU tests (closed forms, brute
-force, library cross-checks, the grouping figure). The intermediate layers of the
+force, library cross-checks, the grouping figure; for span completion, hand-worked
+cases, a characterisation of the segmentation and a cross-check of the external-score
+mode against deviation-ranked top-k). The intermediate layers of the
 multi-layer chain are pinned only through the invariants of the single layer and
 the all-recompute reduction of the whole stack.
 """
@@ -140,11 +142,20 @@ def kv_deviation(k_new, v_new, k_old, v_old, mode: str = "kv") -> np.ndarray:
     return np.sqrt(dk + dv)
 
 
-def topk_count(ratio: float, n_ctx: int, n_cand: int) -> int:
-    """k = round(ratio * N) with halves rounded up (CacheClip walkthrough, section
-    6.2: k = round(recomp_ratio * N)), N = cached rows of the request, clamped to the
-    number of candidates."""
-    return int(min(np.floor(float(ratio) * n_ctx + 0.5), n_cand))
+def topk_count(ratio: float, n_ctx: int, n_cand: int, rule: str = "round") -> int:
+    """Top-k size from the recompute ratio, clamped to the number of candidates.
+    rule "round": k = round(ratio * N) with halves rounded up (CacheClip walkthrough,
+    section 6.2: k = round(recomp_ratio * N)); rule "ceil": K = ceil(rho * N)
+    (SpecCache notes 2.2). N = cached rows of the request; the product is taken in
+    float64."""
+    x = float(ratio) * n_ctx
+    if rule == "ceil":
+        k = np.ceil(x)
+    elif rule == "round":
+        k = np.floor(x + 0.5)
+    else:
+        raise ValueError(rule)
+    return int(min(k, n_cand))
 
 
 def topk_rows(dev: np.ndarray, rows: np.ndarray, k: int) -> np.ndarray:
@@ -175,6 +186,76 @@ def group_windows(cand_seq: Sequence[int], seq_len: int, w: int, tau: int) -> Li
         if int(member[start:start + w].sum()) >= tau:
             keep[start:start + w] = True
     return [int(i) for i in np.nonzero(keep)[0]]
+
+
+# --------------------------------------------------------------------------- #
+# span completion of a score-ranked selection
+# --------------------------------------------------------------------------- #
+
+
+def normalise_scores(score: np.ndarray) -> np.ndarray:
+    """Min-max normalisation of a token score sequence to [0, 1] (SpecCache notes 2.3,
+    span segmentation). Constant scores give 0/0 = NaN everywhere (IEEE); the span
+    rule below then merges nothing."""
+    s = np.asarray(score, np.float64)
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return (s - s.min()) / (s.max() - s.min())
+
+
+def relative_change(norm: np.ndarray) -> np.ndarray:
+    """delta_i = |I~_{i+1} - I~_i| / I~_i for consecutive tokens of the sequence
+    (SpecCache notes 2.3), evaluated in IEEE float64: a token at the minimum gives
+    +inf (or NaN when its successor is also at the minimum)."""
+    with np.errstate(invalid="ignore", divide="ignore"):
+        return np.abs(norm[1:] - norm[:-1]) / norm[:-1]
+
+
+def segment_spans(score: np.ndarray, tau_smooth: float, max_len: int) -> List[tuple]:
+    """Split a token sequence into spans [u, v] (inclusive) of locally smooth scores
+    (SpecCache notes 2.3): walking left to right, the next token joins the current
+    span while delta < tau_smooth holds (a NaN delta does not hold) and the span is
+    shorter than max_len; otherwise a new span starts at that token."""
+    n = len(score)
+    if n == 0:
+        return []
+    delta = relative_change(normalise_scores(score))
+    spans = []
+    u = 0
+    for i in range(n - 1):
+        if delta[i] < tau_smooth and i - u + 1 < max_len:
+            continue
+        spans.append((u, i))
+        u = i + 1
+    spans.append((u, n - 1))
+    return spans
+
+
+def complete_spans(score: np.ndarray, init: np.ndarray, tau_smooth: float, max_len: int,
+                   tau_cover: float) -> np.ndarray:
+    """Coverage-based span completion (SpecCache notes 2.3): a span whose share of
+    initially selected tokens, |T_init & [u, v]| / (v - u + 1) in float64, is at least
+    tau_cover is added whole; the result is T_init united with those spans."""
+    init = np.asarray(init, bool)
+    out = init.copy()
+    for u, v in segment_spans(score, tau_smooth, max_len):
+        cover = float(init[u:v + 1].sum()) / float(v - u + 1)
+        if cover >= tau_cover:
+            out[u:v + 1] = True
+    return out
+
+
+def budget_cap(score: np.ndarray, chosen: np.ndarray, m: int) -> np.ndarray:
+    """Global budget after span completion (SpecCache notes 2.3): when more than m
+    tokens are chosen, keep the m with the highest score (equal scores: the earlier
+    token) and drop the rest."""
+    chosen = np.asarray(chosen, bool)
+    if chosen.sum() <= m:
+        return chosen.copy()
+    idx = np.nonzero(chosen)[0]
+    keep = topk_rows(np.asarray(score, np.float64)[idx], idx, m)
+    out = np.zeros_like(chosen)
+    out[keep] = True
+    return out
 
 
 def attention(q: np.ndarray, q_rows: np.ndarray, k: np.ndarray, v: np.ndarray,
@@ -215,43 +296,100 @@ def residual_rmsnorm(x: np.ndarray, o: np.ndarray, eps: float = 1e-6) -> np.ndar
 # --------------------------------------------------------------------------- #
 
 
+def _score_selection(score_r: np.ndarray, c_r: np.ndarray, n_ctx: int, ratio: float,
+                     k_rule: str, window: int, tau: int, span_max: int, tau_smooth: float,
+                     tau_cover: float, cap_ratio: float):
+    """Selection of one request's candidates c_r (ascending rows) from external token
+    scores score_r (SpecCache notes 2.2-2.3; CacheClip paper 4.2-4.3 for the scores
+    with window grouping): T_init = the top K by score, then optional window grouping
+    or span completion over the candidate sequence, then the optional budget cap.
+    Returns (T_init rows, selected rows)."""
+    k = topk_count(ratio, n_ctx, len(c_r), k_rule)
+    s0 = topk_rows(score_r, c_r, k)
+    if span_max > 0:
+        init = np.isin(c_r, s0)
+        chosen = complete_spans(score_r, init, tau_smooth, span_max, tau_cover)
+        if cap_ratio > 0:
+            chosen = budget_cap(score_r, chosen, topk_count(cap_ratio, n_ctx, len(c_r), k_rule))
+        return s0, c_r[chosen]
+    if window > 0:
+        slot = {int(j): i for i, j in enumerate(c_r)}
+        kept = group_windows([slot[int(j)] for j in s0], len(c_r), window, tau)
+        return s0, (c_r[np.asarray(kept, np.int64)] if kept else np.zeros(0, np.int64))
+    return s0, s0
+
+
 def fuse_layer(*, hidden, w_qkv, k_cache, v_cache, req_offsets, chunk_offsets,
                chunk_src_pos, positions, n_heads, n_kv, head_dim, rope_base,
                ratio, mode: str = "topk", window: int = 0, tau: int = 0,
                dev_mode: str = "kv", cand: Optional[np.ndarray] = None,
                sel_override: Optional[np.ndarray] = None,
-               attn_sample: Optional[np.ndarray] = None) -> Dict[str, np.ndarray]:
+               attn_sample: Optional[np.ndarray] = None, k_rule: str = "round",
+               scores: Optional[np.ndarray] = None, span_max: int = 0,
+               tau_smooth: float = 0.4, tau_cover: float = 0.7, cap_ratio: float = 0.0,
+               fresh_all: bool = False) -> Dict[str, np.ndarray]:
     """One selective-recompute layer, all float64 (CacheBlend walkthrough,
-    "Selective KV recompute" and "Implementation"; CacheClip paper 4.1-4.3).
+    "Selective KV recompute" and "Implementation"; CacheClip paper 4.1-4.3; SpecCache
+    notes 2.1-2.3).
 
     Inputs are float64 arrays (already widened from storage). cand = candidate rows
-    (None = every cached row). mode "topk" scores candidates and keeps the top
-    round(ratio*N_ctx) per request; mode "given" keeps the candidates as they are.
-    sel_override replaces the selected set (used to compare downstream stages on
-    another implementation's selection). Returns the selected rows (ascending,
-    fresh rows included), per-request offsets, the fused caches, the attention
-    output rows and the per-row deviation (NaN where not scored)."""
+    (None = every cached row). mode "topk" scores candidates by KV deviation and keeps
+    the top k per request (k from ratio * N_ctx by k_rule); mode "given" keeps the
+    candidates as they are; mode "scores" ranks the candidates by the caller's
+    per-row scores instead (no deviation is needed to choose, so only the selected
+    rows are recomputed), with window grouping or span completion (span_max > 0,
+    tau_smooth, tau_cover, cap_ratio = budget as a ratio of N_ctx, 0 = none).
+    fresh_all: every recomputed row takes its fresh K/V, not only the selected ones
+    (CacheBlend walkthrough, "The chicken-and-egg problem": the figure of gradual
+    filtering shows every candidate of a layer recomputed). sel_override replaces
+    the selected set (used to compare downstream stages on another implementation's
+    selection). Returns the selected rows (ascending, fresh rows included),
+    per-request offsets, the fused caches, the attention output rows and the per-row
+    deviation (NaN where not scored; in mode "scores", the deviation of the
+    recomputed cached rows)."""
     T = hidden.shape[0]
     d = head_dim
-    if window > 0 and cand is not None:
+    if (window > 0 or span_max > 0) and cand is not None:
         raise ValueError("grouping scans the whole cached sequence: cand must be None")
     req, src = row_layout(req_offsets, chunk_offsets, chunk_src_pos, T)
     cached = src >= 0
     fresh = ~cached
     pos = np.asarray(positions, np.int64)
+    n_req = len(req_offsets) - 1
 
     # 1. positional recovery of every cached key
     k_tilde = rerotate(k_cache, pos, src, rope_base)
 
-    # 2. candidate set C and the rows recomputed to score them: C plus fresh rows
+    # 2. candidate set C
     if cand is None:
         is_cand = cached.copy()
     else:
         is_cand = np.zeros(T, bool)
         is_cand[np.asarray(cand, np.int64)] = True
         is_cand &= cached
-    rec = np.nonzero(is_cand | fresh)[0]
 
+    # 2b. with external scores the selection comes first; C shrinks to it
+    sel_parts = []
+    s0_parts = []
+    kth = []
+    if mode == "scores":
+        score = np.asarray(scores, np.float64)
+        for r in range(n_req):
+            rows_r = np.arange(req_offsets[r], req_offsets[r + 1])
+            c_r = rows_r[is_cand[rows_r]]
+            n_ctx = int(cached[rows_r].sum())
+            s0, s = _score_selection(score[c_r], c_r, n_ctx, ratio, k_rule, window, tau,
+                                     span_max, tau_smooth, tau_cover, cap_ratio)
+            s0_parts.append(s0)
+            kth.append(score[s0].min() if len(s0) else np.nan)
+            sel_parts.append(np.union1d(s, rows_r[fresh[rows_r]]))
+        is_cand = np.zeros(T, bool)
+        for s in sel_parts:
+            is_cand[s] = True
+        is_cand &= cached
+
+    # 2c. the rows recomputed: C plus fresh rows
+    rec = np.nonzero(is_cand | fresh)[0]
     _, kf, vf = project(hidden[rec], w_qkv, n_heads, n_kv, d)
     kf = rope(kf, pos[rec], rope_base)
     k_new = np.zeros_like(k_cache)
@@ -265,38 +403,39 @@ def fuse_layer(*, hidden, w_qkv, k_cache, v_cache, req_offsets, chunk_offsets,
         dev[ci] = kv_deviation(k_new[ci], v_new[ci], k_tilde[ci], v_cache[ci], dev_mode)
 
     # 4. selection per request
-    sel_parts = []
-    s0_parts = []
-    kth = []
-    for r in range(len(req_offsets) - 1):
-        rows_r = np.arange(req_offsets[r], req_offsets[r + 1])
-        c_r = rows_r[is_cand[rows_r]]
-        n_ctx = int(cached[rows_r].sum())
-        if mode == "given":
-            s0 = c_r
-            kth.append(np.nan)
-        else:
-            k = topk_count(ratio, n_ctx, len(c_r))
-            s0 = topk_rows(dev[c_r], c_r, k)
-            kth.append(dev[s0].min() if len(s0) else np.nan)
-        s0_parts.append(s0)
-        if window > 0:
-            seq = rows_r[cached[rows_r]]  # the request's cached tokens, in order
-            slot = {int(j): i for i, j in enumerate(seq)}
-            kept = group_windows([slot[int(j)] for j in s0], len(seq), window, tau)
-            s = seq[np.asarray(kept, np.int64)] if kept else np.zeros(0, np.int64)
-        else:
-            s = s0
-        sel_parts.append(np.union1d(s, rows_r[fresh[rows_r]]))
+    if mode != "scores":
+        for r in range(n_req):
+            rows_r = np.arange(req_offsets[r], req_offsets[r + 1])
+            c_r = rows_r[is_cand[rows_r]]
+            n_ctx = int(cached[rows_r].sum())
+            if mode == "given":
+                s0 = c_r
+                kth.append(np.nan)
+            elif mode == "topk":
+                k = topk_count(ratio, n_ctx, len(c_r), k_rule)
+                s0 = topk_rows(dev[c_r], c_r, k)
+                kth.append(dev[s0].min() if len(s0) else np.nan)
+            else:
+                raise ValueError(mode)
+            s0_parts.append(s0)
+            if window > 0:
+                seq = rows_r[cached[rows_r]]  # the request's cached tokens, in order
+                slot = {int(j): i for i, j in enumerate(seq)}
+                kept = group_windows([slot[int(j)] for j in s0], len(seq), window, tau)
+                s = seq[np.asarray(kept, np.int64)] if kept else np.zeros(0, np.int64)
+            else:
+                s = s0
+            sel_parts.append(np.union1d(s, rows_r[fresh[rows_r]]))
     if sel_override is not None:
         sel = np.asarray(sel_override, np.int64)
     else:
         sel = np.concatenate(sel_parts) if sel_parts else np.zeros(0, np.int64)
     sel_offsets = np.zeros(len(req_offsets), np.int64)
-    for r in range(len(req_offsets) - 1):
+    for r in range(n_req):
         sel_offsets[r + 1] = sel_offsets[r] + int(np.sum(req[sel] == r))
 
-    # 5. expand: selected rows take their recomputed K/V, the rest keep the cache
+    # 5. expand: selected rows (every recomputed row with fresh_all) take their
+    #    recomputed K/V, the rest keep the cache
     if sel_override is not None:
         missing = np.setdiff1d(sel, rec)
         if len(missing):  # an override may name rows that were not recomputed
@@ -304,8 +443,9 @@ def fuse_layer(*, hidden, w_qkv, k_cache, v_cache, req_offsets, chunk_offsets,
             k_new[missing], v_new[missing] = rope(km, pos[missing], rope_base), vm
     k_out = k_tilde.copy()
     v_out = v_cache.copy()
-    k_out[sel] = k_new[sel]
-    v_out[sel] = v_new[sel]
+    upd = np.union1d(sel, rec) if fresh_all else sel
+    k_out[upd] = k_new[upd]
+    v_out[upd] = v_new[upd]
 
     # 6. queries of the selected rows and their attention over the fused cache
     #    (attn_sample: positions into the selection whose rows are evaluated;

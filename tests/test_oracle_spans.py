@@ -1,0 +1,245 @@
+"""Pins of the oracle's score-driven selection: the ceil rule for K, min-max
+normalisation, span segmentation, coverage completion and the budget cap (SpecCache
+notes 2.2-2.3), and of the layer in external-score mode. Each test checks against
+something other than the oracle's own formula: hand-worked values (tests/golden),
+a library routine, a characterisation that fixes the segmentation uniquely, brute
+force, or another mode of the layer that must agree. CPU only."""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from oracle import ref
+from selective_recompute_prefill_amd import inputs
+
+
+def _golden(golden_dir):
+    return json.load(open(os.path.join(golden_dir, "span_completion.json")))
+
+
+def _scores(case):
+    s = case["scores"]
+    if isinstance(s, str):  # "10 + 0.01 i, i < 20"
+        return 10.0 + 0.01 * np.arange(20)
+    return np.asarray(s, np.float64)
+
+
+def test_topk_count_ceil_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "topk_counts.json")))
+    for c in g["cases"]:
+        assert ref.topk_count(c["ratio"], c["n"], 10 ** 9, "ceil") == c["ceil"], c
+    assert ref.topk_count(0.2, 6, 10, "ceil") == 2 and ref.topk_count(0.2, 6, 10) == 1
+
+
+def test_normalise_and_delta_golden(golden_dir):
+    for c in _golden(golden_dir)["normalise"]:
+        norm = ref.normalise_scores(_scores(c))
+        np.testing.assert_array_equal(norm, np.asarray(c["norm"]))
+        want = np.array([np.inf if v == "inf" else v for v in c["delta"]], np.float64)
+        np.testing.assert_allclose(ref.relative_change(norm), want, rtol=1e-15, atol=0)
+
+
+def test_normalise_matches_sklearn():
+    from sklearn.preprocessing import minmax_scale
+    rng = np.random.default_rng(3)
+    for n in (2, 7, 300):
+        s = rng.lognormal(0.0, 1.0, n)
+        np.testing.assert_allclose(ref.normalise_scores(s), minmax_scale(s), rtol=0, atol=1e-15)
+
+
+def test_spans_golden(golden_dir):
+    for c in _golden(golden_dir)["spans"]:
+        got = ref.segment_spans(_scores(c), c["tau_smooth"], c["max_len"])
+        assert [list(p) for p in got] == c["spans"], c["work"]
+
+
+def _spans_satisfy_rule(score, spans, tau, max_len):
+    """The segmentation rule as a set of conditions on a partition, which the greedy
+    walk of the pages is the only one to meet: spans tile the sequence in order, none
+    is longer than max_len, every neighbour pair inside a span changes by less than
+    tau, and a cut between spans falls either where the change is not below tau or
+    right after a span of the maximum length."""
+    norm = (score - score.min()) / (score.max() - score.min()) if np.ptp(score) > 0 else None
+    def smooth(i):  # tokens i and i+1 may share a span
+        if norm is None or norm[i] == 0:
+            return False
+        return abs(norm[i + 1] - norm[i]) / norm[i] < tau
+    n = len(score)
+    assert spans[0][0] == 0 and spans[-1][1] == n - 1
+    for (u, v), (u2, _) in zip(spans, spans[1:]):
+        assert u2 == v + 1
+    for u, v in spans:
+        assert 1 <= v - u + 1 <= max_len
+        assert all(smooth(i) for i in range(u, v))
+        if v < n - 1:
+            assert (not smooth(v)) or v - u + 1 == max_len
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_spans_characterisation(seed):
+    rng = np.random.default_rng(100 + seed)
+    n = int(rng.integers(1, 200))
+    # runs of similar scores (multi-token units) between jumps
+    levels = rng.lognormal(0.0, 0.7, n)
+    run = rng.integers(1, 9, n)
+    score = np.repeat(levels, run)[:n] * (1 + 0.05 * rng.standard_normal(n))
+    if seed == 0:
+        score = np.full(n, 2.0)
+    tau = [0.4, 0.1, 0.8, 0.0][seed % 4]
+    max_len = [16, 4, 1, 40][seed % 4]
+    spans = ref.segment_spans(score, tau, max_len)
+    _spans_satisfy_rule(score, spans, tau, max_len)
+
+
+def test_completion_golden(golden_dir):
+    for c in _golden(golden_dir)["completion"]:
+        s = _scores(c)
+        rows = np.arange(len(s))
+        k = ref.topk_count(c["rho"], len(s), len(s), c["rule"])
+        assert k == c["k"]
+        init = ref.topk_rows(s, rows, k)
+        assert list(init) == c["init"]
+        out = ref.complete_spans(s, np.isin(rows, init), 0.4, 16, c["tau_cover"])
+        assert list(np.nonzero(out)[0]) == c["selected"], c["work"]
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_completion_characterisation(seed):
+    """T_init is kept; a span is taken whole exactly when its covered share reaches
+    tau_cover, and otherwise keeps only its T_init tokens. Degenerate settings reduce
+    to T_init (tau_cover above 1, single-token spans, tau_smooth 0) or to every token
+    (tau_cover 0)."""
+    rng = np.random.default_rng(200 + seed)
+    n = int(rng.integers(5, 120))
+    score = np.repeat(rng.lognormal(0, 0.6, n), rng.integers(1, 6, n))[:n]
+    score = score * (1 + 0.03 * rng.standard_normal(n))
+    init = rng.random(n) < 0.3
+    tau_c = float(rng.choice([0.5, 0.7, 0.9]))
+    out = ref.complete_spans(score, init, 0.4, 16, tau_c)
+    assert np.all(out[init])
+    for u, v in ref.segment_spans(score, 0.4, 16):
+        share = init[u:v + 1].sum() / (v - u + 1)
+        if share >= tau_c:
+            assert out[u:v + 1].all()
+        else:
+            np.testing.assert_array_equal(out[u:v + 1], init[u:v + 1])
+    np.testing.assert_array_equal(ref.complete_spans(score, init, 0.4, 16, 1.5), init)
+    np.testing.assert_array_equal(ref.complete_spans(score, init, 0.4, 1, tau_c), init)
+    np.testing.assert_array_equal(ref.complete_spans(score, init, 0.0, 16, tau_c), init)
+    assert ref.complete_spans(score, init, 0.4, 16, 0.0).all()
+
+
+def test_cap_golden(golden_dir):
+    for c in _golden(golden_dir)["cap"]:
+        s = _scores(c)
+        chosen = np.isin(np.arange(len(s)), c["chosen"])
+        kept = ref.budget_cap(s, chosen, c["m"])
+        assert list(np.nonzero(kept)[0]) == c["kept"], c["work"]
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_cap_brute_force(seed):
+    rng = np.random.default_rng(300 + seed)
+    n = int(rng.integers(1, 60))
+    s = rng.integers(0, 6, n).astype(np.float64)  # many ties
+    chosen = rng.random(n) < 0.6
+    m = int(rng.integers(0, n + 2))
+    order = sorted(np.nonzero(chosen)[0], key=lambda i: (-s[i], i))
+    want = np.zeros(n, bool)
+    want[order[:m]] = True
+    np.testing.assert_array_equal(ref.budget_cap(s, chosen, m), want)
+
+
+# --------------------------------------------------------------------------- #
+# the layer in external-score mode
+# --------------------------------------------------------------------------- #
+
+def _layer_inputs(spec):
+    w = inputs.generate(spec)
+    lay = w.layout
+    src = inputs.encode_positions(lay)
+    cr = src >= 0
+    x = inputs.stored_to_f64(w.hidden, spec.dtype)
+    wq = ref.widen(w.layers[0].w_qkv, spec.dtype)
+    xe = w.encode_input(0)
+    T = lay.total_rows
+    kc = np.zeros((T, spec.n_kv_heads, spec.head_dim))
+    vc = np.zeros_like(kc)
+    kc[cr], vc[cr] = ref.encode_kv(xe[cr], wq, src[cr], spec.n_heads, spec.n_kv_heads,
+                                   spec.head_dim, spec.rope_base)
+    kw = dict(hidden=x, w_qkv=wq, k_cache=kc, v_cache=vc, req_offsets=lay.req_offsets,
+              chunk_offsets=lay.chunk_offsets, chunk_src_pos=lay.chunk_src_pos,
+              positions=lay.positions, n_heads=spec.n_heads, n_kv=spec.n_kv_heads,
+              head_dim=spec.head_dim, rope_base=spec.rope_base)
+    return w, kw
+
+
+def _spec():
+    return inputs.small_spec("mini", dtype="f32")
+
+
+@pytest.mark.parametrize("window,tau", [(0, 0), (8, 4)])
+def test_scores_mode_with_deviation_scores_equals_topk(window, tau):
+    """Ranking by externally supplied scores that happen to be the layer's own KV
+    deviations selects exactly what deviation-ranked top-k selects, with and without
+    window grouping, and every downstream output agrees."""
+    spec = _spec()
+    _, kw = _layer_inputs(spec)
+    a = ref.fuse_layer(ratio=0.2, mode="topk", window=window, tau=tau, **kw)
+    dev = np.nan_to_num(a["dev"], nan=0.0)
+    b = ref.fuse_layer(ratio=0.2, mode="scores", scores=dev, window=window, tau=tau, **kw)
+    np.testing.assert_array_equal(a["sel_idx"], b["sel_idx"])
+    np.testing.assert_array_equal(a["sel_offsets"], b["sel_offsets"])
+    for key in ("k_cache", "v_cache", "attn_out"):
+        np.testing.assert_allclose(a[key], b[key], rtol=0, atol=1e-12)
+
+
+def test_scores_mode_caches_and_given_equivalence():
+    """The rows chosen from scores carry full-prefill K/V at their global positions,
+    every other cached row keeps its re-rotated cache, and the layer equals GIVEN mode
+    fed the same rows."""
+    spec = _spec()
+    w, kw = _layer_inputs(spec)
+    rng = np.random.default_rng(7)
+    T = kw["hidden"].shape[0]
+    scores = np.repeat(rng.lognormal(0, 0.5, T), 3)[:T]
+    o = ref.fuse_layer(ratio=0.15, mode="scores", scores=scores, span_max=16, tau_smooth=0.4,
+                       tau_cover=0.7, cap_ratio=0.3, k_rule="ceil", **kw)
+    full = ref.full_prefill_layer(hidden=kw["hidden"], w_qkv=kw["w_qkv"],
+                                  req_offsets=kw["req_offsets"], positions=kw["positions"],
+                                  n_heads=spec.n_heads, n_kv=spec.n_kv_heads,
+                                  head_dim=spec.head_dim, rope_base=spec.rope_base)
+    sel = o["sel_idx"]
+    np.testing.assert_allclose(o["k_cache"][sel], full["k"][sel], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(o["v_cache"][sel], full["v"][sel], rtol=0, atol=1e-10)
+    _, src = ref.row_layout(kw["req_offsets"], kw["chunk_offsets"], kw["chunk_src_pos"], T)
+    rest = np.setdiff1d(np.nonzero(src >= 0)[0], sel)
+    np.testing.assert_array_equal(o["k_cache"][rest], o["k_tilde"][rest])
+    np.testing.assert_array_equal(o["v_cache"][rest], kw["v_cache"][rest])
+    g = ref.fuse_layer(ratio=0.0, mode="given", cand=sel, **kw)
+    np.testing.assert_array_equal(g["sel_idx"], sel)
+    np.testing.assert_allclose(g["attn_out"], o["attn_out"], rtol=0, atol=1e-12)
+    # the cap binds the completed set and keeps T_init
+    n_ctx = int((src >= 0).sum())
+    assert len(np.intersect1d(sel, np.nonzero(src >= 0)[0])) <= ref.topk_count(0.3, n_ctx, T, "ceil")
+    assert set(o["s0"]) <= set(sel)
+
+
+def test_fresh_all_writes_every_recomputed_row():
+    """With fresh K/V written for every recomputed row, layer 1 (every cached row a
+    candidate) leaves the whole cache at full-prefill K/V whatever the ratio, while
+    the selection and its queries are unchanged."""
+    spec = _spec()
+    _, kw = _layer_inputs(spec)
+    full = ref.full_prefill_layer(hidden=kw["hidden"], w_qkv=kw["w_qkv"],
+                                  req_offsets=kw["req_offsets"], positions=kw["positions"],
+                                  n_heads=spec.n_heads, n_kv=spec.n_kv_heads,
+                                  head_dim=spec.head_dim, rope_base=spec.rope_base)
+    a = ref.fuse_layer(ratio=0.1, **kw)
+    b = ref.fuse_layer(ratio=0.1, fresh_all=True, **kw)
+    np.testing.assert_array_equal(a["sel_idx"], b["sel_idx"])
+    np.testing.assert_allclose(b["k_cache"], full["k"], rtol=0, atol=1e-10)
+    np.testing.assert_allclose(b["v_cache"], full["v"], rtol=0, atol=1e-10)
+    sel = b["sel_idx"]
+    np.testing.assert_allclose(b["attn_out"], full["attn_out"][sel], rtol=0, atol=1e-10)
