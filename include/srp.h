@@ -46,11 +46,18 @@ typedef enum { SRP_F32 = 0, SRP_BF16 = 1 } srp_dtype;
 
 /* Selection modes (CacheBlend walkthrough, "Implementation": a per-layer
  * check_flag says whether the layer selects tokens by deviation or uses the
- * indices it was given). */
+ * indices it was given; CacheClip paper 4.2 and SpecCache notes 2.2 rank tokens by
+ * scores from a small auxiliary model instead). */
 typedef enum {
-  SRP_SEL_TOPK = 0, /* score candidates by KV deviation, keep the top k      */
-  SRP_SEL_GIVEN = 1 /* keep the candidates as given (no scoring)            */
+  SRP_SEL_TOPK = 0,  /* score candidates by KV deviation, keep the top k      */
+  SRP_SEL_GIVEN = 1, /* keep the candidates as given (no scoring)            */
+  SRP_SEL_SCORES = 2 /* rank candidates by caller-supplied per-row scores;
+                        only the chosen rows are recomputed                  */
 } srp_sel_mode;
+
+/* How k follows from the ratio: round half up (CacheClip walkthrough 6.2) or
+ * ceiling (SpecCache notes 2.2); the product ratio * N is taken in double. */
+typedef enum { SRP_K_ROUND = 0, SRP_K_CEIL = 1 } srp_k_rule;
 
 /* What the deviation measures (the CacheBlend walkthrough compares K and V; the
  * CacheClip paper's account of CacheBlend compares value matrices only). */
@@ -92,18 +99,37 @@ typedef struct {
                                    increasing inside each request                 */
 } srp_batch;
 
-/* Token selection of one layer. k = round(ratio * N_ctx) per request (halves up),
- * N_ctx = the request's cached rows, clamped to its candidate count (CacheClip
- * walkthrough 6.2). Ties in deviation go to the lower row index. window > 0 turns
- * on sliding-window grouping (CacheClip paper 4.3): over the request's cached rows
- * in order, a window of `window` rows starting on a top-k row that holds at least
- * `tau` top-k rows is recomputed whole; top-k rows covered by no such window are
- * dropped. Grouping requires cand == NULL. Candidates (gradual filtering across
- * layers, CacheBlend walkthrough "The chicken-and-egg problem"): cand == NULL means
- * every cached row; otherwise cand/cand_offsets is a CSR list per request of row
- * ids, ascending inside each request -- the sel_idx/sel_offsets of the previous
- * layer can be passed as is (fresh rows in it are ignored, they are always
- * recomputed). */
+/* Token selection of one layer. k = round(ratio * N_ctx) per request (halves up;
+ * k_rule SRP_K_CEIL: ceil), N_ctx = the request's cached rows, clamped to its
+ * candidate count (CacheClip walkthrough 6.2). Ties in the ranking go to the lower
+ * row index. window > 0 turns on sliding-window grouping (CacheClip paper 4.3): over
+ * the request's cached rows in order, a window of `window` rows starting on a top-k
+ * row that holds at least `tau` top-k rows is recomputed whole; top-k rows covered
+ * by no such window are dropped. Grouping requires cand == NULL. Candidates
+ * (gradual filtering across layers, CacheBlend walkthrough "The chicken-and-egg
+ * problem"): cand == NULL means every cached row; otherwise cand/cand_offsets is a
+ * CSR list per request of row ids, ascending inside each request -- the
+ * sel_idx/sel_offsets of the previous layer can be passed as is (fresh rows in it
+ * are ignored, they are always recomputed).
+ *
+ * SRP_SEL_SCORES ranks the candidates by scores[row] (device, fp32, finite; e.g.
+ * an auxiliary model's attention column means, CacheClip paper 4.2, or its
+ * deep-layer hidden-state norms, SpecCache notes 2.2) and keeps the top k; grouping
+ * then applies as above, or span completion (SpecCache notes 2.3) when span_max > 0:
+ * the request's cached rows in order are cut into spans of at most span_max rows,
+ * a row joining its predecessor's span while |s~_j - s~_i| / s~_i < tau_smooth for
+ * the min-max normalised scores s~ (evaluated in double; a NaN or infinite change
+ * starts a new span); every span in which the top-k rows make up a share >=
+ * tau_cover (in double) is added whole; then, if cap_ratio > 0, only the
+ * k(cap_ratio) highest-scored rows of the result are kept. Span completion requires
+ * cand == NULL and window == 0; SCORES mode requires max_req_rows <= 22528. The
+ * rows not chosen are not recomputed; dev_out then reports the deviation of the
+ * chosen cached rows.
+ *
+ * fresh_all = 1 writes fresh K/V into the cache for every recomputed row (every
+ * candidate in TOPK mode), not only the selected ones, as in the CacheBlend
+ * walkthrough's figure of gradual filtering; attention and sel_idx are unchanged
+ * by it. All fields past cand_offsets are zero for the defaults. */
 typedef struct {
   int32_t mode;     /* srp_sel_mode                                             */
   double ratio;     /* in [0, 1]                                                */
@@ -112,6 +138,13 @@ typedef struct {
   int32_t dev_mode; /* srp_dev_mode                                             */
   const int32_t *cand;        /* device, NULL = all cached rows                  */
   const int32_t *cand_offsets; /* device [n_req+1], required with cand            */
+  int32_t k_rule;   /* srp_k_rule                                               */
+  int32_t span_max; /* SCORES: 0 = no span completion, else 1..1024 (pages: 16) */
+  const float *scores; /* device [T], SCORES mode only (NULL otherwise)          */
+  double tau_smooth;   /* span segmentation threshold, >= 0 (pages: 0.4)        */
+  double tau_cover;    /* span coverage threshold, in [0, 1] (pages: 0.7)       */
+  double cap_ratio;    /* budget after completion: 0 = none, else in [ratio, 1] */
+  int32_t fresh_all;   /* 0 or 1                                                */
 } srp_select;
 
 /* Bytes of scratch that srp_fuse_layer needs for these arguments. */

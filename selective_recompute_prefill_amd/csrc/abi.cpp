@@ -138,9 +138,12 @@ int check_batch(const srp_batch *b) {
 
 int check_select(const srp_select *s) {
   if (!s) return fail(SRP_E_INVALID, "select is NULL");
-  if (s->mode != SRP_SEL_TOPK && s->mode != SRP_SEL_GIVEN) return fail(SRP_E_INVALID, "selection mode %d unknown", s->mode);
+  if (s->mode != SRP_SEL_TOPK && s->mode != SRP_SEL_GIVEN && s->mode != SRP_SEL_SCORES)
+    return fail(SRP_E_INVALID, "selection mode %d unknown", s->mode);
   if (!(s->ratio >= 0.0 && s->ratio <= 1.0)) return fail(SRP_E_INVALID, "ratio must lie in [0, 1]");
   if (s->dev_mode != SRP_DEV_KV && s->dev_mode != SRP_DEV_V) return fail(SRP_E_INVALID, "dev_mode %d unknown", s->dev_mode);
+  if (s->k_rule != SRP_K_ROUND && s->k_rule != SRP_K_CEIL) return fail(SRP_E_INVALID, "k_rule %d unknown", s->k_rule);
+  if (s->fresh_all != 0 && s->fresh_all != 1) return fail(SRP_E_INVALID, "fresh_all must be 0 or 1");
   if (s->window < 0) return fail(SRP_E_INVALID, "window must be >= 0");
   if (s->window > 0) {
     if (s->tau < 1 || s->tau > s->window) return fail(SRP_E_INVALID, "tau must lie in [1, window]");
@@ -148,6 +151,29 @@ int check_select(const srp_select *s) {
   }
   if (s->cand && !s->cand_offsets) return fail(SRP_E_INVALID, "cand needs cand_offsets");
   if (s->mode == SRP_SEL_GIVEN && !s->cand) return fail(SRP_E_INVALID, "SRP_SEL_GIVEN needs a candidate list");
+  if ((s->mode == SRP_SEL_SCORES) != (s->scores != nullptr))
+    return fail(SRP_E_INVALID, "scores are given exactly in SRP_SEL_SCORES mode");
+  if (s->span_max != 0) {
+    if (s->mode != SRP_SEL_SCORES) return fail(SRP_E_INVALID, "span completion needs SRP_SEL_SCORES");
+    if (s->span_max < 1 || s->span_max > 1024) return fail(SRP_E_INVALID, "span_max must lie in [1, 1024]");
+    if (s->window > 0) return fail(SRP_E_INVALID, "span completion and window grouping exclude each other");
+    if (s->cand) return fail(SRP_E_INVALID, "span completion scans every cached row: cand must be NULL");
+    if (!(s->tau_smooth >= 0.0)) return fail(SRP_E_INVALID, "tau_smooth must be >= 0");
+    if (!(s->tau_cover >= 0.0 && s->tau_cover <= 1.0)) return fail(SRP_E_INVALID, "tau_cover must lie in [0, 1]");
+  }
+  if (s->cap_ratio != 0.0) {
+    if (s->span_max == 0) return fail(SRP_E_INVALID, "cap_ratio applies to span completion only");
+    if (!(s->cap_ratio >= s->ratio && s->cap_ratio <= 1.0))
+      return fail(SRP_E_INVALID, "cap_ratio must lie in [ratio, 1]");
+  }
+  return SRP_OK;
+}
+
+// Checks that depend on both the batch and the selection.
+int check_select_batch(const srp_batch *b, const srp_select *s) {
+  if (s->mode == SRP_SEL_SCORES && b->max_req_rows > kLdsEntries)
+    return fail(SRP_E_UNSUPPORTED, "SRP_SEL_SCORES handles requests of at most %d rows (max_req_rows %d)",
+                kLdsEntries, b->max_req_rows);
   return SRP_OK;
 }
 
@@ -168,6 +194,7 @@ int srp_workspace_size(const srp_dims *dims, const srp_batch *batch, const srp_s
   CHECK(check_dims(dims));
   CHECK(check_batch(batch));
   CHECK(check_select(sel));
+  CHECK(check_select_batch(batch, sel));
   if (!bytes) return fail(SRP_E_INVALID, "bytes is NULL");
   *bytes = carve(*dims, *batch, nullptr).bytes;
   return SRP_OK;
@@ -181,6 +208,7 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   CHECK(check_dims(dims));
   CHECK(check_batch(batch));
   CHECK(check_select(sel));
+  CHECK(check_select_batch(batch, sel));
   const srp_dims &d = *dims;
   const srp_batch &b = *batch;
   const int T = b.total_rows;
@@ -216,14 +244,31 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   sa.nkv = d.n_kv_heads;
   sa.dev_out = dev_out;
   sa.tile_rows = attn_tile_rows(d.dtype, d.n_heads, d.n_kv_heads);
+  sa.k_ceil = sel->k_rule == SRP_K_CEIL;
+  sa.scores = sel->scores;
+  sa.span_max = sel->span_max;
+  sa.tau_smooth = sel->tau_smooth;
+  sa.tau_cover = sel->tau_cover;
+  sa.cap_ratio = sel->cap_ratio;
+  sa.fresh_all = sel->fresh_all;
+  // with external scores the rows are chosen first and then handled as a given list
+  const bool by_scores = sel->mode == SRP_SEL_SCORES;
+  sa.listed = sel->cand != nullptr || by_scores;
+  SelectArgs sd = sa;
+  if (by_scores) {
+    sd.mode = SRP_SEL_GIVEN;
+    sd.window = 0;
+    sd.span_max = 0;
+  }
 
-  // 1. row metadata; candidate list and the recomputed rows R when given
+  // 1. row metadata; candidate list, the choice by scores, and the recomputed rows
+  //    R when they are listed
   StageMarks marks(s);
   marks.mark(0);
   SRP_HIP(launch_prepare(sa, w, s));
   // 2. positional recovery of cached rows outside R (inside R the projection
   //    epilogue rotates them next to the deviation)
-  if (sel->cand && T > 0)
+  if (sa.listed && T > 0)
     SRP_HIP(launch_rerotate(d.dtype, T, d.n_kv_heads, d.head_dim, b.chunk_offsets, b.n_chunks,
                             b.chunk_src_pos, b.positions, w.rowflag, rt, k_cache, s));
   // 3. K/V projection of R with the rotation / deviation epilogue
@@ -231,9 +276,9 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   g.dtype = d.dtype;
   g.A = hidden;
   g.K = d.hidden;
-  g.a_rows = sel->cand ? w.rlist : nullptr;
+  g.a_rows = sa.listed ? w.rlist : nullptr;
   g.M_host = T;
-  g.M_dev = sel->cand ? w.ctr + kCtrREntries : nullptr;
+  g.M_dev = sa.listed ? w.ctr + kCtrREntries : nullptr;
   g.M_cap = T;
   g.B = (const char *)w_qkv + (size_t)qd * d.hidden * es;
   g.N = 2 * kvd;
@@ -254,11 +299,11 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   SRP_HIP(launch_gemm(g, s));
   marks.mark(2);
   // 4. top-k / grouping per request, CSR offsets, attention tiles
-  SRP_HIP(launch_select(sa, w, s));
-  SRP_HIP(launch_finalize(sa, w, sel_offsets, s));
+  SRP_HIP(launch_select(sd, w, s));
+  SRP_HIP(launch_finalize(sd, w, sel_offsets, s));
   marks.mark(3);
   // 5. sel_idx and the scatter of fresh K/V into the cache
-  SRP_HIP(launch_compact_scatter(sa, w, d.dtype, kvd, sel_idx, sel_offsets, k_cache, v_cache, s));
+  SRP_HIP(launch_compact_scatter(sd, w, d.dtype, kvd, sel_idx, sel_offsets, k_cache, v_cache, s));
   if (d.dtype == SRP_BF16 && T > 0)
     SRP_HIP(launch_v_transpose(T, d.n_kv_heads, d.head_dim, v_cache, w.vt, vt_stride(T), s));
   marks.mark(4);

@@ -85,11 +85,11 @@ __global__ __launch_bounds__(1024) void r_write_kernel(SelectArgs a, Workspace w
 // the per-head partials), entry flags, and the optional deviation output
 // ------------------------------------------------------------------------- //
 __global__ __launch_bounds__(256) void keys_kernel(SelectArgs a, Workspace w) {
-  const int *roff = a.cand ? w.roff : a.req_offsets;
+  const int *roff = a.listed ? w.roff : a.req_offsets;
   const int nR = roff[a.n_req];
   const int P0 = a.dev_mode == SRP_DEV_V ? a.nkv : 0, P1 = 2 * a.nkv;
   for (int e = blockIdx.x * blockDim.x + threadIdx.x; e < nR; e += gridDim.x * blockDim.x) {
-    const int row = a.cand ? w.rlist[e] : e;
+    const int row = a.listed ? w.rlist[e] : e;
     if (w.row_delta[row] == kFresh) {
       w.eflag[e] = kFreshF;
       continue;
@@ -116,13 +116,22 @@ __device__ __forceinline__ void my_segment(int n, int &lo, int &hi) {
 constexpr int kHistBins = 4096;
 constexpr int kPage = 32768;  // entries whose flags are staged in LDS at a time
 
+// k from the ratio: round half up, or ceil; the product is rounded on its own (no
+// fused multiply-add), as a plain double evaluation of the formula does.
+__device__ __forceinline__ int k_from_ratio(double ratio, int n_ctx, int n_cand, int k_ceil) {
+#pragma clang fp contract(off)
+  const double x = ratio * (double)n_ctx;
+  const double kd = k_ceil ? ceil(x) : floor(x + 0.5);
+  return kd < (double)n_cand ? (int)kd : n_cand;
+}
+
 __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, Workspace w) {
   __shared__ int sh[17];
   __shared__ int hist[kHistBins];
   __shared__ int digit_info[2];
   __shared__ uint8_t pg[kPage];
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
-  const int *roff = a.cand ? w.roff : a.req_offsets;
+  const int *roff = a.listed ? w.roff : a.req_offsets;
   const int e0 = roff[r], e1 = roff[r + 1];
   const int rq0 = a.req_offsets[r], rq1 = a.req_offsets[r + 1];
 
@@ -134,13 +143,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, Workspace w)
   const int n_ctx = block_sum(my_ctx, sh);
   const int n_cand = block_sum(my_cand, sh);
 
-  int k;
-  if (a.mode == SRP_SEL_GIVEN) {
-    k = n_cand;
-  } else {
-    const double kd = floor(a.ratio * (double)n_ctx + 0.5);
-    k = kd < (double)n_cand ? (int)kd : n_cand;
-  }
+  const int k = a.mode == SRP_SEL_GIVEN ? n_cand : k_from_ratio(a.ratio, n_ctx, n_cand, a.k_ceil);
 
   if (k >= n_cand) {
     for (int e = e0 + tid; e < e1; e += nt)
@@ -289,7 +292,7 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, Workspace w)
     for (int i = lo; i < hi; ++i) {
       if ((pg[i] & kFreshF) || (pg[i] & want)) {
         const int e = pb + i;
-        w.tsel_row[e0 + p] = a.cand ? w.rlist[e] : e;
+        w.tsel_row[e0 + p] = a.listed ? w.rlist[e] : e;
         w.tsel_ent[e0 + p] = e;
         ++p;
       }
@@ -305,18 +308,16 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, Workspace w)
 // entries): keys and flags are loaded once; after marking, the key storage holds
 // the grouping sequence as 16-bit entry offsets and prefix counts
 // ------------------------------------------------------------------------- //
-constexpr int kLdsEntries = 22528;
-
 __device__ __forceinline__ int radix_digit_pass(const uint32_t *keys, const uint8_t *fl, int n,
-                                                uint32_t prefix, uint32_t pmask, int shift, int nb,
-                                                int need, int *hist, int *sh, int *digit_info,
-                                                int *above_out) {
+                                                uint8_t in_bit, uint32_t prefix, uint32_t pmask,
+                                                int shift, int nb, int need, int *hist, int *sh,
+                                                int *digit_info, int *above_out) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const uint32_t dmask = (uint32_t)nb - 1u;
   for (int b = tid; b < nb; b += nt) hist[b] = 0;
   __syncthreads();
   for (int i = tid; i < n; i += nt) {
-    if (!(fl[i] & kCand)) continue;
+    if (!(fl[i] & in_bit)) continue;
     const uint32_t key = keys[i];
     if ((key & pmask) == prefix) atomicAdd(&hist[(key >> shift) & dmask], 1);
   }
@@ -347,6 +348,114 @@ __device__ __forceinline__ int radix_digit_pass(const uint32_t *keys, const uint
   return d;
 }
 
+// Marks out_bit on the k entries with the largest keys among the n_in entries
+// flagged in_bit: an MSB-first radix select (digits of 12, 12 and 8 bits) finds the
+// k-th largest key; larger keys are taken, and equal keys in entry order.
+__device__ void lds_mark_top(const uint32_t *keys, uint8_t *fl, int n, uint8_t in_bit,
+                             uint8_t out_bit, int k, int n_in, int *hist, int *sh,
+                             int *digit_info) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (k >= n_in) {
+    for (int i = tid; i < n; i += nt)
+      if (fl[i] & in_bit) fl[i] |= out_bit;
+  } else if (k > 0) {
+    uint32_t prefix = 0, pmask = 0;
+    int need = k;
+    const int shifts[3] = {20, 8, 0}, widths[3] = {12, 12, 8};
+    for (int pass = 0; pass < 3; ++pass) {
+      int above;
+      const int d = radix_digit_pass(keys, fl, n, in_bit, prefix, pmask, shifts[pass],
+                                     1 << widths[pass], need, hist, sh, digit_info, &above);
+      need -= above;
+      prefix |= (uint32_t)d << shifts[pass];
+      pmask |= ((1u << widths[pass]) - 1u) << shifts[pass];
+    }
+    int my_eq = 0;
+    for (int i = tid; i < n; i += nt) {
+      if (!(fl[i] & in_bit)) continue;
+      if (keys[i] > prefix) fl[i] |= out_bit;
+      else if (keys[i] == prefix) ++my_eq;
+    }
+    const int eq_tot = block_sum(my_eq, sh);
+    if (eq_tot == need) {
+      for (int i = tid; i < n; i += nt)
+        if ((fl[i] & in_bit) && keys[i] == prefix) fl[i] |= out_bit;
+    } else {
+      // several equal keys at the threshold: the first `need` in entry order
+      int lo, hi;
+      my_segment(n, lo, hi);
+      int c = 0;
+      for (int i = lo; i < hi; ++i) c += ((fl[i] & in_bit) && keys[i] == prefix) ? 1 : 0;
+      int t;
+      int rank = block_excl_scan(c, sh, &t);
+      for (int i = lo; i < hi; ++i)
+        if ((fl[i] & in_bit) && keys[i] == prefix) {
+          if (rank < need) fl[i] |= out_bit;
+          ++rank;
+        }
+    }
+  }
+  __syncthreads();
+}
+
+// Sliding-window grouping over the sequence of kCand entries in order: a window of
+// `win` slots starting on a kTop slot that holds at least `tau` kTop slots marks
+// each of its slots kSel. seq16 (2 * kLdsEntries u16) holds slot -> entry and the
+// inclusive kTop count per slot; sq (a byte per slot) and scan (blockDim ints) are
+// scratch.
+__device__ void lds_window_group(uint8_t *fl, int n, int win, int tau, uint16_t *seq16,
+                                 uint8_t *sq, int *scan, int *sh) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  uint16_t *seq_ent = seq16;                // [n] slot -> entry offset
+  uint16_t *seq_pre = seq16 + kLdsEntries;  // [n] inclusive top count
+  int lo, hi;
+  my_segment(n, lo, hi);
+  int c = 0, tp = 0;
+  for (int i = lo; i < hi; ++i)
+    if (fl[i] & kCand) { ++c; tp += (fl[i] & kTop) ? 1 : 0; }
+  int n_seq, n_top;
+  int slot = block_excl_scan(c, sh, &n_seq);
+  int run = block_excl_scan(tp, sh, &n_top);
+  for (int i = lo; i < hi; ++i) {
+    const uint8_t f = fl[i];
+    if (!(f & kCand)) continue;
+    const int top = (f & kTop) ? 1 : 0;
+    run += top;
+    seq_ent[slot] = (uint16_t)i;
+    seq_pre[slot] = (uint16_t)run;
+    sq[slot] = (uint8_t)top;
+    ++slot;
+  }
+  __syncthreads();
+  for (int t = tid; t < n_seq; t += nt) {
+    if ((sq[t] & 1) && t + win <= n_seq) {
+      const int cnt = (int)seq_pre[t + win - 1] - (t > 0 ? (int)seq_pre[t - 1] : 0);
+      if (cnt >= tau) sq[t] |= 2;
+    }
+  }
+  __syncthreads();
+  // a slot is kept when the latest passing window start at or before it lies
+  // within the window: a max-scan of passing starts over contiguous segments
+  int lo2, hi2;
+  my_segment(n_seq, lo2, hi2);
+  int last = -1;
+  for (int t = lo2; t < hi2; ++t) last = (sq[t] & 2) ? t : last;
+  scan[tid] = last;
+  __syncthreads();
+  for (int o = 1; o < nt; o <<= 1) {
+    const int v = tid >= o ? scan[tid - o] : -1;
+    __syncthreads();
+    if (v > scan[tid]) scan[tid] = v;
+    __syncthreads();
+  }
+  int rs = tid > 0 ? scan[tid - 1] : -1;
+  for (int t = lo2; t < hi2; ++t) {
+    if (sq[t] & 2) rs = t;
+    if (rs >= 0 && rs > t - win) fl[seq_ent[t]] |= kSel;
+  }
+  __syncthreads();
+}
+
 __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspace w) {
   __shared__ int sh[17];
   __shared__ int hist[kHistBins];
@@ -356,7 +465,7 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
   __shared__ uint8_t sq_s[kLdsEntries];      // grouping: bit 0 top-k slot, bit 1 passing window
   __shared__ int sh_max[1024];               // grouping: max-scan of passing starts
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
-  const int *roff = a.cand ? w.roff : a.req_offsets;
+  const int *roff = a.listed ? w.roff : a.req_offsets;
   const int e0 = roff[r], e1 = roff[r + 1], n = e1 - e0;
 
   int my_cand = 0;
@@ -381,7 +490,7 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
     }
   }
   int my_ctx = 0;
-  if (a.cand) {
+  if (a.listed) {
     for (int j = a.req_offsets[r] + tid; j < a.req_offsets[r + 1]; j += nt) my_ctx += w.row_delta[j] != kFresh;
   } else {
     my_ctx = my_cand;  // every cached row of the request is a candidate
@@ -389,109 +498,11 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
   const int n_cand = block_sum(my_cand, sh);
   const int n_ctx = block_sum(my_ctx, sh);
 
-  int k;
-  if (a.mode == SRP_SEL_GIVEN) {
-    k = n_cand;
-  } else {
-    const double kd = floor(a.ratio * (double)n_ctx + 0.5);
-    k = kd < (double)n_cand ? (int)kd : n_cand;
-  }
-  if (k >= n_cand) {
-    for (int i = tid; i < n; i += nt)
-      if (fl_s[i] & kCand) fl_s[i] |= kTop;
-  } else if (k > 0) {
-    uint32_t prefix = 0, pmask = 0;
-    int need = k;
-    const int shifts[3] = {20, 8, 0}, widths[3] = {12, 12, 8};
-    for (int pass = 0; pass < 3; ++pass) {
-      int above;
-      const int d = radix_digit_pass(keys_s, fl_s, n, prefix, pmask, shifts[pass], 1 << widths[pass],
-                                     need, hist, sh, digit_info, &above);
-      need -= above;
-      prefix |= (uint32_t)d << shifts[pass];
-      pmask |= ((1u << widths[pass]) - 1u) << shifts[pass];
-    }
-    int my_eq = 0;
-    for (int i = tid; i < n; i += nt) {
-      if (!(fl_s[i] & kCand)) continue;
-      if (keys_s[i] > prefix) fl_s[i] |= kTop;
-      else if (keys_s[i] == prefix) ++my_eq;
-    }
-    const int eq_tot = block_sum(my_eq, sh);
-    if (eq_tot == need) {
-      for (int i = tid; i < n; i += nt)
-        if ((fl_s[i] & kCand) && keys_s[i] == prefix) fl_s[i] |= kTop;
-    } else {
-      // several equal keys at the threshold: the first `need` in row order
-      int lo, hi;
-      my_segment(n, lo, hi);
-      int c = 0;
-      for (int i = lo; i < hi; ++i) c += ((fl_s[i] & kCand) && keys_s[i] == prefix) ? 1 : 0;
-      int t;
-      int rank = block_excl_scan(c, sh, &t);
-      for (int i = lo; i < hi; ++i)
-        if ((fl_s[i] & kCand) && keys_s[i] == prefix) {
-          if (rank < need) fl_s[i] |= kTop;
-          ++rank;
-        }
-    }
-  }
-  __syncthreads();
+  const int k = a.mode == SRP_SEL_GIVEN ? n_cand : k_from_ratio(a.ratio, n_ctx, n_cand, a.k_ceil);
+  lds_mark_top(keys_s, fl_s, n, kCand, kTop, k, n_cand, hist, sh, digit_info);
 
-  if (a.window > 0) {
-    const int win = a.window;
-    uint16_t *seq_ent = reinterpret_cast<uint16_t *>(keys_s);   // [n] slot -> entry offset
-    uint16_t *seq_pre = seq_ent + kLdsEntries;                  // [n] inclusive top count
-    int lo, hi;
-    my_segment(n, lo, hi);
-    int c = 0, tp = 0;
-    for (int i = lo; i < hi; ++i)
-      if (fl_s[i] & kCand) { ++c; tp += (fl_s[i] & kTop) ? 1 : 0; }
-    int n_seq, n_top;
-    int slot = block_excl_scan(c, sh, &n_seq);
-    int run = block_excl_scan(tp, sh, &n_top);
-    for (int i = lo; i < hi; ++i) {
-      const uint8_t f = fl_s[i];
-      if (!(f & kCand)) continue;
-      const int top = (f & kTop) ? 1 : 0;
-      run += top;
-      seq_ent[slot] = (uint16_t)i;
-      seq_pre[slot] = (uint16_t)run;
-      sq_s[slot] = (uint8_t)top;
-      ++slot;
-    }
-    __syncthreads();
-    for (int t = tid; t < n_seq; t += nt) {
-      if ((sq_s[t] & 1) && t + win <= n_seq) {
-        const int cnt = (int)seq_pre[t + win - 1] - (t > 0 ? (int)seq_pre[t - 1] : 0);
-        if (cnt >= a.tau) sq_s[t] |= 2;
-      }
-    }
-    __syncthreads();
-    // a slot is kept when the latest passing window start at or before it lies
-    // within the window: a max-scan of passing starts over contiguous segments
-    {
-      int lo2, hi2;
-      my_segment(n_seq, lo2, hi2);
-      int last = -1;
-      for (int t = lo2; t < hi2; ++t) last = (sq_s[t] & 2) ? t : last;
-      // latest passing start before this segment: max over earlier segments
-      sh_max[tid] = last;
-      __syncthreads();
-      for (int o = 1; o < nt; o <<= 1) {
-        const int v = tid >= o ? sh_max[tid - o] : -1;
-        __syncthreads();
-        if (v > sh_max[tid]) sh_max[tid] = v;
-        __syncthreads();
-      }
-      int run = tid > 0 ? sh_max[tid - 1] : -1;
-      for (int t = lo2; t < hi2; ++t) {
-        if (sq_s[t] & 2) run = t;
-        if (run >= 0 && run > t - win) fl_s[seq_ent[t]] |= kSel;
-      }
-    }
-    __syncthreads();
-  }
+  if (a.window > 0)
+    lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, sh_max, sh);
 
   // compact the request's selection (fresh rows included) in row order
   const uint8_t want = a.window > 0 ? kSel : kTop;
@@ -504,12 +515,244 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
   for (int i = lo; i < hi; ++i) {
     if ((fl_s[i] & kFreshF) || (fl_s[i] & want)) {
       const int e = e0 + i;
-      w.tsel_row[e0 + p] = a.cand ? w.rlist[e] : e;
+      w.tsel_row[e0 + p] = a.listed ? w.rlist[e] : e;
       w.tsel_ent[e0 + p] = e;
       ++p;
     }
   }
   if (tid == 0) w.sel_cnt[r] = total;
+}
+
+// ------------------------------------------------------------------------- //
+// selection by external scores (one work-group per request, resident in LDS),
+// run before any projection: the chosen rows become the candidate marks of the
+// R list, which the rest of the layer treats as a given list
+// ------------------------------------------------------------------------- //
+constexpr uint8_t kBrk = 16;    // spans: no join with the next candidate
+constexpr uint8_t kSpan0 = 32;  // spans: a span starts at this entry
+constexpr uint8_t kCap = 64;    // budget cap: kept
+
+// Order-preserving map of a finite float onto uint32 (-0 is taken as +0), and back.
+__device__ __forceinline__ uint32_t score_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+__device__ __forceinline__ float key_score(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
+}
+
+// Block-wide min and max of uint32 values (every thread gets both).
+__device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, int *sa, int *sb) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t a = (uint32_t)__shfl_xor((int)mn, o), b = (uint32_t)__shfl_xor((int)mx, o);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if (lane == 0) {
+    sa[wid] = (int)mn;
+    sb[wid] = (int)mx;
+  }
+  __syncthreads();
+  for (int q = 0; q < nw; ++q) {
+    const uint32_t a = (uint32_t)sa[q], b = (uint32_t)sb[q];
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  __syncthreads();
+}
+
+// Relative change of the normalised score from entry i to the next candidate j does
+// not stay below tau: evaluated in double as written, (s - min) / (max - min) for
+// each side, then |s~_j - s~_i| / s~_i; a NaN or infinite change breaks the span.
+__device__ __forceinline__ bool span_breaks(uint32_t ki, uint32_t kj, double mn, double range,
+                                            double tau) {
+#pragma clang fp contract(off)
+  const double ti = ((double)key_score(ki) - mn) / range;
+  const double tj = ((double)key_score(kj) - mn) / range;
+  const double delta = fabs(tj - ti) / ti;
+  return !(delta < tau);
+}
+
+// Span completion over the sequence of kCand entries in order, T_init = kTop: the
+// sequence is cut into spans (a new span where the relative change breaks, or
+// after span_max entries), and a span whose kTop share reaches tau_cover marks all
+// of its entries kSel; other spans mark their kTop entries. Returns the kSel count.
+// sa, sb: blockDim ints of scratch.
+__device__ int lds_span_complete(const uint32_t *keys, uint8_t *fl, int n, int span_max,
+                                 double tau_smooth, double tau_cover, int *sa, int *sb, int *sh) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  uint32_t kmin = 0xffffffffu, kmax = 0u;
+  for (int i = tid; i < n; i += nt)
+    if (fl[i] & kCand) {
+      kmin = keys[i] < kmin ? keys[i] : kmin;
+      kmax = keys[i] > kmax ? keys[i] : kmax;
+    }
+  block_minmax(kmin, kmax, sa, sb);
+  const double mn = (double)key_score(kmin), mx = (double)key_score(kmax);
+  const double range = mx - mn;
+
+  // first and last candidate of every thread's segment; the candidates just
+  // outside a segment come from a suffix-min and a prefix-max over the threads
+  int lo, hi;
+  my_segment(n, lo, hi);
+  int first = INT_MAX, last = -1, cnt = 0;
+  for (int i = lo; i < hi; ++i)
+    if (fl[i] & kCand) {
+      first = first == INT_MAX ? i : first;
+      last = i;
+      ++cnt;
+    }
+  sa[tid] = first;
+  sb[tid] = last;
+  __syncthreads();
+  for (int o = 1; o < nt; o <<= 1) {
+    const int va = tid + o < nt ? sa[tid + o] : INT_MAX;
+    const int vb = tid >= o ? sb[tid - o] : -1;
+    __syncthreads();
+    if (va < sa[tid]) sa[tid] = va;
+    if (vb > sb[tid]) sb[tid] = vb;
+    __syncthreads();
+  }
+  const int next_first = tid + 1 < nt ? sa[tid + 1] : INT_MAX;
+  const int prev_last = tid > 0 ? sb[tid - 1] : -1;
+  __syncthreads();
+
+  // kBrk on every candidate that does not join its successor (and on the last)
+  {
+    int prev = -1;
+    for (int i = lo; i < hi; ++i) {
+      if (!(fl[i] & kCand)) continue;
+      if (prev >= 0 && span_breaks(keys[prev], keys[i], mn, range, tau_smooth)) fl[prev] |= kBrk;
+      prev = i;
+    }
+    if (prev >= 0 && (next_first >= n || span_breaks(keys[prev], keys[next_first], mn, range, tau_smooth)))
+      fl[prev] |= kBrk;
+  }
+  __syncthreads();
+
+  // slots; a run of joined candidates starts after a kBrk (or at the first
+  // candidate) and is cut into spans of span_max slots from its start
+  int tot;
+  const int slot0 = block_excl_scan(cnt, sh, &tot);
+  int local_start = -1;
+  {
+    int prev = prev_last, slot = slot0;
+    for (int i = lo; i < hi; ++i) {
+      if (!(fl[i] & kCand)) continue;
+      if (prev < 0 || (fl[prev] & kBrk)) local_start = slot;
+      prev = i;
+      ++slot;
+    }
+  }
+  sa[tid] = local_start;
+  __syncthreads();
+  for (int o = 1; o < nt; o <<= 1) {
+    const int v = tid >= o ? sa[tid - o] : -1;
+    __syncthreads();
+    if (v > sa[tid]) sa[tid] = v;
+    __syncthreads();
+  }
+  {
+    int run0 = tid > 0 ? sa[tid - 1] : -1;
+    int prev = prev_last, slot = slot0;
+    for (int i = lo; i < hi; ++i) {
+      if (!(fl[i] & kCand)) continue;
+      if (prev < 0 || (fl[prev] & kBrk)) run0 = slot;
+      if ((slot - run0) % span_max == 0) fl[i] |= kSpan0;
+      prev = i;
+      ++slot;
+    }
+  }
+  __syncthreads();
+
+  // each span start walks its span (at most span_max candidates) twice: coverage,
+  // then marks; every candidate belongs to exactly one span, so marks never collide
+  int my_sel = 0;
+  for (int i = lo; i < hi; ++i) {
+    if (!(fl[i] & kSpan0)) continue;
+    int len = 0, top = 0;
+    for (int j = i;;) {
+      const uint8_t f = fl[j];
+      ++len;
+      top += (f & kTop) ? 1 : 0;
+      if ((f & kBrk) || len == span_max) break;
+      do { ++j; } while (j < n && !(fl[j] & kCand));
+      if (j >= n) break;
+    }
+    const bool covered = (double)top / (double)len >= tau_cover;
+    my_sel += covered ? len : top;
+    for (int j = i, c = 0; c < len; ++c) {
+      if (covered || (fl[j] & kTop)) fl[j] |= kSel;
+      do { ++j; } while (j < n && !(fl[j] & kCand));
+    }
+  }
+  const int n_sel = block_sum(my_sel, sh);
+  return n_sel;
+}
+
+__global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Workspace w) {
+  __shared__ int sh[17];
+  __shared__ int hist[kHistBins];
+  __shared__ int digit_info[2];
+  __shared__ uint32_t keys_s[kLdsEntries];  // window grouping: seq_ent (u16) | seq_pre (u16)
+  __shared__ uint8_t fl_s[kLdsEntries];
+  __shared__ uint8_t sq_s[kLdsEntries];
+  __shared__ int sh_a[1024];
+  __shared__ int sh_b[1024];
+  const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
+  const int rq0 = a.req_offsets[r], n = a.req_offsets[r + 1] - rq0;
+
+  int my_ctx = 0, my_cand = 0;
+  for (int i = tid; i < n; i += 4 * nt) {
+    int dl[4];
+    uint8_t rf[4];
+    float sc[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = i + u * nt;
+      dl[u] = j < n ? w.row_delta[rq0 + j] : kFresh;
+      rf[u] = (j < n && a.cand) ? w.rowflag[rq0 + j] : 0;
+      sc[u] = j < n ? a.scores[rq0 + j] : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int j = i + u * nt;
+      if (j < n) {
+        const bool fresh = dl[u] == kFresh;
+        const bool cand = !fresh && (a.cand ? rf[u] == kCand : true);
+        fl_s[j] = fresh ? kFreshF : (cand ? kCand : 0);
+        keys_s[j] = cand ? score_key(sc[u]) : 0u;
+        my_ctx += fresh ? 0 : 1;
+        my_cand += cand ? 1 : 0;
+      }
+    }
+  }
+  const int n_ctx = block_sum(my_ctx, sh);
+  const int n_cand = block_sum(my_cand, sh);
+
+  const int k = k_from_ratio(a.ratio, n_ctx, n_cand, a.k_ceil);
+  lds_mark_top(keys_s, fl_s, n, kCand, kTop, k, n_cand, hist, sh, digit_info);
+
+  uint8_t chosen = kTop;
+  if (a.span_max > 0) {
+    const int n_sel = lds_span_complete(keys_s, fl_s, n, a.span_max, a.tau_smooth, a.tau_cover,
+                                        sh_a, sh_b, sh);
+    chosen = kSel;
+    if (a.cap_ratio > 0.0) {
+      const int m = k_from_ratio(a.cap_ratio, n_ctx, n_cand, a.k_ceil);
+      if (n_sel > m) {
+        lds_mark_top(keys_s, fl_s, n, kSel, kCap, m, n_sel, hist, sh, digit_info);
+        chosen = kCap;
+      }
+    }
+  } else if (a.window > 0) {
+    lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, sh_a, sh);
+    chosen = kSel;
+  }
+  __syncthreads();
+  for (int i = tid; i < n; i += nt) w.rowflag[rq0 + i] = (fl_s[i] & chosen) ? kCand : 0;
 }
 
 // ------------------------------------------------------------------------- //
@@ -565,7 +808,8 @@ __global__ __launch_bounds__(1024) void finalize_kernel(SelectArgs a, Workspace 
 }
 
 // ------------------------------------------------------------------------- //
-// compaction to sel_idx and scatter of the fresh K/V rows (one wave per entry)
+// compaction to sel_idx and scatter of the fresh K/V rows (one wave per entry);
+// with fresh_all every recomputed entry's fresh K/V goes to its row instead
 // ------------------------------------------------------------------------- //
 template <typename T>
 __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Workspace w, int kvdim,
@@ -574,21 +818,28 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Work
   const int lane = threadIdx.x & 63;
   const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
-  const int *roff = a.cand ? w.roff : a.req_offsets;
+  const int *roff = a.listed ? w.roff : a.req_offsets;
   const int nR = roff[a.n_req];
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
   const int chunks = kvdim / V;
   for (int q = wave; q < nR; q += nwaves) {
     const int r = upper_index(roff, a.n_req + 1, q);
     const int i = q - roff[r];
-    if (i >= w.sel_cnt[r]) continue;
-    const int out = sel_offsets[r] + i;
-    const int row = w.tsel_row[q];
-    const int e = w.tsel_ent[q];
-    if (lane == 0) {
-      sel_idx[out] = row;
-      w.sel_ent[out] = e;
+    int row = -1, e = -1;
+    if (i < w.sel_cnt[r]) {
+      const int out = sel_offsets[r] + i;
+      row = w.tsel_row[q];
+      e = w.tsel_ent[q];
+      if (lane == 0) {
+        sel_idx[out] = row;
+        w.sel_ent[out] = e;
+      }
     }
+    if (a.fresh_all) {
+      e = q;
+      row = a.listed ? w.rlist[q] : q;
+    }
+    if (e < 0) continue;
     const T *f = (const T *)w.fresh_kv + (size_t)e * 2 * kvdim;
     for (int c = lane; c < chunks; c += 64) {
       *reinterpret_cast<uint4 *>(k_cache + (size_t)row * kvdim + c * V) =
@@ -612,6 +863,10 @@ hipError_t launch_prepare(const SelectArgs &a, const Workspace &w, hipStream_t s
     int grid = (a.T + 255) / 256;
     grid = grid < 1024 ? (grid > 0 ? grid : 1) : 1024;
     hipLaunchKernelGGL(mark_cand_kernel, dim3(grid), dim3(256), 0, s, a, w);
+  }
+  if (a.mode == SRP_SEL_SCORES)
+    hipLaunchKernelGGL(score_select_kernel, dim3(a.n_req), dim3(1024), 0, s, a, w);
+  if (a.listed) {
     const int bpr = blocks_per_req(a.max_req_rows);
     hipLaunchKernelGGL(r_count_kernel, dim3(a.n_req * bpr), dim3(1024), 0, s, a, w, bpr);
     hipLaunchKernelGGL(r_scan_kernel, dim3(1), dim3(1024), 0, s, a, w, bpr);

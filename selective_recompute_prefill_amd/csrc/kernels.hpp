@@ -42,6 +42,10 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 
+// Rows of one request that the LDS-resident selection kernels hold (larger
+// requests take the global-memory path; external-score selection needs this bound).
+constexpr int kLdsEntries = 22528;
+
 struct SelectArgs {
   int n_req, T, max_req_rows;
   const int32_t *req_offsets, *chunk_offsets, *chunk_src_pos, *positions;
@@ -52,9 +56,17 @@ struct SelectArgs {
   int nkv;
   float *dev_out;
   int tile_rows;  // selected rows per attention tile
+  int k_ceil;     // k = ceil(ratio * N) instead of round half up
+  bool listed;    // the recomputed rows are an explicit per-request list (R list)
+  // external scores and span completion (SRP_SEL_SCORES)
+  const float *scores;
+  int span_max;
+  double tau_smooth, tau_cover, cap_ratio;
+  int fresh_all;  // scatter fresh K/V of every recomputed row
 };
-// Row metadata (delta, request), dev_out prefill with NaN, candidate marking and
-// the R list (candidate rows plus fresh rows, per request) when cand is given.
+// Row metadata (delta, request), dev_out prefill with NaN, candidate marking, the
+// score-based choice of rows in SRP_SEL_SCORES, and the R list (candidate or
+// chosen rows plus fresh rows, per request) when the rows are listed.
 hipError_t launch_prepare(const SelectArgs &a, const Workspace &w, hipStream_t s);
 hipError_t launch_select(const SelectArgs &a, const Workspace &w, hipStream_t s);
 hipError_t launch_finalize(const SelectArgs &a, const Workspace &w, int32_t *sel_offsets,

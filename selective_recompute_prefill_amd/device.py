@@ -67,10 +67,8 @@ class LayerCall:
         self.workspace: Optional[torch.Tensor] = None
         self.device = device
 
-    def select(self, ratio: float, *, mode=S.SRP_SEL_TOPK, window=0, tau=0,
-               dev_mode=S.SRP_DEV_KV, cand=None, cand_offsets=None) -> S.Select:
-        return S.make_select(ratio, mode=mode, window=window, tau=tau, dev_mode=dev_mode,
-                             cand=cand, cand_offsets=cand_offsets)
+    def select(self, ratio: float, **kw) -> S.Select:
+        return S.make_select(ratio, **kw)
 
     def ensure_workspace(self, sel: S.Select) -> int:
         n = S.srp_workspace_size(self.dims, self.batch, sel)

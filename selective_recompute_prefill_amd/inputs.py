@@ -17,7 +17,10 @@ the CacheClip paper's latency table, 15% as CacheBlend's quality floor):
   the chunk-local positions (the perturbation stands in for the missing cross-chunk
   attention of an independently encoded chunk);
 * draw order X, W_q, W_k, W_v, n, eps, then permutations; multi-layer stacks draw
-  X then (W_q, W_k, W_v, n, eps) per layer; the seed is 20260000 + config id.
+  X then (W_q, W_k, W_v, n, eps) per layer; the seed is 20260000 + config id;
+* external importance scores (selection by a small model's scores) come from
+  draw_scores, a stream of their own: units of 1-6 rows at a lognormal(0, 0.5)
+  level with 2% per-row jitter.
 
 Storage: fp32 configs keep float32 arrays; bf16 configs keep uint16 bit patterns
 (value rounded to float32, then to bfloat16, each round-to-nearest-even). The
@@ -274,6 +277,21 @@ class Workload:
 
 def _normal(rng, shape, std=1.0):
     return rng.standard_normal(shape) * std
+
+
+def draw_scores(n_rows: int, seed: int, unit_max: int = 6, spread: float = 0.5,
+                jitter: float = 0.02) -> np.ndarray:
+    """Seeded per-row importance scores as a small auxiliary model would hand them
+    over (deep-layer hidden-state norms, SpecCache notes 2.2; attention column means,
+    CacheClip paper 4.2): positive, and shaped into multi-token units of 1..unit_max
+    rows that share a lognormal(0, spread) level up to a relative jitter, so that
+    smooth spans and sharp edges both occur. float32 [n_rows]; the draws only."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    lens = rng.integers(1, unit_max + 1, n_rows + 1)
+    levels = rng.lognormal(0.0, spread, n_rows + 1)
+    base = np.repeat(levels, lens)[:n_rows]
+    noise = rng.standard_normal(n_rows)
+    return (base * (1.0 + jitter * noise)).astype(np.float32)
 
 
 def generate(spec: Spec) -> Workload:

@@ -15,7 +15,8 @@ LIB_PATH = os.environ.get("SRP_LIB", os.path.join(_PKG, "libsrp.so"))
 
 SRP_OK, SRP_E_INVALID, SRP_E_WORKSPACE, SRP_E_UNSUPPORTED, SRP_E_HIP, SRP_E_BATCH = 0, -1, -2, -3, -4, -5
 SRP_F32, SRP_BF16 = 0, 1
-SRP_SEL_TOPK, SRP_SEL_GIVEN = 0, 1
+SRP_SEL_TOPK, SRP_SEL_GIVEN, SRP_SEL_SCORES = 0, 1, 2
+SRP_K_ROUND, SRP_K_CEIL = 0, 1
 SRP_DEV_KV, SRP_DEV_V = 0, 1
 
 EXPORTS = ("srp_workspace_size", "srp_fuse_layer", "srp_encode_kv", "srp_rerotate_kv",
@@ -48,7 +49,10 @@ class Select(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("ratio", ctypes.c_double),
                 ("window", ctypes.c_int32), ("tau", ctypes.c_int32),
                 ("dev_mode", ctypes.c_int32), ("cand", ctypes.c_void_p),
-                ("cand_offsets", ctypes.c_void_p)]
+                ("cand_offsets", ctypes.c_void_p), ("k_rule", ctypes.c_int32),
+                ("span_max", ctypes.c_int32), ("scores", ctypes.c_void_p),
+                ("tau_smooth", ctypes.c_double), ("tau_cover", ctypes.c_double),
+                ("cap_ratio", ctypes.c_double), ("fresh_all", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -121,8 +125,13 @@ def make_batch(req_offsets, chunk_offsets, chunk_src_pos, positions, *, total_ro
 
 
 def make_select(ratio: float, *, mode=SRP_SEL_TOPK, window=0, tau=0, dev_mode=SRP_DEV_KV,
-                cand=None, cand_offsets=None) -> Select:
-    return Select(mode, float(ratio), int(window), int(tau), dev_mode, _ptr(cand), _ptr(cand_offsets))
+                cand=None, cand_offsets=None, k_rule=SRP_K_ROUND, scores=None, span_max=0,
+                tau_smooth=0.0, tau_cover=0.0, cap_ratio=0.0, fresh_all=False) -> Select:
+    """Selection descriptor; `scores` (fp32 device tensor [T]) goes with SRP_SEL_SCORES.
+    SpecCache's span completion is span_max=16, tau_smooth=0.4, tau_cover=0.7."""
+    return Select(mode, float(ratio), int(window), int(tau), dev_mode, _ptr(cand), _ptr(cand_offsets),
+                  int(k_rule), int(span_max), _ptr(scores), float(tau_smooth), float(tau_cover),
+                  float(cap_ratio), int(bool(fresh_all)))
 
 
 def srp_workspace_size(dims: Dims, batch: Batch, sel: Select) -> int:

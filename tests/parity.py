@@ -11,6 +11,14 @@ from selective_recompute_prefill_amd import inputs
 
 # Tolerances: rel-L2 and max-abs per output, by storage dtype.
 TOL = {"bf16": (1e-2, 3e-2), "f32": (1e-5, 1e-5)}
+# The fixed max-abs bound holds for unit-scale operands (|K|, |V| below about 4 on
+# the workloads' selections). bf16 rounding errors grow with the magnitude of the
+# operands (a store of v errs by up to |v| 2^-9; rounded queries and probabilities
+# perturb an attention row in proportion to its values), so where large-magnitude
+# rows stay in the cache the bound scales: max-abs <= bound * max(1, mag / MAG_UNIT),
+# mag = the stored value itself for K/V, the largest |V| among the row's visible keys
+# for attention.
+MAG_UNIT = 4.0
 NEAR_TIE = 1e-4  # relative deviation gap below which two candidates may swap
 
 
@@ -47,7 +55,7 @@ def gpu_f64(a: np.ndarray, dtype: str) -> np.ndarray:
     return ref.widen(a, dtype)
 
 
-def assert_close(got: np.ndarray, want: np.ndarray, dtype: str, what: str):
+def assert_close(got: np.ndarray, want: np.ndarray, dtype: str, what: str, mag=None):
     rl, ma = TOL[dtype]
     got = np.asarray(got, np.float64)
     want = np.asarray(want, np.float64)
@@ -57,9 +65,27 @@ def assert_close(got: np.ndarray, want: np.ndarray, dtype: str, what: str):
     err = got - want
     nrm = np.linalg.norm(want)
     rel = np.linalg.norm(err) / (nrm if nrm > 0 else 1.0)
-    mx = np.abs(err).max()
+    bound = ma * np.maximum(1.0, np.broadcast_to(mag, want.shape) / MAG_UNIT) if mag is not None \
+        else np.full(want.shape, ma)
+    worst = int(np.argmax(np.abs(err) - bound))
+    mx, bw = float(np.abs(err).flat[worst]), float(bound.flat[worst])
     assert np.isfinite(got).all(), f"{what}: non-finite output"
-    assert rel <= rl and mx <= ma, f"{what}: rel-L2 {rel:.3e} (<= {rl}), max-abs {mx:.3e} (<= {ma})"
+    assert rel <= rl and mx <= bw, (f"{what}: rel-L2 {rel:.3e} (<= {rl}), abs err {mx:.3e} at "
+                                    f"|value| {abs(float(want.flat[worst])):.3g} (<= {bw:.3e})")
+
+
+def visible_vmax(v_cache: np.ndarray, rows: np.ndarray, req_offsets, n_heads: int) -> np.ndarray:
+    """[len(rows), n_heads, 1]: the largest |V| of head h's KV group over the keys row
+    j sees (its request's rows up to j; positions ascend with rows in a request)."""
+    nkv = v_cache.shape[1]
+    m = np.abs(v_cache).max(axis=2)  # [T, nkv]
+    pm = np.empty_like(m)
+    for r in range(len(req_offsets) - 1):
+        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
+        if b > a:
+            pm[a:b] = np.maximum.accumulate(m[a:b], axis=0)
+    g = (np.arange(n_heads) * nkv) // n_heads
+    return pm[np.asarray(rows, np.int64)][:, g][:, :, None]
 
 
 def check_selection(gpu_sel: np.ndarray, ref_out: dict, req_of_row: np.ndarray, what: str):

@@ -65,6 +65,19 @@ def test_bad_dims(dims_kw, code):
     (dict(ratio=0.2, cand=8), S.SRP_E_INVALID),
     (dict(ratio=0.2, mode=S.SRP_SEL_GIVEN), S.SRP_E_INVALID),
     (dict(ratio=0.2, dev_mode=3), S.SRP_E_INVALID),
+    (dict(ratio=0.2, k_rule=2), S.SRP_E_INVALID),
+    (dict(ratio=0.2, mode=S.SRP_SEL_SCORES), S.SRP_E_INVALID),
+    (dict(ratio=0.2, scores=8), S.SRP_E_INVALID),
+    (dict(ratio=0.2, span_max=16, tau_smooth=0.4, tau_cover=0.7), S.SRP_E_INVALID),
+    (dict(ratio=0.2, mode=S.SRP_SEL_SCORES, scores=8, span_max=2000), S.SRP_E_INVALID),
+    (dict(ratio=0.2, mode=S.SRP_SEL_SCORES, scores=8, span_max=16, window=8, tau=4), S.SRP_E_INVALID),
+    (dict(ratio=0.2, mode=S.SRP_SEL_SCORES, scores=8, span_max=16, cand=8, cand_offsets=8),
+     S.SRP_E_INVALID),
+    (dict(ratio=0.2, mode=S.SRP_SEL_SCORES, scores=8, span_max=16, tau_cover=1.5), S.SRP_E_INVALID),
+    (dict(ratio=0.2, mode=S.SRP_SEL_SCORES, scores=8, span_max=16, tau_smooth=float("nan")),
+     S.SRP_E_INVALID),
+    (dict(ratio=0.2, mode=S.SRP_SEL_SCORES, scores=8, cap_ratio=0.5), S.SRP_E_INVALID),
+    (dict(ratio=0.2, mode=S.SRP_SEL_SCORES, scores=8, span_max=16, cap_ratio=0.1), S.SRP_E_INVALID),
 ])
 def test_bad_select(sel, code):
     ratio = sel.pop("ratio")
@@ -72,6 +85,25 @@ def test_bad_select(sel, code):
         S.srp_workspace_size(_dims(), _batch(), S.make_select(ratio, **sel))
     assert e.value.code == code
     assert len(S.lib().srp_last_error()) > 0
+
+
+def test_fresh_all_flag_is_checked():
+    sel = S.make_select(0.2)
+    sel.fresh_all = 2
+    with pytest.raises(S.SrpError) as e:
+        S.srp_workspace_size(_dims(), _batch(), sel)
+    assert e.value.code == S.SRP_E_INVALID
+
+
+def test_scores_mode_accepted_and_bounded():
+    ok = S.make_select(0.2, mode=S.SRP_SEL_SCORES, scores=8, span_max=16, tau_smooth=0.4,
+                       tau_cover=0.7, cap_ratio=0.3, k_rule=S.SRP_K_CEIL)
+    assert S.srp_workspace_size(_dims(), _batch(), ok) > 0
+    big = _batch(total_rows=30000, max_req_rows=30000)
+    with pytest.raises(S.SrpError) as e:
+        S.srp_workspace_size(_dims(), big, ok)
+    assert e.value.code == S.SRP_E_UNSUPPORTED
+    S.srp_workspace_size(_dims(), big, S.make_select(0.2, fresh_all=True))
 
 
 def test_bad_batch():
@@ -107,3 +139,5 @@ def test_struct_layouts_match_header():
     assert ctypes.sizeof(S.Dims) == 32 and S.Dims.rope_base.offset == 16
     assert S.Batch.req_offsets.offset == 24 and ctypes.sizeof(S.Batch) == 56
     assert S.Select.ratio.offset == 8 and S.Select.cand.offset == 32
+    assert S.Select.scores.offset == 56 and S.Select.fresh_all.offset == 88
+    assert ctypes.sizeof(S.Select) == 96

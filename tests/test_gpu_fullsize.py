@@ -19,7 +19,8 @@ from selective_recompute_prefill_amd import inputs
 from selective_recompute_prefill_amd import srp as S
 from selective_recompute_prefill_amd.device import LayerCall, download, ints, upload
 
-from parity import assert_close, check_selection, csr_ok, oracle_caches, oracle_layer
+from parity import (assert_close, check_selection, csr_ok, oracle_caches, oracle_layer,
+                    visible_vmax)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -47,24 +48,35 @@ def _gpu_layer(spec, lay, hidden_st, wq_st, kc_st, vc_st, ratio, **sel_kw):
     return got
 
 
-def _compare_layer(spec, lay, got, hidden_st, wq_st, kc_st, vc_st, want, okw, what, sample=True):
-    """Selection (near-ties), K/V (all rows), deviations, attention (sample)."""
+def _compare_layer(spec, lay, got, hidden_st, wq_st, kc_st, vc_st, want, okw, what, sample=True,
+                   exact=False):
+    """Selection (near-ties unless exact), K/V (all rows), deviations, attention
+    (sample)."""
     req, src = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
     csr_ok(got["sel_idx"], got["sel_offsets"], lay.req_offsets)
-    if okw.get("window", 0) == 0:
+    if exact:
+        assert np.array_equal(got["sel_idx"], want["sel_idx"]), what + ": selection differs"
+    elif okw.get("window", 0) == 0:
         check_selection(got["sel_idx"], want, req, what)
     sp = _sample_positions(len(got["sel_idx"])) if sample else None
-    if not np.array_equal(got["sel_idx"], want["sel_idx"]) or sample:
+    if exact and sample:
+        pass  # want already holds the sampled attention rows of this selection
+    elif not np.array_equal(got["sel_idx"], want["sel_idx"]) or sample:
         want = oracle_layer(spec, lay, hidden_st, wq_st, kc_st, vc_st, sel_override=got["sel_idx"],
                             attn_sample=sp, **okw)
     dt = spec.dtype
-    assert_close(ref.widen(got["k_cache"], dt), want["k_cache"], dt, what + " K")
-    assert_close(ref.widen(got["v_cache"], dt), want["v_cache"], dt, what + " V")
+    # a choice by scores leaves high-noise (large-magnitude) rows in the cache
+    scaled = okw.get("mode") == "scores"
+    mag = lambda a: np.abs(a) if scaled else None
+    assert_close(ref.widen(got["k_cache"], dt), want["k_cache"], dt, what + " K", mag(want["k_cache"]))
+    assert_close(ref.widen(got["v_cache"], dt), want["v_cache"], dt, what + " V", mag(want["v_cache"]))
     ga = ref.widen(got["attn_out"], dt)
+    rows = got["sel_idx"] if sp is None else got["sel_idx"][sp]
+    amag = visible_vmax(want["v_cache"], rows, lay.req_offsets, spec.n_heads) if scaled else None
     if sp is not None:
-        assert_close(ga[sp], want["attn_out"][sp], dt, what + " attention (sampled rows)")
+        assert_close(ga[sp], want["attn_out"][sp], dt, what + " attention (sampled rows)", amag)
     else:
-        assert_close(ga, want["attn_out"], dt, what + " attention")
+        assert_close(ga, want["attn_out"], dt, what + " attention", amag)
     scored = np.isfinite(want["dev"])
     rel = np.abs(got["dev"][:lay.total_rows][scored] - want["dev"][scored]) / want["dev"][scored]
     assert rel.max() < 1e-4, f"{what}: deviation rel err {rel.max():.2e}"
@@ -108,6 +120,31 @@ def test_config2_16k_grouped_layer():
     kept = ref.group_windows(np.searchsorted(seq, s0_gpu), len(seq), 8, 4)
     assert np.array_equal(got["sel_idx"], np.union1d(seq[np.asarray(kept)], fresh))
     _compare_layer(spec, lay, got, w.hidden, wq, kc, vc, want, okw, "config2")
+
+
+def test_config2_16k_scores_span_completion():
+    """The 16K layer with rows chosen from external scores (SpecCache's settings:
+    K = ceil(0.2 N), spans of at most 16 at tau_smooth 0.4, completion at tau_cover
+    0.7, a budget of 25%): the choice is exact, caches and sampled attention rows
+    within tolerance."""
+    spec = inputs.CONFIGS[2]
+    w = inputs.generate(spec)
+    lay = w.layout
+    kc, vc = oracle_caches(w)
+    wq = w.layers[0].w_qkv
+    sc = inputs.draw_scores(lay.total_rows, 22)
+    kw = dict(span_max=16, tau_smooth=0.4, tau_cover=0.7, cap_ratio=0.25)
+    _say(f"[gpu] config2 scores T={lay.total_rows}")
+    got = _gpu_layer(spec, lay, w.hidden, wq, kc, vc, spec.ratio, mode=S.SRP_SEL_SCORES,
+                     scores=torch.as_tensor(sc, device="cuda"), k_rule=S.SRP_K_CEIL, **kw)
+    okw = dict(ratio=spec.ratio, window=0, tau=0, mode="scores", scores=sc.astype(np.float64),
+               k_rule="ceil", **kw)
+    sp = _sample_positions(len(got["sel_idx"]))
+    want = oracle_layer(spec, lay, w.hidden, wq, kc, vc, attn_sample=sp, **okw)
+    assert np.array_equal(got["sel_idx"], want["sel_idx"])
+    assert len(want["sel_idx"]) > len(want["s0"]) + 96  # completion added rows
+    _compare_layer(spec, lay, got, w.hidden, wq, kc, vc, want, okw, "config2 scores", sample=True,
+                   exact=True)
 
 
 def _csr(rows, req_offsets):

@@ -17,7 +17,8 @@ from selective_recompute_prefill_amd import inputs
 from selective_recompute_prefill_amd import srp as S
 from selective_recompute_prefill_amd.device import LayerCall, download, ints, upload
 
-from parity import assert_close, check_selection, csr_ok, oracle_caches, oracle_layer
+from parity import (assert_close, check_selection, csr_ok, oracle_caches, oracle_layer,
+                    visible_vmax)
 
 pytestmark = pytest.mark.gpu
 
@@ -57,7 +58,10 @@ def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel
 
     req, _ = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
     csr_ok(got["sel_idx"], got["sel_offsets"], lay.req_offsets)
-    if sel_kw.get("window", 0) > 0 and check_group_s0:
+    if okw.get("mode") == "scores":
+        # the choice from given scores is exact on both sides (fp32 ranks, fp64 spans)
+        assert np.array_equal(got["sel_idx"], want["sel_idx"]), what + ": selection from scores differs"
+    elif sel_kw.get("window", 0) > 0 and check_group_s0:
         # compare the top-k sets, then the grouping of the GPU's own top-k set
         call0 = LayerCall(spec, lay)
         kc0, vc0 = upload(kc_st, spec.dtype), upload(vc_st, spec.dtype)
@@ -85,9 +89,13 @@ def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel
     assert np.array_equal(got["sel_offsets"], want["sel_offsets"])
 
     dt = spec.dtype
-    assert_close(ref.widen(k_out, dt), want["k_cache"], dt, what + " K cache")
-    assert_close(ref.widen(v_out, dt), want["v_cache"], dt, what + " V cache")
-    assert_close(ref.widen(got["attn_out"], dt), want["attn_out"], dt, what + " attention")
+    # a choice by scores leaves high-noise (large-magnitude) rows in the cache
+    scaled = okw.get("mode") == "scores"
+    mag = lambda a: np.abs(a) if scaled else None
+    assert_close(ref.widen(k_out, dt), want["k_cache"], dt, what + " K cache", mag(want["k_cache"]))
+    assert_close(ref.widen(v_out, dt), want["v_cache"], dt, what + " V cache", mag(want["v_cache"]))
+    amag = visible_vmax(want["v_cache"], want["sel_idx"], lay.req_offsets, spec.n_heads) if scaled else None
+    assert_close(ref.widen(got["attn_out"], dt), want["attn_out"], dt, what + " attention", amag)
     # deviations of scored rows (fp32 on the GPU)
     scored = np.isfinite(want["dev"])
     assert np.array_equal(np.isfinite(got["dev"][:lay.total_rows]), scored)
@@ -205,6 +213,125 @@ def test_deterministic_bitwise():
         outs.append((res["sel_idx"], res["attn_out"], download(k), download(v), res["dev"]))
     for a, b in zip(*outs):
         assert np.array_equal(a, b, equal_nan=True) if a.dtype.kind == "f" else np.array_equal(a, b)
+
+
+# --------------------------------------------------------------------------- #
+# selection by external scores; fresh K/V for every recomputed row
+# --------------------------------------------------------------------------- #
+
+SPEC_SPANS = dict(span_max=16, tau_smooth=0.4, tau_cover=0.7)
+
+
+def _scores_case(spec, scores, sel_kw, what, w=None, kc=None, vc=None, cand=None):
+    w = w or inputs.generate(spec)
+    if kc is None:
+        kc, vc = oracle_caches(w)
+    sc = torch.as_tensor(scores, dtype=torch.float32, device="cuda")
+    skw = dict(sel_kw, mode=S.SRP_SEL_SCORES, scores=sc)
+    okw = dict(mode="scores", scores=scores.astype(np.float64),
+               k_rule="ceil" if sel_kw.get("k_rule", 0) == S.SRP_K_CEIL else "round",
+               span_max=sel_kw.get("span_max", 0), tau_smooth=sel_kw.get("tau_smooth", 0.0),
+               tau_cover=sel_kw.get("tau_cover", 0.0), cap_ratio=sel_kw.get("cap_ratio", 0.0))
+    if cand is not None:
+        c, off = cand
+        skw.update(cand=ints(c), cand_offsets=ints(off))
+        okw["cand"] = c
+    skw.setdefault("window", 0)
+    skw.setdefault("tau", 0)
+    return run_case(spec, w=w, kc_st=kc, vc_st=vc, sel_kw=skw, oracle_kw=okw, what=what)
+
+
+def test_scores_topk_only():
+    spec = inputs.small_spec()
+    T = inputs.generate(spec).layout.total_rows
+    _scores_case(spec, inputs.draw_scores(T, 11), dict(ratio=0.2), "scores-topk")
+
+
+@pytest.mark.parametrize("k_rule,cap,cover", [(S.SRP_K_CEIL, 0.0, 0.7), (S.SRP_K_CEIL, 0.205, 0.5),
+                                               (S.SRP_K_ROUND, 0.0, 0.5)])
+def test_scores_span_completion(k_rule, cap, cover):
+    spec = inputs.small_spec()
+    T = inputs.generate(spec).layout.total_rows
+    kw = dict(SPEC_SPANS, tau_cover=cover)
+    got, want, _ = _scores_case(spec, inputs.draw_scores(T, 12),
+                                dict(ratio=0.2, k_rule=k_rule, cap_ratio=cap, **kw),
+                                f"scores-spans-{k_rule}-{cap}-{cover}")
+    # completion added cached rows beyond T_init; a cap bounds each request's cached rows
+    lay = inputs.generate(spec).layout
+    req, src = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
+    sel = got["sel_idx"]
+    cached_sel = sel[src[sel] >= 0]
+    assert len(np.setdiff1d(cached_sel, want["s0"])) > 0
+    if cap > 0:
+        for r in range(lay.n_req):
+            n_ctx = int(np.sum((req == r) & (src >= 0)))
+            m = ref.topk_count(cap, n_ctx, n_ctx, "ceil" if k_rule == S.SRP_K_CEIL else "round")
+            assert np.sum(req[cached_sel] == r) == m  # the cap binds on this input
+
+
+def test_scores_window_grouping():
+    spec = inputs.small_spec()
+    T = inputs.generate(spec).layout.total_rows
+    _scores_case(spec, inputs.draw_scores(T, 13), dict(ratio=0.2, window=8, tau=4), "scores-window")
+
+
+def test_scores_with_candidate_list():
+    spec = inputs.small_spec()
+    w = inputs.generate(spec)
+    lay = w.layout
+    rng = np.random.default_rng(6)
+    cand, off = [], [0]
+    for r in range(lay.n_req):
+        rows = np.arange(lay.req_offsets[r], lay.req_offsets[r + 1])
+        pick = np.sort(rng.choice(rows, len(rows) // 2, replace=False))
+        cand.append(pick)
+        off.append(off[-1] + len(pick))
+    _scores_case(spec, inputs.draw_scores(lay.total_rows, 14), dict(ratio=0.15), "scores-cand", w=w,
+                 cand=(np.concatenate(cand), np.asarray(off)))
+
+
+@pytest.mark.parametrize("case", ["constant", "signed", "unit-spans", "cover-zero", "ratio-one",
+                                  "ratio-zero", "long-spans"])
+def test_scores_edge_cases(case):
+    spec = inputs.small_spec()
+    T = inputs.generate(spec).layout.total_rows
+    sc = inputs.draw_scores(T, 15)
+    kw = dict(ratio=0.2, **SPEC_SPANS)
+    if case == "constant":       # every score equal: ties go to the lowest rows
+        sc = np.full(T, 1.5, np.float32)
+    elif case == "signed":       # negative scores and both zeros rank by value
+        sc = (sc - np.median(sc)).astype(np.float32)
+        sc[::7] = 0.0
+        sc[3::7] = -0.0
+    elif case == "unit-spans":
+        kw["span_max"] = 1
+    elif case == "cover-zero":   # every span is completed
+        kw["tau_cover"] = 0.0
+    elif case == "ratio-one":
+        kw["ratio"] = 1.0
+    elif case == "ratio-zero":   # nothing chosen: only the query tail is recomputed
+        kw["ratio"] = 0.0
+    elif case == "long-spans":
+        kw.update(span_max=1024, tau_smooth=3.0, tau_cover=0.3, cap_ratio=0.5)
+    _scores_case(spec, sc, kw, f"scores-{case}")
+
+
+@pytest.mark.parametrize("mode", ["topk", "cand"])
+def test_fresh_all(mode):
+    spec = inputs.small_spec()
+    w = inputs.generate(spec)
+    kc, vc = oracle_caches(w)
+    if mode == "topk":
+        run_case(spec, w=w, kc_st=kc, vc_st=vc, sel_kw=dict(ratio=0.15, fresh_all=True),
+                 oracle_kw=dict(fresh_all=True), what="fresh-all")
+        return
+    lay = w.layout
+    cand = np.concatenate([np.arange(lay.req_offsets[r], lay.req_offsets[r + 1])[::3]
+                           for r in range(lay.n_req)])
+    off = np.searchsorted(cand, lay.req_offsets)
+    run_case(spec, w=w, kc_st=kc, vc_st=vc,
+             sel_kw=dict(ratio=0.1, cand=ints(cand), cand_offsets=ints(off), fresh_all=True),
+             oracle_kw=dict(cand=cand, fresh_all=True), what="fresh-all-cand")
 
 
 # --------------------------------------------------------------------------- #
