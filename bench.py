@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4])
     p.add_argument("--ratio", type=float, default=None, help="override the workload's ratio")
+    p.add_argument("--select", choices=["deviation", "scores"], default="deviation",
+                   help="rank rows by KV deviation (default) or by external per-row scores with "
+                        "span completion (single-layer workloads)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--cpu-sample-chunks", type=int, default=0,
                    help="chunks of the request the oracle is timed on (0: all of them)")
@@ -67,23 +70,28 @@ def parse():
 def algorithmic_work(spec, lay, sel, ratio_rows):
     """Per-stage algorithmic flops and bytes of one layer call (see the design notes):
     bytes count what the method must move once, flops count the products it must
-    form; both use the actual selection."""
+    form; both use the actual selection. ratio_rows: n_ctx (cached rows), n_rec
+    (rows projected to K/V: candidates or chosen rows, plus fresh rows), n_rec_ctx
+    (the cached ones among them; the other cached rows are re-rotated on their own
+    in the prepare stage), scores (external scores read by the prepare stage)."""
     import numpy as np
     e = 2 if spec.dtype == "bf16" else 4
     H, kvd, qd = spec.hidden, spec.kvdim, spec.qdim
     T = lay.total_rows
     n_ctx = ratio_rows["n_ctx"]
-    n_rec = ratio_rows["n_rec"]  # rows projected to K/V (candidates + fresh)
+    n_rec = ratio_rows["n_rec"]
+    n_rc = ratio_rows.get("n_rec_ctx", n_ctx)
     n_sel = len(sel)
     req_start = np.zeros(T, np.int64)
     for r in range(lay.n_req):
         req_start[lay.req_offsets[r]:lay.req_offsets[r + 1]] = lay.req_offsets[r]
     pairs = int((sel - req_start[sel] + 1).sum()) if n_sel else 0
+    prep = T * 4 * 3 + (T * 4 if ratio_rows.get("scores") else 0) + e * 2 * (n_ctx - n_rc) * kvd
     return {
-        "prepare": {"bytes": T * 4 * 3},
+        "prepare": {"bytes": prep},
         "kv_proj": {"flops": 2.0 * n_rec * H * 2 * kvd,
                     # A rows, W_k/W_v, cached K read + K~ write, cached V read, fresh K/V write
-                    "bytes": e * (n_rec * H + 2 * kvd * H + 2 * n_ctx * kvd + n_ctx * kvd + 2 * n_rec * kvd)},
+                    "bytes": e * (n_rec * H + 2 * kvd * H + 2 * n_rc * kvd + n_rc * kvd + 2 * n_rec * kvd)},
         "select": {"bytes": n_rec * 2 * spec.n_kv_heads * 4 + n_rec * 4 * 4},
         "scatter": {"bytes": e * 2 * n_sel * 2 * kvd},
         "q_proj": {"flops": 2.0 * n_sel * H * qd, "bytes": e * (n_sel * H + qd * H + n_sel * qd)},
@@ -221,9 +229,10 @@ def copy_calibration(mib):
     print(json.dumps({"copy_mib": mib, "repeats": 5}), flush=True)
 
 
-def cpu_baseline(spec, n_chunks_sample):
+def cpu_baseline(spec, n_chunks_sample, scores_kw=None):
     """Time the fp64 oracle on a bounded sample of the workload: the first
-    n_chunks_sample chunks of one request (with its prefix and query tail)."""
+    n_chunks_sample chunks of one request (with its prefix and query tail).
+    scores_kw: the external-score selection settings (scores drawn for the sample)."""
     import numpy as np
     from oracle import ref
     from selective_recompute_prefill_amd import inputs
@@ -251,12 +260,15 @@ def cpu_baseline(spec, n_chunks_sample):
     vc = ref.widen(inputs.store(vc, sub.dtype), sub.dtype)
     x = ref.widen(w.hidden, sub.dtype)
     ratio = sub.layer_ratios()[0]
+    skw = dict(window=sub.window, tau=sub.tau)
+    if scores_kw is not None:
+        skw = dict(scores_kw, window=0, tau=0, mode="scores",
+                   scores=inputs.draw_scores(lay.total_rows, SCORES_SEED).astype(np.float64))
     t0 = time.perf_counter()
     ref.fuse_layer(hidden=x, w_qkv=wq, k_cache=kc, v_cache=vc, req_offsets=lay.req_offsets,
                    chunk_offsets=lay.chunk_offsets, chunk_src_pos=lay.chunk_src_pos,
                    positions=lay.positions, n_heads=sub.n_heads, n_kv=sub.n_kv_heads,
-                   head_dim=sub.head_dim, rope_base=sub.rope_base, ratio=ratio,
-                   window=sub.window, tau=sub.tau)
+                   head_dim=sub.head_dim, rope_base=sub.rope_base, ratio=ratio, **skw)
     dt = time.perf_counter() - t0
     n_ctx = int(cr.sum())
     return {"value": n_ctx / dt, "unit": "context tokens/s per layer", "cores": int(threads),
@@ -267,6 +279,13 @@ def cpu_baseline(spec, n_chunks_sample):
                           "oracle's rate at full length" if n_ch < len(spec.chunk_lens) else
                           " (one request of the workload, timed once)")),
             "seconds": dt}
+
+
+# External-score selection on the benchmark: SpecCache's settings (K = ceil(rho N),
+# spans of at most 16 rows at tau_smooth 0.4, completion at tau_cover 0.7) with a
+# budget of 25% of the cached rows; scores from the seeded generator.
+SCORES_SEED = 22
+SCORES_SETTINGS = dict(k_rule="ceil", span_max=16, tau_smooth=0.4, tau_cover=0.7, cap_ratio=0.25)
 
 
 def main():
@@ -333,6 +352,14 @@ def main():
 
     n_copies = args.steps + args.warmup
     sel_kw = dict(window=spec.window, tau=spec.tau)
+    by_scores = args.select == "scores"
+    if by_scores:
+        if nl != 1:
+            print("--select scores applies to single-layer workloads", file=sys.stderr)
+            sys.exit(2)
+        scores_dev = torch.as_tensor(inputs.draw_scores(T, SCORES_SEED), device=dev)
+        sel_kw = dict(SCORES_SETTINGS, mode=S.SRP_SEL_SCORES, scores=scores_dev,
+                      k_rule=S.SRP_K_CEIL)
     # pristine cache copies, one per step and layer
     pristine = [[(c[0].clone(), c[1].clone()) for c in caches] for _ in range(n_copies)]
     hiddens = [hidden0.clone() for _ in range(n_copies)] if nl > 1 else [hidden0]
@@ -382,8 +409,13 @@ def main():
     names = [S.srp_profile_stage_name(i) for i in range(S.SRP_N_STAGES)]
     st = np.asarray(stage_ms, np.float64).reshape(args.steps, nl, S.SRP_N_STAGES)
     # per-stage work of the first layer (the layer the metric is quoted on)
-    n_rec = T  # single-shot layer: every row is projected to K/V
-    work = algorithmic_work(spec, lay, sel if nl == 1 else _first_layer_sel(call, spec, lay, hidden0, wqs, pristine, sel_kw, ratios), {"n_ctx": n_ctx, "n_rec": n_rec})
+    sel0 = sel if nl == 1 else _first_layer_sel(call, spec, lay, hidden0, wqs, pristine, sel_kw, ratios)
+    if by_scores:  # only the chosen rows (and fresh rows) are projected
+        n_rc = int((src[sel0] >= 0).sum())
+        rows = {"n_ctx": n_ctx, "n_rec": len(sel0), "n_rec_ctx": n_rc, "scores": True}
+    else:  # the first layer projects every row to K/V
+        rows = {"n_ctx": n_ctx, "n_rec": T}
+    work = algorithmic_work(spec, lay, sel0, rows)
     stages = {}
     peak_fl = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
     for i, nm in enumerate(names):
@@ -405,7 +437,7 @@ def main():
             "frac": stages[dom]["frac_mfma"], "traffic": None,
             "flops_per_launch": work[dom]["flops"], "avg_launch_ms": stages[dom]["ms"]}
 
-    if args.workload == 2 and args.ratio is None:
+    if args.workload == 2 and args.ratio is None and not by_scores:
         # HBM bytes per launch from the recorded counter runs of this workload
         roof["traffic"] = recorded_traffic(roof["kernel"])
 
@@ -423,7 +455,9 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if spec.dtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOAD_NAMES[args.workload] + (f" (ratio {args.ratio})" if args.ratio else ""),
+        "config": {"workload": WORKLOAD_NAMES[args.workload] + (f" (ratio {args.ratio})" if args.ratio else "")
+                   + ("; rows chosen by external scores: K = ceil(0.2 N), spans <= 16 at 0.4, "
+                      "cover 0.7, budget 0.25" if by_scores else ""),
                    "global_batch": lay.n_req, "seq_len": int(lay.req_offsets[1]),
                    "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_per_layer, 4),
@@ -434,7 +468,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(spec, args.cpu_sample_chunks)
+        out["cpu_baseline"] = cpu_baseline(spec, args.cpu_sample_chunks,
+                                           SCORES_SETTINGS if by_scores else None)
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)

@@ -528,7 +528,7 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
 // run before any projection: the chosen rows become the candidate marks of the
 // R list, which the rest of the layer treats as a given list
 // ------------------------------------------------------------------------- //
-constexpr uint8_t kBrk = 16;    // spans: no join with the next candidate
+constexpr uint8_t kBrk = 16;    // spans: the candidate starts a run (does not join its predecessor)
 constexpr uint8_t kSpan0 = 32;  // spans: a span starts at this entry
 constexpr uint8_t kCap = 64;    // budget cap: kept
 
@@ -563,131 +563,156 @@ __device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, int *sa
   __syncthreads();
 }
 
-// Relative change of the normalised score from entry i to the next candidate j does
-// not stay below tau: evaluated in double as written, (s - min) / (max - min) for
-// each side, then |s~_j - s~_i| / s~_i; a NaN or infinite change breaks the span.
-__device__ __forceinline__ bool span_breaks(uint32_t ki, uint32_t kj, double mn, double range,
-                                            double tau) {
-#pragma clang fp contract(off)
-  const double ti = ((double)key_score(ki) - mn) / range;
-  const double tj = ((double)key_score(kj) - mn) / range;
-  const double delta = fabs(tj - ti) / ti;
-  return !(delta < tau);
+// In place over blockDim ints each: up[t] <- max(up[0..t]), down[t] <- min(down[t..])
+// (Hillis-Steele; both arrays written by their owners before the call).
+__device__ void block_scan_max_min(int *up, int *down) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  __syncthreads();
+  for (int o = 1; o < nt; o <<= 1) {
+    const int vu = tid >= o ? up[tid - o] : INT_MIN;
+    const int vd = tid + o < nt ? down[tid + o] : INT_MAX;
+    __syncthreads();
+    if (vu > up[tid]) up[tid] = vu;
+    if (vd < down[tid]) down[tid] = vd;
+    __syncthreads();
+  }
 }
 
-// Span completion over the sequence of kCand entries in order, T_init = kTop: the
-// sequence is cut into spans (a new span where the relative change breaks, or
-// after span_max entries), and a span whose kTop share reaches tau_cover marks all
-// of its entries kSel; other spans mark their kTop entries. Returns the kSel count.
-// sa, sb: blockDim ints of scratch.
-__device__ int lds_span_complete(const uint32_t *keys, uint8_t *fl, int n, int span_max,
-                                 double tau_smooth, double tau_cover, int *sa, int *sb, int *sh) {
+// Min-max normalised score, in double as written: (s - min) / (max - min).
+__device__ __forceinline__ double norm_score(uint32_t key, double mn, double range) {
+#pragma clang fp contract(off)
+  return ((double)key_score(key) - mn) / range;
+}
+
+// Candidate j joins the span of its predecessor i while the relative change
+// |s~_j - s~_i| / s~_i stays below tau (double; a NaN or infinite change does not).
+__device__ __forceinline__ bool joins(double ti, double tj, double tau) {
+#pragma clang fp contract(off)
+  const double delta = fabs(tj - ti) / ti;
+  return delta < tau;
+}
+
+constexpr int kSegMax = (kLdsEntries + 1023) / 1024;  // entries per thread at most
+
+// Span completion over the sequence of kCand entries in order, T_init = kTop. Every
+// thread holds its contiguous share of entries in registers: a candidate either
+// joins its predecessor or starts a run; runs are cut into spans of span_max slots
+// from their start; each candidate adds (its kTop, 1) to a counter at its span's
+// first entry (LDS atomics into ctr, which aliases the key storage), and a span
+// whose kTop share reaches tau_cover marks every candidate kSel (others mark their
+// kTop candidates). Returns the kSel count. sa..sd: blockDim ints of scratch each.
+__device__ int lds_span_complete(uint32_t *keys, uint8_t *fl, int n, int span_max, double tau_smooth,
+                                 double tau_cover, int *sa, int *sb, int *sc, int *sd, int *sh) {
   const int tid = threadIdx.x, nt = blockDim.x;
+  const int per = (n + nt - 1) / nt;  // <= kSegMax
+  const int lo = min(n, tid * per), hi = min(n, lo + per);
+  uint8_t f[kSegMax];
+  uint32_t kk[kSegMax];
+#pragma unroll
+  for (int u = 0; u < kSegMax; ++u) {
+    const bool in = lo + u < hi;
+    f[u] = in ? fl[lo + u] : (uint8_t)0;
+    kk[u] = in ? keys[lo + u] : 0u;
+  }
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  for (int i = tid; i < n; i += nt)
-    if (fl[i] & kCand) {
-      kmin = keys[i] < kmin ? keys[i] : kmin;
-      kmax = keys[i] > kmax ? keys[i] : kmax;
+  int cnt = 0, first = INT_MAX, last = -1;
+#pragma unroll
+  for (int u = 0; u < kSegMax; ++u)
+    if (f[u] & kCand) {
+      kmin = kk[u] < kmin ? kk[u] : kmin;
+      kmax = kk[u] > kmax ? kk[u] : kmax;
+      ++cnt;
+      first = first == INT_MAX ? lo + u : first;
+      last = lo + u;
     }
   block_minmax(kmin, kmax, sa, sb);
-  const double mn = (double)key_score(kmin), mx = (double)key_score(kmax);
-  const double range = mx - mn;
+  const double mn = (double)key_score(kmin);
+  const double range = (double)key_score(kmax) - mn;
 
-  // first and last candidate of every thread's segment; the candidates just
-  // outside a segment come from a suffix-min and a prefix-max over the threads
-  int lo, hi;
-  my_segment(n, lo, hi);
-  int first = INT_MAX, last = -1, cnt = 0;
-  for (int i = lo; i < hi; ++i)
-    if (fl[i] & kCand) {
-      first = first == INT_MAX ? i : first;
-      last = i;
-      ++cnt;
-    }
-  sa[tid] = first;
-  sb[tid] = last;
-  __syncthreads();
-  for (int o = 1; o < nt; o <<= 1) {
-    const int va = tid + o < nt ? sa[tid + o] : INT_MAX;
-    const int vb = tid >= o ? sb[tid - o] : -1;
-    __syncthreads();
-    if (va < sa[tid]) sa[tid] = va;
-    if (vb > sb[tid]) sb[tid] = vb;
-    __syncthreads();
-  }
-  const int next_first = tid + 1 < nt ? sa[tid + 1] : INT_MAX;
-  const int prev_last = tid > 0 ? sb[tid - 1] : -1;
-  __syncthreads();
+  // the last candidate before this share
+  sa[tid] = last;
+  sb[tid] = first;
+  block_scan_max_min(sa, sb);
+  const int prev_last = tid > 0 ? sa[tid - 1] : -1;
 
-  // kBrk on every candidate that does not join its successor (and on the last)
+  // joins (kBrk marks a candidate that starts a run) and the last run start
+  int slot0, n_seq;
+  slot0 = block_excl_scan(cnt, sh, &n_seq);
+  int run_last = -1;
   {
-    int prev = -1;
-    for (int i = lo; i < hi; ++i) {
-      if (!(fl[i] & kCand)) continue;
-      if (prev >= 0 && span_breaks(keys[prev], keys[i], mn, range, tau_smooth)) fl[prev] |= kBrk;
-      prev = i;
-    }
-    if (prev >= 0 && (next_first >= n || span_breaks(keys[prev], keys[next_first], mn, range, tau_smooth)))
-      fl[prev] |= kBrk;
-  }
-  __syncthreads();
-
-  // slots; a run of joined candidates starts after a kBrk (or at the first
-  // candidate) and is cut into spans of span_max slots from its start
-  int tot;
-  const int slot0 = block_excl_scan(cnt, sh, &tot);
-  int local_start = -1;
-  {
-    int prev = prev_last, slot = slot0;
-    for (int i = lo; i < hi; ++i) {
-      if (!(fl[i] & kCand)) continue;
-      if (prev < 0 || (fl[prev] & kBrk)) local_start = slot;
-      prev = i;
+    bool has_prev = prev_last >= 0;
+    double tp = has_prev ? norm_score(keys[prev_last], mn, range) : 0.0;
+    int slot = slot0;
+#pragma unroll
+    for (int u = 0; u < kSegMax; ++u) {
+      if (!(f[u] & kCand)) continue;
+      const double tu = norm_score(kk[u], mn, range);
+      if (!(has_prev && joins(tp, tu, tau_smooth))) {
+        f[u] |= kBrk;
+        run_last = slot;
+      }
+      has_prev = true;
+      tp = tu;
       ++slot;
     }
   }
-  sa[tid] = local_start;
-  __syncthreads();
-  for (int o = 1; o < nt; o <<= 1) {
-    const int v = tid >= o ? sa[tid - o] : -1;
-    __syncthreads();
-    if (v > sa[tid]) sa[tid] = v;
-    __syncthreads();
-  }
+  __syncthreads();  // every read of the keys is done: the storage becomes counters
+  uint32_t *ctr = keys;
+#pragma unroll
+  for (int u = 0; u < kSegMax; ++u)
+    if (lo + u < hi) ctr[lo + u] = 0u;
+  sc[tid] = run_last;
+  sd[tid] = INT_MAX;
+  block_scan_max_min(sc, sd);
+
+  // span starts: every span_max slots from the run start
+  int start_last = -1;
   {
-    int run0 = tid > 0 ? sa[tid - 1] : -1;
-    int prev = prev_last, slot = slot0;
-    for (int i = lo; i < hi; ++i) {
-      if (!(fl[i] & kCand)) continue;
-      if (prev < 0 || (fl[prev] & kBrk)) run0 = slot;
-      if ((slot - run0) % span_max == 0) fl[i] |= kSpan0;
-      prev = i;
+    int run0 = tid > 0 ? sc[tid - 1] : -1, slot = slot0;
+#pragma unroll
+    for (int u = 0; u < kSegMax; ++u) {
+      if (!(f[u] & kCand)) continue;
+      if (f[u] & kBrk) run0 = slot;
+      if ((slot - run0) % span_max == 0) {
+        f[u] |= kSpan0;
+        start_last = lo + u;
+      }
       ++slot;
     }
   }
   __syncthreads();
+  sa[tid] = start_last;
+  sb[tid] = INT_MAX;
+  block_scan_max_min(sa, sb);
 
-  // each span start walks its span (at most span_max candidates) twice: coverage,
-  // then marks; every candidate belongs to exactly one span, so marks never collide
+  // per-span counters: kTop count (high half) and length (low half)
+  int s0e[kSegMax];
+  {
+    int cur = tid > 0 ? sa[tid - 1] : -1;
+#pragma unroll
+    for (int u = 0; u < kSegMax; ++u) {
+      s0e[u] = 0;
+      if (!(f[u] & kCand)) continue;
+      if (f[u] & kSpan0) cur = lo + u;
+      s0e[u] = cur;
+      atomicAdd(&ctr[cur], ((f[u] & kTop) ? 0x10000u : 0u) + 1u);
+    }
+  }
+  __syncthreads();
   int my_sel = 0;
-  for (int i = lo; i < hi; ++i) {
-    if (!(fl[i] & kSpan0)) continue;
-    int len = 0, top = 0;
-    for (int j = i;;) {
-      const uint8_t f = fl[j];
-      ++len;
-      top += (f & kTop) ? 1 : 0;
-      if ((f & kBrk) || len == span_max) break;
-      do { ++j; } while (j < n && !(fl[j] & kCand));
-      if (j >= n) break;
-    }
-    const bool covered = (double)top / (double)len >= tau_cover;
-    my_sel += covered ? len : top;
-    for (int j = i, c = 0; c < len; ++c) {
-      if (covered || (fl[j] & kTop)) fl[j] |= kSel;
-      do { ++j; } while (j < n && !(fl[j] & kCand));
+#pragma unroll
+  for (int u = 0; u < kSegMax; ++u) {
+    if (!(f[u] & kCand)) continue;
+    const uint32_t v = ctr[s0e[u]];
+    const bool covered = (double)(v >> 16) / (double)(v & 0xffffu) >= tau_cover;
+    if (covered || (f[u] & kTop)) {
+      f[u] |= kSel;
+      ++my_sel;
     }
   }
+#pragma unroll
+  for (int u = 0; u < kSegMax; ++u)
+    if (lo + u < hi) fl[lo + u] = f[u];
   const int n_sel = block_sum(my_sel, sh);
   return n_sel;
 }
@@ -699,10 +724,10 @@ __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Worksp
   __shared__ uint32_t keys_s[kLdsEntries];  // window grouping: seq_ent (u16) | seq_pre (u16)
   __shared__ uint8_t fl_s[kLdsEntries];
   __shared__ uint8_t sq_s[kLdsEntries];
-  __shared__ int sh_a[1024];
-  __shared__ int sh_b[1024];
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int rq0 = a.req_offsets[r], n = a.req_offsets[r + 1] - rq0;
+  // after the top-k marking the histogram storage serves as four scan arrays
+  int *scan0 = hist, *scan1 = hist + 1024, *scan2 = hist + 2048, *scan3 = hist + 3072;
 
   int my_ctx = 0, my_cand = 0;
   for (int i = tid; i < n; i += 4 * nt) {
@@ -738,17 +763,20 @@ __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Worksp
   uint8_t chosen = kTop;
   if (a.span_max > 0) {
     const int n_sel = lds_span_complete(keys_s, fl_s, n, a.span_max, a.tau_smooth, a.tau_cover,
-                                        sh_a, sh_b, sh);
+                                        scan0, scan1, scan2, scan3, sh);
     chosen = kSel;
     if (a.cap_ratio > 0.0) {
       const int m = k_from_ratio(a.cap_ratio, n_ctx, n_cand, a.k_ceil);
       if (n_sel > m) {
+        // the key storage held the span counters: reload the keys of the chosen rows
+        for (int i = tid; i < n; i += nt) keys_s[i] = (fl_s[i] & kSel) ? score_key(a.scores[rq0 + i]) : 0u;
+        __syncthreads();
         lds_mark_top(keys_s, fl_s, n, kSel, kCap, m, n_sel, hist, sh, digit_info);
         chosen = kCap;
       }
     }
   } else if (a.window > 0) {
-    lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, sh_a, sh);
+    lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, scan0, sh);
     chosen = kSel;
   }
   __syncthreads();
