@@ -269,8 +269,8 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   // 2. positional recovery of cached rows outside R (inside R the projection
   //    epilogue rotates them next to the deviation)
   if (sa.listed && T > 0)
-    SRP_HIP(launch_rerotate(d.dtype, T, d.n_kv_heads, d.head_dim, b.chunk_offsets, b.n_chunks,
-                            b.chunk_src_pos, b.positions, w.rowflag, rt, k_cache, s));
+    SRP_HIP(launch_rerotate(d.dtype, T, d.n_kv_heads, d.head_dim, w.row_delta, b.chunk_offsets,
+                            b.n_chunks, b.chunk_src_pos, b.positions, w.rowflag, rt, k_cache, s));
   // 3. K/V projection of R with the rotation / deviation epilogue
   GemmArgs g{};
   g.dtype = d.dtype;
@@ -416,7 +416,7 @@ int srp_rerotate_kv(const srp_dims *dims, const srp_batch *batch, void *k_cache,
   if (!k_cache) return fail(SRP_E_INVALID, "k_cache is NULL");
   RopeTable rt;
   CHECK(get_table(dims->head_dim, dims->rope_base, batch->max_position, &rt));
-  SRP_HIP(launch_rerotate(dims->dtype, batch->total_rows, dims->n_kv_heads, dims->head_dim,
+  SRP_HIP(launch_rerotate(dims->dtype, batch->total_rows, dims->n_kv_heads, dims->head_dim, nullptr,
                           batch->chunk_offsets, batch->n_chunks, batch->chunk_src_pos,
                           batch->positions, nullptr, rt, k_cache, (hipStream_t)stream));
   return SRP_OK;

@@ -4,51 +4,84 @@
 
 namespace srp {
 
-// K[j] <- R(pos_j - src_j) K[j] for cached rows. One thread per 4 rotation pairs of
-// one head of one row: consecutive threads cover consecutive 8-byte (bf16) or
-// 16-byte (fp32) pieces of the two halves of a head, so the row streams coalesced.
+// K[j] <- R(pos_j - src_j) K[j] for cached rows. One thread per 16-byte piece of
+// the first half of a head and the matching piece of the second half (8 rotation
+// pairs in bf16, 4 in fp32): consecutive threads cover consecutive pieces, so a
+// row streams coalesced. The rotation index comes from row_delta when the caller
+// has it (kFresh: no cache), else from the chunk layout.
+__device__ __forceinline__ void ld16(const uint16_t *p, float v[8]) {
+  const uint4 t = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {t.x, t.y, t.z, t.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = __uint_as_float(w[k] << 16);
+    v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void st16(uint16_t *p, const float v[8]) {
+  uint4 t;
+  t.x = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  t.y = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  t.z = (uint32_t)f2bf(v[4]) | ((uint32_t)f2bf(v[5]) << 16);
+  t.w = (uint32_t)f2bf(v[6]) | ((uint32_t)f2bf(v[7]) << 16);
+  *reinterpret_cast<uint4 *>(p) = t;
+}
+__device__ __forceinline__ void ld16(const float *p, float v[4]) { ld4(p, v); }
+__device__ __forceinline__ void st16(float *p, const float v[4]) { st4(p, v); }
+
 template <typename T>
 __global__ __launch_bounds__(256) void rerotate_kernel(int T_rows, int nkv, int d,
+                                                      const int32_t *row_delta,
                                                       const int32_t *chunk_offsets, int n_chunks,
                                                       const int32_t *chunk_src_pos,
                                                       const int32_t *positions, const uint8_t *skip,
                                                       RopeTable rt, T *k_cache) {
-  const int half = d >> 1, per_head = half >> 2, per_row = nkv * per_head;
-  const long n = (long)T_rows * per_row;
-  for (long it = blockIdx.x * (long)blockDim.x + threadIdx.x; it < n; it += (long)gridDim.x * blockDim.x) {
-    const int j = (int)(it / per_row);
-    const int rem = (int)(it - (long)j * per_row);
-    const int gh = rem / per_head, i0 = (rem - gh * per_head) * 4;
-    if (skip && skip[j]) continue;
-    const int c = upper_index(chunk_offsets, n_chunks + 1, j);
-    const int src0 = chunk_src_pos[c];
-    if (src0 < 0) continue;
-    const int delta = positions[j] - (src0 + j - chunk_offsets[c]);
-    if (delta == 0) continue;
+  constexpr int P = 16 / sizeof(T);  // rotation pairs per thread
+  const int half = d >> 1, per_head = half / P, per_row = nkv * per_head;
+  const int n = T_rows * per_row;
+  for (int it = blockIdx.x * blockDim.x + threadIdx.x; it < n; it += gridDim.x * blockDim.x) {
+    const int j = it / per_row;
+    const int rem = it - j * per_row;
+    const int gh = rem / per_head, i0 = (rem - gh * per_head) * P;
+    int delta;
+    if (row_delta) {
+      delta = row_delta[j];
+      if (delta == kFresh) continue;
+    } else {
+      const int c = upper_index(chunk_offsets, n_chunks + 1, j);
+      const int src0 = chunk_src_pos[c];
+      if (src0 < 0) continue;
+      delta = positions[j] - (src0 + j - chunk_offsets[c]);
+    }
+    if (delta == 0 || (skip && skip[j])) continue;
     T *p = k_cache + ((size_t)j * nkv + gh) * d;
-    float a[4], b[4];
-    ld4(p + i0, a);
-    ld4(p + half + i0, b);
-    rope4(a, b, rt, delta, i0);
-    st4(p + i0, a);
-    st4(p + half + i0, b);
+    float a[P], b[P];
+    ld16(p + i0, a);
+    ld16(p + half + i0, b);
+#pragma unroll
+    for (int q = 0; q < P; q += 4) rope4(a + q, b + q, rt, delta, i0 + q);
+    st16(p + i0, a);
+    st16(p + half + i0, b);
   }
 }
 
-hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *chunk_offsets,
-                           int n_chunks, const int32_t *chunk_src_pos, const int32_t *positions,
-                           const uint8_t *skip, const RopeTable &rt, void *k_cache, hipStream_t s) {
-  const long n = (long)T * nkv * (d / 8);
+hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *row_delta,
+                           const int32_t *chunk_offsets, int n_chunks, const int32_t *chunk_src_pos,
+                           const int32_t *positions, const uint8_t *skip, const RopeTable &rt,
+                           void *k_cache, hipStream_t s) {
+  const int P = dtype == SRP_BF16 ? 8 : 4;
+  const long n = (long)T * nkv * (d / 2 / P);
   if (n <= 0) return hipSuccess;
+  if (n > INT_MAX) return hipErrorInvalidValue;  // the kernel indexes pieces with int
   long grid = (n + 255) / 256;
   grid = grid < 8192 ? grid : 8192;
   if (dtype == SRP_BF16)
     hipLaunchKernelGGL(rerotate_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, s, T, nkv, d,
-                       chunk_offsets, n_chunks, chunk_src_pos, positions, skip, rt,
+                       row_delta, chunk_offsets, n_chunks, chunk_src_pos, positions, skip, rt,
                        (uint16_t *)k_cache);
   else
     hipLaunchKernelGGL(rerotate_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, T, nkv, d,
-                       chunk_offsets, n_chunks, chunk_src_pos, positions, skip, rt,
+                       row_delta, chunk_offsets, n_chunks, chunk_src_pos, positions, skip, rt,
                        (float *)k_cache);
   return hipGetLastError();
 }

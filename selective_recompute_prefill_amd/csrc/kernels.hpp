@@ -75,11 +75,12 @@ hipError_t launch_compact_scatter(const SelectArgs &a, const Workspace &w, int d
                                   int32_t *sel_idx, const int32_t *sel_offsets, void *k_cache,
                                   void *v_cache, hipStream_t s);
 // Re-rotation of cached rows; with `skip` (row flags) rows flagged as candidates
-// are left alone (the projection epilogue rotates those).
-hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *chunk_offsets,
-                           int n_chunks, const int32_t *chunk_src_pos,
-                           const int32_t *positions, const uint8_t *skip, const RopeTable &rt,
-                           void *k_cache, hipStream_t s);
+// are left alone (the projection epilogue rotates those). row_delta (optional):
+// the rotation index of each row (kFresh: none), else derived from the layout.
+hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *row_delta,
+                           const int32_t *chunk_offsets, int n_chunks,
+                           const int32_t *chunk_src_pos, const int32_t *positions,
+                           const uint8_t *skip, const RopeTable &rt, void *k_cache, hipStream_t s);
 
 struct AttnArgs {
   int dtype;
