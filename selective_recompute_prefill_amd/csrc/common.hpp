@@ -206,7 +206,7 @@ struct Workspace {
   size_t bytes;
 };
 // split-K partial tiles of the projection GEMMs' last round
-constexpr int kGemmParts = 128;
+constexpr int kGemmParts = 256;
 constexpr size_t kGemmPartFloats = 256 * 256;
 constexpr int kCtrTotalSel = 0;
 constexpr int kCtrTiles = 1;
