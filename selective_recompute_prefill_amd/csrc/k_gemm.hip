@@ -390,6 +390,40 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
 // Finishes the split tail tiles: work-group = (tail tile, 32-row block); adds
 // the tile's K-piece partials and runs the epilogue on them.
 constexpr int kFixRows = 32;
+
+// Cs[r][c] = sum over the split pieces of part[piece][r][c] for kFixRows rows of BN
+// columns, 4 columns per thread and step (256 threads).
+template <int NS, int BN, int LDC>
+__device__ __forceinline__ void fix_sum(const float *base, int split, float *Cs) {
+  constexpr int PER = kFixRows * BN / 4 / 256;
+  static_assert(PER % 2 == 0, "column groups in pairs");
+  for (int u0 = 0; u0 < PER; u0 += 2) {
+    float4 v[NS][2];
+#pragma unroll
+    for (int j = 0; j < NS; ++j) {
+      const int jj = j < split ? j : split - 1;
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int idx = threadIdx.x + (u0 + u) * 256;
+        const int r = idx / (BN / 4), c4 = (idx - r * (BN / 4)) * 4;
+        v[j][u] = *reinterpret_cast<const float4 *>(base + (size_t)jj * kGemmPartFloats + (size_t)r * BN + c4);
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 2; ++u) {
+      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int j = 0; j < NS; ++j) {
+        const float wj = j < split ? 1.f : 0.f;
+        acc.x += wj * v[j][u].x; acc.y += wj * v[j][u].y; acc.z += wj * v[j][u].z; acc.w += wj * v[j][u].w;
+      }
+      const int idx = threadIdx.x + (u0 + u) * 256;
+      const int r = idx / (BN / 4), c4 = (idx - r * (BN / 4)) * 4;
+      *reinterpret_cast<float4 *>(Cs + r * LDC + c4) = acc;
+    }
+  }
+}
+
 template <int MODE, typename C>
 __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   constexpr int LDC = C::BN + 4;
@@ -406,37 +440,16 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   const int m0 = mt * C::BM + rb * kFixRows, n0 = nt * C::BN;
   if (m0 >= M) return;
   load_row_meta<MODE, kFixRows>(meta, m0, M, g);
-  // sum of the pieces, 4 columns per thread and step. The loads of all
-  // kMaxSplit slots (unused ones clamped to a valid slot and weighted 0) and of
-  // two column groups are issued together, so the sum waits for one round trip.
-  constexpr int PER = kFixRows * C::BN / 4 / 256;
-  static_assert(PER % 2 == 0, "column groups in pairs");
-  for (int u0 = 0; u0 < PER; u0 += 2) {
-    float4 v[kMaxSplit][2];
-#pragma unroll
-    for (int j = 0; j < kMaxSplit; ++j) {
-      const int jj = j < sp.split ? j : sp.split - 1;
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const int idx = threadIdx.x + (u0 + u) * 256;
-        const int r = idx / (C::BN / 4), c4 = (idx - r * (C::BN / 4)) * 4;
-        v[j][u] = *reinterpret_cast<const float4 *>(
-            g.part + (size_t)(ti * sp.split + jj) * kGemmPartFloats + (size_t)(rb * kFixRows + r) * C::BN + c4);
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll
-      for (int j = 0; j < kMaxSplit; ++j) {
-        const float wj = j < sp.split ? 1.f : 0.f;
-        acc.x += wj * v[j][u].x; acc.y += wj * v[j][u].y; acc.z += wj * v[j][u].z; acc.w += wj * v[j][u].w;
-      }
-      const int idx = threadIdx.x + (u0 + u) * 256;
-      const int r = idx / (C::BN / 4), c4 = (idx - r * (C::BN / 4)) * 4;
-      *reinterpret_cast<float4 *>(Cs + r * LDC + c4) = acc;
-    }
-  }
+  // sum of the pieces into Cs: the loads of NS slots (NS = the split rounded up to
+  // 2, 4 or 8; slots past the split clamped to a valid one and weighted 0) and of two
+  // column groups are issued together, so the sum waits for one round trip
+  const float *base = g.part + (size_t)ti * sp.split * kGemmPartFloats + (size_t)rb * kFixRows * C::BN;
+  if (sp.split <= 2)
+    fix_sum<2, C::BN, LDC>(base, sp.split, Cs);
+  else if (sp.split <= 4)
+    fix_sum<4, C::BN, LDC>(base, sp.split, Cs);
+  else
+    fix_sum<kMaxSplit, C::BN, LDC>(base, sp.split, Cs);
   __syncthreads();
 #pragma unroll 1
   for (int cb = 0; cb < C::BN / kBN; ++cb)

@@ -348,9 +348,34 @@ __device__ __forceinline__ int radix_digit_pass(const uint32_t *keys, const uint
   return d;
 }
 
+// Block-wide min and max of uint32 values (every thread gets both); sa and sb hold
+// one int per wave.
+__device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, int *sa, int *sb) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) {
+    const uint32_t a = (uint32_t)__shfl_xor((int)mn, o), b = (uint32_t)__shfl_xor((int)mx, o);
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  if (lane == 0) {
+    sa[wid] = (int)mn;
+    sb[wid] = (int)mx;
+  }
+  __syncthreads();
+  for (int q = 0; q < nw; ++q) {
+    const uint32_t a = (uint32_t)sa[q], b = (uint32_t)sb[q];
+    mn = a < mn ? a : mn;
+    mx = b > mx ? b : mx;
+  }
+  __syncthreads();
+}
+
 // Marks out_bit on the k entries with the largest keys among the n_in entries
-// flagged in_bit: an MSB-first radix select (digits of 12, 12 and 8 bits) finds the
-// k-th largest key; larger keys are taken, and equal keys in entry order.
+// flagged in_bit: an MSB-first radix select finds the k-th largest key; larger keys
+// are taken, and equal keys in entry order. The bits above the highest one in which
+// the smallest and largest key differ are common to every key, so the digits (12,
+// 12, then the rest) start below them: keys that cluster in a few exponents still
+// spread over the histogram instead of piling onto a few contended bins.
 __device__ void lds_mark_top(const uint32_t *keys, uint8_t *fl, int n, uint8_t in_bit,
                              uint8_t out_bit, int k, int n_in, int *hist, int *sh,
                              int *digit_info) {
@@ -359,16 +384,28 @@ __device__ void lds_mark_top(const uint32_t *keys, uint8_t *fl, int n, uint8_t i
     for (int i = tid; i < n; i += nt)
       if (fl[i] & in_bit) fl[i] |= out_bit;
   } else if (k > 0) {
-    uint32_t prefix = 0, pmask = 0;
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+    for (int i = tid; i < n; i += nt)
+      if (fl[i] & in_bit) {
+        kmin = keys[i] < kmin ? keys[i] : kmin;
+        kmax = keys[i] > kmax ? keys[i] : kmax;
+      }
+    block_minmax(kmin, kmax, hist, hist + 32);
+    const uint32_t diff = kmin ^ kmax;
+    int rem = diff ? 32 - __clz(diff) : 0;  // low bits still undecided
+    uint32_t pmask = rem == 32 ? 0u : ~((1u << rem) - 1u);
+    uint32_t prefix = kmin & pmask;
     int need = k;
-    const int shifts[3] = {20, 8, 0}, widths[3] = {12, 12, 8};
-    for (int pass = 0; pass < 3; ++pass) {
+    while (rem > 0) {
+      const int width = rem < 12 ? rem : 12;
+      const int shift = rem - width;
       int above;
-      const int d = radix_digit_pass(keys, fl, n, in_bit, prefix, pmask, shifts[pass],
-                                     1 << widths[pass], need, hist, sh, digit_info, &above);
+      const int d = radix_digit_pass(keys, fl, n, in_bit, prefix, pmask, shift, 1 << width, need,
+                                     hist, sh, digit_info, &above);
       need -= above;
-      prefix |= (uint32_t)d << shifts[pass];
-      pmask |= ((1u << widths[pass]) - 1u) << shifts[pass];
+      prefix |= (uint32_t)d << shift;
+      pmask |= ((1u << width) - 1u) << shift;
+      rem = shift;
     }
     int my_eq = 0;
     for (int i = tid; i < n; i += nt) {
@@ -542,40 +579,37 @@ __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
 }
 
-// Block-wide min and max of uint32 values (every thread gets both).
-__device__ __forceinline__ void block_minmax(uint32_t &mn, uint32_t &mx, int *sa, int *sb) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  for (int o = 32; o > 0; o >>= 1) {
-    const uint32_t a = (uint32_t)__shfl_xor((int)mn, o), b = (uint32_t)__shfl_xor((int)mx, o);
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-  }
-  if (lane == 0) {
-    sa[wid] = (int)mn;
-    sb[wid] = (int)mx;
-  }
-  __syncthreads();
-  for (int q = 0; q < nw; ++q) {
-    const uint32_t a = (uint32_t)sa[q], b = (uint32_t)sb[q];
-    mn = a < mn ? a : mn;
-    mx = b > mx ? b : mx;
-  }
-  __syncthreads();
+// Inclusive max-scan over the wave with DPP lane shifts (INT_MIN fills lanes
+// without a source, the identity of max).
+__device__ __forceinline__ int wave_incl_max(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
 }
 
-// In place over blockDim ints each: up[t] <- max(up[0..t]), down[t] <- min(down[t..])
-// (Hillis-Steele; both arrays written by their owners before the call).
-__device__ void block_scan_max_min(int *up, int *down) {
-  const int tid = threadIdx.x, nt = blockDim.x;
+// Max over the values of the threads before this one (INT_MIN for thread 0).
+// `sh` needs 17 ints of LDS.
+__device__ __forceinline__ int block_excl_max(int v, int *sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int inc = wave_incl_max(v);
+  const int up = __shfl_up(inc, 1, 64);
+  if (lane == 63) sh[wid] = inc;
   __syncthreads();
-  for (int o = 1; o < nt; o <<= 1) {
-    const int vu = tid >= o ? up[tid - o] : INT_MIN;
-    const int vd = tid + o < nt ? down[tid + o] : INT_MAX;
-    __syncthreads();
-    if (vu > up[tid]) up[tid] = vu;
-    if (vd < down[tid]) down[tid] = vd;
-    __syncthreads();
+  if (wid == 0) {
+    // wave 0: exclusive max over the wave totals
+    const int t = lane < nw ? sh[lane] : INT_MIN;
+    const int ti = wave_incl_max(t);
+    if (lane < nw) sh[lane + 1] = ti;
+    if (lane == 0) sh[0] = INT_MIN;
   }
+  __syncthreads();
+  const int res = max(sh[wid], lane > 0 ? up : INT_MIN);
+  __syncthreads();
+  return res;
 }
 
 // Min-max normalised score, in double as written: (s - min) / (max - min).
@@ -600,9 +634,9 @@ constexpr int kSegMax = (kLdsEntries + 1023) / 1024;  // entries per thread at m
 // from their start; each candidate adds (its kTop, 1) to a counter at its span's
 // first entry (LDS atomics into ctr, which aliases the key storage), and a span
 // whose kTop share reaches tau_cover marks every candidate kSel (others mark their
-// kTop candidates). Returns the kSel count. sa..sd: blockDim ints of scratch each.
+// kTop candidates). Returns the kSel count. sa, sb: 16 ints of scratch each.
 __device__ int lds_span_complete(uint32_t *keys, uint8_t *fl, int n, int span_max, double tau_smooth,
-                                 double tau_cover, int *sa, int *sb, int *sc, int *sd, int *sh) {
+                                 double tau_cover, int *sa, int *sb, int *sh) {
   const int tid = threadIdx.x, nt = blockDim.x;
   const int per = (n + nt - 1) / nt;  // <= kSegMax
   const int lo = min(n, tid * per), hi = min(n, lo + per);
@@ -615,14 +649,13 @@ __device__ int lds_span_complete(uint32_t *keys, uint8_t *fl, int n, int span_ma
     kk[u] = in ? keys[lo + u] : 0u;
   }
   uint32_t kmin = 0xffffffffu, kmax = 0u;
-  int cnt = 0, first = INT_MAX, last = -1;
+  int cnt = 0, last = -1;
 #pragma unroll
   for (int u = 0; u < kSegMax; ++u)
     if (f[u] & kCand) {
       kmin = kk[u] < kmin ? kk[u] : kmin;
       kmax = kk[u] > kmax ? kk[u] : kmax;
       ++cnt;
-      first = first == INT_MAX ? lo + u : first;
       last = lo + u;
     }
   block_minmax(kmin, kmax, sa, sb);
@@ -630,10 +663,7 @@ __device__ int lds_span_complete(uint32_t *keys, uint8_t *fl, int n, int span_ma
   const double range = (double)key_score(kmax) - mn;
 
   // the last candidate before this share
-  sa[tid] = last;
-  sb[tid] = first;
-  block_scan_max_min(sa, sb);
-  const int prev_last = tid > 0 ? sa[tid - 1] : -1;
+  const int prev_last = max(block_excl_max(last, sh), -1);
 
   // joins (kBrk marks a candidate that starts a run) and the last run start
   int slot0, n_seq;
@@ -661,14 +691,12 @@ __device__ int lds_span_complete(uint32_t *keys, uint8_t *fl, int n, int span_ma
 #pragma unroll
   for (int u = 0; u < kSegMax; ++u)
     if (lo + u < hi) ctr[lo + u] = 0u;
-  sc[tid] = run_last;
-  sd[tid] = INT_MAX;
-  block_scan_max_min(sc, sd);
+  const int run_in = max(block_excl_max(run_last, sh), -1);
 
   // span starts: every span_max slots from the run start
   int start_last = -1;
   {
-    int run0 = tid > 0 ? sc[tid - 1] : -1, slot = slot0;
+    int run0 = run_in, slot = slot0;
 #pragma unroll
     for (int u = 0; u < kSegMax; ++u) {
       if (!(f[u] & kCand)) continue;
@@ -680,15 +708,12 @@ __device__ int lds_span_complete(uint32_t *keys, uint8_t *fl, int n, int span_ma
       ++slot;
     }
   }
-  __syncthreads();
-  sa[tid] = start_last;
-  sb[tid] = INT_MAX;
-  block_scan_max_min(sa, sb);
+  const int start_in = max(block_excl_max(start_last, sh), -1);
 
   // per-span counters: kTop count (high half) and length (low half)
   int s0e[kSegMax];
   {
-    int cur = tid > 0 ? sa[tid - 1] : -1;
+    int cur = start_in;
 #pragma unroll
     for (int u = 0; u < kSegMax; ++u) {
       s0e[u] = 0;
@@ -727,7 +752,7 @@ __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Worksp
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int rq0 = a.req_offsets[r], n = a.req_offsets[r + 1] - rq0;
   // after the top-k marking the histogram storage serves as four scan arrays
-  int *scan0 = hist, *scan1 = hist + 1024, *scan2 = hist + 2048, *scan3 = hist + 3072;
+  int *scan0 = hist, *scan1 = hist + 1024;
 
   int my_ctx = 0, my_cand = 0;
   for (int i = tid; i < n; i += 4 * nt) {
@@ -763,7 +788,7 @@ __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Worksp
   uint8_t chosen = kTop;
   if (a.span_max > 0) {
     const int n_sel = lds_span_complete(keys_s, fl_s, n, a.span_max, a.tau_smooth, a.tau_cover,
-                                        scan0, scan1, scan2, scan3, sh);
+                                        scan0, scan1, sh);
     chosen = kSel;
     if (a.cap_ratio > 0.0) {
       const int m = k_from_ratio(a.cap_ratio, n_ctx, n_cand, a.k_ceil);
