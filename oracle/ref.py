@@ -471,14 +471,17 @@ def fuse_stack(*, hidden, layers: Sequence[dict], req_offsets, chunk_offsets,
                chunk_src_pos, positions, n_heads, n_kv, head_dim, rope_base,
                ratios: Sequence[float], window: int = 0, tau: int = 0,
                dev_mode: str = "kv", rms_eps: float = 1e-6,
-               round_hidden=None) -> List[Dict[str, np.ndarray]]:
+               round_hidden=None, k_rule: str = "round", fresh_all: bool = False,
+               first_kw: Optional[dict] = None) -> List[Dict[str, np.ndarray]]:
     """Gradual filtering across stacked layers (CacheBlend walkthrough, "The
     chicken-and-egg problem": layer 1 scores every token, each later layer scores
     only the previous layer's selection, so the set only shrinks; the fusor is
     sequential, "The system"). layers[l] = dict(w_qkv, k_cache, v_cache) in float64.
     Between layers x[j] <- RMSNorm(x[j] + o[j]) on the selected rows; rows outside
     the selection are not read again. round_hidden, if given, is applied to the new
-    hidden rows (the storage rounding of a bf16 model's hidden state)."""
+    hidden rows (the storage rounding of a bf16 model's hidden state). k_rule and
+    fresh_all apply to every layer; first_kw holds further selection settings of
+    layer 1 only (e.g. mode "scores" with its scores and span settings)."""
     x = hidden.copy()
     outs = []
     cand = None
@@ -488,8 +491,10 @@ def fuse_stack(*, hidden, layers: Sequence[dict], req_offsets, chunk_offsets,
                        chunk_offsets=chunk_offsets, chunk_src_pos=chunk_src_pos,
                        positions=positions, n_heads=n_heads, n_kv=n_kv,
                        head_dim=head_dim, rope_base=rope_base, ratio=ratios[l],
-                       mode="topk", window=window if l == 0 else 0, tau=tau,
-                       dev_mode=dev_mode, cand=cand)
+                       **dict(dict(mode="topk", window=window if l == 0 else 0, tau=tau,
+                                   dev_mode=dev_mode, cand=cand, k_rule=k_rule,
+                                   fresh_all=fresh_all),
+                              **(first_kw or {} if l == 0 else {})))
         o["hidden_in"] = x.copy()
         sel = o["sel_idx"]
         y = residual_rmsnorm(x[sel], o["attn_out"].reshape(len(sel), -1), rms_eps)
@@ -500,6 +505,21 @@ def fuse_stack(*, hidden, layers: Sequence[dict], req_offsets, chunk_offsets,
         _, src = row_layout(req_offsets, chunk_offsets, chunk_src_pos, x.shape[0])
         cand = sel[src[sel] >= 0]
     return outs
+
+
+def controller_ratio(full_layer_ms: float, load_ms: float, r_floor: float = 0.15) -> float:
+    """Recompute ratio of the loading controller (CacheBlend walkthrough, "Making the
+    recompute free"): the recompute delay of ratio r is r times the profiled full
+    prefill of the layer, the load delay is the layer's KV bytes over the measured
+    load throughput; the ratio that makes the two equal, raised to the quality floor
+    r* (15% on the page) and capped at 1 (everything recomputed)."""
+    r_equal = load_ms / full_layer_ms
+    return float(min(max(r_equal, r_floor), 1.0))
+
+
+def load_ms(kv_bytes: float, gbps: float) -> float:
+    """Load delay in ms: bytes over throughput (GB/s = 1e9 bytes/s)."""
+    return kv_bytes / (gbps * 1e9) * 1e3
 
 
 def full_prefill_layer(*, hidden, w_qkv, req_offsets, positions, n_heads, n_kv,

@@ -243,3 +243,28 @@ def test_fresh_all_writes_every_recomputed_row():
     np.testing.assert_allclose(b["v_cache"], full["v"], rtol=0, atol=1e-10)
     sel = b["sel_idx"]
     np.testing.assert_allclose(b["attn_out"], full["attn_out"][sel], rtol=0, atol=1e-10)
+
+
+# --------------------------------------------------------------------------- #
+# loading controller
+# --------------------------------------------------------------------------- #
+
+def test_controller_ratio_golden(golden_dir):
+    g = json.load(open(os.path.join(golden_dir, "controller_ratio.json")))
+    for c in g["cases"]:
+        assert ref.controller_ratio(c["full_ms"], c["load_ms"], c["floor"]) == pytest.approx(c["ratio"], abs=1e-15), c["work"]
+    for c in g["load"]:
+        assert ref.load_ms(c["bytes"], c["gbps"]) == pytest.approx(c["load_ms"], rel=1e-15), c["work"]
+
+
+def test_controller_ratio_hides_recompute():
+    """At the controller's ratio above the floor the recompute delay equals the load
+    delay (the recompute hides behind the load); below it, the floor wins."""
+    for full in (0.3, 1.0, 7.5):
+        for load in (0.01, 0.2, 0.9, 5.0):
+            r = ref.controller_ratio(full, load, 0.15)
+            if 0.15 < r < 1.0:
+                assert r * full == pytest.approx(load, rel=1e-12)
+            else:
+                assert r in (0.15, 1.0)
+                assert (r == 0.15) == (load / full <= 0.15)
