@@ -494,7 +494,7 @@ def fuse_stack(*, hidden, layers: Sequence[dict], req_offsets, chunk_offsets,
                        **dict(dict(mode="topk", window=window if l == 0 else 0, tau=tau,
                                    dev_mode=dev_mode, cand=cand, k_rule=k_rule,
                                    fresh_all=fresh_all),
-                              **(first_kw or {} if l == 0 else {})))
+                              **((first_kw or {}) if l == 0 else {})))
         o["hidden_in"] = x.copy()
         sel = o["sel_idx"]
         y = residual_rmsnorm(x[sel], o["attn_out"].reshape(len(sel), -1), rms_eps)
