@@ -202,6 +202,58 @@ int srp_residual_rmsnorm(const srp_dims *dims, void *hidden, const void *attn_ou
                          int32_t n_req, int32_t sel_capacity, float eps,
                          srp_stream_t stream);
 
+/* ------------------------------------------------------------------------- */
+/* A stack of layers with its caches loaded from host memory while it runs.    */
+/* ------------------------------------------------------------------------- */
+
+/* One layer of srp_fuse_stack. */
+typedef struct {
+  const void *w_qkv;  /* device [(nh+2nkv)*d, hidden] weights (layout above)          */
+  void *k_cache;      /* device [T, nkv, d]: the layer's chunk caches, fused in place */
+  void *v_cache;      /* device [T, nkv, d]                                            */
+  const void *k_host; /* host [T, nkv, d] copied into k_cache before the layer runs;
+                         page-locked memory (hipHostMalloc) for an asynchronous copy;
+                         NULL: k_cache already holds the cache                        */
+  const void *v_host; /* same for V; given exactly when k_host is                      */
+  double ratio;       /* the layer's recompute ratio, in [0, 1]                        */
+} srp_layer;
+
+/* Bytes of scratch that srp_fuse_stack needs (srp_workspace_size plus the carried
+ * candidate list). */
+int srp_stack_workspace_size(const srp_dims *dims, const srp_batch *batch,
+                             const srp_select *first, size_t *bytes);
+
+/* n_layers stacked layers with gradual filtering (CacheBlend walkthrough, "The
+ * chicken-and-egg problem") and their cache loads overlapped with the recompute
+ * (CacheBlend walkthrough, "Making the recompute free": a layer can be recomputed as
+ * soon as its cache has landed in GPU memory; Cache-Craft summary, section 4: the
+ * caches of later layers are loaded ahead).
+ *   Layer 0 selects with `first` (its ratio field is ignored; layers[0].ratio
+ *   applies); layer l >= 1 ranks by KV deviation only the previous layer's selection
+ *   (fresh rows are always recomputed) at layers[l].ratio, with first's dev_mode,
+ *   k_rule and fresh_all. After every layer hidden[j] <- RMSNorm(hidden[j] +
+ *   attn[j]) on its selected rows (srp_residual_rmsnorm, eps rms_eps), so hidden
+ *   ends as the stack's output. sel_idx, sel_offsets and attn_out end as the last
+ *   layer's; every layer's fused cache stays in its k_cache / v_cache.
+ *   Loads: every host cache is copied on copy_stream in layer order, each layer's
+ *   pair followed by an event that `stream` waits for before that layer, so the copy
+ *   of layer l+1 runs while layer l computes. copy_stream == stream (e.g. both NULL)
+ *   puts the copies in line. Work is only enqueued: synchronising with `stream`
+ *   covers the copies too. The host caches must stay valid until then.
+ * Errors as for srp_fuse_layer; nothing is enqueued when an argument check fails. */
+int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_select *first,
+                   int32_t n_layers, const srp_layer *layers, void *hidden, float rms_eps,
+                   int32_t *sel_idx, int32_t *sel_offsets, void *attn_out, void *workspace,
+                   size_t workspace_bytes, srp_stream_t stream, srp_stream_t copy_stream);
+
+/* The loading controller's recompute ratio (CacheBlend walkthrough, "Making the
+ * recompute free"): recompute delay = ratio x full_layer_ms (the profiled full
+ * prefill of a layer), load delay = load_ms (a layer's KV bytes over the measured
+ * load throughput); *ratio = the ratio at which the two are equal, raised to r_floor
+ * (15% on the page) and capped at 1. Host arithmetic only. SRP_E_INVALID unless
+ * full_layer_ms > 0, load_ms >= 0 and 0 <= r_floor <= 1. */
+int srp_controller_ratio(double full_layer_ms, double load_ms, double r_floor, double *ratio);
+
 /* Debug check of a batch's device arrays against the rules of srp_batch (copies
  * them to the host and synchronises). SRP_OK or SRP_E_BATCH with a message. */
 int srp_validate_batch(const srp_batch *batch, srp_stream_t stream);

@@ -437,6 +437,128 @@ int srp_residual_rmsnorm(const srp_dims *dims, void *hidden, const void *attn_ou
   return SRP_OK;
 }
 
+// ------------------------------------------------------------------------- //
+// stack executor: cache loads on a copy stream, layers on the compute stream
+// ------------------------------------------------------------------------- //
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+int srp_stack_workspace_size(const srp_dims *dims, const srp_batch *batch, const srp_select *first,
+                             size_t *bytes) {
+  g_err.clear();
+  if (!bytes) return fail(SRP_E_INVALID, "bytes is NULL");
+  size_t layer = 0;
+  CHECK(srp_workspace_size(dims, batch, first, &layer));
+  *bytes = align256(layer) + align256((size_t)(batch->total_rows > 0 ? batch->total_rows : 1) * 4) +
+           align256((size_t)(batch->n_req + 1) * 4);
+  return SRP_OK;
+}
+
+int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_select *first,
+                   int32_t n_layers, const srp_layer *layers, void *hidden, float rms_eps,
+                   int32_t *sel_idx, int32_t *sel_offsets, void *attn_out, void *workspace,
+                   size_t workspace_bytes, srp_stream_t stream, srp_stream_t copy_stream) {
+  g_err.clear();
+  CHECK(check_dims(dims));
+  CHECK(check_batch(batch));
+  CHECK(check_select(first));
+  CHECK(check_select_batch(batch, first));
+  if (n_layers < 1 || !layers) return fail(SRP_E_INVALID, "n_layers must be >= 1 with a layer array");
+  if (dims->n_heads * dims->head_dim != dims->hidden)
+    return fail(SRP_E_INVALID, "the chain step needs n_heads * head_dim == hidden");
+  if (!(rms_eps >= 0.f)) return fail(SRP_E_INVALID, "rms_eps must be >= 0");
+  const srp_batch &b = *batch;
+  const int T = b.total_rows;
+  for (int l = 0; l < n_layers; ++l) {
+    const srp_layer &L = layers[l];
+    if (!(L.ratio >= 0.0 && L.ratio <= 1.0)) return fail(SRP_E_INVALID, "layer %d: ratio must lie in [0, 1]", l);
+    if ((L.k_host == nullptr) != (L.v_host == nullptr))
+      return fail(SRP_E_INVALID, "layer %d: k_host and v_host go together", l);
+    if (T > 0 && (!L.w_qkv || !L.k_cache || !L.v_cache))
+      return fail(SRP_E_INVALID, "layer %d: NULL device tensor", l);
+  }
+  if (T > 0 && (!hidden || !sel_idx || !attn_out)) return fail(SRP_E_INVALID, "tensor arguments must not be NULL");
+  if (!sel_offsets) return fail(SRP_E_INVALID, "sel_offsets must not be NULL");
+  size_t need = 0, layer_ws = 0;
+  CHECK(srp_stack_workspace_size(dims, batch, first, &need));
+  CHECK(srp_workspace_size(dims, batch, first, &layer_ws));
+  if (!workspace || workspace_bytes < need)
+    return fail(SRP_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  char *ws = (char *)workspace;
+  int32_t *cand_idx = (int32_t *)(ws + align256(layer_ws));
+  int32_t *cand_off = (int32_t *)((char *)cand_idx + align256((size_t)(T > 0 ? T : 1) * 4));
+  hipStream_t s = (hipStream_t)stream, cs = (hipStream_t)copy_stream;
+  const size_t cache_bytes = (size_t)T * dims->n_kv_heads * dims->head_dim * (dims->dtype == SRP_BF16 ? 2 : 4);
+
+  // one event per loaded layer, created for this call (concurrent calls never share
+  // one) and released once its wait is enqueued
+  std::vector<hipEvent_t> ev(n_layers, nullptr);
+  auto release = [&]() {
+    for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+  };
+  for (int l = 0; l < n_layers; ++l) {
+    if (!layers[l].k_host || cache_bytes == 0) continue;
+    hipError_t e = hipEventCreateWithFlags(&ev[l], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipMemcpyAsync(layers[l].k_cache, layers[l].k_host, cache_bytes, hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess) e = hipMemcpyAsync(layers[l].v_cache, layers[l].v_host, cache_bytes, hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess) e = hipEventRecord(ev[l], cs);
+    if (e != hipSuccess) {
+      release();
+      return fail(SRP_E_HIP, "loading layer %d: %s", l, hipGetErrorString(e));
+    }
+  }
+  int rc = SRP_OK;
+  for (int l = 0; l < n_layers && rc == SRP_OK; ++l) {
+    if (ev[l]) {
+      const hipError_t e = hipStreamWaitEvent(s, ev[l], 0);
+      if (e != hipSuccess) {
+        rc = fail(SRP_E_HIP, "waiting for layer %d: %s", l, hipGetErrorString(e));
+        break;
+      }
+    }
+    srp_select sl = *first;
+    sl.ratio = layers[l].ratio;
+    if (l > 0) {
+      sl = srp_select{};
+      sl.mode = SRP_SEL_TOPK;
+      sl.ratio = layers[l].ratio;
+      sl.dev_mode = first->dev_mode;
+      sl.k_rule = first->k_rule;
+      sl.fresh_all = first->fresh_all;
+      sl.cand = cand_idx;
+      sl.cand_offsets = cand_off;
+    }
+    rc = srp_fuse_layer(dims, batch, &sl, hidden, layers[l].w_qkv, layers[l].k_cache, layers[l].v_cache,
+                        sel_idx, sel_offsets, attn_out, nullptr, workspace, layer_ws, stream);
+    if (rc != SRP_OK) break;
+    if (l + 1 < n_layers) {
+      // the next layer's candidates: this layer's selection
+      hipError_t e = hipMemcpyAsync(cand_idx, sel_idx, (size_t)(T > 0 ? T : 1) * 4, hipMemcpyDeviceToDevice, s);
+      if (e == hipSuccess)
+        e = hipMemcpyAsync(cand_off, sel_offsets, (size_t)(b.n_req + 1) * 4, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) {
+        rc = fail(SRP_E_HIP, "carrying the selection of layer %d: %s", l, hipGetErrorString(e));
+        break;
+      }
+    }
+    rc = srp_residual_rmsnorm(dims, hidden, attn_out, sel_idx, sel_offsets, b.n_req, T, rms_eps, stream);
+  }
+  release();
+  return rc;
+}
+
+int srp_controller_ratio(double full_layer_ms, double load_ms, double r_floor, double *ratio) {
+  g_err.clear();
+  if (!ratio) return fail(SRP_E_INVALID, "ratio is NULL");
+  if (!(full_layer_ms > 0.0) || !(load_ms >= 0.0) || !(r_floor >= 0.0 && r_floor <= 1.0) ||
+      !std::isfinite(full_layer_ms) || !std::isfinite(load_ms))
+    return fail(SRP_E_INVALID, "need full_layer_ms > 0, load_ms >= 0 and 0 <= r_floor <= 1");
+  const double r_equal = load_ms / full_layer_ms;
+  const double r = r_equal > r_floor ? r_equal : r_floor;
+  *ratio = r < 1.0 ? r : 1.0;
+  return SRP_OK;
+}
+
 int srp_validate_batch(const srp_batch *batch, srp_stream_t stream) {
   g_err.clear();
   CHECK(check_batch(batch));

@@ -20,7 +20,8 @@ SRP_K_ROUND, SRP_K_CEIL = 0, 1
 SRP_DEV_KV, SRP_DEV_V = 0, 1
 
 EXPORTS = ("srp_workspace_size", "srp_fuse_layer", "srp_encode_kv", "srp_rerotate_kv",
-           "srp_residual_rmsnorm", "srp_validate_batch", "srp_profile_begin", "srp_profile_end",
+           "srp_residual_rmsnorm", "srp_stack_workspace_size", "srp_fuse_stack",
+           "srp_controller_ratio", "srp_validate_batch", "srp_profile_begin", "srp_profile_end",
            "srp_profile_stage_name", "srp_last_error", "srp_version")
 SRP_N_STAGES = 6
 
@@ -55,6 +56,12 @@ class Select(ctypes.Structure):
                 ("cap_ratio", ctypes.c_double), ("fresh_all", ctypes.c_int32)]
 
 
+class Layer(ctypes.Structure):
+    _fields_ = [("w_qkv", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
+                ("v_cache", ctypes.c_void_p), ("k_host", ctypes.c_void_p),
+                ("v_host", ctypes.c_void_p), ("ratio", ctypes.c_double)]
+
+
 _lib: Optional[ctypes.CDLL] = None
 
 
@@ -73,13 +80,19 @@ def lib() -> ctypes.CDLL:
         L.srp_encode_kv.argtypes = [P(Dims), i32, i32, vp, vp, vp, vp, vp, vp]
         L.srp_rerotate_kv.argtypes = [P(Dims), P(Batch), vp, vp]
         L.srp_residual_rmsnorm.argtypes = [P(Dims), vp, vp, vp, vp, i32, i32, ctypes.c_float, vp]
+        L.srp_stack_workspace_size.argtypes = [P(Dims), P(Batch), P(Select), P(sz)]
+        L.srp_fuse_stack.argtypes = [P(Dims), P(Batch), P(Select), i32, P(Layer), vp, ctypes.c_float,
+                                     vp, vp, vp, vp, sz, vp, vp]
+        L.srp_controller_ratio.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double,
+                                           P(ctypes.c_double)]
         L.srp_validate_batch.argtypes = [P(Batch), vp]
         L.srp_profile_begin.argtypes = [i32]
         L.srp_profile_end.argtypes = [P(ctypes.c_float), i32, P(i32)]
         L.srp_profile_stage_name.argtypes = [i32]
         L.srp_profile_stage_name.restype = ctypes.c_char_p
         for f in ("srp_workspace_size", "srp_fuse_layer", "srp_encode_kv", "srp_rerotate_kv",
-                  "srp_residual_rmsnorm", "srp_validate_batch", "srp_profile_begin",
+                  "srp_residual_rmsnorm", "srp_stack_workspace_size", "srp_fuse_stack",
+                  "srp_controller_ratio", "srp_validate_batch", "srp_profile_begin",
                   "srp_profile_end"):
             getattr(L, f).restype = ctypes.c_int
         L.srp_last_error.restype = ctypes.c_char_p
@@ -167,6 +180,39 @@ def srp_residual_rmsnorm(dims: Dims, hidden, attn_out, sel_idx, sel_offsets, n_r
     return _check(lib().srp_residual_rmsnorm(ctypes.byref(dims), _ptr(hidden), _ptr(attn_out),
                                              _ptr(sel_idx), _ptr(sel_offsets), int(n_req),
                                              int(sel_capacity), float(eps), _stream(stream)))
+
+
+def make_layer(w_qkv, k_cache, v_cache, ratio: float, k_host=None, v_host=None) -> Layer:
+    """Layer descriptor for srp_fuse_stack; k_host / v_host are host tensors in
+    page-locked memory (torch pin_memory=True) or None when the device caches are
+    already filled."""
+    return Layer(_ptr(w_qkv), _ptr(k_cache), _ptr(v_cache), _ptr(k_host), _ptr(v_host), float(ratio))
+
+
+def srp_stack_workspace_size(dims: Dims, batch: Batch, first: Select) -> int:
+    n = ctypes.c_size_t(0)
+    _check(lib().srp_stack_workspace_size(ctypes.byref(dims), ctypes.byref(batch), ctypes.byref(first),
+                                          ctypes.byref(n)))
+    return n.value
+
+
+def srp_fuse_stack(dims: Dims, batch: Batch, first: Select, layers, hidden, rms_eps: float,
+                   sel_idx, sel_offsets, attn_out, workspace, workspace_bytes: int, stream=None,
+                   copy_stream=None) -> int:
+    """layers: a sequence of Layer. copy_stream None = the compute stream (in line)."""
+    arr = (Layer * len(layers))(*layers)
+    st = _stream(stream)
+    cs = st if copy_stream is None else _stream(copy_stream)
+    return _check(lib().srp_fuse_stack(ctypes.byref(dims), ctypes.byref(batch), ctypes.byref(first),
+                                       len(layers), arr, _ptr(hidden), float(rms_eps), _ptr(sel_idx),
+                                       _ptr(sel_offsets), _ptr(attn_out), _ptr(workspace),
+                                       workspace_bytes, st, cs))
+
+
+def srp_controller_ratio(full_layer_ms: float, load_ms: float, r_floor: float = 0.15) -> float:
+    r = ctypes.c_double(0.0)
+    _check(lib().srp_controller_ratio(float(full_layer_ms), float(load_ms), float(r_floor), ctypes.byref(r)))
+    return r.value
 
 
 def srp_validate_batch(batch: Batch, stream=None) -> int:

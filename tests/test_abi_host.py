@@ -134,6 +134,50 @@ def test_workspace_monotone():
     assert growth(S.SRP_F32) > growth(S.SRP_BF16)
 
 
+def test_controller_ratio_matches_oracle(golden_dir):
+    import json
+    import os as _os
+    g = json.load(open(_os.path.join(golden_dir, "controller_ratio.json")))
+    for c in g["cases"]:
+        assert S.srp_controller_ratio(c["full_ms"], c["load_ms"], c["floor"]) == pytest.approx(c["ratio"], abs=1e-15)
+    for bad in [(0.0, 1.0, 0.15), (1.0, -1.0, 0.15), (1.0, 1.0, 1.5), (float("nan"), 1.0, 0.1)]:
+        with pytest.raises(S.SrpError):
+            S.srp_controller_ratio(*bad)
+
+
+def test_stack_argument_checks():
+    d, b, s = _dims(hidden=1024), _batch(), S.make_select(0.2)  # nh * d == hidden
+    n = S.srp_stack_workspace_size(d, b, s)
+    assert n > S.srp_workspace_size(d, b, s)
+    lay = S.make_layer(8, 8, 8, 0.2)
+    cases = [
+        dict(layers=[]),                                              # no layers
+        dict(layers=[S.make_layer(8, 8, 8, 1.5)]),                    # ratio
+        dict(layers=[S.make_layer(8, 8, 8, 0.2, k_host=8)]),          # k_host without v_host
+        dict(layers=[S.make_layer(None, 8, 8, 0.2)]),                 # no weights
+        dict(layers=[lay], hidden=None),
+    ]
+    for c in cases:
+        layers = c.get("layers")
+        args = dict(hidden=8, ws=8, wsb=n)
+        args.update({k: v for k, v in c.items() if k != "layers"})
+        with pytest.raises(S.SrpError) as e:
+            if not layers:
+                S.lib().srp_fuse_stack  # the binding needs a non-empty array; call the C entry
+                rc = S.lib().srp_fuse_stack(ctypes.byref(d), ctypes.byref(b), ctypes.byref(s), 0, None,
+                                            8, 1e-6, 8, 8, 8, 8, n, None, None)
+                S._check(rc)
+            else:
+                S.srp_fuse_stack(d, b, s, layers, args["hidden"], 1e-6, 8, 8, 8, args["ws"], args["wsb"], 0, 0)
+        assert e.value.code == S.SRP_E_INVALID
+    with pytest.raises(S.SrpError) as e:
+        S.srp_fuse_stack(d, b, s, [lay], 8, 1e-6, 8, 8, 8, 8, n - 1, 0, 0)
+    assert e.value.code == S.SRP_E_WORKSPACE
+    with pytest.raises(S.SrpError) as e:  # the chain step needs nh * d == hidden
+        S.srp_fuse_stack(_dims(hidden=768), b, s, [lay], 8, 1e-6, 8, 8, 8, 8, n, 0, 0)
+    assert e.value.code == S.SRP_E_INVALID
+
+
 def test_struct_layouts_match_header():
     # offsets the C compiler gives these structs on x86-64 (int32 then aligned double)
     assert ctypes.sizeof(S.Dims) == 32 and S.Dims.rope_base.offset == 16
@@ -141,3 +185,4 @@ def test_struct_layouts_match_header():
     assert S.Select.ratio.offset == 8 and S.Select.cand.offset == 32
     assert S.Select.scores.offset == 56 and S.Select.fresh_all.offset == 88
     assert ctypes.sizeof(S.Select) == 96
+    assert S.Layer.ratio.offset == 40 and ctypes.sizeof(S.Layer) == 48
