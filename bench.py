@@ -44,6 +44,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4])
     p.add_argument("--ratio", type=float, default=None, help="override the workload's ratio")
+    p.add_argument("--pipeline", action="store_true",
+                   help="multi-layer workloads: also time the stack with its chunk caches loaded "
+                        "from page-locked host memory, in line and on a copy stream (srp_fuse_stack)")
     p.add_argument("--select", choices=["deviation", "scores"], default="deviation",
                    help="rank rows by KV deviation (default) or by external per-row scores with "
                         "span completion (single-layer workloads)")
@@ -362,6 +365,8 @@ def main():
                       k_rule=S.SRP_K_CEIL)
     # pristine cache copies, one per step and layer
     pristine = [[(c[0].clone(), c[1].clone()) for c in caches] for _ in range(n_copies)]
+    # page-locked host copies of the chunk caches for the load pipelining runs
+    host_caches = [(c[0].cpu().pin_memory(), c[1].cpu().pin_memory()) for c in caches] if args.pipeline else None
     hiddens = [hidden0.clone() for _ in range(n_copies)] if nl > 1 else [hidden0]
     del caches
     torch.cuda.synchronize()
@@ -442,6 +447,13 @@ def main():
         roof["traffic"] = recorded_traffic(roof["kernel"])
 
     value = n_ctx / (ms_per_layer * 1e-3)
+    pipe = None
+    if args.pipeline:
+        if nl < 2:
+            print("--pipeline needs a multi-layer workload (--workload 3)", file=sys.stderr)
+            sys.exit(2)
+        pipe = bench_pipeline(args, spec, lay, call, wqs, pristine, host_caches, hidden0, sel_kw, ratios,
+                              T, n_ctx)
     out = {
         "metric": "context tokens fused/s per layer at 20% recompute; ms/layer at 16K; % roofline",
         "value": round(value, 1),
@@ -466,6 +478,8 @@ def main():
         "roofline": roof,
         "stages": stages,
     }
+    if pipe is not None:
+        out["load_pipelining"] = pipe
     if not args.no_cpu_baseline:
         print("[bench] timing the oracle on the host", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(spec, args.cpu_sample_chunks,
@@ -473,6 +487,108 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+
+
+def bench_pipeline(args, spec, lay, call, wqs, pristine, host, hidden0, sel_kw, ratios, T, n_ctx):
+    """The stack through srp_fuse_stack three ways: caches already on the device, caches
+    copied from page-locked host memory in line on the compute stream, and copied on a
+    separate copy stream so that later layers' loads overlap earlier layers' recompute.
+    Also the measured host-to-device throughput, the profiled full-prefill time of a
+    layer and the loading controller's ratio from them (CacheBlend walkthrough, "Making
+    the recompute free"). The host-load times are PCIe-inclusive."""
+    import torch
+    from selective_recompute_prefill_amd import srp as S
+    nl = len(wqs)
+    dev = "cuda"
+    first = call.select(ratios[0], **sel_kw)
+    ws_n = S.srp_stack_workspace_size(call.dims, call.batch, first)
+    ws = torch.empty(ws_n, dtype=torch.uint8, device=dev)
+    # the timed layer calls above rewrote the device copies in place: restore them
+    for cp in pristine:
+        for l in range(nl):
+            cp[l][0].copy_(host[l][0])
+            cp[l][1].copy_(host[l][1])
+    torch.cuda.synchronize()
+    dev_kv = [(torch.empty_like(pristine[0][l][0]), torch.empty_like(pristine[0][l][1])) for l in range(nl)]
+    cache_bytes = sum(h[0].numel() * h[0].element_size() * 2 for h in host)
+    side = torch.cuda.Stream()
+    cur = torch.cuda.current_stream()
+    n_copies = len(pristine)
+
+    def run(mode, i):
+        h = hidden0.clone()
+        if mode == "resident":
+            layers = [S.make_layer(wqs[l], pristine[i % n_copies][l][0], pristine[i % n_copies][l][1], ratios[l])
+                      for l in range(nl)]
+        else:
+            layers = [S.make_layer(wqs[l], dev_kv[l][0], dev_kv[l][1], ratios[l], k_host=host[l][0],
+                                   v_host=host[l][1]) for l in range(nl)]
+        return h, layers
+
+    def timed(mode):
+        cs = side if mode == "pipelined" else None
+        reps = args.steps
+        prep = [run(mode, i) for i in range(args.warmup + reps)]
+        for i in range(args.warmup):
+            h, layers = prep[i]
+            S.srp_fuse_stack(call.dims, call.batch, first, layers, h, 1e-6, call.sel_idx, call.sel_offsets,
+                             call.attn_out, ws, ws_n, None, cs)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(cur)
+        for i in range(reps):
+            h, layers = prep[args.warmup + i]
+            S.srp_fuse_stack(call.dims, call.batch, first, layers, h, 1e-6, call.sel_idx, call.sel_offsets,
+                             call.attn_out, ws, ws_n, None, cs)
+        e1.record(cur)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    print("[bench] pipelining: stack with resident / in-line / side-stream cache loads", file=sys.stderr, flush=True)
+    ms = {m: timed(m) for m in ("resident", "in_line", "pipelined")}
+    # host-to-device throughput of page-locked memory (one layer's K and V, repeated)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record(cur)
+    for _ in range(reps):
+        for l in range(nl):
+            dev_kv[l][0].copy_(host[l][0], non_blocking=True)
+            dev_kv[l][1].copy_(host[l][1], non_blocking=True)
+    e1.record(cur)
+    torch.cuda.synchronize()
+    h2d_gbps = cache_bytes * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    layer_bytes = cache_bytes / nl
+    load_ms = layer_bytes / (h2d_gbps * 1e9) * 1e3
+    # profiled full prefill of one layer: the first layer at ratio 1
+    kc, vc = torch.empty_like(dev_kv[0][0]), torch.empty_like(dev_kv[0][1])
+    full = []
+    for i in range(4):
+        h = hidden0.clone()
+        kc.copy_(host[0][0])
+        vc.copy_(host[0][1])
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(cur)
+        call.fuse(call.select(1.0), h, wqs[0], kc, vc, dev_out=False)
+        b.record(cur)
+        torch.cuda.synchronize()
+        if i:
+            full.append(a.elapsed_time(b))
+    full_ms = sum(full) / len(full)
+    ratio = S.srp_controller_ratio(full_ms, load_ms, 0.15)
+    load_total = ms["in_line"] - ms["resident"]
+    return {
+        "ms_resident": round(ms["resident"], 4),
+        "ms_in_line_loads": round(ms["in_line"], 4),
+        "ms_pipelined_loads": round(ms["pipelined"], 4),
+        "hidden_load_fraction": round((ms["in_line"] - ms["pipelined"]) / load_total, 4) if load_total > 0 else None,
+        "context_tokens_per_s_per_layer_pipelined_pcie": round(n_ctx / (ms["pipelined"] / nl * 1e-3), 1),
+        "h2d_gbps": round(h2d_gbps, 2),
+        "kv_bytes_per_layer": int(layer_bytes),
+        "load_ms_per_layer": round(load_ms, 4),
+        "full_prefill_ms_per_layer": round(full_ms, 4),
+        "controller_ratio": round(ratio, 4),
+        "ratios_used": list(ratios),
+    }
 
 
 def _to_f64(a, dtype):

@@ -237,8 +237,9 @@ int srp_stack_workspace_size(const srp_dims *dims, const srp_batch *batch,
  *   layer's; every layer's fused cache stays in its k_cache / v_cache.
  *   Loads: every host cache is copied on copy_stream in layer order, each layer's
  *   pair followed by an event that `stream` waits for before that layer, so the copy
- *   of layer l+1 runs while layer l computes. copy_stream == stream (e.g. both NULL)
- *   puts the copies in line. Work is only enqueued: synchronising with `stream`
+ *   of layer l+1 runs while layer l computes. The copies start after the work
+ *   enqueued on `stream` before the call (which may still use the destinations).
+ *   copy_stream == stream (e.g. both NULL) puts the copies in line. Work is only enqueued: synchronising with `stream`
  *   covers the copies too. The host caches must stay valid until then.
  * Errors as for srp_fuse_layer; nothing is enqueued when an argument check fails. */
 int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_select *first,

@@ -490,12 +490,24 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
   const size_t cache_bytes = (size_t)T * dims->n_kv_heads * dims->head_dim * (dims->dtype == SRP_BF16 ? 2 : 4);
 
   // one event per loaded layer, created for this call (concurrent calls never share
-  // one) and released once its wait is enqueued
-  std::vector<hipEvent_t> ev(n_layers, nullptr);
+  // one) and released once its wait is enqueued; ev.back() orders the copies after
+  // the work already on the compute stream, which may still use the destinations
+  std::vector<hipEvent_t> ev(n_layers + 1, nullptr);
   auto release = [&]() {
     for (hipEvent_t e : ev)
       if (e) (void)hipEventDestroy(e);
   };
+  bool loads = false;
+  for (int l = 0; l < n_layers; ++l) loads |= layers[l].k_host != nullptr;
+  if (loads && cache_bytes > 0 && cs != s) {
+    hipError_t e = hipEventCreateWithFlags(&ev[n_layers], hipEventDisableTiming);
+    if (e == hipSuccess) e = hipEventRecord(ev[n_layers], s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[n_layers], 0);
+    if (e != hipSuccess) {
+      release();
+      return fail(SRP_E_HIP, "ordering the loads: %s", hipGetErrorString(e));
+    }
+  }
   for (int l = 0; l < n_layers; ++l) {
     if (!layers[l].k_host || cache_bytes == 0) continue;
     hipError_t e = hipEventCreateWithFlags(&ev[l], hipEventDisableTiming);
