@@ -83,7 +83,17 @@ typedef struct {
  * is a cached chunk whose first row was encoded at position chunk_src_pos[c] (its
  * rows at consecutive positions), or a fresh segment (chunk_src_pos[c] = -1: the
  * query tail or a chunk whose cache is missing), whose rows are always recomputed
- * and whose input cache rows are ignored. */
+ * and whose input cache rows are ignored.
+ *
+ * Cache layout. block_rows = 0: row j of the batch is row j of k_cache / v_cache.
+ * block_rows > 0 (paged; Cache-Craft summary, section 4: each chunk maps to
+ * 16-token memory blocks through address pointers, padded at its end): k_cache /
+ * v_cache point at a pool of blocks of block_rows rows, and row i of segment c
+ * lives at pool row block_table[seg_block[c] + i / block_rows] * block_rows +
+ * i % block_rows. Fresh segments need blocks too (their fresh K/V are written
+ * there). Distinct rows must map to distinct pool rows (srp_validate_batch checks
+ * this). Only srp_fuse_layer, srp_rerotate_kv and srp_fuse_stack without host
+ * loads read this layout; srp_encode_kv writes rows contiguously. */
 typedef struct {
   int32_t n_req;        /* host: number of requests (>= 1)                         */
   int32_t n_chunks;     /* host: number of segments (>= 1)                         */
@@ -97,6 +107,12 @@ typedef struct {
   const int32_t *chunk_src_pos; /* device [n_chunks], >= 0 cached, -1 fresh       */
   const int32_t *positions;     /* device [T], global positions, strictly
                                    increasing inside each request                 */
+  int32_t block_rows;           /* host: 0 = contiguous cache rows; else the rows
+                                   per block of a paged cache pool (16 on the
+                                   pages), 1..4096                               */
+  const int32_t *seg_block;     /* device [n_chunks], paged only: index into
+                                   block_table of each segment's first block      */
+  const int32_t *block_table;   /* device, paged only: pool block ids             */
 } srp_batch;
 
 /* Token selection of one layer. k = round(ratio * N_ctx) per request (halves up;

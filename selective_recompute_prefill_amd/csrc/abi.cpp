@@ -1,5 +1,6 @@
 // C ABI of libsrp (include/srp.h): argument checks, rotary tables, workspace
 // carve-up and the launch sequence of one fused layer on the caller's stream.
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -133,6 +134,9 @@ int check_batch(const srp_batch *b) {
   if (b->total_rows > 0 && b->max_req_rows < 1) return fail(SRP_E_INVALID, "max_req_rows must be >= 1");
   if (!b->req_offsets || !b->chunk_offsets || !b->chunk_src_pos || (b->total_rows > 0 && !b->positions))
     return fail(SRP_E_INVALID, "batch device arrays must not be NULL");
+  if (b->block_rows < 0 || b->block_rows > 4096) return fail(SRP_E_INVALID, "block_rows must lie in [0, 4096]");
+  if (b->block_rows > 0 && (!b->seg_block || !b->block_table))
+    return fail(SRP_E_INVALID, "a paged cache needs seg_block and block_table");
   return SRP_OK;
 }
 
@@ -251,6 +255,9 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   sa.tau_cover = sel->tau_cover;
   sa.cap_ratio = sel->cap_ratio;
   sa.fresh_all = sel->fresh_all;
+  sa.block_rows = b.block_rows;
+  sa.seg_block = b.seg_block;
+  sa.block_table = b.block_table;
   // with external scores the rows are chosen first and then handled as a given list
   const bool by_scores = sel->mode == SRP_SEL_SCORES;
   sa.listed = sel->cand != nullptr || by_scores;
@@ -269,7 +276,8 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   // 2. positional recovery of cached rows outside R (inside R the projection
   //    epilogue rotates them next to the deviation)
   if (sa.listed && T > 0)
-    SRP_HIP(launch_rerotate(d.dtype, T, d.n_kv_heads, d.head_dim, w.row_delta, b.chunk_offsets,
+    SRP_HIP(launch_rerotate(d.dtype, T, d.n_kv_heads, d.head_dim, w.row_delta, w.row_slot,
+                            PagedMap{b.block_rows, b.seg_block, b.block_table}, b.chunk_offsets,
                             b.n_chunks, b.chunk_src_pos, b.positions, w.rowflag, rt, k_cache, s));
   // 3. K/V projection of R with the rotation / deviation epilogue
   GemmArgs g{};
@@ -293,6 +301,7 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   g.v_cache = v_cache;
   g.fresh = w.fresh_kv;
   g.dev_part = w.dev_part;
+  g.row_slot = w.row_slot;
   g.part = w.gemm_part;
   g.part_cap = w.gemm_part ? kGemmParts : 0;
   marks.mark(1);
@@ -304,8 +313,16 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   marks.mark(3);
   // 5. sel_idx and the scatter of fresh K/V into the cache
   SRP_HIP(launch_compact_scatter(sd, w, d.dtype, kvd, sel_idx, sel_offsets, k_cache, v_cache, s));
+  // a paged cache is gathered in row order for the attention's key and value tiles
+  const void *k_att = k_cache, *v_att = v_cache;
+  if (w.row_slot && T > 0) {
+    SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, k_cache, w.k_lin, s));
+    SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, v_cache, w.v_lin, s));
+    k_att = w.k_lin;
+    v_att = w.v_lin;
+  }
   if (d.dtype == SRP_BF16 && T > 0)
-    SRP_HIP(launch_v_transpose(T, d.n_kv_heads, d.head_dim, v_cache, w.vt, vt_stride(T), s));
+    SRP_HIP(launch_v_transpose(T, d.n_kv_heads, d.head_dim, v_att, w.vt, vt_stride(T), s));
   marks.mark(4);
   // 6. Q projection of the selected rows
   GemmArgs gq = g;
@@ -331,8 +348,8 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   aa.tiles = w.tiles;
   aa.n_tiles = w.ctr + kCtrTiles;
   aa.max_tiles = max_attn_tiles(T, b.n_req);
-  aa.k_cache = k_cache;
-  aa.v_cache = v_cache;
+  aa.k_cache = k_att;
+  aa.v_cache = v_att;
   aa.vt = w.vt;
   aa.vt_stride = vt_stride(T);
   aa.total_rows = T;
@@ -416,7 +433,8 @@ int srp_rerotate_kv(const srp_dims *dims, const srp_batch *batch, void *k_cache,
   if (!k_cache) return fail(SRP_E_INVALID, "k_cache is NULL");
   RopeTable rt;
   CHECK(get_table(dims->head_dim, dims->rope_base, batch->max_position, &rt));
-  SRP_HIP(launch_rerotate(dims->dtype, batch->total_rows, dims->n_kv_heads, dims->head_dim, nullptr,
+  SRP_HIP(launch_rerotate(dims->dtype, batch->total_rows, dims->n_kv_heads, dims->head_dim, nullptr, nullptr,
+                          PagedMap{batch->block_rows, batch->seg_block, batch->block_table},
                           batch->chunk_offsets, batch->n_chunks, batch->chunk_src_pos,
                           batch->positions, nullptr, rt, k_cache, (hipStream_t)stream));
   return SRP_OK;
@@ -499,6 +517,8 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
   };
   bool loads = false;
   for (int l = 0; l < n_layers; ++l) loads |= layers[l].k_host != nullptr;
+  if (loads && b.block_rows > 0)
+    return fail(SRP_E_UNSUPPORTED, "host loads fill contiguous caches (block_rows must be 0)");
   if (loads && cache_bytes > 0 && cs != s) {
     hipError_t e = hipEventCreateWithFlags(&ev[n_layers], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventRecord(ev[n_layers], s);
@@ -611,6 +631,33 @@ int srp_validate_batch(const srp_batch *batch, srp_stream_t stream) {
           return fail(SRP_E_BATCH, "|pos - src| of row %d reaches max_position", j);
       }
     }
+  }
+  if (b.block_rows > 0 && T > 0) {
+    // paged cache: every row maps to its own pool row
+    const int B = b.block_rows;
+    std::vector<int32_t> sb(b.n_chunks);
+    SRP_HIP(hipMemcpy(sb.data(), b.seg_block, sb.size() * 4, hipMemcpyDeviceToHost));
+    long n_tab = 0;
+    for (int c = 0; c < b.n_chunks; ++c) {
+      const int len = co[c + 1] - co[c];
+      if (len == 0) continue;
+      if (sb[c] < 0) return fail(SRP_E_BATCH, "seg_block[%d] < 0", c);
+      const long end = (long)sb[c] + (len + B - 1) / B;
+      n_tab = end > n_tab ? end : n_tab;
+    }
+    std::vector<int32_t> tab(n_tab > 0 ? n_tab : 1);
+    if (n_tab > 0) SRP_HIP(hipMemcpy(tab.data(), b.block_table, (size_t)n_tab * 4, hipMemcpyDeviceToHost));
+    std::vector<long> rows;
+    rows.reserve(T);
+    for (int c = 0; c < b.n_chunks; ++c)
+      for (int i = 0; i < co[c + 1] - co[c]; ++i) {
+        const int blk = tab[sb[c] + i / B];
+        if (blk < 0) return fail(SRP_E_BATCH, "negative block id for row %d", co[c] + i);
+        rows.push_back((long)blk * B + i % B);
+      }
+    std::sort(rows.begin(), rows.end());
+    for (size_t i = 1; i < rows.size(); ++i)
+      if (rows[i] == rows[i - 1]) return fail(SRP_E_BATCH, "two rows map to pool row %ld", rows[i]);
   }
   return SRP_OK;
 }

@@ -203,6 +203,8 @@ struct Workspace {
   int32_t *tiles;      // [3 * max_tiles] attention tiles (first sel, count, req)
   int32_t *ctr;        // [16] device counters (see kCtr*)
   float *gemm_part;    // bf16: [kGemmParts][kGemmPartFloats] split-K partial tiles
+  int32_t *row_slot;   // paged cache: [T] pool row of each batch row (else NULL)
+  void *k_lin, *v_lin; // paged cache: [T][kvdim] the fused cache gathered in row order
   size_t bytes;
 };
 // split-K partial tiles of the projection GEMMs' last round
@@ -258,6 +260,11 @@ inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base) {
   w.tiles = (int32_t *)take((size_t)3 * max_attn_tiles((int)T, (int)nr) * 4);
   w.ctr = (int32_t *)take(16 * 4);
   w.gemm_part = d.dtype == SRP_BF16 ? (float *)take((size_t)kGemmParts * kGemmPartFloats * 4) : nullptr;
+  if (b.block_rows > 0) {
+    w.row_slot = (int32_t *)take(T * 4);
+    w.k_lin = take(T * kvd * es);
+    w.v_lin = take(T * kvd * es);
+  }
   w.bytes = off;
   return w;
 }

@@ -22,18 +22,21 @@ constexpr int kLDC = kBN + 4;  // fp32 kernel staging stride
 // Per-row metadata of a tile (token row, position, position delta), loaded
 // once per tile so the epilogue's global loads do not wait on each other.
 struct EpiRow {
-  int row, pos, delta;
+  int row, pos, delta, cache;  // token row, position, rotation index, cache row
 };
 
 template <int MODE, int ROWS>
 __device__ __forceinline__ void load_row_meta(EpiRow *meta, int m0, int M, const GemmArgs &g) {
   for (int r = threadIdx.x; r < ROWS; r += blockDim.x) {
     const int m = m0 + r;
-    EpiRow e{-1, 0, kFresh};
+    EpiRow e{-1, 0, kFresh, -1};
     if (m < M) {
       e.row = (MODE != EPI_ENC && g.a_rows) ? g.a_rows[m] : m;
       e.pos = g.positions[e.row];
-      if (MODE == EPI_KV) e.delta = g.row_delta[e.row];
+      if (MODE == EPI_KV) {
+        e.delta = g.row_delta[e.row];
+        e.cache = g.row_slot ? g.row_slot[e.row] : e.row;
+      }
     }
     meta[r] = e;
   }
@@ -88,7 +91,7 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow 
       if (valid && part == 0) rope_coef(g.rope, e.pos, i0, c1[j], s1[j]);
       if (MODE == EPI_KV && valid && e.delta != kFresh) {
         const int gh = (nu - part * kvd) / d;
-        const T *c = (const T *)(part ? g.v_cache : g.k_cache) + (size_t)e.row * kvd + gh * d;
+        const T *c = (const T *)(part ? g.v_cache : g.k_cache) + (size_t)e.cache * kvd + gh * d;
         ld4(c + i0, ca[j]);
         ld4(c + half + i0, cb[j]);
         if (part == 0) rope_coef(g.rope, e.delta, i0, c2[j], s2[j]);
@@ -137,7 +140,7 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow 
                 // positional recovery of the cached key, kept in fp32 for the
                 // deviation and written back to the cache
                 rotate4(ca[j], cb[j], c2[j], s2[j]);
-                T *c = (T *)g.k_cache + (size_t)e.row * kvd + gh * d;
+                T *c = (T *)g.k_cache + (size_t)e.cache * kvd + gh * d;
                 st4(c + i0, ca[j]);
                 st4(c + half + i0, cb[j]);
               }

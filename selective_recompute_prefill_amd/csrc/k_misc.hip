@@ -31,8 +31,8 @@ __device__ __forceinline__ void st16(float *p, const float v[4]) { st4(p, v); }
 
 template <typename T>
 __global__ __launch_bounds__(256) void rerotate_kernel(int T_rows, int nkv, int d,
-                                                      const int32_t *row_delta,
-                                                      const int32_t *chunk_offsets, int n_chunks,
+                                                      const int32_t *row_delta, const int32_t *row_slot,
+                                                      PagedMap pm, const int32_t *chunk_offsets, int n_chunks,
                                                       const int32_t *chunk_src_pos,
                                                       const int32_t *positions, const uint8_t *skip,
                                                       RopeTable rt, T *k_cache) {
@@ -43,18 +43,20 @@ __global__ __launch_bounds__(256) void rerotate_kernel(int T_rows, int nkv, int 
     const int j = it / per_row;
     const int rem = it - j * per_row;
     const int gh = rem / per_head, i0 = (rem - gh * per_head) * P;
-    int delta;
+    int delta, cr = j;  // rotation index, cache row
     if (row_delta) {
       delta = row_delta[j];
       if (delta == kFresh) continue;
+      if (row_slot) cr = row_slot[j];
     } else {
       const int c = upper_index(chunk_offsets, n_chunks + 1, j);
       const int src0 = chunk_src_pos[c];
       if (src0 < 0) continue;
       delta = positions[j] - (src0 + j - chunk_offsets[c]);
+      if (pm.block_rows > 0) cr = paged_row(pm, c, j - chunk_offsets[c]);
     }
     if (delta == 0 || (skip && skip[j])) continue;
-    T *p = k_cache + ((size_t)j * nkv + gh) * d;
+    T *p = k_cache + ((size_t)cr * nkv + gh) * d;
     float a[P], b[P];
     ld16(p + i0, a);
     ld16(p + half + i0, b);
@@ -66,9 +68,9 @@ __global__ __launch_bounds__(256) void rerotate_kernel(int T_rows, int nkv, int 
 }
 
 hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *row_delta,
-                           const int32_t *chunk_offsets, int n_chunks, const int32_t *chunk_src_pos,
-                           const int32_t *positions, const uint8_t *skip, const RopeTable &rt,
-                           void *k_cache, hipStream_t s) {
+                           const int32_t *row_slot, const PagedMap &pm, const int32_t *chunk_offsets,
+                           int n_chunks, const int32_t *chunk_src_pos, const int32_t *positions,
+                           const uint8_t *skip, const RopeTable &rt, void *k_cache, hipStream_t s) {
   const int P = dtype == SRP_BF16 ? 8 : 4;
   const long n = (long)T * nkv * (d / 2 / P);
   if (n <= 0) return hipSuccess;
@@ -77,12 +79,35 @@ hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *row_
   grid = grid < 8192 ? grid : 8192;
   if (dtype == SRP_BF16)
     hipLaunchKernelGGL(rerotate_kernel<uint16_t>, dim3((unsigned)grid), dim3(256), 0, s, T, nkv, d,
-                       row_delta, chunk_offsets, n_chunks, chunk_src_pos, positions, skip, rt,
-                       (uint16_t *)k_cache);
+                       row_delta, row_slot, pm, chunk_offsets, n_chunks, chunk_src_pos, positions, skip,
+                       rt, (uint16_t *)k_cache);
   else
     hipLaunchKernelGGL(rerotate_kernel<float>, dim3((unsigned)grid), dim3(256), 0, s, T, nkv, d,
-                       row_delta, chunk_offsets, n_chunks, chunk_src_pos, positions, skip, rt,
-                       (float *)k_cache);
+                       row_delta, row_slot, pm, chunk_offsets, n_chunks, chunk_src_pos, positions, skip,
+                       rt, (float *)k_cache);
+  return hipGetLastError();
+}
+
+// dst[j] = src[row_slot[j]], rows of row_bytes (a multiple of 16): one wave per
+// row, 16 bytes per lane and step.
+__global__ __launch_bounds__(256) void gather_rows_kernel(int T_rows, int row_chunks, const int32_t *row_slot,
+                                                         const uint4 *src, uint4 *dst) {
+  const int lane = threadIdx.x & 63;
+  const int wave = (blockIdx.x * blockDim.x + threadIdx.x) >> 6;
+  const int nwaves = (gridDim.x * blockDim.x) >> 6;
+  for (int j = wave; j < T_rows; j += nwaves) {
+    const size_t from = (size_t)row_slot[j] * row_chunks, to = (size_t)j * row_chunks;
+    for (int c = lane; c < row_chunks; c += 64) dst[to + c] = src[from + c];
+  }
+}
+
+hipError_t launch_gather_rows(int T, size_t row_bytes, const int32_t *row_slot, const void *src,
+                              void *dst, hipStream_t s) {
+  if (T <= 0) return hipSuccess;
+  int grid = (T * 64 + 255) / 256;
+  grid = grid < 4096 ? grid : 4096;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(grid), dim3(256), 0, s, T, (int)(row_bytes / 16), row_slot,
+                     (const uint4 *)src, (uint4 *)dst);
   return hipGetLastError();
 }
 

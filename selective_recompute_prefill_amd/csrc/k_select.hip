@@ -21,6 +21,8 @@ __global__ void row_meta_kernel(SelectArgs a, Workspace w) {
     const int src0 = a.chunk_src_pos[c];
     w.row_delta[j] = src0 >= 0 ? a.positions[j] - (src0 + j - a.chunk_offsets[c]) : kFresh;
     w.row_req[j] = upper_index(a.req_offsets, a.n_req + 1, j);
+    if (a.block_rows > 0)
+      w.row_slot[j] = paged_row(PagedMap{a.block_rows, a.seg_block, a.block_table}, c, j - a.chunk_offsets[c]);
     w.rowflag[j] = 0;
     if (a.dev_out) a.dev_out[j] = __int_as_float(0x7fc00000);
   }
@@ -894,10 +896,11 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Work
     }
     if (e < 0) continue;
     const T *f = (const T *)w.fresh_kv + (size_t)e * 2 * kvdim;
+    const int cr = w.row_slot ? w.row_slot[row] : row;  // cache row
     for (int c = lane; c < chunks; c += 64) {
-      *reinterpret_cast<uint4 *>(k_cache + (size_t)row * kvdim + c * V) =
+      *reinterpret_cast<uint4 *>(k_cache + (size_t)cr * kvdim + c * V) =
           *reinterpret_cast<const uint4 *>(f + c * V);
-      *reinterpret_cast<uint4 *>(v_cache + (size_t)row * kvdim + c * V) =
+      *reinterpret_cast<uint4 *>(v_cache + (size_t)cr * kvdim + c * V) =
           *reinterpret_cast<const uint4 *>(f + kvdim + c * V);
     }
   }

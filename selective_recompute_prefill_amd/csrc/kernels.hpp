@@ -36,6 +36,7 @@ struct GemmArgs {
   float *dev_part;
   void *q_out;
   float q_scale;  // EPI_Q: factor applied to the roped queries
+  const int32_t *row_slot;  // EPI_KV: cache row of each token row (paged cache), or NULL
   float *part;    // bf16: fp32 partial tiles of split tail tiles (kGemmPartFloats each), or NULL
   int part_cap;   // partial-tile slots at `part`
   int grid_main;  // set by launch_gemm: work-groups of the main kernel
@@ -63,6 +64,10 @@ struct SelectArgs {
   int span_max;
   double tau_smooth, tau_cover, cap_ratio;
   int fresh_all;  // scatter fresh K/V of every recomputed row
+  // paged cache (block_rows > 0): pool row of segment c's row i =
+  // block_table[seg_block[c] + i / block_rows] * block_rows + i % block_rows
+  int block_rows;
+  const int32_t *seg_block, *block_table;
 };
 // Row metadata (delta, request), dev_out prefill with NaN, candidate marking, the
 // score-based choice of rows in SRP_SEL_SCORES, and the R list (candidate or
@@ -74,13 +79,27 @@ hipError_t launch_finalize(const SelectArgs &a, const Workspace &w, int32_t *sel
 hipError_t launch_compact_scatter(const SelectArgs &a, const Workspace &w, int dtype, int kvdim,
                                   int32_t *sel_idx, const int32_t *sel_offsets, void *k_cache,
                                   void *v_cache, hipStream_t s);
+// Pool rows of a paged cache (block_rows = 0: row j is cache row j).
+struct PagedMap {
+  int block_rows;
+  const int32_t *seg_block, *block_table;
+};
+__device__ __forceinline__ int paged_row(const PagedMap &pm, int c, int i) {
+  return pm.block_table[pm.seg_block[c] + i / pm.block_rows] * pm.block_rows + i % pm.block_rows;
+}
+
 // Re-rotation of cached rows; with `skip` (row flags) rows flagged as candidates
-// are left alone (the projection epilogue rotates those). row_delta (optional):
-// the rotation index of each row (kFresh: none), else derived from the layout.
+// are left alone (the projection epilogue rotates those). row_delta and row_slot
+// (optional): the rotation index (kFresh: none) and cache row of each row, else
+// derived from the layout and `pm`.
 hipError_t launch_rerotate(int dtype, int T, int nkv, int d, const int32_t *row_delta,
+                           const int32_t *row_slot, const PagedMap &pm,
                            const int32_t *chunk_offsets, int n_chunks,
                            const int32_t *chunk_src_pos, const int32_t *positions,
                            const uint8_t *skip, const RopeTable &rt, void *k_cache, hipStream_t s);
+// Paged cache: dst[j] = src[row_slot[j]] for the T rows of row_bytes each.
+hipError_t launch_gather_rows(int T, size_t row_bytes, const int32_t *row_slot, const void *src,
+                              void *dst, hipStream_t s);
 
 struct AttnArgs {
   int dtype;

@@ -279,6 +279,27 @@ def _normal(rng, shape, std=1.0):
     return rng.standard_normal(shape) * std
 
 
+def paged_layout(layout: "Layout", block_rows: int = 16, seed: int = 1, spare: int = 5):
+    """A block pool for the layout's cache rows (Cache-Craft summary, section 4: each
+    chunk maps to 16-token memory blocks, padded at its end): segment c takes
+    ceil(len_c / block_rows) blocks, placed at shuffled pool positions among `spare`
+    unused ones. Returns seg_block (int32 [n_chunks], index of each segment's first
+    table entry), block_table (int32), the pool row of every batch row (int64 [T])
+    and the pool's row count. Index arrays only."""
+    co = np.asarray(layout.chunk_offsets, np.int64)
+    lens = np.diff(co)
+    nb = (lens + block_rows - 1) // block_rows
+    seg_block = np.concatenate([[0], np.cumsum(nb)[:-1]]).astype(np.int32)
+    total = int(nb.sum())
+    rng = np.random.default_rng(seed)
+    table = rng.permutation(total + spare)[:total].astype(np.int32)
+    slot = np.zeros(layout.total_rows, np.int64)
+    for c in range(len(lens)):
+        i = np.arange(lens[c])
+        slot[co[c] + i] = table[seg_block[c] + i // block_rows] * block_rows + i % block_rows
+    return seg_block, table, slot, (total + spare) * block_rows
+
+
 def draw_scores(n_rows: int, seed: int, unit_max: int = 6, spread: float = 0.5,
                 jitter: float = 0.02) -> np.ndarray:
     """Seeded per-row importance scores as a small auxiliary model would hand them

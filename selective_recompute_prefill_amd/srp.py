@@ -43,7 +43,9 @@ class Batch(ctypes.Structure):
                 ("total_rows", ctypes.c_int32), ("max_req_rows", ctypes.c_int32),
                 ("max_position", ctypes.c_int32),
                 ("req_offsets", ctypes.c_void_p), ("chunk_offsets", ctypes.c_void_p),
-                ("chunk_src_pos", ctypes.c_void_p), ("positions", ctypes.c_void_p)]
+                ("chunk_src_pos", ctypes.c_void_p), ("positions", ctypes.c_void_p),
+                ("block_rows", ctypes.c_int32), ("seg_block", ctypes.c_void_p),
+                ("block_table", ctypes.c_void_p)]
 
 
 class Select(ctypes.Structure):
@@ -130,11 +132,13 @@ def make_dims(hidden, n_heads, n_kv_heads, head_dim, rope_base=10000.0, dtype=SR
 
 
 def make_batch(req_offsets, chunk_offsets, chunk_src_pos, positions, *, total_rows: int,
-               max_req_rows: int, max_position: int) -> Batch:
-    """Batch descriptor over int32 device tensors (sizes are host ints)."""
+               max_req_rows: int, max_position: int, block_rows: int = 0, seg_block=None,
+               block_table=None) -> Batch:
+    """Batch descriptor over int32 device tensors (sizes are host ints). block_rows > 0
+    with seg_block / block_table describes a paged cache pool."""
     return Batch(len(req_offsets) - 1, len(chunk_offsets) - 1, int(total_rows), int(max_req_rows),
                  int(max_position), _ptr(req_offsets), _ptr(chunk_offsets), _ptr(chunk_src_pos),
-                 _ptr(positions))
+                 _ptr(positions), int(block_rows), _ptr(seg_block), _ptr(block_table))
 
 
 def make_select(ratio: float, *, mode=SRP_SEL_TOPK, window=0, tau=0, dev_mode=SRP_DEV_KV,

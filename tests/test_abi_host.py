@@ -107,7 +107,9 @@ def test_scores_mode_accepted_and_bounded():
 
 
 def test_bad_batch():
-    for kw in [dict(n_req=0), dict(total_rows=-1), dict(max_position=0), dict(req_offsets=None)]:
+    for kw in [dict(n_req=0), dict(total_rows=-1), dict(max_position=0), dict(req_offsets=None),
+               dict(block_rows=-1), dict(block_rows=5000, seg_block=8, block_table=8),
+               dict(block_rows=16), dict(block_rows=16, seg_block=8)]:
         with pytest.raises(S.SrpError):
             S.srp_workspace_size(_dims(), _batch(**kw), S.make_select(0.2))
 
@@ -118,6 +120,15 @@ def test_workspace_too_small_is_rejected_before_launch():
     with pytest.raises(S.SrpError) as e:
         S.srp_fuse_layer(d, b, s, 8, 8, 8, 8, 8, 8, 8, None, 8, n - 1, 0)
     assert e.value.code == S.SRP_E_WORKSPACE
+
+
+def test_paged_workspace_holds_the_gathered_cache():
+    s = S.make_select(0.2)
+    flat = S.srp_workspace_size(_dims(), _batch(total_rows=1000, max_req_rows=1000), s)
+    paged = S.srp_workspace_size(_dims(), _batch(total_rows=1000, max_req_rows=1000, block_rows=16,
+                                                 seg_block=8, block_table=8), s)
+    # row slots plus gathered K and V (1000 rows x 2 heads x 128 x 2 bytes each)
+    assert paged - flat >= 1000 * 4 + 2 * 1000 * 256 * 2
 
 
 def test_workspace_monotone():
@@ -181,7 +192,8 @@ def test_stack_argument_checks():
 def test_struct_layouts_match_header():
     # offsets the C compiler gives these structs on x86-64 (int32 then aligned double)
     assert ctypes.sizeof(S.Dims) == 32 and S.Dims.rope_base.offset == 16
-    assert S.Batch.req_offsets.offset == 24 and ctypes.sizeof(S.Batch) == 56
+    assert S.Batch.req_offsets.offset == 24 and S.Batch.block_rows.offset == 56
+    assert S.Batch.block_table.offset == 72 and ctypes.sizeof(S.Batch) == 80
     assert S.Select.ratio.offset == 8 and S.Select.cand.offset == 32
     assert S.Select.scores.offset == 56 and S.Select.fresh_all.offset == 88
     assert ctypes.sizeof(S.Select) == 96
