@@ -47,6 +47,8 @@ def parse():
     p.add_argument("--pipeline", action="store_true",
                    help="multi-layer workloads: also time the stack with its chunk caches loaded "
                         "from page-locked host memory, in line and on a copy stream (srp_fuse_stack)")
+    p.add_argument("--paged", action="store_true",
+                   help="keep the chunk caches in a pool of 16-row blocks reached through a block table")
     p.add_argument("--select", choices=["deviation", "scores"], default="deviation",
                    help="rank rows by KV deviation (default) or by external per-row scores with "
                         "span completion (single-layer workloads)")
@@ -299,6 +301,9 @@ def main():
     if args.summarize_pmc:
         print(summarize_pmc(*args.summarize_pmc, args.copy_mib), end="")
         return
+    if args.paged and args.pipeline:
+        print("--pipeline loads contiguous caches; it does not combine with --paged", file=sys.stderr)
+        sys.exit(2)
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
               f"multi-GPU path", file=sys.stderr)
@@ -353,6 +358,25 @@ def main():
     del x_dev
     torch.cuda.synchronize()
 
+    if args.paged:
+        # the caches move into a shuffled pool of 16-row blocks (each segment padded
+        # to whole blocks); the batch then addresses them through the block table
+        from selective_recompute_prefill_amd.device import ints
+        seg_block, table, slot, pool_rows = inputs.paged_layout(lay, 16, seed=1)
+        idx = torch.as_tensor(slot, device=dev)
+        pooled = []
+        for kc, vc in caches:
+            pk = torch.zeros((pool_rows,) + tuple(kc.shape[1:]), dtype=kc.dtype, device=dev)
+            pv = torch.zeros_like(pk)
+            pk.index_copy_(0, idx, kc)
+            pv.index_copy_(0, idx, vc)
+            pooled.append((pk, pv))
+        caches = pooled
+        call.seg_block, call.block_table = ints(seg_block, dev), ints(table, dev)
+        call.batch = S.make_batch(call.req_offsets, call.chunk_offsets, call.chunk_src_pos, call.positions,
+                                  total_rows=T, max_req_rows=call.max_req_rows, max_position=lay.max_position,
+                                  block_rows=16, seg_block=call.seg_block, block_table=call.block_table)
+        S.srp_validate_batch(call.batch)
     n_copies = args.steps + args.warmup
     sel_kw = dict(window=spec.window, tau=spec.tau)
     by_scores = args.select == "scores"
@@ -442,7 +466,7 @@ def main():
             "frac": stages[dom]["frac_mfma"], "traffic": None,
             "flops_per_launch": work[dom]["flops"], "avg_launch_ms": stages[dom]["ms"]}
 
-    if args.workload == 2 and args.ratio is None and not by_scores:
+    if args.workload == 2 and args.ratio is None and not by_scores and not args.paged:
         # HBM bytes per launch from the recorded counter runs of this workload
         roof["traffic"] = recorded_traffic(roof["kernel"])
 
@@ -469,7 +493,8 @@ def main():
         "data": "synthetic",
         "config": {"workload": WORKLOAD_NAMES[args.workload] + (f" (ratio {args.ratio})" if args.ratio else "")
                    + ("; rows chosen by external scores: K = ceil(0.2 N), spans <= 16 at 0.4, "
-                      "cover 0.7, budget 0.25" if by_scores else ""),
+                      "cover 0.7, budget 0.25" if by_scores else "")
+                   + ("; caches in a pool of 16-row blocks" if args.paged else ""),
                    "global_batch": lay.n_req, "seq_len": int(lay.req_offsets[1]),
                    "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_per_layer, 4),

@@ -313,16 +313,19 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   marks.mark(3);
   // 5. sel_idx and the scatter of fresh K/V into the cache
   SRP_HIP(launch_compact_scatter(sd, w, d.dtype, kvd, sel_idx, sel_offsets, k_cache, v_cache, s));
-  // a paged cache is gathered in row order for the attention's key and value tiles
+  // a paged cache is gathered in row order for the attention's key tiles (and, in
+  // fp32, its value rows); the bf16 value transpose reads the pool rows itself
   const void *k_att = k_cache, *v_att = v_cache;
   if (w.row_slot && T > 0) {
     SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, k_cache, w.k_lin, s));
-    SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, v_cache, w.v_lin, s));
     k_att = w.k_lin;
-    v_att = w.v_lin;
+    if (d.dtype != SRP_BF16) {
+      SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, v_cache, w.v_lin, s));
+      v_att = w.v_lin;
+    }
   }
   if (d.dtype == SRP_BF16 && T > 0)
-    SRP_HIP(launch_v_transpose(T, d.n_kv_heads, d.head_dim, v_att, w.vt, vt_stride(T), s));
+    SRP_HIP(launch_v_transpose(T, d.n_kv_heads, d.head_dim, v_cache, w.row_slot, w.vt, vt_stride(T), s));
   marks.mark(4);
   // 6. Q projection of the selected rows
   GemmArgs gq = g;

@@ -204,7 +204,7 @@ struct Workspace {
   int32_t *ctr;        // [16] device counters (see kCtr*)
   float *gemm_part;    // bf16: [kGemmParts][kGemmPartFloats] split-K partial tiles
   int32_t *row_slot;   // paged cache: [T] pool row of each batch row (else NULL)
-  void *k_lin, *v_lin; // paged cache: [T][kvdim] the fused cache gathered in row order
+  void *k_lin, *v_lin; // paged cache: [T][kvdim] fused K (and fp32 V) gathered in row order
   size_t bytes;
 };
 // split-K partial tiles of the projection GEMMs' last round
@@ -263,7 +263,7 @@ inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base) {
   if (b.block_rows > 0) {
     w.row_slot = (int32_t *)take(T * 4);
     w.k_lin = take(T * kvd * es);
-    w.v_lin = take(T * kvd * es);
+    w.v_lin = d.dtype == SRP_BF16 ? nullptr : take(T * kvd * es);  // bf16 transposes V from the pool
   }
   w.bytes = off;
   return w;

@@ -340,7 +340,7 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
 // Inside every 16-key group the keys are stored in the order 0-3, 8-11, 4-7,
 // 12-15 (the PV operand's lane order); keys at or past T are zero.
 __global__ __launch_bounds__(256) void v_transpose_kernel(int T, int D, int nkv, const uint16_t *v,
-                                                         uint16_t *vt, int vts) {
+                                                         const int32_t *row_slot, uint16_t *vt, int vts) {
   __shared__ uint16_t tile[128][64 + 2];
   const int r0 = blockIdx.x * 64, g = blockIdx.y, tid = threadIdx.x;
   const int kvd = nkv * D, dch = D / 8;
@@ -348,7 +348,8 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(int T, int D, int nkv,
     const int key = c / dch, dc = c - key * dch;
     const int row = r0 + key;
     u32x4 x = {0, 0, 0, 0};
-    if (row < T) x = *reinterpret_cast<const u32x4 *>(v + (size_t)row * kvd + g * D + dc * 8);
+    if (row < T)
+      x = *reinterpret_cast<const u32x4 *>(v + (size_t)(row_slot ? row_slot[row] : row) * kvd + g * D + dc * 8);
     // stored position of this key: swap bits 2 and 3 of its index
     const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
 #pragma unroll
@@ -368,10 +369,10 @@ __global__ __launch_bounds__(256) void v_transpose_kernel(int T, int D, int nkv,
   }
 }
 
-hipError_t launch_v_transpose(int T, int nkv, int d, const void *v_cache, void *vt, int vt_stride,
-                              hipStream_t s) {
+hipError_t launch_v_transpose(int T, int nkv, int d, const void *v_cache, const int32_t *row_slot,
+                              void *vt, int vt_stride, hipStream_t s) {
   hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)(vt_stride / 64), (unsigned)nkv), dim3(256),
-                     0, s, T, d, nkv, (const uint16_t *)v_cache, (uint16_t *)vt, vt_stride);
+                     0, s, T, d, nkv, (const uint16_t *)v_cache, row_slot, (uint16_t *)vt, vt_stride);
   return hipGetLastError();
 }
 

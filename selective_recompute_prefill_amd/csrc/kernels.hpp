@@ -117,9 +117,10 @@ struct AttnArgs {
   void *out;               // [n_sel][nh][d]
 };
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
-// bf16: vt[g][i][j] = v_cache[j][g][i] for j < T, zero for T <= j < vt_stride.
-hipError_t launch_v_transpose(int T, int nkv, int d, const void *v_cache, void *vt, int vt_stride,
-                              hipStream_t s);
+// bf16: vt[g][i][j] = v_cache[slot(j)][g][i] for j < T (slot(j) = row_slot[j], or j
+// when row_slot is NULL), zero for T <= j < vt_stride.
+hipError_t launch_v_transpose(int T, int nkv, int d, const void *v_cache, const int32_t *row_slot,
+                              void *vt, int vt_stride, hipStream_t s);
 // Selected rows per attention tile for this shape (a multiple of 32).
 int attn_tile_rows(int dtype, int nh, int nkv);
 
