@@ -193,14 +193,30 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
     const float c0 = first ? 0.f : -m;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { s[0][e] = c0; s[1][e] = c0; }
+    // K fragments are read two k-steps ahead of their MFMAs; the scheduling
+    // barriers keep the compiler from sinking each read next to its use, which
+    // would make every MFMA pair wait a whole LDS round trip
+    constexpr int KPF = 3;
+    bf16x8 kf[KPF][2];
+#pragma unroll
+    for (int p = 0; p < KPF - 1; ++p)
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+        kf[p][hb] = *reinterpret_cast<const bf16x8 *>(St + koff[p] + hb * 32 * (D * 2));
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int ks = 0; ks < D / 16; ++ks) {
+      if (ks + KPF - 1 < D / 16) {
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb)
+          kf[(ks + KPF - 1) % KPF][hb] =
+              *reinterpret_cast<const bf16x8 *>(St + koff[ks + KPF - 1] + hb * 32 * (D * 2));
+      }
+      __builtin_amdgcn_sched_barrier(0);
       const bf16x8 q8 = __builtin_bit_cast(bf16x8, qf[ks]);
 #pragma unroll
-      for (int hb = 0; hb < 2; ++hb) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8 *>(St + koff[ks] + hb * 32 * (D * 2));
-        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, q8, s[hb], 0, 0, 0);
-      }
+      for (int hb = 0; hb < 2; ++hb)
+        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % KPF][hb], q8, s[hb], 0, 0, 0);
     }
     if (kb < key_start || kb + kBK - 1 > w_first) {
 #pragma unroll
