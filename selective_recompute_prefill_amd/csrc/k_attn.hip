@@ -193,30 +193,37 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
     const float c0 = first ? 0.f : -m;
 #pragma unroll
     for (int e = 0; e < 16; ++e) { s[0][e] = c0; s[1][e] = c0; }
-    // K fragments are read two k-steps ahead of their MFMAs; the scheduling
-    // barriers keep the compiler from sinking each read next to its use, which
-    // would make every MFMA pair wait a whole LDS round trip
-    constexpr int KPF = 3;
-    bf16x8 kf[KPF][2];
+    // the two 32-key halves one after the other, so the first half's max runs on
+    // the VALU while the second half's MFMAs run. K fragments are read two steps
+    // ahead of their MFMAs; the scheduling barriers keep the compiler from sinking
+    // each read next to its use (every MFMA would wait a whole LDS round trip),
+    // and the empty asm keeps the first half's max from sinking below the loop
+    constexpr int KPF = 3, NS = D / 16;
+    bf16x8 kf[KPF];
+    auto kfrag = [&](int t) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8 *>(St + koff[t % NS] + (t / NS) * 32 * (D * 2));
+    };
 #pragma unroll
-    for (int p = 0; p < KPF - 1; ++p)
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-        kf[p][hb] = *reinterpret_cast<const bf16x8 *>(St + koff[p] + hb * 32 * (D * 2));
+    for (int p = 0; p < KPF - 1; ++p) kf[p] = kfrag(p);
     __builtin_amdgcn_sched_barrier(0);
+    auto max16 = [&](const floatx16 &v) __attribute__((always_inline)) {
+      float x = __builtin_fmaxf(v[0], v[1]);
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks) {
-      if (ks + KPF - 1 < D / 16) {
+      for (int e = 2; e < 16; e += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, v[e]), v[e + 1]);
+      return x;
+    };
+    float mx0 = 0.f;
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb)
-          kf[(ks + KPF - 1) % KPF][hb] =
-              *reinterpret_cast<const bf16x8 *>(St + koff[ks + KPF - 1] + hb * 32 * (D * 2));
-      }
+    for (int t = 0; t < 2 * NS; ++t) {
+      if (t + KPF - 1 < 2 * NS) kf[(t + KPF - 1) % KPF] = kfrag(t + KPF - 1);
       __builtin_amdgcn_sched_barrier(0);
-      const bf16x8 q8 = __builtin_bit_cast(bf16x8, qf[ks]);
-#pragma unroll
-      for (int hb = 0; hb < 2; ++hb)
-        s[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[ks % KPF][hb], q8, s[hb], 0, 0, 0);
+      const bf16x8 q8 = __builtin_bit_cast(bf16x8, qf[t % NS]);
+      if (t < NS) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % KPF], q8, s[0], 0, 0, 0);
+      else s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % KPF], q8, s[1], 0, 0, 0);
+      if (t == NS) {
+        mx0 = max16(s[0]);  // runs under the second half's MFMAs
+        asm volatile("" : "+v"(mx0));
+      }
     }
     if (kb < key_start || kb + kBK - 1 > w_first) {
 #pragma unroll
@@ -227,11 +234,10 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
           if (krow > qrow || krow < key_start) s[hb][e] = -INFINITY;
         }
     }
-    float mx = __builtin_fmaxf(__builtin_fmaxf(s[0][0], s[0][1]), s[0][2]);
-#pragma unroll
-    for (int e = 3; e < 31; e += 2)
-      mx = __builtin_fmaxf(__builtin_fmaxf(mx, s[e >> 4][e & 15]), s[(e + 1) >> 4][(e + 1) & 15]);
-    mx = pair_max(__builtin_fmaxf(mx, s[1][15]));
+    float mx;
+    if (kb < key_start || kb + kBK - 1 > w_first) mx = __builtin_fmaxf(max16(s[0]), max16(s[1]));  // masked
+    else mx = __builtin_fmaxf(mx0, max16(s[1]));
+    mx = pair_max(mx);
     if (first) {
       // the first tile sets the reference max (it holds the request's first
       // row, which every query sees, so mx is finite)
