@@ -308,8 +308,7 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   SRP_HIP(launch_gemm(g, s));
   marks.mark(2);
   // 4. top-k / grouping per request, CSR offsets, attention tiles
-  SRP_HIP(launch_select(sd, w, s));
-  SRP_HIP(launch_finalize(sd, w, sel_offsets, s));
+  SRP_HIP(launch_select(sd, w, sel_offsets, s));
   marks.mark(3);
   // 5. sel_idx and the scatter of fresh K/V into the cache
   SRP_HIP(launch_compact_scatter(sd, w, d.dtype, kvd, sel_idx, sel_offsets, k_cache, v_cache, s));

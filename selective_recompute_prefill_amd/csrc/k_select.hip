@@ -306,6 +306,59 @@ __global__ __launch_bounds__(1024) void select_kernel(SelectArgs a, Workspace w)
 }
 
 // ------------------------------------------------------------------------- //
+// finalize: CSR offsets and the attention tile list (longest first)
+// ------------------------------------------------------------------------- //
+// CSR offsets and the attention tile list of the whole batch (one work-group of
+// 1024 threads, after every request's sel_cnt is written).
+__device__ void finalize_body(const SelectArgs &a, const Workspace &w, int32_t *sel_offsets, int *sh) {
+  const int nr = a.n_req, tid = threadIdx.x;
+  int32_t *ntile = w.blkcnt;            // [nr] tiles per request
+  int32_t *tpre = w.blkcnt + nr + 1;    // [nr+1] exclusive prefix of ntile
+  int carry = 0, tcarry = 0;
+  for (int base = 0; base < nr; base += 1024) {
+    const int r = base + tid;
+    const int c = r < nr ? w.sel_cnt[r] : 0;
+    const int nt = (c + a.tile_rows - 1) / a.tile_rows;
+    int tot, ttot;
+    const int p = block_excl_scan(c, sh, &tot) + carry;
+    const int tp = block_excl_scan(nt, sh, &ttot) + tcarry;
+    if (r < nr) {
+      sel_offsets[r] = p;
+      ntile[r] = nt;
+      tpre[r] = tp;
+    }
+    carry += tot;
+    tcarry += ttot;
+  }
+  if (tid == 0) {
+    sel_offsets[nr] = carry;
+    tpre[nr] = tcarry;
+    w.ctr[kCtrTotalSel] = carry;
+    w.ctr[kCtrTiles] = tcarry;
+  }
+  __threadfence_block();
+  __syncthreads();
+  // tile i of request r is emitted at E = (tiles of any request with index > i)
+  // + (requests before r that also have a tile i): descending tile index first,
+  // so the longest causal ranges start first.
+  for (int f = tid; f < tcarry; f += 1024) {
+    const int r = upper_index(tpre, nr + 1, f);
+    const int i = f - tpre[r];
+    int E = 0;
+    for (int q = 0; q < nr; ++q) {
+      const int t = ntile[q];
+      E += t - 1 - i > 0 ? t - 1 - i : 0;
+      if (q < r && t > i) ++E;
+    }
+    const int c = w.sel_cnt[r];
+    const int tr = a.tile_rows;
+    w.tiles[3 * E + 0] = sel_offsets[r] + i * tr;
+    w.tiles[3 * E + 1] = c - i * tr < tr ? c - i * tr : tr;
+    w.tiles[3 * E + 2] = r;
+  }
+}
+
+// ------------------------------------------------------------------------- //
 // selection with the request resident in LDS (requests of up to kLdsEntries
 // entries): keys and flags are loaded once; after marking, the key storage holds
 // the grouping sequence as 16-bit entry offsets and prefix counts
@@ -437,13 +490,45 @@ __device__ void lds_mark_top(const uint32_t *keys, uint8_t *fl, int n, uint8_t i
   __syncthreads();
 }
 
+// Inclusive max-scan over the wave with DPP lane shifts (INT_MIN fills lanes
+// without a source, the identity of max).
+__device__ __forceinline__ int wave_incl_max(int v) {
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x111, 0xf, 0xf, false));  // row_shr:1
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x112, 0xf, 0xf, false));  // row_shr:2
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x114, 0xf, 0xf, false));  // row_shr:4
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x118, 0xf, 0xf, false));  // row_shr:8
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return v;
+}
+
+// Max over the values of the threads before this one (INT_MIN for thread 0).
+// `sh` needs 17 ints of LDS.
+__device__ __forceinline__ int block_excl_max(int v, int *sh) {
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int inc = wave_incl_max(v);
+  const int up = __shfl_up(inc, 1, 64);
+  if (lane == 63) sh[wid] = inc;
+  __syncthreads();
+  if (wid == 0) {
+    // wave 0: exclusive max over the wave totals
+    const int t = lane < nw ? sh[lane] : INT_MIN;
+    const int ti = wave_incl_max(t);
+    if (lane < nw) sh[lane + 1] = ti;
+    if (lane == 0) sh[0] = INT_MIN;
+  }
+  __syncthreads();
+  const int res = max(sh[wid], lane > 0 ? up : INT_MIN);
+  __syncthreads();
+  return res;
+}
+
 // Sliding-window grouping over the sequence of kCand entries in order: a window of
 // `win` slots starting on a kTop slot that holds at least `tau` kTop slots marks
 // each of its slots kSel. seq16 (2 * kLdsEntries u16) holds slot -> entry and the
-// inclusive kTop count per slot; sq (a byte per slot) and scan (blockDim ints) are
-// scratch.
+// inclusive kTop count per slot; sq (a byte per slot) is scratch.
 __device__ void lds_window_group(uint8_t *fl, int n, int win, int tau, uint16_t *seq16,
-                                 uint8_t *sq, int *scan, int *sh) {
+                                 uint8_t *sq, int *sh) {
   const int tid = threadIdx.x, nt = blockDim.x;
   uint16_t *seq_ent = seq16;                // [n] slot -> entry offset
   uint16_t *seq_pre = seq16 + kLdsEntries;  // [n] inclusive top count
@@ -479,15 +564,7 @@ __device__ void lds_window_group(uint8_t *fl, int n, int win, int tau, uint16_t 
   my_segment(n_seq, lo2, hi2);
   int last = -1;
   for (int t = lo2; t < hi2; ++t) last = (sq[t] & 2) ? t : last;
-  scan[tid] = last;
-  __syncthreads();
-  for (int o = 1; o < nt; o <<= 1) {
-    const int v = tid >= o ? scan[tid - o] : -1;
-    __syncthreads();
-    if (v > scan[tid]) scan[tid] = v;
-    __syncthreads();
-  }
-  int rs = tid > 0 ? scan[tid - 1] : -1;
+  int rs = max(block_excl_max(last, sh), -1);
   for (int t = lo2; t < hi2; ++t) {
     if (sq[t] & 2) rs = t;
     if (rs >= 0 && rs > t - win) fl[seq_ent[t]] |= kSel;
@@ -495,14 +572,13 @@ __device__ void lds_window_group(uint8_t *fl, int n, int win, int tau, uint16_t 
   __syncthreads();
 }
 
-__global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspace w) {
+__global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspace w, int32_t *sel_offsets) {
   __shared__ int sh[17];
   __shared__ int hist[kHistBins];
   __shared__ int digit_info[2];
   __shared__ uint32_t keys_s[kLdsEntries];  // later: seq_ent (u16) | seq_pre (u16)
   __shared__ uint8_t fl_s[kLdsEntries];
   __shared__ uint8_t sq_s[kLdsEntries];      // grouping: bit 0 top-k slot, bit 1 passing window
-  __shared__ int sh_max[1024];               // grouping: max-scan of passing starts
   const int r = blockIdx.x, tid = threadIdx.x, nt = blockDim.x;
   const int *roff = a.listed ? w.roff : a.req_offsets;
   const int e0 = roff[r], e1 = roff[r + 1], n = e1 - e0;
@@ -541,7 +617,7 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
   lds_mark_top(keys_s, fl_s, n, kCand, kTop, k, n_cand, hist, sh, digit_info);
 
   if (a.window > 0)
-    lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, sh_max, sh);
+    lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, sh);
 
   // compact the request's selection (fresh rows included) in row order
   const uint8_t want = a.window > 0 ? kSel : kTop;
@@ -560,6 +636,12 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
     }
   }
   if (tid == 0) w.sel_cnt[r] = total;
+  if (sel_offsets) {
+    // a single request: this work-group also finalizes the batch
+    __threadfence_block();
+    __syncthreads();
+    finalize_body(a, w, sel_offsets, sh);
+  }
 }
 
 // ------------------------------------------------------------------------- //
@@ -579,39 +661,6 @@ __device__ __forceinline__ uint32_t score_key(float f) {
 }
 __device__ __forceinline__ float key_score(uint32_t k) {
   return __uint_as_float((k & 0x80000000u) ? (k & 0x7fffffffu) : ~k);
-}
-
-// Inclusive max-scan over the wave with DPP lane shifts (INT_MIN fills lanes
-// without a source, the identity of max).
-__device__ __forceinline__ int wave_incl_max(int v) {
-  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x111, 0xf, 0xf, false));  // row_shr:1
-  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x112, 0xf, 0xf, false));  // row_shr:2
-  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x114, 0xf, 0xf, false));  // row_shr:4
-  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x118, 0xf, 0xf, false));  // row_shr:8
-  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x142, 0xa, 0xf, false));  // row_bcast:15
-  v = max(v, __builtin_amdgcn_update_dpp(INT_MIN, v, 0x143, 0xc, 0xf, false));  // row_bcast:31
-  return v;
-}
-
-// Max over the values of the threads before this one (INT_MIN for thread 0).
-// `sh` needs 17 ints of LDS.
-__device__ __forceinline__ int block_excl_max(int v, int *sh) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  const int inc = wave_incl_max(v);
-  const int up = __shfl_up(inc, 1, 64);
-  if (lane == 63) sh[wid] = inc;
-  __syncthreads();
-  if (wid == 0) {
-    // wave 0: exclusive max over the wave totals
-    const int t = lane < nw ? sh[lane] : INT_MIN;
-    const int ti = wave_incl_max(t);
-    if (lane < nw) sh[lane + 1] = ti;
-    if (lane == 0) sh[0] = INT_MIN;
-  }
-  __syncthreads();
-  const int res = max(sh[wid], lane > 0 ? up : INT_MIN);
-  __syncthreads();
-  return res;
 }
 
 // Min-max normalised score, in double as written: (s - min) / (max - min).
@@ -803,63 +852,16 @@ __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Worksp
       }
     }
   } else if (a.window > 0) {
-    lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, scan0, sh);
+    lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, sh);
     chosen = kSel;
   }
   __syncthreads();
   for (int i = tid; i < n; i += nt) w.rowflag[rq0 + i] = (fl_s[i] & chosen) ? kCand : 0;
 }
 
-// ------------------------------------------------------------------------- //
-// finalize: CSR offsets and the attention tile list (longest first)
-// ------------------------------------------------------------------------- //
 __global__ __launch_bounds__(1024) void finalize_kernel(SelectArgs a, Workspace w, int32_t *sel_offsets) {
   __shared__ int sh[17];
-  const int nr = a.n_req, tid = threadIdx.x;
-  int32_t *ntile = w.blkcnt;            // [nr] tiles per request
-  int32_t *tpre = w.blkcnt + nr + 1;    // [nr+1] exclusive prefix of ntile
-  int carry = 0, tcarry = 0;
-  for (int base = 0; base < nr; base += 1024) {
-    const int r = base + tid;
-    const int c = r < nr ? w.sel_cnt[r] : 0;
-    const int nt = (c + a.tile_rows - 1) / a.tile_rows;
-    int tot, ttot;
-    const int p = block_excl_scan(c, sh, &tot) + carry;
-    const int tp = block_excl_scan(nt, sh, &ttot) + tcarry;
-    if (r < nr) {
-      sel_offsets[r] = p;
-      ntile[r] = nt;
-      tpre[r] = tp;
-    }
-    carry += tot;
-    tcarry += ttot;
-  }
-  if (tid == 0) {
-    sel_offsets[nr] = carry;
-    tpre[nr] = tcarry;
-    w.ctr[kCtrTotalSel] = carry;
-    w.ctr[kCtrTiles] = tcarry;
-  }
-  __threadfence_block();
-  __syncthreads();
-  // tile i of request r is emitted at E = (tiles of any request with index > i)
-  // + (requests before r that also have a tile i): descending tile index first,
-  // so the longest causal ranges start first.
-  for (int f = tid; f < tcarry; f += 1024) {
-    const int r = upper_index(tpre, nr + 1, f);
-    const int i = f - tpre[r];
-    int E = 0;
-    for (int q = 0; q < nr; ++q) {
-      const int t = ntile[q];
-      E += t - 1 - i > 0 ? t - 1 - i : 0;
-      if (q < r && t > i) ++E;
-    }
-    const int c = w.sel_cnt[r];
-    const int tr = a.tile_rows;
-    w.tiles[3 * E + 0] = sel_offsets[r] + i * tr;
-    w.tiles[3 * E + 1] = c - i * tr < tr ? c - i * tr : tr;
-    w.tiles[3 * E + 2] = r;
-  }
+  finalize_body(a, w, sel_offsets, sh);
 }
 
 // ------------------------------------------------------------------------- //
@@ -931,22 +933,22 @@ hipError_t launch_prepare(const SelectArgs &a, const Workspace &w, hipStream_t s
   return hipGetLastError();
 }
 
-hipError_t launch_select(const SelectArgs &a, const Workspace &w, hipStream_t s) {
+hipError_t launch_select(const SelectArgs &a, const Workspace &w, int32_t *sel_offsets, hipStream_t s) {
   int grid = (a.T + 255) / 256;
   grid = grid < 2048 ? (grid > 0 ? grid : 1) : 2048;
   hipLaunchKernelGGL(keys_kernel, dim3(grid), dim3(256), 0, s, a, w);
   if (a.max_req_rows <= kLdsEntries) {
-    hipLaunchKernelGGL(select_lds_kernel, dim3(a.n_req), dim3(1024), 0, s, a, w);
-    return hipGetLastError();
+    // a single request's work-group finalizes the batch itself
+    hipLaunchKernelGGL(select_lds_kernel, dim3(a.n_req), dim3(1024), 0, s, a, w,
+                       a.n_req == 1 ? sel_offsets : nullptr);
+    if (a.n_req == 1) return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL(select_kernel, dim3(a.n_req), dim3(1024), 0, s, a, w);
   }
-  hipLaunchKernelGGL(select_kernel, dim3(a.n_req), dim3(1024), 0, s, a, w);
-  return hipGetLastError();
-}
-
-hipError_t launch_finalize(const SelectArgs &a, const Workspace &w, int32_t *sel_offsets, hipStream_t s) {
   hipLaunchKernelGGL(finalize_kernel, dim3(1), dim3(1024), 0, s, a, w, sel_offsets);
   return hipGetLastError();
 }
+
 
 hipError_t launch_compact_scatter(const SelectArgs &a, const Workspace &w, int dtype, int kvdim,
                                   int32_t *sel_idx, const int32_t *sel_offsets, void *k_cache,

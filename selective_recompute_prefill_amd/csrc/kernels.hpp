@@ -73,9 +73,9 @@ struct SelectArgs {
 // score-based choice of rows in SRP_SEL_SCORES, and the R list (candidate or
 // chosen rows plus fresh rows, per request) when the rows are listed.
 hipError_t launch_prepare(const SelectArgs &a, const Workspace &w, hipStream_t s);
-hipError_t launch_select(const SelectArgs &a, const Workspace &w, hipStream_t s);
-hipError_t launch_finalize(const SelectArgs &a, const Workspace &w, int32_t *sel_offsets,
-                           hipStream_t s);
+// Keys, top-k / grouping per request, then the CSR offsets and attention tiles.
+hipError_t launch_select(const SelectArgs &a, const Workspace &w, int32_t *sel_offsets,
+                         hipStream_t s);
 hipError_t launch_compact_scatter(const SelectArgs &a, const Workspace &w, int dtype, int kvdim,
                                   int32_t *sel_idx, const int32_t *sel_offsets, void *k_cache,
                                   void *v_cache, hipStream_t s);
