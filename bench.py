@@ -48,6 +48,8 @@ def parse():
     p.add_argument("--pipeline", action="store_true",
                    help="multi-layer workloads: also time the stack with its chunk caches loaded "
                         "from page-locked host memory, in line and on a copy stream (srp_fuse_stack)")
+    p.add_argument("--dev", choices=["kv", "v"], default="kv",
+                   help="deviation over K and V (default) or V only (projects K for the selection only)")
     p.add_argument("--paged", action="store_true",
                    help="keep the chunk caches in a pool of 16-row blocks reached through a block table")
     p.add_argument("--select", choices=["deviation", "scores"], default="deviation",
@@ -93,6 +95,21 @@ def algorithmic_work(spec, lay, sel, ratio_rows):
         req_start[lay.req_offsets[r]:lay.req_offsets[r + 1]] = lay.req_offsets[r]
     pairs = int((sel - req_start[sel] + 1).sum()) if n_sel else 0
     prep = T * 4 * 3 + (T * 4 if ratio_rows.get("scores") else 0) + e * 2 * (n_ctx - n_rc) * kvd
+    if ratio_rows.get("v_only"):
+        # V of the candidates only; every cached key is re-rotated in the prepare
+        # stage and the selection's keys come out of the Q projection
+        prep = T * 4 * 3 + e * 2 * n_ctx * kvd
+        return {
+            "prepare": {"bytes": prep},
+            "kv_proj": {"flops": 2.0 * n_rec * H * kvd,
+                        "bytes": e * (n_rec * H + kvd * H + n_rc * kvd + n_rec * kvd)},
+            "select": {"bytes": n_rec * 2 * spec.n_kv_heads * 4 + n_rec * 4 * 4},
+            "scatter": {"bytes": e * 2 * n_sel * kvd},
+            "q_proj": {"flops": 2.0 * n_sel * H * (qd + kvd),
+                       "bytes": e * (n_sel * H + (qd + kvd) * H + n_sel * (qd + kvd))},
+            "attention": {"flops": 4.0 * spec.n_heads * spec.head_dim * pairs,
+                          "bytes": e * (n_sel * qd * 2 + 2 * n_ctx * kvd), "pairs": pairs},
+        }
     return {
         "prepare": {"bytes": prep},
         "kv_proj": {"flops": 2.0 * n_rec * H * 2 * kvd,
@@ -380,6 +397,8 @@ def main():
         S.srp_validate_batch(call.batch)
     n_copies = args.steps + args.warmup
     sel_kw = dict(window=spec.window, tau=spec.tau)
+    if args.dev == "v":
+        sel_kw["dev_mode"] = S.SRP_DEV_V
     by_scores = args.select == "scores"
     if by_scores:
         if nl != 1:
@@ -460,7 +479,7 @@ def main():
         n_rc = int((src[sel0] >= 0).sum())
         rows = {"n_ctx": n_ctx, "n_rec": len(sel0), "n_rec_ctx": n_rc, "scores": True}
     else:  # the first layer projects every row to K/V
-        rows = {"n_ctx": n_ctx, "n_rec": T}
+        rows = {"n_ctx": n_ctx, "n_rec": T, "v_only": args.dev == "v"}
     work = algorithmic_work(spec, lay, sel0, rows)
     stages = {}
     peak_fl = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
@@ -483,7 +502,7 @@ def main():
             "frac": stages[dom]["frac_mfma"], "traffic": None,
             "flops_per_launch": work[dom]["flops"], "avg_launch_ms": stages[dom]["ms"]}
 
-    if args.workload == 2 and args.ratio is None and not by_scores and not args.paged:
+    if args.workload == 2 and args.ratio is None and not by_scores and not args.paged and args.dev == "kv":
         # HBM bytes per launch from the recorded counter runs of this workload
         roof["traffic"] = recorded_traffic(roof["kernel"])
 
@@ -511,7 +530,8 @@ def main():
         "config": {"workload": WORKLOAD_NAMES[args.workload] + (f" (ratio {args.ratio})" if args.ratio else "")
                    + ("; rows chosen by external scores: K = ceil(0.2 N), spans <= 16 at 0.4, "
                       "cover 0.7, budget 0.25" if by_scores else "")
-                   + ("; caches in a pool of 16-row blocks" if args.paged else ""),
+                   + ("; caches in a pool of 16-row blocks" if args.paged else "")
+                   + ("; V-only deviation" if args.dev == "v" else ""),
                    "global_batch": lay.n_req, "seq_len": int(lay.req_offsets[1]),
                    "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_per_layer, 4),

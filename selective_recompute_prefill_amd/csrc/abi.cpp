@@ -267,6 +267,11 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
     sd.window = 0;
     sd.span_max = 0;
   }
+  // V-only deviation needs only the V projection of the candidates: their fresh
+  // keys are dropped unless selected, so K is projected for the selection alone,
+  // together with Q (CacheClip paper's account of CacheBlend: value matrices)
+  const bool v_only = sel->mode == SRP_SEL_TOPK && sel->dev_mode == SRP_DEV_V && !sel->fresh_all;
+  sd.v_only = v_only;
 
   // 1. row metadata; candidate list, the choice by scores, and the recomputed rows
   //    R when they are listed
@@ -274,12 +279,15 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   marks.mark(0);
   SRP_HIP(launch_prepare(sa, w, s));
   // 2. positional recovery of cached rows outside R (inside R the projection
-  //    epilogue rotates them next to the deviation)
-  if (sa.listed && T > 0)
+  //    epilogue rotates them next to the deviation; with V-only deviation, of
+  //    every cached row)
+  if ((sa.listed || v_only) && T > 0)
     SRP_HIP(launch_rerotate(d.dtype, T, d.n_kv_heads, d.head_dim, w.row_delta, w.row_slot,
                             PagedMap{b.block_rows, b.seg_block, b.block_table}, b.chunk_offsets,
-                            b.n_chunks, b.chunk_src_pos, b.positions, w.rowflag, rt, k_cache, s));
-  // 3. K/V projection of R with the rotation / deviation epilogue
+                            b.n_chunks, b.chunk_src_pos, b.positions, v_only ? nullptr : w.rowflag, rt,
+                            k_cache, s));
+  // 3. K/V projection of R with the rotation / deviation epilogue (V alone with
+  //    V-only deviation)
   GemmArgs g{};
   g.dtype = d.dtype;
   g.A = hidden;
@@ -288,9 +296,9 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   g.M_host = T;
   g.M_dev = sa.listed ? w.ctr + kCtrREntries : nullptr;
   g.M_cap = T;
-  g.B = (const char *)w_qkv + (size_t)qd * d.hidden * es;
-  g.N = 2 * kvd;
-  g.mode = EPI_KV;
+  g.B = (const char *)w_qkv + (size_t)(v_only ? qd + kvd : qd) * d.hidden * es;
+  g.N = v_only ? kvd : 2 * kvd;
+  g.mode = v_only ? EPI_V : EPI_KV;
   g.nh = d.n_heads;
   g.nkv = d.n_kv_heads;
   g.d = d.head_dim;
@@ -315,28 +323,30 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   // a paged cache is gathered in row order for the attention's key tiles (and, in
   // fp32, its value rows); the bf16 value transpose reads the pool rows itself
   const void *k_att = k_cache, *v_att = v_cache;
-  if (w.row_slot && T > 0) {
-    SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, k_cache, w.k_lin, s));
-    k_att = w.k_lin;
-    if (d.dtype != SRP_BF16) {
-      SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, v_cache, w.v_lin, s));
-      v_att = w.v_lin;
-    }
+  if (w.row_slot && T > 0 && d.dtype != SRP_BF16) {
+    SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, v_cache, w.v_lin, s));
+    v_att = w.v_lin;
   }
   if (d.dtype == SRP_BF16 && T > 0)
     SRP_HIP(launch_v_transpose(T, d.n_kv_heads, d.head_dim, v_cache, w.row_slot, w.vt, vt_stride(T), s));
   marks.mark(4);
-  // 6. Q projection of the selected rows
+  // 6. Q projection of the selected rows (with V-only deviation also their fresh
+  //    keys, straight into the cache)
   GemmArgs gq = g;
   gq.a_rows = sel_idx;
   gq.M_dev = w.ctr + kCtrTotalSel;
   gq.B = w_qkv;
-  gq.N = qd;
-  gq.mode = EPI_Q;
+  gq.N = v_only ? qd + kvd : qd;
+  gq.mode = v_only ? EPI_QK : EPI_Q;
   gq.q_out = w.q;
   // bf16 attention works in base 2 on pre-scaled queries; the fp32 kernel scales itself
   gq.q_scale = d.dtype == SRP_BF16 ? (float)(1.4426950408889634 / std::sqrt((double)d.head_dim)) : 1.0f;
   SRP_HIP(launch_gemm(gq, s));
+  if (w.row_slot && T > 0) {
+    // the fused keys are final only now
+    SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, k_cache, w.k_lin, s));
+    k_att = w.k_lin;
+  }
   marks.mark(5);
   // 7. attention of the selected rows over the fused cache
   AttnArgs aa{};

@@ -33,10 +33,8 @@ __device__ __forceinline__ void load_row_meta(EpiRow *meta, int m0, int M, const
     if (m < M) {
       e.row = (MODE != EPI_ENC && g.a_rows) ? g.a_rows[m] : m;
       e.pos = g.positions[e.row];
-      if (MODE == EPI_KV) {
-        e.delta = g.row_delta[e.row];
-        e.cache = g.row_slot ? g.row_slot[e.row] : e.row;
-      }
+      if (MODE == EPI_KV || MODE == EPI_V) e.delta = g.row_delta[e.row];
+      if (MODE == EPI_KV || MODE == EPI_V || MODE == EPI_QK) e.cache = g.row_slot ? g.row_slot[e.row] : e.row;
     }
     meta[r] = e;
   }
@@ -66,15 +64,32 @@ __device__ __forceinline__ void rotate4(float a[4], float b[4], const float c[4]
 // row r is tile row m_base + r, its metadata meta[r]) with NT threads: item =
 // (row, head unit, 4 rotation pairs). Items go in batches of B whose global
 // loads (rotation coefficients, cached K/V) are all issued before any of the
-// batch's stores.
+// batch's stores. A head unit is a Q, K or V head by the mode and its column.
 template <typename T, int ROWS, int MODE, int NT, int B>
 __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow *meta, int m_base,
                                          int n0, const GemmArgs &g) {
   constexpr int ITEMS = ROWS * 16 / NT;
   static_assert(ROWS * 16 % NT == 0 && ITEMS % B == 0, "items split evenly");
+  constexpr bool SCORE = MODE == EPI_KV || MODE == EPI_V;  // fresh K/V + deviation
   const int d = g.d, half = d >> 1;
   const int tpu = d >> 3;  // threads per head unit (4 pairs each)
-  const int kvd = g.nkv * d;
+  const int kvd = g.nkv * d, qd = g.nh * d;
+  // part of the unit at global column nu (0 = Q, 1 = K, 2 = V) and its head index
+  auto unit = [&](int nu, int &part, int &hidx) __attribute__((always_inline)) {
+    if (MODE == EPI_Q) {
+      part = 0;
+      hidx = nu / d;
+    } else if (MODE == EPI_QK) {
+      part = nu < qd ? 0 : 1;
+      hidx = (nu - (part ? qd : 0)) / d;
+    } else if (MODE == EPI_V) {
+      part = 2;
+      hidx = nu / d;
+    } else {
+      part = nu < kvd ? 1 : 2;
+      hidx = (nu - (part == 2 ? kvd : 0)) / d;
+    }
+  };
 #pragma unroll 1
   for (int kb = 0; kb < ITEMS; kb += B) {
     float c1[B][4], s1[B][4], c2[B][4], s2[B][4], ca[B][4], cb[B][4];
@@ -87,14 +102,14 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow 
       const int nu = n0 + u * d, i0 = t * 4;
       const EpiRow e = meta[r];
       const bool valid = e.row >= 0 && nu < g.N;
-      const int part = MODE == EPI_Q ? 0 : (nu >= kvd);
-      if (valid && part == 0) rope_coef(g.rope, e.pos, i0, c1[j], s1[j]);
-      if (MODE == EPI_KV && valid && e.delta != kFresh) {
-        const int gh = (nu - part * kvd) / d;
-        const T *c = (const T *)(part ? g.v_cache : g.k_cache) + (size_t)e.cache * kvd + gh * d;
+      int part, hidx;
+      unit(nu, part, hidx);
+      if (valid && part <= 1) rope_coef(g.rope, e.pos, i0, c1[j], s1[j]);
+      if (SCORE && valid && e.delta != kFresh) {
+        const T *c = (const T *)(part == 2 ? g.v_cache : g.k_cache) + (size_t)e.cache * kvd + hidx * d;
         ld4(c + i0, ca[j]);
         ld4(c + half + i0, cb[j]);
-        if (part == 0) rope_coef(g.rope, e.delta, i0, c2[j], s2[j]);
+        if (part == 1) rope_coef(g.rope, e.delta, i0, c2[j], s2[j]);
       }
     }
     // compute and store
@@ -107,6 +122,8 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow 
       const int m = m_base + r;
       const EpiRow e = meta[r];
       const bool valid = e.row >= 0 && nu < g.N;
+      int part, hidx;
+      unit(nu, part, hidx);
       float a[4], b[4];
       const float *src = Cs + r * ldc + u * d;
 #pragma unroll
@@ -114,46 +131,45 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow 
       float part_sum = 0.f;
       int slot = -1;
       if (valid) {
-        if (MODE == EPI_Q) {
-          const int h = nu / d;
-          rotate4(a, b, c1[j], s1[j]);
+        if (part <= 1) rotate4(a, b, c1[j], s1[j]);
+        if (part == 0) {
 #pragma unroll
           for (int k = 0; k < 4; ++k) { a[k] *= g.q_scale; b[k] *= g.q_scale; }
-          T *q = (T *)g.q_out + (size_t)m * g.nh * d + h * d;
+          T *q = (T *)g.q_out + (size_t)m * qd + hidx * d;
           st4(q + i0, a);
           st4(q + half + i0, b);
+        } else if (MODE == EPI_QK) {
+          // fresh key of a selected row, straight into its cache row
+          T *o = (T *)g.k_cache + (size_t)e.cache * kvd + hidx * d;
+          st4(o + i0, a);
+          st4(o + half + i0, b);
+        } else if (MODE == EPI_ENC) {
+          T *o = (T *)(part == 2 ? g.v_cache : g.k_cache) + (size_t)m * kvd + hidx * d;
+          st4(o + i0, a);
+          st4(o + half + i0, b);
         } else {
-          const int part = nu >= kvd;
-          const int gh = (nu - part * kvd) / d;
-          if (part == 0) rotate4(a, b, c1[j], s1[j]);
-          if (MODE == EPI_ENC) {
-            T *o = (T *)(part ? g.v_cache : g.k_cache) + (size_t)m * kvd + gh * d;
-            st4(o + i0, a);
-            st4(o + half + i0, b);
-          } else {
-            T *f = (T *)g.fresh + (size_t)m * 2 * kvd + part * kvd + gh * d;
-            st4(f + i0, a);
-            st4(f + half + i0, b);
-            slot = part * g.nkv + gh;
-            if (e.delta != kFresh) {
-              if (part == 0) {
-                // positional recovery of the cached key, kept in fp32 for the
-                // deviation and written back to the cache
-                rotate4(ca[j], cb[j], c2[j], s2[j]);
-                T *c = (T *)g.k_cache + (size_t)e.cache * kvd + gh * d;
-                st4(c + i0, ca[j]);
-                st4(c + half + i0, cb[j]);
-              }
+          T *f = (T *)g.fresh + (size_t)m * 2 * kvd + (part - 1) * kvd + hidx * d;
+          st4(f + i0, a);
+          st4(f + half + i0, b);
+          slot = (part - 1) * g.nkv + hidx;
+          if (e.delta != kFresh) {
+            if (part == 1) {
+              // positional recovery of the cached key, kept in fp32 for the
+              // deviation and written back to the cache
+              rotate4(ca[j], cb[j], c2[j], s2[j]);
+              T *c = (T *)g.k_cache + (size_t)e.cache * kvd + hidx * d;
+              st4(c + i0, ca[j]);
+              st4(c + half + i0, cb[j]);
+            }
 #pragma unroll
-              for (int k = 0; k < 4; ++k) {
-                const float x = a[k] - ca[j][k], y = b[k] - cb[j][k];
-                part_sum += x * x + y * y;
-              }
+            for (int k = 0; k < 4; ++k) {
+              const float x = a[k] - ca[j][k], y = b[k] - cb[j][k];
+              part_sum += x * x + y * y;
             }
           }
         }
       }
-      if (MODE == EPI_KV) {
+      if (SCORE) {
         // fixed-order reduction over the head's tpu lanes (aligned groups)
         for (int o = 1; o < tpu; o <<= 1) part_sum += __shfl_xor(part_sum, o, 64);
         if (valid && t == 0) g.dev_part[(size_t)m * 2 * g.nkv + slot] = part_sum;
@@ -576,6 +592,8 @@ hipError_t launch_gemm(const GemmArgs &g0, hipStream_t s) {
   switch (g.mode) {
     case EPI_KV: SRP_GEMM_LAUNCH(EPI_KV); break;
     case EPI_Q: SRP_GEMM_LAUNCH(EPI_Q); break;
+    case EPI_V: SRP_GEMM_LAUNCH(EPI_V); break;
+    case EPI_QK: SRP_GEMM_LAUNCH(EPI_QK); break;
     default: SRP_GEMM_LAUNCH(EPI_ENC); break;
   }
 #undef SRP_GEMM_LAUNCH

@@ -900,8 +900,9 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Work
     const T *f = (const T *)w.fresh_kv + (size_t)e * 2 * kvdim;
     const int cr = w.row_slot ? w.row_slot[row] : row;  // cache row
     for (int c = lane; c < chunks; c += 64) {
-      *reinterpret_cast<uint4 *>(k_cache + (size_t)cr * kvdim + c * V) =
-          *reinterpret_cast<const uint4 *>(f + c * V);
+      if (!a.v_only)
+        *reinterpret_cast<uint4 *>(k_cache + (size_t)cr * kvdim + c * V) =
+            *reinterpret_cast<const uint4 *>(f + c * V);
       *reinterpret_cast<uint4 *>(v_cache + (size_t)cr * kvdim + c * V) =
           *reinterpret_cast<const uint4 *>(f + kvdim + c * V);
     }

@@ -5,7 +5,7 @@
 
 namespace srp {
 
-enum EpiMode { EPI_KV = 0, EPI_Q = 1, EPI_ENC = 2 };
+enum EpiMode { EPI_KV = 0, EPI_Q = 1, EPI_ENC = 2, EPI_V = 3, EPI_QK = 4 };
 
 // C[m, n] = sum_k A[row(m), k] * B[n, k], followed by an epilogue on each
 // head-sized unit of a row:
@@ -16,6 +16,10 @@ enum EpiMode { EPI_KV = 0, EPI_Q = 1, EPI_ENC = 2 };
 //  EPI_Q  : n are Q heads, roped and multiplied by q_scale; written to q_out [m][qdim].
 //  EPI_ENC: like EPI_KV's layout, K roped at positions[m]; K -> k_cache[m],
 //           V -> v_cache[m].
+//  EPI_V  : n are V heads only: fresh V to the V half of `fresh`, squared
+//           deviation from the cached V to dev_part (V-only deviation).
+//  EPI_QK : n < qdim are Q heads (as EPI_Q), the rest K heads, roped at the
+//           row's position and written to the row's cache row in k_cache.
 struct GemmArgs {
   int dtype;
   const void *A;       // [*, K]
@@ -64,6 +68,7 @@ struct SelectArgs {
   int span_max;
   double tau_smooth, tau_cover, cap_ratio;
   int fresh_all;  // scatter fresh K/V of every recomputed row
+  bool v_only;    // V-only fast path: only fresh V is scattered (K comes with Q)
   // paged cache (block_rows > 0): pool row of segment c's row i =
   // block_table[seg_block[c] + i / block_rows] * block_rows + i % block_rows
   int block_rows;

@@ -138,6 +138,30 @@ def test_mini_v_only_deviation():
              what="mini-v")
 
 
+@pytest.mark.parametrize("case", ["grouped", "cand", "f32", "ratio-one", "fresh-all"])
+def test_v_only_deviation_paths(case):
+    """V-only deviation projects only V for the candidates and K with Q for the
+    selection; every variant must still match the oracle."""
+    spec = inputs.small_spec(dtype="f32" if case == "f32" else "bf16")
+    sel_kw, okw = dict(dev_mode=S.SRP_DEV_V), dict(dev_mode="v")
+    if case == "grouped":
+        sel_kw.update(window=8, tau=4)
+    elif case == "ratio-one":
+        sel_kw["ratio"] = 1.0
+        okw["ratio"] = 1.0
+    elif case == "fresh-all":  # takes the general path (fresh K of every candidate)
+        sel_kw["fresh_all"] = True
+        okw["fresh_all"] = True
+    elif case == "cand":
+        lay = inputs.generate(spec).layout
+        cand = np.concatenate([np.arange(lay.req_offsets[r], lay.req_offsets[r + 1])[1::3]
+                               for r in range(lay.n_req)])
+        off = np.searchsorted(cand, lay.req_offsets)
+        sel_kw.update(ratio=0.1, cand=ints(cand), cand_offsets=ints(off))
+        okw.update(ratio=0.1, cand=cand)
+    run_case(spec, sel_kw=sel_kw, oracle_kw=okw, what=f"v-only {case}")
+
+
 @pytest.mark.parametrize("ratio", [0.0, 1.0, 0.5])
 def test_mini_ratio_edges(ratio):
     run_case(inputs.small_spec(), sel_kw=dict(ratio=ratio), what=f"mini-r{ratio}")

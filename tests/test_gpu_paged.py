@@ -97,6 +97,12 @@ def test_paged_scores_and_fresh_all():
     run_both(spec, lambda: dict(ratio=0.2, fresh_all=True), "fresh-all", seed=2)
 
 
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_paged_v_only_deviation(dtype):
+    spec = inputs.small_spec(dtype=dtype)
+    run_both(spec, lambda: dict(ratio=0.2, dev_mode=S.SRP_DEV_V), f"v-only {dtype}")
+
+
 def test_paged_candidate_list():
     spec = inputs.small_spec()
     lay = inputs.generate(spec).layout
