@@ -180,7 +180,7 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow 
 
 // ------------------------------------------------------------------------- //
 // tile scheduling: persistent loop, each XCD (blockIdx % 8) walks a contiguous
-// range of row-major tiles so the row block of A it reads stays in its L2
+// range of tiles so the operand slabs its work-groups read stay in its L2
 // ------------------------------------------------------------------------- //
 struct TileIter {
   int x, loc, per_x, chunk, total;
@@ -233,6 +233,31 @@ struct GemmCfg {
   static_assert(BN % kBN == 0, "the epilogue works on 128-column blocks");
 };
 
+// Tile order of the bf16 kernels: groups of gm row tiles, column-major inside a
+// group. An XCD runs c = min(work-groups per XCD, its share of tiles) consecutive
+// tiles at once; choosing gm to minimise gm + ceil(c / gm) makes them a near-square
+// block, so each k-step the XCD's L2 fetches gm A slabs and ceil(c / gm) B slabs
+// (row-major order fetches every B slab whenever a row of tiles is wider than c).
+struct TileMap {
+  int mt_n, nt_n, gm;
+  __device__ TileMap(int mt_n_, int nt_n_, int whole, int grid) : mt_n(mt_n_), nt_n(nt_n_), gm(1) {
+    const int per_x = grid >> 3, share = (whole + 7) >> 3;
+    const int c = per_x < share ? per_x : share;
+    int best = 1 << 30;
+    for (int r = 1; r <= mt_n && r <= c; ++r) {
+      const int cols = (c + r - 1) / r;
+      if (cols > nt_n) continue;
+      if (r + cols < best) best = r + cols, gm = r;
+    }
+  }
+  __device__ void mn(int t, int &mt, int &nt) const {
+    const int gsz = gm * nt_n, grp = t / gsz, idx = t - grp * gsz, r0 = grp * gm;
+    const int gh = mt_n - r0 < gm ? mt_n - r0 : gm;
+    nt = idx / gh;
+    mt = r0 + (idx - nt * gh);
+  }
+};
+
 // Work split: the full rounds of tiles (floor(T / P) per work-group) run whole;
 // the R tiles of the last, partial round are split along K into s pieces each
 // (s <= P / R), whose fp32 partial tiles a second kernel adds up and finishes
@@ -266,6 +291,7 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
   const int K = g.K, N = g.N;
   const int mt_n = (M + C::BM - 1) / C::BM, nt_n = (N + C::BN - 1) / C::BN;
   const SplitPlan sp = split_plan(mt_n * nt_n, gridDim.x, g.part_cap);
+  const TileMap tm(mt_n, nt_n, sp.full, gridDim.x);
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = w / C::WN, wn = w - wm * C::WN;
@@ -352,7 +378,8 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
   if (sp.split > 1 && (int)blockIdx.x < sp.tail * sp.split) {
     const int piece = blockIdx.x;
     const int tile = sp.full + piece / sp.split, j = piece - (piece / sp.split) * sp.split;
-    const int mt = tile / nt_n, nt = tile - mt * nt_n;
+    int mt, nt;
+    tm.mn(tile, mt, nt);
     const int k0 = (int)((long)KT * j / sp.split), k1 = (int)((long)KT * (j + 1) / sp.split);
     mainloop(mt * C::BM, nt * C::BN, k0, k1 - k0, [] {});
     float *dst = g.part + (size_t)piece * kGemmPartFloats;
@@ -369,12 +396,13 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
     __syncthreads();  // the ring is free before the next tile's copies
   }
 
-  // 2. whole tiles: each XCD walks a contiguous range of row-major tiles
+  // 2. whole tiles: each XCD walks a contiguous range of tiles in TileMap order
   const TileIter ti(sp.full);
   for (int lt = ti.loc;; lt += ti.per_x) {
     const int tile = ti.tile(lt);
     if (tile < 0) break;
-    const int mt = tile / nt_n, nt = tile - mt * nt_n;
+    int mt, nt;
+    tm.mn(tile, mt, nt);
     const int m0 = mt * C::BM, n0 = nt * C::BN;
     // the epilogue's row metadata loads while the first copies are in flight
     mainloop(m0, n0, 0, KT, [&] { load_row_meta<MODE, C::BM>(meta, m0, M, g); });
@@ -455,7 +483,8 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   const int ti = blockIdx.x / RB, rb = blockIdx.x - ti * RB;
   if (sp.split < 2 || ti >= sp.tail) return;
   const int tile = sp.full + ti;
-  const int mt = tile / nt_n, nt = tile - mt * nt_n;
+  int mt, nt;
+  TileMap(mt_n, nt_n, sp.full, g.grid_main).mn(tile, mt, nt);
   const int m0 = mt * C::BM + rb * kFixRows, n0 = nt * C::BN;
   if (m0 >= M) return;
   load_row_meta<MODE, kFixRows>(meta, m0, M, g);
