@@ -48,6 +48,12 @@ __device__ __forceinline__ float pair_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// Software pipelined: each wave overlaps the score MFMAs of key tile j+1 with the
+// exponentials of tile j, and the PV MFMAs of tile j with the mask and max of
+// tile j+1, so its own VALU work runs under its own matrix work. Waves 4-7 run
+// half an iteration behind waves 0-3 (one barrier per tile, at a different point
+// of the iteration for each group), so the two waves on a SIMD are in opposite
+// halves. A five-slot ring gives each tile's copy two iterations to land.
 template <int D>
 __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   // K tile: 64 rows of D bf16 (D*2 bytes), 16-byte chunk c of row r stored at
@@ -56,21 +62,28 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   // per cycle; the fragment reads put 16 consecutive rows in those lanes, and
   // both layouts give them 16 different bank groups.
   constexpr int KT = kBK * D * 2, VT = D * kBK * 2, STAGE = KT + VT;
-  constexpr int KCH = D / 8;               // chunks per K row
-  constexpr int KROWS = 64 / KCH;          // K rows per wave copy
-  constexpr int KJ = kBK / KROWS / kAW;    // K copies per wave per tile
-  constexpr int VJ = D / 8 / kAW;          // V^T copies per wave per tile (8 rows each)
+  constexpr int KCH = D / 8;
+  constexpr int KROWS = 64 / KCH;
+  constexpr int KJ = kBK / KROWS / kAW;
+  constexpr int VJ = D / 8 / kAW;
   constexpr int LOADS = KJ + VJ;
+  constexpr int NS = D / 16;
+  constexpr int PFD = 3;  // LDS fragment reads issued this many MFMAs ahead
   static_assert(KJ >= 1 && VJ >= 1, "every wave copies K and V^T rows");
-  // three ring slots as separate LDS objects: every access below names its slot
-  // at compile time, so a read of one slot never waits on copies into another
+  constexpr int NSL = 5;  // ring slots
+  // the ring slots as separate LDS objects: every access below names its slot at
+  // compile time
   __shared__ __align__(16) char st0[STAGE];
   __shared__ __align__(16) char st1[STAGE];
   __shared__ __align__(16) char st2[STAGE];
+  __shared__ __align__(16) char st3[STAGE];
+  __shared__ __align__(16) char st4[STAGE];
   auto slot_ptr = [&](auto I) __attribute__((always_inline)) -> char * {
     if constexpr (decltype(I)::value == 0) return st0;
     else if constexpr (decltype(I)::value == 1) return st1;
-    else return st2;
+    else if constexpr (decltype(I)::value == 2) return st2;
+    else if constexpr (decltype(I)::value == 3) return st3;
+    else return st4;
   };
 
   const int n_tiles = *a.n_tiles;
@@ -88,7 +101,7 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   const int nblk = (key_end - key_base + kBK - 1) / kBK;
 
   const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave index (uniform)
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int qi = lane & 31, gph = lane >> 5;
   const int col = 32 * w + qi;
   const int qq = col / G, hh = col - qq * G;
@@ -101,6 +114,8 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   const bool wactive = wq_lo < nq;
   const int w_first = wactive ? a.sel_idx[q0 + wq_lo] : key_end;
   const int w_last = wactive ? a.sel_idx[q0 + wq_hi] : key_start - 1;
+  // key tiles this wave computes (those starting at or before its last query)
+  const int nact = wactive ? min(nblk, (w_last - key_base) / kBK + 1) : 0;
   const size_t row_bytes = (size_t)a.nkv * D * 2;
   const char *Kg = (const char *)a.k_cache + (size_t)g * D * 2;
   const char *Vg = (const char *)a.vt + (size_t)g * D * a.vt_stride * 2;
@@ -108,7 +123,8 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
 
   // Wave w copies K rows KROWS*i.. (i = w + 8j) and V^T rows 8i.. per tile; each
   // lane's source offset inside a copy is a constant (the swizzle term only
-  // depends on the lane for these row groups).
+  // depends on the lane for these row groups). Rows past key_end are clamped to
+  // the last valid row; such keys come after every query of the tile and are masked.
   const int k_lrow = lane / KCH, k_logical = (lane % KCH) ^ ((KROWS * w + k_lrow) & (KCH - 1));
   const uint32_t k_lane_off = (uint32_t)(k_lrow * row_bytes + k_logical * 16);
   const int v_lrow = lane >> 3, v_logical = (lane & 7) ^ (((8 * w + v_lrow) >> 1) & 7);
@@ -123,8 +139,6 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
       if (!partial) {
         src = Kg + (size_t)(kb + KROWS * i) * row_bytes + k_lane_off;
       } else {
-        // rows past key_end are clamped to the last valid row; such keys come
-        // after every query of the tile and are masked
         const int row = min(kb + KROWS * i + k_lrow, key_end - 1);
         src = Kg + (size_t)row * row_bytes + k_logical * 16;
       }
@@ -138,93 +152,62 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
 
   // Q fragments (B operand of S^T = K Q^T): lane holds its column's query row,
   // d range ks*16 + gph*8 .. +8, in registers for the whole tile
-  u32x4 qf[D / 16];
+  u32x4 qf[NS];
   {
     const uint16_t *qp =
         (const uint16_t *)a.q + ((size_t)(q0 + (cvalid ? qq : 0)) * a.nh + g * G + hh) * D + gph * 8;
 #pragma unroll
-    for (int ks = 0; ks < D / 16; ++ks)
+    for (int ks = 0; ks < NS; ++ks)
       qf[ks] = cvalid ? *reinterpret_cast<const u32x4 *>(qp + ks * 16) : u32x4{0, 0, 0, 0};
   }
   // the Q loads complete before the first tile copy is issued: the copies are
   // invisible to the compiler's wait counting, which would otherwise wait for
-  // every outstanding load (the whole prefetch ring) at each use of Q
+  // every outstanding load (the whole ring) at each use of Q
   wait_vmcnt<0>();
   floatx16 acc[D / 32];
 #pragma unroll
   for (int b = 0; b < D / 32; ++b)
 #pragma unroll
     for (int e = 0; e < 16; ++e) acc[b][e] = 0.f;
-  // Scores are in base-2 units (queries carry log2(e)/sqrt(d)). The score
-  // accumulators start at -m, so they come out of the MFMA already relative to
-  // the reference max m, which is raised only when a tile's max exceeds it by
-  // more than 8: probabilities stay below 2^8 and rescales are rare.
-  // l is this lane's share of the row sum (its keys of each 16-key step); the
-  // two lanes of a column are added at the end.
+  // Scores are in base-2 units (queries carry log2(e)/sqrt(d)). The score chains
+  // start at -m, so they come out of the MFMA already relative to the reference
+  // max m, which is raised only when a tile's max exceeds it by more than 8:
+  // probabilities stay below 2^8 and rescales are rare. l is this lane's share
+  // of the row sum (its keys of each 16-key step); the two lanes of a column are
+  // added at the end.
   float m = 0.f, l = 0.f;
-  bool first = true;
+  floatx16 cneg;  // -m in every element: the first accumulator of each score chain
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
-
-  // per-lane LDS byte offsets of the K and V^T fragments inside a slot
-  uint32_t koff[D / 16];
+  uint32_t koff[NS];
 #pragma unroll
-  for (int ks = 0; ks < D / 16; ++ks) koff[ks] = qi * (D * 2) + (((2 * ks + gph) ^ (qi & (KCH - 1))) * 16);
+  for (int ks = 0; ks < NS; ++ks) koff[ks] = qi * (D * 2) + (((2 * ks + gph) ^ (qi & (KCH - 1))) * 16);
   uint32_t voff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) voff[c] = KT + qi * 128 + (((2 * c + gph) ^ ((qi >> 1) & 7)) * 16);
 
-  using I0 = std::integral_constant<int, 0>;
-  using I1 = std::integral_constant<int, 1>;
-  using I2 = std::integral_constant<int, 2>;
-  // Ping-pong schedule in half-steps: waves 0-3 run phase 1 of tile j (S^T,
-  // mask, max, rescale: MFMA-bound) while waves 4-7 run phase 2 of tile j-1
-  // (exp, row sums, PV: exp-heavy), then they swap, so the two waves sharing a
-  // SIMD keep its matrix and vector units busy together. Every half-step ends
-  // in a barrier; the copy of tile j+2 starts after the barrier that ends
-  // half-step 2j, when slot (j+2)%3 = (j-1)%3 has been read for the last time
-  // (by waves 4-7, phase 2 of tile j-1), and is waited for at the end of
-  // half-step 2j+3, just before waves 0-3 start on it.
-  floatx16 s[2];
-  auto phase1 = [&](auto SLOT, int blk) __attribute__((always_inline)) {
-    const int kb = key_base + blk * kBK;
-    if (kb > w_last) return;
+  // S^T of the first tile (both 32-key halves) into s, starting from c0; K
+  // fragments two steps ahead, kept in that order by the scheduling barriers
+  auto qk = [&](auto SLOT, floatx16 (&s)[2], float c0) __attribute__((always_inline)) {
     const char *St = slot_ptr(SLOT);
-    // S^T[key][column] - m for both 32-key halves, two independent MFMA chains
-    const float c0 = first ? 0.f : -m;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) { s[0][e] = c0; s[1][e] = c0; }
-    // the two 32-key halves one after the other, so the first half's max runs on
-    // the VALU while the second half's MFMAs run. K fragments are read two steps
-    // ahead of their MFMAs; the scheduling barriers keep the compiler from sinking
-    // each read next to its use (every MFMA would wait a whole LDS round trip),
-    // and the empty asm keeps the first half's max from sinking below the loop
-    constexpr int KPF = 3, NS = D / 16;
-    bf16x8 kf[KPF];
     auto kfrag = [&](int t) __attribute__((always_inline)) {
       return *reinterpret_cast<const bf16x8 *>(St + koff[t % NS] + (t / NS) * 32 * (D * 2));
     };
 #pragma unroll
-    for (int p = 0; p < KPF - 1; ++p) kf[p] = kfrag(p);
+    for (int e = 0; e < 16; ++e) { s[0][e] = c0; s[1][e] = c0; }
+    bf16x8 kf[3];
+    kf[0] = kfrag(0);
+    kf[1] = kfrag(1);
     __builtin_amdgcn_sched_barrier(0);
-    auto max16 = [&](const floatx16 &v) __attribute__((always_inline)) {
-      float x = __builtin_fmaxf(v[0], v[1]);
-#pragma unroll
-      for (int e = 2; e < 16; e += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, v[e]), v[e + 1]);
-      return x;
-    };
-    float mx0 = 0.f;
 #pragma unroll
     for (int t = 0; t < 2 * NS; ++t) {
-      if (t + KPF - 1 < 2 * NS) kf[(t + KPF - 1) % KPF] = kfrag(t + KPF - 1);
-      __builtin_amdgcn_sched_barrier(0);
+      if (t + 2 < 2 * NS) kf[(t + 2) % 3] = kfrag(t + 2);
       const bf16x8 q8 = __builtin_bit_cast(bf16x8, qf[t % NS]);
-      if (t < NS) s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % KPF], q8, s[0], 0, 0, 0);
-      else s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % KPF], q8, s[1], 0, 0, 0);
-      if (t == NS) {
-        mx0 = max16(s[0]);  // runs under the second half's MFMAs
-        asm volatile("" : "+v"(mx0));
-      }
+      s[t / NS] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % 3], q8, s[t / NS], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+  };
+  // causal / request mask of the tile at kb, then the column max
+  auto mask_max = [&](floatx16 (&s)[2], int kb) __attribute__((always_inline)) {
     if (kb < key_start || kb + kBK - 1 > w_first) {
 #pragma unroll
       for (int hb = 0; hb < 2; ++hb)
@@ -234,113 +217,189 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
           if (krow > qrow || krow < key_start) s[hb][e] = -INFINITY;
         }
     }
-    float mx;
-    if (kb < key_start || kb + kBK - 1 > w_first) mx = __builtin_fmaxf(max16(s[0]), max16(s[1]));  // masked
-    else mx = __builtin_fmaxf(mx0, max16(s[1]));
-    mx = pair_max(mx);
-    if (first) {
-      // the first tile sets the reference max (it holds the request's first
-      // row, which every query sees, so mx is finite)
-      first = false;
-      m = mx;
+    float x = __builtin_fmaxf(s[0][0], s[0][1]);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) { s[0][e] -= mx; s[1][e] -= mx; }
-    } else {
-      const bool up = mx > 8.f;
-      if (__any(up)) {
-        const float dlt = up ? mx : 0.f;
-        const float alpha = __builtin_amdgcn_exp2f(-dlt);
-        m += dlt;
-        l *= alpha;
+    for (int e = 2; e < 16; e += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, s[0][e]), s[0][e + 1]);
 #pragma unroll
-        for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) { s[0][e] -= dlt; s[1][e] -= dlt; }
-      }
-    }
+    for (int e = 0; e < 16; e += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, s[1][e]), s[1][e + 1]);
+    return pair_max(x);
   };
-  auto phase2 = [&](auto SLOT, int blk) __attribute__((always_inline)) {
-    if (key_base + blk * kBK > w_last) return;
-    const char *St = slot_ptr(SLOT);
+  // lazy rescale after the max mx of the next tile (relative to m): only when it
+  // rises by more than 8, after the PV product of the current tile
+  auto rescale = [&](floatx16 (&s)[2], float mx) __attribute__((always_inline)) {
+    const bool up = mx > 8.f;
+    if (__any(up)) {
+      const float dlt = up ? mx : 0.f;
+      const float alpha = __builtin_amdgcn_exp2f(-dlt);
+      m += dlt;
 #pragma unroll
-    for (int hb = 0; hb < 2; ++hb) {
-      // probabilities in bf16 (the PV operand); the row sum uses the same
-      // rounded values. Elements 8hf..8hf+7 of the half are keys
-      // 16c + 8(j/4) + 4(l/32) + j%4 of k-step c = 2hb + hf: the order in which
-      // the V^T copy stores each 16-key group
+      for (int e = 0; e < 16; ++e) cneg[e] = -m;
+      l *= alpha;
 #pragma unroll
-      for (int hf = 0; hf < 2; ++hf) {
-        bf16x8 pf;
+      for (int b = 0; b < D / 32; ++b)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) pf[j] = (__bf16)__builtin_amdgcn_exp2f(s[hb][hf * 8 + j]);
+        for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const bf16x2 pr = {pf[2 * j], pf[2 * j + 1]};
-          l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
-        }
-        const int c = hb * 2 + hf;
-#pragma unroll
-        for (int b = 0; b < D / 32; ++b) {
-          const bf16x8 vf = *reinterpret_cast<const bf16x8 *>(St + voff[c] + b * 32 * 128);
-          acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf, acc[b], 0, 0, 0);
-        }
-      }
+      for (int e = 0; e < 16; ++e) { s[0][e] -= dlt; s[1][e] -= dlt; }
     }
-  };
-  // end of half-step h (h = -1: the prologue)
-  auto sync = [&](int h) __attribute__((always_inline)) {
-    if (h & 1) {
-      // the next half-step starts tile (h+1)/2: its copies must be complete;
-      // those of the tile after it may still be in flight
-      if ((h + 1) / 2 + 1 < nblk) wait_vmcnt<LOADS>();
-      else wait_vmcnt<0>();
-    }
-    __builtin_amdgcn_s_barrier();
-  };
-  auto issue_after = [&](auto SLOT, int h) __attribute__((always_inline)) {
-    // after the barrier ending even half-step h = 2j: copy tile j+2
-    if (h / 2 + 2 < nblk) issue(SLOT, h / 2 + 2);
   };
 
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using I3 = std::integral_constant<int, 3>;
+  using I4 = std::integral_constant<int, 4>;
+  floatx16 sa[2], sb[2];
+  // tiles 0-3 in flight; 0 and 1 are read before the first barrier of the loop
   issue(I0{}, 0);
   if (nblk > 1) issue(I1{}, 1);
-  sync(-1);
-  const bool lead = w < kAW / 2;
-  if (!lead) {
-    sync(0);
-    issue_after(I2{}, 0);
+  if (nblk > 2) issue(I2{}, 2);
+  if (nblk > 3) issue(I3{}, 3);
+  if (nblk > 3) wait_vmcnt<2 * LOADS>();
+  else if (nblk > 2) wait_vmcnt<LOADS>();
+  else wait_vmcnt<0>();
+  __builtin_amdgcn_s_barrier();
+  if (nact > 0) {
+    // the first tile sets the reference max (it holds the request's first row,
+    // which every query sees, so the max is finite)
+    qk(I0{}, sa, 0.f);
+    const float mx = mask_max(sa, key_base);
+    m = mx;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) cneg[e] = -m;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) { sa[0][e] -= mx; sa[1][e] -= mx; }
   }
-  // tile j uses slot j % 3; the loop is unrolled by three so slots are
-  // constants. Both groups run the same phase code; only the barrier
-  // bookkeeping between phases depends on the group (waves 0-3 end half-steps
-  // 2j and 2j+1 around tile j, waves 4-7 end 2j+1 and 2j+2).
-  auto tile = [&](auto SLOT, int j) __attribute__((always_inline)) {
-    constexpr int sl = decltype(SLOT)::value;
-    using NEXT2 = std::integral_constant<int, (sl + 2) % 3>;
-    using NEXT3 = std::integral_constant<int, (sl + 3) % 3>;
-    phase1(SLOT, j);
-    if (lead) {
-      sync(2 * j);
-      issue_after(NEXT2{}, 2 * j);
-    } else {
-      sync(2 * j + 1);
-    }
-    phase2(SLOT, j);
-    if (lead) {
-      sync(2 * j + 1);
-    } else {
-      sync(2 * j + 2);
-      issue_after(NEXT3{}, 2 * j + 2);
+  // One step of the overlapped part of iteration j: the MFMA of step t, then
+  // VALU work that does not depend on it, with fragment reads PFD steps ahead;
+  // the scheduling barriers keep that order (the compiler would otherwise move
+  // every LDS read to the top and run out of registers).
+  // Part 1: the score MFMAs of tile j+1 (chain 0 for keys 0-31, chain 1 for keys
+  // 32-63) with the probabilities of tile j: step t exponentiates elements
+  // 2(t%4), 2(t%4)+1 of k-step c = t/4 (half c/2, elements 8(c%2)+...).
+  auto part1 = [&](auto NSLOT, floatx16 (&cur)[2], floatx16 (&nxt)[2], u32x4 (&pw)[4])
+      __attribute__((always_inline)) {
+    const char *St = slot_ptr(NSLOT);
+    auto kfrag = [&](int t) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8 *>(St + koff[t % NS] + (t / NS) * 32 * (D * 2));
+    };
+    bf16x8 kf[PFD + 1];
+#pragma unroll
+    for (int t = 0; t < PFD; ++t) kf[t] = kfrag(t);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < 2 * NS; ++t) {
+      if (t + PFD < 2 * NS) kf[(t + PFD) % (PFD + 1)] = kfrag(t + PFD);
+      const bf16x8 q8 = __builtin_bit_cast(bf16x8, qf[t % NS]);
+      // each chain starts from -m held in registers (no per-tile initialisation)
+      nxt[t / NS] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (PFD + 1)], q8, t % NS == 0 ? cneg : nxt[t / NS], 0, 0, 0);
+      // VALU share of this step (16 steps of D = 128; D = 64 has 8, two shares each)
+#pragma unroll
+      for (int u = 0; u < 16 / (2 * NS); ++u) {
+        const int v = t * (16 / (2 * NS)) + u;  // 0..15
+        const int c = v / 4, jj = 2 * (v % 4);
+        const bf16x2 pr = {(__bf16)__builtin_amdgcn_exp2f(cur[c / 2][(c % 2) * 8 + jj]),
+                           (__bf16)__builtin_amdgcn_exp2f(cur[c / 2][(c % 2) * 8 + jj + 1])};
+        uint32_t word = __builtin_bit_cast(uint32_t, pr);
+        l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+        // the empty asm pins the work to this step (it would otherwise sink to
+        // its first use, the PV MFMAs)
+        asm volatile("" : "+v"(word), "+v"(l));
+        pw[c][v % 4] = word;
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
   };
-  for (int j0 = 0; j0 < nblk; j0 += 3) {
-    tile(I0{}, j0);
-    if (j0 + 1 < nblk) tile(I1{}, j0 + 1);
-    if (j0 + 2 < nblk) tile(I2{}, j0 + 2);
+  // Part 2: the PV MFMAs of tile j with the column max of tile j+1 (masked first
+  // when the tile needs it)
+  auto part2 = [&](auto SLOT, floatx16 (&nxt)[2], const u32x4 (&pw)[4], int kb_next)
+      __attribute__((always_inline)) {
+    const char *St = slot_ptr(SLOT);
+    auto vfrag = [&](int t) __attribute__((always_inline)) {
+      return *reinterpret_cast<const bf16x8 *>(St + voff[t / (D / 32)] + (t % (D / 32)) * 32 * 128);
+    };
+    if (kb_next < key_start || kb_next + kBK - 1 > w_first) {
+#pragma unroll
+      for (int hb = 0; hb < 2; ++hb)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const int krow = kb_next + hb * 32 + (e >> 2) * 8 + gph * 4 + (e & 3);
+          if (krow > qrow || krow < key_start) nxt[hb][e] = -INFINITY;
+        }
+    }
+    constexpr int NPV = 4 * (D / 32);  // PV MFMAs per tile
+    bf16x8 vf[PFD + 1];
+#pragma unroll
+    for (int t = 0; t < PFD; ++t) vf[t] = vfrag(t);
+    float x = -INFINITY;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int t = 0; t < NPV; ++t) {
+      if (t + PFD < NPV) vf[(t + PFD) % (PFD + 1)] = vfrag(t + PFD);
+      const int b = t % (D / 32);
+      acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t % (PFD + 1)], __builtin_bit_cast(bf16x8, pw[t / (D / 32)]),
+                                                       acc[b], 0, 0, 0);
+#pragma unroll
+      for (int u = 0; u < 32 / NPV; u += 2) {
+        const int v = t * (32 / NPV) + u;  // 0..31
+        x = __builtin_fmaxf(x, __builtin_fmaxf(nxt[v / 16][v % 16], nxt[v / 16][v % 16 + 1]));
+      }
+      asm volatile("" : "+v"(x));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    return pair_max(x);
+  };
+  // iteration j: tile j's scores are in `cur`, tile j+1's go to `nxt`. A wave's
+  // last tile runs the same code (its score MFMAs read a stale slot and their
+  // results are dropped): one straight-line body keeps the compiler from
+  // merging the two paths' exponentials ahead of the MFMAs.
+  // Barrier b_j ends iteration j (for waves 0-3; waves 4-7 meet it between
+  // their two parts); before it every wave waits for its copies of tile j+2,
+  // after it tile j+4 is issued into the slot of tile j-1, which no wave reads
+  // after b_j.
+  auto barrier_after = [&](int j) __attribute__((always_inline)) {
+    if (j + 3 < nblk) wait_vmcnt<LOADS>();
+    else wait_vmcnt<0>();
+    __builtin_amdgcn_s_barrier();
+  };
+  const bool lead = w < kAW / 2;
+  auto iter = [&](auto SLOT, int j, floatx16 (&cur)[2], floatx16 (&nxt)[2]) __attribute__((always_inline)) {
+    constexpr int sl = decltype(SLOT)::value;
+    using NEXT = std::integral_constant<int, (sl + 1) % NSL>;
+    using FREE3 = std::integral_constant<int, (sl + 3) % NSL>;
+    using FREE4 = std::integral_constant<int, (sl + 4) % NSL>;
+    // Waves 4-7 run half an iteration behind: their barrier b_j falls between
+    // the score MFMAs of tile j+1 and the PV MFMAs of tile j, so on each SIMD one
+    // wave's exponentials overlap the other's PV product. They issue tile j+4
+    // right after b_j; waves 0-3 issue it at the start of iteration j+1.
+    const bool second = !lead;
+    if (!second && j >= 1 && j + 3 < nblk) issue(FREE3{}, j + 3);
+    u32x4 pw[4];
+    if (j < nact) part1(NEXT{}, cur, nxt, pw);
+    if (second && j + 1 < nblk) {
+      barrier_after(j);
+      if (j + 4 < nblk) issue(FREE4{}, j + 4);
+    }
+    if (j < nact) {
+      const float mx = part2(SLOT, nxt, pw, key_base + (j + 1) * kBK);
+      if (j + 1 < nact) rescale(nxt, mx);
+    }
+    if (!second && j + 1 < nblk) barrier_after(j);
+  };
+  // unrolled by ten so slots and score buffers are both constants
+  for (int j0 = 0; j0 < nblk; j0 += 10) {
+    iter(I0{}, j0, sa, sb);
+    if (j0 + 1 < nblk) iter(I1{}, j0 + 1, sb, sa);
+    if (j0 + 2 < nblk) iter(I2{}, j0 + 2, sa, sb);
+    if (j0 + 3 < nblk) iter(I3{}, j0 + 3, sb, sa);
+    if (j0 + 4 < nblk) iter(I4{}, j0 + 4, sa, sb);
+    if (j0 + 5 < nblk) iter(I0{}, j0 + 5, sb, sa);
+    if (j0 + 6 < nblk) iter(I1{}, j0 + 6, sa, sb);
+    if (j0 + 7 < nblk) iter(I2{}, j0 + 7, sb, sa);
+    if (j0 + 8 < nblk) iter(I3{}, j0 + 8, sa, sb);
+    if (j0 + 9 < nblk) iter(I4{}, j0 + 9, sb, sa);
   }
-  if (lead) sync(2 * nblk);
 
   const float lt = pair_sum(l);
   if (cvalid) {
