@@ -266,7 +266,7 @@ constexpr int kMaxSplit = 8;
 struct SplitPlan {
   int tiles, full, tail, split;  // T, tiles run whole, tail tiles, pieces per tail tile
 };
-__device__ __forceinline__ SplitPlan split_plan(int tiles, int grid, int part_cap) {
+__host__ __device__ inline SplitPlan split_plan(int tiles, int grid, int part_cap) {
   SplitPlan sp{tiles, tiles, 0, 1};
   const int tail = tiles % grid;
   if (tail == 0 || part_cap <= 0) return sp;
@@ -434,9 +434,10 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
   }
 }
 
-// Finishes the split tail tiles: work-group = (tail tile, 32-row block); adds
-// the tile's K-piece partials and runs the epilogue on them.
-constexpr int kFixRows = 32;
+// Finishes the split tail tiles, one item (tail tile, block of 16 rows) at a
+// time: adds the tile's K-piece partials and runs the epilogue on them. Small
+// items keep many work-groups busy on a few tail tiles.
+constexpr int kFixRows = 16;
 
 // Cs[r][c] = sum over the split pieces of part[piece][r][c] for kFixRows rows of BN
 // columns, 4 columns per thread and step (256 threads).
@@ -479,29 +480,35 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
   const int M = g.M_dev ? *g.M_dev : g.M_host;
   const int mt_n = (M + C::BM - 1) / C::BM, nt_n = (g.N + C::BN - 1) / C::BN;
   const SplitPlan sp = split_plan(mt_n * nt_n, g.grid_main, g.part_cap);
+  if (sp.split < 2) return;
   constexpr int RB = C::BM / kFixRows;
-  const int ti = blockIdx.x / RB, rb = blockIdx.x - ti * RB;
-  if (sp.split < 2 || ti >= sp.tail) return;
-  const int tile = sp.full + ti;
-  int mt, nt;
-  TileMap(mt_n, nt_n, sp.full, g.grid_main).mn(tile, mt, nt);
-  const int m0 = mt * C::BM + rb * kFixRows, n0 = nt * C::BN;
-  if (m0 >= M) return;
-  load_row_meta<MODE, kFixRows>(meta, m0, M, g);
-  // sum of the pieces into Cs: the loads of NS slots (NS = the split rounded up to
-  // 2, 4 or 8; slots past the split clamped to a valid one and weighted 0) and of two
-  // column groups are issued together, so the sum waits for one round trip
-  const float *base = g.part + (size_t)ti * sp.split * kGemmPartFloats + (size_t)rb * kFixRows * C::BN;
-  if (sp.split <= 2)
-    fix_sum<2, C::BN, LDC>(base, sp.split, Cs);
-  else if (sp.split <= 4)
-    fix_sum<4, C::BN, LDC>(base, sp.split, Cs);
-  else
-    fix_sum<kMaxSplit, C::BN, LDC>(base, sp.split, Cs);
-  __syncthreads();
+  const TileMap tm(mt_n, nt_n, sp.full, g.grid_main);
+  // items (tail tile, block of kFixRows rows), strided over the grid
 #pragma unroll 1
-  for (int cb = 0; cb < C::BN / kBN; ++cb)
-    epilogue<uint16_t, kFixRows, MODE, 256, 2>(Cs + cb * kBN, LDC, meta, m0, n0 + cb * kBN, g);
+  for (int item = blockIdx.x; item < sp.tail * RB; item += gridDim.x) {
+    const int ti = item / RB, rb = item - ti * RB;
+    const int tile = sp.full + ti;
+    int mt, nt;
+    tm.mn(tile, mt, nt);
+    const int m0 = mt * C::BM + rb * kFixRows, n0 = nt * C::BN;
+    if (m0 >= M) continue;
+    __syncthreads();  // the previous item's epilogue no longer reads meta or Cs
+    load_row_meta<MODE, kFixRows>(meta, m0, M, g);
+    // sum of the pieces into Cs: the loads of NS slots (NS = the split rounded up to
+    // 2, 4 or 8; slots past the split clamped to a valid one and weighted 0) and of two
+    // column groups are issued together, so the sum waits for one round trip
+    const float *base = g.part + (size_t)ti * sp.split * kGemmPartFloats + (size_t)rb * kFixRows * C::BN;
+    if (sp.split <= 2)
+      fix_sum<2, C::BN, LDC>(base, sp.split, Cs);
+    else if (sp.split <= 4)
+      fix_sum<4, C::BN, LDC>(base, sp.split, Cs);
+    else
+      fix_sum<kMaxSplit, C::BN, LDC>(base, sp.split, Cs);
+    __syncthreads();
+#pragma unroll 1
+    for (int cb = 0; cb < C::BN / kBN; ++cb)
+      epilogue<uint16_t, kFixRows, MODE, 256, 1>(Cs + cb * kBN, LDC, meta, m0, n0 + cb * kBN, g);
+  }
 }
 
 // 256x256 tiles, 8 waves of 128x64, two 64-deep ring slots (128 KB), one
@@ -607,9 +614,21 @@ hipError_t launch_gemm(const GemmArgs &g0, hipStream_t s) {
   g.grid_main = (int)grid;
   if (!bf || !g.part) g.part_cap = 0;
   const dim3 gr((unsigned)grid), bl(bf ? C::THREADS : 256);
-  // fix-up grid: every tail tile a split can produce (at most part_cap / 2)
-  const long fix_tiles = g.part_cap / 2 < tiles ? g.part_cap / 2 : tiles;
-  const dim3 fgr((unsigned)(fix_tiles > 0 ? fix_tiles * (C::BM / kFixRows) : 1));
+  // fix-up: with M known here the split plan is known too (no launch without a
+  // split, one work-group per item); with M on the device, 256 work-groups
+  // stride over whatever items the plan has
+  long fix_items = 0;
+  if (bf && g.part_cap > 0) {
+    if (!g.M_dev) {
+      const int mt_n = (g.M_host + C::BM - 1) / C::BM, nt_n = (g.N + C::BN - 1) / C::BN;
+      const SplitPlan sp = split_plan(mt_n * nt_n, (int)grid, g.part_cap);
+      fix_items = sp.split < 2 ? 0 : (long)sp.tail * (C::BM / kFixRows);
+    } else {
+      fix_items = 256;
+    }
+  }
+  const long fix_tiles = fix_items;
+  const dim3 fgr((unsigned)(fix_items > 0 ? (fix_items < 256 ? fix_items : 256) : 1));
 #define SRP_GEMM_LAUNCH(M)                                                     \
   if (bf) {                                                                    \
     hipLaunchKernelGGL((gemm_bf16_kernel<M, C>), gr, bl, 0, s, g);             \
