@@ -490,6 +490,101 @@ __device__ void lds_mark_top(const uint32_t *keys, uint8_t *fl, int n, uint8_t i
   __syncthreads();
 }
 
+// The same top-k marking with this thread's keys in registers: kr[j] is the key
+// of entry tid + j * blockDim.x and bit j of cmask says whether that entry is
+// flagged in_bit. Minimum, maximum, histograms and marks read no LDS; ties at
+// the threshold fall back to the ordered walk over the LDS copy of the keys.
+template <int PER>
+__device__ void reg_mark_top(const uint32_t (&kr)[PER], uint32_t cmask, const uint32_t *keys, uint8_t *fl,
+                             int n, uint8_t in_bit, uint8_t out_bit, int k, int n_in, int *hist,
+                             int *sh, int *digit_info) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  if (k >= n_in) {
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (cmask >> j & 1u) fl[tid + j * nt] |= out_bit;
+  } else if (k > 0) {
+    uint32_t kmin = 0xffffffffu, kmax = 0u;
+#pragma unroll
+    for (int j = 0; j < PER; ++j)
+      if (cmask >> j & 1u) {
+        kmin = kr[j] < kmin ? kr[j] : kmin;
+        kmax = kr[j] > kmax ? kr[j] : kmax;
+      }
+    block_minmax(kmin, kmax, hist, hist + 32);
+    const uint32_t diff = kmin ^ kmax;
+    int rem = diff ? 32 - __clz(diff) : 0;
+    uint32_t pmask = rem == 32 ? 0u : ~((1u << rem) - 1u);
+    uint32_t prefix = kmin & pmask;
+    int need = k;
+    while (rem > 0) {
+      const int width = rem < 12 ? rem : 12;
+      const int shift = rem - width;
+      const int nb = 1 << width;
+      const uint32_t dmask = (uint32_t)nb - 1u;
+      for (int b = tid; b < nb; b += nt) hist[b] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if ((cmask >> j & 1u) && (kr[j] & pmask) == prefix) atomicAdd(&hist[(kr[j] >> shift) & dmask], 1);
+      __syncthreads();
+      int c[4], s4 = 0;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int dg = nb - 1 - 4 * tid - q;
+        c[q] = dg >= 0 ? hist[dg] : 0;
+        s4 += c[q];
+      }
+      int tot;
+      const int above = block_excl_scan(s4, sh, &tot);
+      if (above < need && above + s4 >= need) {
+        int abv = above, dsel = 0;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          if (abv + c[q] >= need) { dsel = nb - 1 - 4 * tid - q; break; }
+          abv += c[q];
+        }
+        digit_info[0] = dsel;
+        digit_info[1] = abv;
+      }
+      __syncthreads();
+      need -= digit_info[1];
+      prefix |= (uint32_t)digit_info[0] << shift;
+      pmask |= dmask << shift;
+      rem = shift;
+      __syncthreads();
+    }
+    int my_eq = 0;
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      if (!(cmask >> j & 1u)) continue;
+      if (kr[j] > prefix) fl[tid + j * nt] |= out_bit;
+      else if (kr[j] == prefix) ++my_eq;
+    }
+    const int eq_tot = block_sum(my_eq, sh);
+    if (eq_tot == need) {
+#pragma unroll
+      for (int j = 0; j < PER; ++j)
+        if ((cmask >> j & 1u) && kr[j] == prefix) fl[tid + j * nt] |= out_bit;
+    } else {
+      // several equal keys at the threshold: the first `need` in entry order
+      __syncthreads();
+      int lo, hi;
+      my_segment(n, lo, hi);
+      int c = 0;
+      for (int i = lo; i < hi; ++i) c += ((fl[i] & in_bit) && keys[i] == prefix) ? 1 : 0;
+      int t;
+      int rank = block_excl_scan(c, sh, &t);
+      for (int i = lo; i < hi; ++i)
+        if ((fl[i] & in_bit) && keys[i] == prefix) {
+          if (rank < need) fl[i] |= out_bit;
+          ++rank;
+        }
+    }
+  }
+  __syncthreads();
+}
+
 // Inclusive max-scan over the wave with DPP lane shifts (INT_MIN fills lanes
 // without a source, the identity of max).
 __device__ __forceinline__ int wave_incl_max(int v) {
@@ -583,25 +678,23 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
   const int *roff = a.listed ? w.roff : a.req_offsets;
   const int e0 = roff[r], e1 = roff[r + 1], n = e1 - e0;
 
+  // entry tid + j * nt of the request: flags to LDS, keys to LDS and registers
+  constexpr int PER = (kLdsEntries + 1023) / 1024;
+  uint32_t kr[PER];
+  uint32_t cmask = 0;
   int my_cand = 0;
-  for (int i = tid; i < n; i += 4 * nt) {
-    // four independent loads of flags and keys per thread before any store
-    uint8_t f[4];
-    uint32_t k4[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = i + u * nt;
-      f[u] = j < n ? w.eflag[e0 + j] : 0;
-      k4[u] = j < n ? w.keys[e0 + j] : 0u;
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = i + u * nt;
-      if (j < n) {
-        fl_s[j] = f[u];
-        keys_s[j] = (f[u] & kCand) ? k4[u] : 0u;
-        my_cand += (f[u] & kCand) ? 1 : 0;
-      }
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + j * nt;
+    const uint8_t f = i < n ? w.eflag[e0 + i] : 0;
+    const uint32_t key = i < n ? w.keys[e0 + i] : 0u;
+    const bool cand = (f & kCand) != 0;
+    kr[j] = cand ? key : 0u;
+    cmask |= (cand ? 1u : 0u) << j;
+    my_cand += cand ? 1 : 0;
+    if (i < n) {
+      fl_s[i] = f;
+      keys_s[i] = kr[j];
     }
   }
   int my_ctx = 0;
@@ -614,7 +707,8 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
   const int n_ctx = block_sum(my_ctx, sh);
 
   const int k = a.mode == SRP_SEL_GIVEN ? n_cand : k_from_ratio(a.ratio, n_ctx, n_cand, a.k_ceil);
-  lds_mark_top(keys_s, fl_s, n, kCand, kTop, k, n_cand, hist, sh, digit_info);
+  __syncthreads();  // flags and keys in LDS (the tie fallback and the grouping read them)
+  reg_mark_top<PER>(kr, cmask, keys_s, fl_s, n, kCand, kTop, k, n_cand, hist, sh, digit_info);
 
   if (a.window > 0)
     lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, sh);
