@@ -615,8 +615,8 @@ hipError_t launch_gemm(const GemmArgs &g0, hipStream_t s) {
   if (!bf || !g.part) g.part_cap = 0;
   const dim3 gr((unsigned)grid), bl(bf ? C::THREADS : 256);
   // fix-up: with M known here the split plan is known too (no launch without a
-  // split, one work-group per item); with M on the device, 256 work-groups
-  // stride over whatever items the plan has
+  // split); with M on the device, as many items as the plan can have for M_cap
+  // rows. Up to 1024 work-groups stride over the items.
   long fix_items = 0;
   if (bf && g.part_cap > 0) {
     if (!g.M_dev) {
@@ -624,11 +624,11 @@ hipError_t launch_gemm(const GemmArgs &g0, hipStream_t s) {
       const SplitPlan sp = split_plan(mt_n * nt_n, (int)grid, g.part_cap);
       fix_items = sp.split < 2 ? 0 : (long)sp.tail * (C::BM / kFixRows);
     } else {
-      fix_items = 256;
+      fix_items = (g.part_cap / 2 < tiles ? g.part_cap / 2 : tiles) * (C::BM / kFixRows);
     }
   }
   const long fix_tiles = fix_items;
-  const dim3 fgr((unsigned)(fix_items > 0 ? (fix_items < 256 ? fix_items : 256) : 1));
+  const dim3 fgr((unsigned)(fix_items > 0 ? (fix_items < 1024 ? fix_items : 1024) : 1));
 #define SRP_GEMM_LAUNCH(M)                                                     \
   if (bf) {                                                                    \
     hipLaunchKernelGGL((gemm_bf16_kernel<M, C>), gr, bl, 0, s, g);             \
