@@ -327,8 +327,6 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
     SRP_HIP(launch_gather_rows(T, (size_t)kvd * es, w.row_slot, v_cache, w.v_lin, s));
     v_att = w.v_lin;
   }
-  if (d.dtype == SRP_BF16 && T > 0)
-    SRP_HIP(launch_v_transpose(T, d.n_kv_heads, d.head_dim, v_cache, w.row_slot, w.vt, vt_stride(T), s));
   marks.mark(4);
   // 6. Q projection of the selected rows (with V-only deviation also their fresh
   //    keys, straight into the cache)
@@ -341,6 +339,16 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   gq.q_out = w.q;
   // bf16 attention works in base 2 on pre-scaled queries; the fp32 kernel scales itself
   gq.q_scale = d.dtype == SRP_BF16 ? (float)(1.4426950408889634 / std::sqrt((double)d.head_dim)) : 1.0f;
+  if (d.dtype == SRP_BF16 && T > 0) {
+    // the work-groups the projection leaves idle transpose the fused V (the
+    // selection's finalize zeroed the chunk counter)
+    gq.vt_src = v_cache;
+    gq.vt_slot = w.row_slot;
+    gq.vt_dst = w.vt;
+    gq.vt_T = T;
+    gq.vt_stride = vt_stride(T);
+    gq.vt_ctr = w.ctr + kCtrVtChunks;
+  }
   SRP_HIP(launch_gemm(gq, s));
   if (w.row_slot && T > 0) {
     // the fused keys are final only now

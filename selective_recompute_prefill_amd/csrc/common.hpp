@@ -213,6 +213,7 @@ constexpr size_t kGemmPartFloats = 256 * 256;
 constexpr int kCtrTotalSel = 0;
 constexpr int kCtrTiles = 1;
 constexpr int kCtrREntries = 2;
+constexpr int kCtrVtChunks = 3;  // V transpose chunks claimed (zeroed by the selection's finalize)
 
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
@@ -221,6 +222,42 @@ inline int max_attn_tiles(int T, int n_req) { return T / kQT + n_req + 1; }
 // Row stride of the transposed V copy: T rounded up to 64 plus one zeroed tile, so
 // a key tile that starts inside the batch never reads past the copy.
 inline int vt_stride(int T) { return (T + 63) / 64 * 64 + 64; }
+
+// One chunk of the transposed V copy for the attention's DMA loads: keys
+// r0..r0+63 of KV head g, with NT threads and a 128 x 66 u16 LDS tile. Row i of
+// head g holds vt[g][i][j] = v[slot(j)][g][i] (slot(j) = row_slot[j], or j when
+// row_slot is NULL); inside every 16-key group the keys are stored in the order
+// 0-3, 8-11, 4-7, 12-15 (the PV operand's lane order); keys at or past T are zero.
+template <int NT>
+__device__ __forceinline__ void vt_chunk(int r0, int g, int T, int D, int nkv, const uint16_t *v,
+                                         const int32_t *row_slot, uint16_t *vt, int vts,
+                                         uint16_t (*tile)[66]) {
+  typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x, kvd = nkv * D, dch = D / 8;
+  for (int c = tid; c < 64 * dch; c += NT) {
+    const int key = c / dch, dc = c - key * dch;
+    const int row = r0 + key;
+    u32x4_t x = {0, 0, 0, 0};
+    if (row < T)
+      x = *reinterpret_cast<const u32x4_t *>(v + (size_t)(row_slot ? row_slot[row] : row) * kvd + g * D + dc * 8);
+    // stored position of this key: swap bits 2 and 3 of its index
+    const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      tile[dc * 8 + 2 * i][pos] = (uint16_t)(x[i] & 0xffffu);
+      tile[dc * 8 + 2 * i + 1][pos] = (uint16_t)(x[i] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < D * 8; c += NT) {
+    const int dd = c >> 3, kc = c & 7;
+    u32x4_t y;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      y[i] = (uint32_t)tile[dd][kc * 8 + 2 * i] | ((uint32_t)tile[dd][kc * 8 + 2 * i + 1] << 16);
+    *reinterpret_cast<u32x4_t *>(vt + ((size_t)g * D + dd) * vts + r0 + kc * 8) = y;
+  }
+}
 
 // Lays the workspace out from `base` (nullptr: just measure).
 inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base) {

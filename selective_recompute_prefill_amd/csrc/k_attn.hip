@@ -417,46 +417,6 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   }
 }
 
-// V transposed for the attention's DMA loads: block (64-row tile, KV head).
-// Inside every 16-key group the keys are stored in the order 0-3, 8-11, 4-7,
-// 12-15 (the PV operand's lane order); keys at or past T are zero.
-__global__ __launch_bounds__(256) void v_transpose_kernel(int T, int D, int nkv, const uint16_t *v,
-                                                         const int32_t *row_slot, uint16_t *vt, int vts) {
-  __shared__ uint16_t tile[128][64 + 2];
-  const int r0 = blockIdx.x * 64, g = blockIdx.y, tid = threadIdx.x;
-  const int kvd = nkv * D, dch = D / 8;
-  for (int c = tid; c < 64 * dch; c += 256) {
-    const int key = c / dch, dc = c - key * dch;
-    const int row = r0 + key;
-    u32x4 x = {0, 0, 0, 0};
-    if (row < T)
-      x = *reinterpret_cast<const u32x4 *>(v + (size_t)(row_slot ? row_slot[row] : row) * kvd + g * D + dc * 8);
-    // stored position of this key: swap bits 2 and 3 of its index
-    const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile[dc * 8 + 2 * i][pos] = (uint16_t)(x[i] & 0xffffu);
-      tile[dc * 8 + 2 * i + 1][pos] = (uint16_t)(x[i] >> 16);
-    }
-  }
-  __syncthreads();
-  for (int c = tid; c < D * 8; c += 256) {
-    const int dd = c >> 3, kc = c & 7;
-    u32x4 y;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      y[i] = (uint32_t)tile[dd][kc * 8 + 2 * i] | ((uint32_t)tile[dd][kc * 8 + 2 * i + 1] << 16);
-    *reinterpret_cast<u32x4 *>(vt + ((size_t)g * D + dd) * vts + r0 + kc * 8) = y;
-  }
-}
-
-hipError_t launch_v_transpose(int T, int nkv, int d, const void *v_cache, const int32_t *row_slot,
-                              void *vt, int vt_stride, hipStream_t s) {
-  hipLaunchKernelGGL(v_transpose_kernel, dim3((unsigned)(vt_stride / 64), (unsigned)nkv), dim3(256),
-                     0, s, T, d, nkv, (const uint16_t *)v_cache, row_slot, (uint16_t *)vt, vt_stride);
-  return hipGetLastError();
-}
-
 // fp32 variant: one wave per head, one query at a time, one key per lane.
 template <int D>
 __global__ __launch_bounds__(512) void attn_f32_kernel(AttnArgs a) {

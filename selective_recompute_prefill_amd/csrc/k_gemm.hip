@@ -432,6 +432,28 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
     }
     __syncthreads();
   }
+
+  // 3. the Q projection leaves work-groups without tiles (fewer tiles than CUs)
+  //    or finishing early: they build the attention's transposed V copy, chunks
+  //    (64 keys, KV head) claimed from a counter, so it runs on otherwise idle CUs
+  if constexpr (MODE == EPI_Q || MODE == EPI_QK) {
+    if (g.vt_dst) {
+      __shared__ int claim;
+      const int rows_n = g.vt_stride / 64, n_chunks = rows_n * g.nkv;
+      auto tile = reinterpret_cast<uint16_t (*)[66]>(smem);
+      static_assert(128 * 66 * 2 <= C::SMEM, "the transpose tile fits the ring");
+      for (;;) {
+        if (tid == 0) claim = atomicAdd(g.vt_ctr, 1);
+        __syncthreads();
+        const int c = claim;
+        if (c >= n_chunks) break;
+        const int hg = c / rows_n;
+        vt_chunk<C::THREADS>((c - hg * rows_n) * 64, hg, g.vt_T, g.d, g.nkv, (const uint16_t *)g.vt_src,
+                             g.vt_slot, (uint16_t *)g.vt_dst, g.vt_stride, tile);
+        __syncthreads();  // the tile and `claim` are reused by the next chunk
+      }
+    }
+  }
 }
 
 // Finishes the split tail tiles, one item (tail tile, block of 16 rows) at a

@@ -335,6 +335,7 @@ __device__ void finalize_body(const SelectArgs &a, const Workspace &w, int32_t *
     tpre[nr] = tcarry;
     w.ctr[kCtrTotalSel] = carry;
     w.ctr[kCtrTiles] = tcarry;
+    w.ctr[kCtrVtChunks] = 0;
   }
   __threadfence_block();
   __syncthreads();

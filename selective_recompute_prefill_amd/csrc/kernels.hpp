@@ -44,6 +44,14 @@ struct GemmArgs {
   float *part;    // bf16: fp32 partial tiles of split tail tiles (kGemmPartFloats each), or NULL
   int part_cap;   // partial-tile slots at `part`
   int grid_main;  // set by launch_gemm: work-groups of the main kernel
+  // EPI_Q / EPI_QK (bf16): the transposed V copy for the attention, built by
+  // work-groups with no tile left (chunks claimed through vt_ctr, which must be
+  // zero at launch); vt_dst NULL: none
+  const void *vt_src;        // fused V cache
+  const int32_t *vt_slot;    // cache row of each batch row (paged), or NULL
+  void *vt_dst;              // [nkv][d][vt_stride]
+  int vt_T, vt_stride;
+  int32_t *vt_ctr;
 };
 hipError_t launch_gemm(const GemmArgs &g, hipStream_t s);
 
@@ -122,10 +130,6 @@ struct AttnArgs {
   void *out;               // [n_sel][nh][d]
 };
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
-// bf16: vt[g][i][j] = v_cache[slot(j)][g][i] for j < T (slot(j) = row_slot[j], or j
-// when row_slot is NULL), zero for T <= j < vt_stride.
-hipError_t launch_v_transpose(int T, int nkv, int d, const void *v_cache, const int32_t *row_slot,
-                              void *vt, int vt_stride, hipStream_t s);
 // Selected rows per attention tile for this shape (a multiple of 32).
 int attn_tile_rows(int dtype, int nh, int nkv);
 
