@@ -95,6 +95,8 @@ def algorithmic_work(spec, lay, sel, ratio_rows):
         req_start[lay.req_offsets[r]:lay.req_offsets[r + 1]] = lay.req_offsets[r]
     pairs = int((sel - req_start[sel] + 1).sum()) if n_sel else 0
     prep = T * 4 * 3 + (T * 4 if ratio_rows.get("scores") else 0) + e * 2 * (n_ctx - n_rc) * kvd
+    # bf16: the Q projection's idle work-groups also build the transposed V copy
+    vt = e * 2 * T * kvd if spec.dtype == "bf16" else 0
     if ratio_rows.get("v_only"):
         # V of the candidates only; every cached key is re-rotated in the prepare
         # stage and the selection's keys come out of the Q projection
@@ -106,7 +108,7 @@ def algorithmic_work(spec, lay, sel, ratio_rows):
             "select": {"bytes": n_rec * 2 * spec.n_kv_heads * 4 + n_rec * 4 * 4},
             "scatter": {"bytes": e * 2 * n_sel * kvd},
             "q_proj": {"flops": 2.0 * n_sel * H * (qd + kvd),
-                       "bytes": e * (n_sel * H + (qd + kvd) * H + n_sel * (qd + kvd))},
+                       "bytes": e * (n_sel * H + (qd + kvd) * H + n_sel * (qd + kvd)) + vt},
             "attention": {"flops": 4.0 * spec.n_heads * spec.head_dim * pairs,
                           "bytes": e * (n_sel * qd * 2 + 2 * n_ctx * kvd), "pairs": pairs},
         }
@@ -117,7 +119,7 @@ def algorithmic_work(spec, lay, sel, ratio_rows):
                     "bytes": e * (n_rec * H + 2 * kvd * H + 2 * n_rc * kvd + n_rc * kvd + 2 * n_rec * kvd)},
         "select": {"bytes": n_rec * 2 * spec.n_kv_heads * 4 + n_rec * 4 * 4},
         "scatter": {"bytes": e * 2 * n_sel * 2 * kvd},
-        "q_proj": {"flops": 2.0 * n_sel * H * qd, "bytes": e * (n_sel * H + qd * H + n_sel * qd)},
+        "q_proj": {"flops": 2.0 * n_sel * H * qd, "bytes": e * (n_sel * H + qd * H + n_sel * qd) + vt},
         "attention": {"flops": 4.0 * spec.n_heads * spec.head_dim * pairs,
                       "bytes": e * (n_sel * qd * 2 + 2 * n_ctx * kvd), "pairs": pairs},
     }
