@@ -492,18 +492,21 @@ __device__ void lds_mark_top(const uint32_t *keys, uint8_t *fl, int n, uint8_t i
 }
 
 // The same top-k marking with this thread's keys in registers: kr[j] is the key
-// of entry tid + j * blockDim.x and bit j of cmask says whether that entry is
-// flagged in_bit. Minimum, maximum, histograms and marks read no LDS; ties at
-// the threshold fall back to the ordered walk over the LDS copy of the keys.
+// and fr[j] the flag byte of entry tid + j * blockDim.x, and bit j of cmask says
+// whether that entry is flagged in_bit. Minimum, maximum and histograms read no
+// LDS, and the marks of keys above the threshold's bin are plain flag stores.
+// Radix passes stop once at most kRankMax keys share the decided prefix: those
+// are gathered and ranked directly (larger keys, then equal keys at lower
+// entries); when every bit is decided, equal keys are taken in entry order.
+constexpr int kRankMax = 256;
 template <int PER>
-__device__ void reg_mark_top(const uint32_t (&kr)[PER], uint32_t cmask, const uint32_t *keys, uint8_t *fl,
-                             int n, uint8_t in_bit, uint8_t out_bit, int k, int n_in, int *hist,
-                             int *sh, int *digit_info) {
+__device__ void reg_mark_top(const uint32_t (&kr)[PER], const uint8_t (&fr)[PER], uint32_t cmask,
+                             const uint32_t *keys, uint8_t *fl, int n, uint8_t in_bit, uint8_t out_bit,
+                             int k, int n_in, int *hist, int *sh, int *digit_info) {
   const int tid = threadIdx.x, nt = blockDim.x;
+  uint32_t tmask = 0;  // entries this thread marks with a plain store at the end
   if (k >= n_in) {
-#pragma unroll
-    for (int j = 0; j < PER; ++j)
-      if (cmask >> j & 1u) fl[tid + j * nt] |= out_bit;
+    tmask = cmask;
   } else if (k > 0) {
     uint32_t kmin = 0xffffffffu, kmax = 0u;
 #pragma unroll
@@ -518,7 +521,8 @@ __device__ void reg_mark_top(const uint32_t (&kr)[PER], uint32_t cmask, const ui
     uint32_t pmask = rem == 32 ? 0u : ~((1u << rem) - 1u);
     uint32_t prefix = kmin & pmask;
     int need = k;
-    while (rem > 0) {
+    int in_bin = n_in;  // keys that share the prefix decided so far
+    while (rem > 0 && in_bin > kRankMax) {
       const int width = rem < 12 ? rem : 12;
       const int shift = rem - width;
       const int nb = 1 << width;
@@ -539,50 +543,84 @@ __device__ void reg_mark_top(const uint32_t (&kr)[PER], uint32_t cmask, const ui
       int tot;
       const int above = block_excl_scan(s4, sh, &tot);
       if (above < need && above + s4 >= need) {
-        int abv = above, dsel = 0;
+        int abv = above, dsel = 0, cnt = 0;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          if (abv + c[q] >= need) { dsel = nb - 1 - 4 * tid - q; break; }
+          if (abv + c[q] >= need) { dsel = nb - 1 - 4 * tid - q; cnt = c[q]; break; }
           abv += c[q];
         }
         digit_info[0] = dsel;
         digit_info[1] = abv;
+        digit_info[2] = cnt;
       }
       __syncthreads();
       need -= digit_info[1];
+      in_bin = digit_info[2];
       prefix |= (uint32_t)digit_info[0] << shift;
       pmask |= dmask << shift;
       rem = shift;
       __syncthreads();
     }
-    int my_eq = 0;
+    // keys above the prefix's bin are taken
 #pragma unroll
-    for (int j = 0; j < PER; ++j) {
-      if (!(cmask >> j & 1u)) continue;
-      if (kr[j] > prefix) fl[tid + j * nt] |= out_bit;
-      else if (kr[j] == prefix) ++my_eq;
-    }
-    const int eq_tot = block_sum(my_eq, sh);
-    if (eq_tot == need) {
+    for (int j = 0; j < PER; ++j)
+      tmask |= ((cmask >> j & 1u) && (kr[j] & pmask) > prefix) ? 1u << j : 0u;
+    if (rem == 0) {
+      // the prefix is the whole key: the first `need` equal keys in entry order
+      uint32_t eq = 0;
+#pragma unroll
+      for (int j = 0; j < PER; ++j) eq |= ((cmask >> j & 1u) && kr[j] == prefix) ? 1u << j : 0u;
+      const int eq_tot = block_sum(__popc(eq), sh);
+      if (eq_tot == need) {
+        tmask |= eq;
+      } else {
+        int lo, hi;
+        my_segment(n, lo, hi);
+        int c = 0;
+        for (int i = lo; i < hi; ++i) c += ((fl[i] & in_bit) && keys[i] == prefix) ? 1 : 0;
+        int t;
+        int rank = block_excl_scan(c, sh, &t);
+        for (int i = lo; i < hi; ++i)
+          if ((fl[i] & in_bit) && keys[i] == prefix) {
+            if (rank < need) fl[i] |= out_bit;
+            ++rank;
+          }
+      }
+    } else {
+      // at most kRankMax keys share the prefix: gather them as (key, ~entry) pairs,
+      // whose order as 64-bit values is the selection order, and count for each
+      // the larger ones, four threads per key
+      uint64_t *bk = reinterpret_cast<uint64_t *>(hist);
+      int *bcnt = hist + 2 * kRankMax;
+      if (tid == 0) *bcnt = 0;
+      __syncthreads();
 #pragma unroll
       for (int j = 0; j < PER; ++j)
-        if ((cmask >> j & 1u) && kr[j] == prefix) fl[tid + j * nt] |= out_bit;
-    } else {
-      // several equal keys at the threshold: the first `need` in entry order
+        if ((cmask >> j & 1u) && (kr[j] & pmask) == prefix)
+          bk[atomicAdd(bcnt, 1)] = ((uint64_t)kr[j] << 32) | (uint32_t)~(uint32_t)(tid + j * nt);
       __syncthreads();
-      int lo, hi;
-      my_segment(n, lo, hi);
-      int c = 0;
-      for (int i = lo; i < hi; ++i) c += ((fl[i] & in_bit) && keys[i] == prefix) ? 1 : 0;
-      int t;
-      int rank = block_excl_scan(c, sh, &t);
-      for (int i = lo; i < hi; ++i)
-        if ((fl[i] & in_bit) && keys[i] == prefix) {
-          if (rank < need) fl[i] |= out_bit;
-          ++rank;
+      const int nbin = *bcnt;
+      const int me = tid >> 2, part = tid & 3;
+      int rank = 0;
+      uint64_t mine = 0;
+      if (me < nbin) {
+        mine = bk[me];
+        for (int q = part; q < nbin; q += 16) {
+          uint64_t o[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) o[u] = q + 4 * u < nbin ? bk[q + 4 * u] : 0;
+#pragma unroll
+          for (int u = 0; u < 4; ++u) rank += o[u] > mine ? 1 : 0;
         }
+      }
+      rank += __shfl_xor(rank, 1);
+      rank += __shfl_xor(rank, 2);
+      if (me < nbin && part == 0 && rank < need) fl[~(uint32_t)mine] |= out_bit;
     }
   }
+#pragma unroll
+  for (int j = 0; j < PER; ++j)
+    if (tmask >> j & 1u) fl[tid + j * nt] = fr[j] | out_bit;
   __syncthreads();
 }
 
@@ -670,8 +708,8 @@ __device__ void lds_window_group(uint8_t *fl, int n, int win, int tau, uint16_t 
 
 __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspace w, int32_t *sel_offsets) {
   __shared__ int sh[17];
-  __shared__ int hist[kHistBins];
-  __shared__ int digit_info[2];
+  __shared__ __align__(16) int hist[kHistBins];  // also the gathered (key, entry) pairs of the ranking
+  __shared__ int digit_info[3];
   __shared__ uint32_t keys_s[kLdsEntries];  // later: seq_ent (u16) | seq_pre (u16)
   __shared__ uint8_t fl_s[kLdsEntries];
   __shared__ uint8_t sq_s[kLdsEntries];      // grouping: bit 0 top-k slot, bit 1 passing window
@@ -682,6 +720,7 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
   // entry tid + j * nt of the request: flags to LDS, keys to LDS and registers
   constexpr int PER = (kLdsEntries + 1023) / 1024;
   uint32_t kr[PER];
+  uint8_t fr[PER];
   uint32_t cmask = 0;
   int my_cand = 0;
 #pragma unroll
@@ -690,6 +729,7 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
     const uint8_t f = i < n ? w.eflag[e0 + i] : 0;
     const uint32_t key = i < n ? w.keys[e0 + i] : 0u;
     const bool cand = (f & kCand) != 0;
+    fr[j] = f;
     kr[j] = cand ? key : 0u;
     cmask |= (cand ? 1u : 0u) << j;
     my_cand += cand ? 1 : 0;
@@ -709,7 +749,7 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
 
   const int k = a.mode == SRP_SEL_GIVEN ? n_cand : k_from_ratio(a.ratio, n_ctx, n_cand, a.k_ceil);
   __syncthreads();  // flags and keys in LDS (the tie fallback and the grouping read them)
-  reg_mark_top<PER>(kr, cmask, keys_s, fl_s, n, kCand, kTop, k, n_cand, hist, sh, digit_info);
+  reg_mark_top<PER>(kr, fr, cmask, keys_s, fl_s, n, kCand, kTop, k, n_cand, hist, sh, digit_info);
 
   if (a.window > 0)
     lds_window_group(fl_s, n, a.window, a.tau, reinterpret_cast<uint16_t *>(keys_s), sq_s, sh);

@@ -183,6 +183,24 @@ def test_exact_ties_take_lowest_rows():
     assert np.array_equal(got["sel_idx"], want["sel_idx"])
 
 
+@pytest.mark.parametrize("rows", [600, 3000])
+def test_exact_tie_groups_take_lowest_rows(rows):
+    # zero hidden rows and keys, cached values at one of four levels: every squared
+    # deviation is exactly 1024 * level^2, so the threshold falls inside a group of
+    # exactly tied rows (within the gathered survivors at 600 rows, after a radix
+    # pass at 3000) and the lowest rows of that group must be taken
+    spec = inputs.small_spec("tie-groups", prefix=0, chunk_lens=(rows // 2, rows - rows // 2), n_query=8,
+                             n_req=1, ratio=0.3, window=0, tau=0)
+    w = inputs.generate(spec)
+    T = w.layout.total_rows
+    level = np.random.default_rng(rows).integers(1, 5, size=T).astype(np.float64)
+    vc = inputs.store(np.broadcast_to(level[:, None, None], (T, spec.n_kv_heads, spec.head_dim)).copy(), "bf16")
+    kc = np.zeros_like(vc)
+    got, want, _ = run_case(spec, w=w, hidden_st=np.zeros_like(w.hidden), kc_st=kc, vc_st=vc,
+                            what=f"tie groups {rows}")
+    assert np.array_equal(got["sel_idx"], want["sel_idx"])
+
+
 def test_missing_chunk_and_negative_delta():
     spec = inputs.small_spec()
     w = inputs.generate(spec)
