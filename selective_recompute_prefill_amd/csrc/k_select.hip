@@ -930,8 +930,8 @@ __device__ int lds_span_complete(uint32_t *keys, uint8_t *fl, int n, int span_ma
 
 __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Workspace w) {
   __shared__ int sh[17];
-  __shared__ int hist[kHistBins];
-  __shared__ int digit_info[2];
+  __shared__ __align__(16) int hist[kHistBins];  // also the gathered (key, entry) pairs of the ranking
+  __shared__ int digit_info[3];
   __shared__ uint32_t keys_s[kLdsEntries];  // window grouping: seq_ent (u16) | seq_pre (u16)
   __shared__ uint8_t fl_s[kLdsEntries];
   __shared__ uint8_t sq_s[kLdsEntries];
@@ -940,36 +940,37 @@ __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Worksp
   // after the top-k marking the histogram storage serves as four scan arrays
   int *scan0 = hist, *scan1 = hist + 1024;
 
+  // entry tid + j * nt of the request: flags to LDS and registers, score keys to
+  // LDS and registers
+  constexpr int PER = (kLdsEntries + 1023) / 1024;
+  uint32_t kr[PER];
+  uint8_t fr[PER];
+  uint32_t cmask = 0;
   int my_ctx = 0, my_cand = 0;
-  for (int i = tid; i < n; i += 4 * nt) {
-    int dl[4];
-    uint8_t rf[4];
-    float sc[4];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = i + u * nt;
-      dl[u] = j < n ? w.row_delta[rq0 + j] : kFresh;
-      rf[u] = (j < n && a.cand) ? w.rowflag[rq0 + j] : 0;
-      sc[u] = j < n ? a.scores[rq0 + j] : 0.f;
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + j * nt;
+    const int dl = i < n ? w.row_delta[rq0 + i] : kFresh;
+    const uint8_t rf = (i < n && a.cand) ? w.rowflag[rq0 + i] : 0;
+    const float sc = i < n ? a.scores[rq0 + i] : 0.f;
+    const bool fresh = dl == kFresh;
+    const bool cand = i < n && !fresh && (a.cand ? rf == kCand : true);
+    fr[j] = fresh ? kFreshF : (cand ? kCand : 0);
+    kr[j] = cand ? score_key(sc) : 0u;
+    cmask |= (cand ? 1u : 0u) << j;
+    if (i < n) {
+      fl_s[i] = fr[j];
+      keys_s[i] = kr[j];
+      my_ctx += fresh ? 0 : 1;
     }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int j = i + u * nt;
-      if (j < n) {
-        const bool fresh = dl[u] == kFresh;
-        const bool cand = !fresh && (a.cand ? rf[u] == kCand : true);
-        fl_s[j] = fresh ? kFreshF : (cand ? kCand : 0);
-        keys_s[j] = cand ? score_key(sc[u]) : 0u;
-        my_ctx += fresh ? 0 : 1;
-        my_cand += cand ? 1 : 0;
-      }
-    }
+    my_cand += cand ? 1 : 0;
   }
   const int n_ctx = block_sum(my_ctx, sh);
   const int n_cand = block_sum(my_cand, sh);
 
   const int k = k_from_ratio(a.ratio, n_ctx, n_cand, a.k_ceil);
-  lds_mark_top(keys_s, fl_s, n, kCand, kTop, k, n_cand, hist, sh, digit_info);
+  __syncthreads();  // flags and keys in LDS
+  reg_mark_top<PER>(kr, fr, cmask, keys_s, fl_s, n, kCand, kTop, k, n_cand, hist, sh, digit_info);
 
   uint8_t chosen = kTop;
   if (a.span_max > 0) {
