@@ -275,13 +275,14 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   // the scheduling barriers keep that order (the compiler would otherwise move
   // every LDS read to the top and run out of registers).
   // Part 1: the score MFMAs of tile j+1 (chain 0 for keys 0-31, chain 1 for keys
-  // 32-63) with the probabilities of tile j: step t exponentiates elements
+  // 32-63, taken in turn so neither waits on its own previous MFMA) with the
+  // probabilities of tile j: step t exponentiates elements
   // 2(t%4), 2(t%4)+1 of k-step c = t/4 (half c/2, elements 8(c%2)+...).
   auto part1 = [&](auto NSLOT, floatx16 (&cur)[2], floatx16 (&nxt)[2], u32x4 (&pw)[4])
       __attribute__((always_inline)) {
     const char *St = slot_ptr(NSLOT);
     auto kfrag = [&](int t) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8 *>(St + koff[t % NS] + (t / NS) * 32 * (D * 2));
+      return *reinterpret_cast<const bf16x8 *>(St + koff[t >> 1] + (t & 1) * 32 * (D * 2));
     };
     bf16x8 kf[PFD + 1];
 #pragma unroll
@@ -290,10 +291,10 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int t = 0; t < 2 * NS; ++t) {
       if (t + PFD < 2 * NS) kf[(t + PFD) % (PFD + 1)] = kfrag(t + PFD);
-      const bf16x8 q8 = __builtin_bit_cast(bf16x8, qf[t % NS]);
+      const bf16x8 q8 = __builtin_bit_cast(bf16x8, qf[t >> 1]);
       // each chain starts from -m held in registers (no per-tile initialisation)
-      nxt[t / NS] =
-          __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (PFD + 1)], q8, t % NS == 0 ? cneg : nxt[t / NS], 0, 0, 0);
+      nxt[t & 1] =
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[t % (PFD + 1)], q8, t < 2 ? cneg : nxt[t & 1], 0, 0, 0);
       // VALU share of this step (16 steps of D = 128; D = 64 has 8, two shares each)
 #pragma unroll
       for (int u = 0; u < 16 / (2 * NS); ++u) {
