@@ -178,6 +178,88 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow 
   }
 }
 
+// Score modes (EPI_KV, EPI_V) on a 256-column tile: each item covers the same
+// (row, 4 rotation pairs) of both 128-column blocks, so the two blocks share the
+// rotation coefficients and one round trip of loads.
+template <typename T, int ROWS, int MODE, int NT>
+__device__ __forceinline__ void epilogue_pair(const float *Cs, int ldc, const EpiRow *meta, int m_base,
+                                              int n0, const GemmArgs &g) {
+  constexpr int ITEMS = ROWS * 16 / NT;
+  static_assert(ROWS * 16 % NT == 0, "items split evenly");
+  const int d = g.d, half = d >> 1;
+  const int tpu = d >> 3;
+  const int kvd = g.nkv * d;
+#pragma unroll 1
+  for (int kb = 0; kb < ITEMS; ++kb) {
+    const int it = threadIdx.x + kb * NT;
+    const int r = it >> 4, qq = it & 15;
+    const int u = qq / tpu, t = qq - u * tpu;
+    const int i0 = t * 4;
+    const int m = m_base + r;
+    const EpiRow e = meta[r];
+    int part[2], hidx[2];
+    bool valid[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int nu = n0 + h * kBN + u * d;
+      valid[h] = e.row >= 0 && nu < g.N;
+      part[h] = MODE == EPI_V ? 2 : (nu < kvd ? 1 : 2);
+      hidx[h] = (nu - (part[h] == 2 && MODE == EPI_KV ? kvd : 0)) / d;
+    }
+    const bool any_k = (valid[0] && part[0] == 1) || (valid[1] && part[1] == 1);
+    const bool cached = e.delta != kFresh;
+    static_assert(sizeof(T) == 2, "bf16 cache rows");
+    float c1[4], s1[4], c2[4], s2[4];
+    uint2 ra[2], rb[2];  // cached bf16 values, widened where used
+    if (any_k) rope_coef(g.rope, e.pos, i0, c1, s1);
+    if (any_k && cached) rope_coef(g.rope, e.delta, i0, c2, s2);
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (valid[h] && cached) {
+        const T *c = (const T *)(part[h] == 2 ? g.v_cache : g.k_cache) + (size_t)e.cache * kvd + hidx[h] * d;
+        ra[h] = *reinterpret_cast<const uint2 *>(c + i0);
+        rb[h] = *reinterpret_cast<const uint2 *>(c + half + i0);
+      }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      float a[4], b[4];
+      const float *src = Cs + r * ldc + h * kBN + u * d;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) { a[k] = src[i0 + k]; b[k] = src[half + i0 + k]; }
+      float part_sum = 0.f;
+      if (valid[h]) {
+        if (part[h] == 1) rotate4(a, b, c1, s1);
+        T *f = (T *)g.fresh + (size_t)m * 2 * kvd + (part[h] - 1) * kvd + hidx[h] * d;
+        st4(f + i0, a);
+        st4(f + half + i0, b);
+        if (cached) {
+          float ca[4], cb[4];
+          ca[0] = __uint_as_float(ra[h].x << 16); ca[1] = __uint_as_float(ra[h].x & 0xffff0000u);
+          ca[2] = __uint_as_float(ra[h].y << 16); ca[3] = __uint_as_float(ra[h].y & 0xffff0000u);
+          cb[0] = __uint_as_float(rb[h].x << 16); cb[1] = __uint_as_float(rb[h].x & 0xffff0000u);
+          cb[2] = __uint_as_float(rb[h].y << 16); cb[3] = __uint_as_float(rb[h].y & 0xffff0000u);
+          if (part[h] == 1) {
+            // positional recovery of the cached key, kept in fp32 for the
+            // deviation and written back to the cache
+            rotate4(ca, cb, c2, s2);
+            T *c = (T *)g.k_cache + (size_t)e.cache * kvd + hidx[h] * d;
+            st4(c + i0, ca);
+            st4(c + half + i0, cb);
+          }
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float x = a[k] - ca[k], y = b[k] - cb[k];
+            part_sum += x * x + y * y;
+          }
+        }
+      }
+      // fixed-order reduction over the head's tpu lanes (aligned groups)
+      for (int o = 1; o < tpu; o <<= 1) part_sum += __shfl_xor(part_sum, o, 64);
+      if (valid[h] && t == 0) g.dev_part[(size_t)m * 2 * g.nkv + (part[h] - 1) * g.nkv + hidx[h]] = part_sum;
+    }
+  }
+}
+
 // ------------------------------------------------------------------------- //
 // tile scheduling: persistent loop, each XCD (blockIdx % 8) walks a contiguous
 // range of tiles so the operand slabs its work-groups read stay in its L2
@@ -425,10 +507,14 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
             }
       }
       __syncthreads();
+      if constexpr ((MODE == EPI_KV || MODE == EPI_V) && C::BN == 2 * kBN) {
+        epilogue_pair<uint16_t, C::EROWS, MODE, C::THREADS>(Cs, C::LDC, meta + p * C::TM, m0 + p * C::TM, n0, g);
+      } else {
 #pragma unroll 1
-      for (int cb = 0; cb < C::BN / kBN; ++cb)
-        epilogue<uint16_t, C::EROWS, MODE, C::THREADS, C::EPI_B>(Cs + cb * kBN, C::LDC, meta + p * C::TM,
-                                                                m0 + p * C::TM, n0 + cb * kBN, g);
+        for (int cb = 0; cb < C::BN / kBN; ++cb)
+          epilogue<uint16_t, C::EROWS, MODE, C::THREADS, C::EPI_B>(Cs + cb * kBN, C::LDC, meta + p * C::TM,
+                                                                  m0 + p * C::TM, n0 + cb * kBN, g);
+      }
     }
     __syncthreads();
   }
