@@ -6,6 +6,8 @@
 // the fp32 kernel is a plain FMA tiling for fp32 workloads. Both stage the
 // accumulator tile in LDS and run the same epilogue, which works on whole heads so
 // that each rotation pair (i, i + d/2) sits in one thread.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace srp {
@@ -181,82 +183,105 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow 
 // Score modes (EPI_KV, EPI_V) on a 256-column tile: each item covers the same
 // (row, 4 rotation pairs) of both 128-column blocks, so the two blocks share the
 // rotation coefficients and one round trip of loads.
-template <typename T, int ROWS, int MODE, int NT>
+template <typename T, int ROWS, int MODE, int NT, int B>
 __device__ __forceinline__ void epilogue_pair(const float *Cs, int ldc, const EpiRow *meta, int m_base,
                                               int n0, const GemmArgs &g) {
   constexpr int ITEMS = ROWS * 16 / NT;
-  static_assert(ROWS * 16 % NT == 0, "items split evenly");
+  static_assert(ROWS * 16 % NT == 0 && ITEMS % B == 0, "items split evenly");
   const int d = g.d, half = d >> 1;
   const int tpu = d >> 3;
   const int kvd = g.nkv * d;
 #pragma unroll 1
-  for (int kb = 0; kb < ITEMS; ++kb) {
-    const int it = threadIdx.x + kb * NT;
-    const int r = it >> 4, qq = it & 15;
-    const int u = qq / tpu, t = qq - u * tpu;
-    const int i0 = t * 4;
-    const int m = m_base + r;
-    const EpiRow e = meta[r];
-    int part[2], hidx[2];
-    bool valid[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int nu = n0 + h * kBN + u * d;
-      valid[h] = e.row >= 0 && nu < g.N;
-      part[h] = MODE == EPI_V ? 2 : (nu < kvd ? 1 : 2);
-      hidx[h] = (nu - (part[h] == 2 && MODE == EPI_KV ? kvd : 0)) / d;
-    }
-    const bool any_k = (valid[0] && part[0] == 1) || (valid[1] && part[1] == 1);
-    const bool cached = e.delta != kFresh;
+  for (int kb = 0; kb < ITEMS; kb += B) {
+    int r[B], u[B], t[B], part[B][2], hidx[B][2];
+    bool valid[B][2], any_k[B], cached[B];
+    EpiRow e[B];
+    float c1[B][4], s1[B][4], c2[B][4], s2[B][4];
+    uint2 ra[B][2], rb[B][2];  // cached bf16 values, widened where used
     static_assert(sizeof(T) == 2, "bf16 cache rows");
-    float c1[4], s1[4], c2[4], s2[4];
-    uint2 ra[2], rb[2];  // cached bf16 values, widened where used
-    if (any_k) rope_coef(g.rope, e.pos, i0, c1, s1);
-    if (any_k && cached) rope_coef(g.rope, e.delta, i0, c2, s2);
+    // loads of the batch
 #pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (valid[h] && cached) {
-        const T *c = (const T *)(part[h] == 2 ? g.v_cache : g.k_cache) + (size_t)e.cache * kvd + hidx[h] * d;
-        ra[h] = *reinterpret_cast<const uint2 *>(c + i0);
-        rb[h] = *reinterpret_cast<const uint2 *>(c + half + i0);
+    for (int j = 0; j < B; ++j) {
+      const int it = threadIdx.x + (kb + j) * NT;
+      r[j] = it >> 4;
+      const int qq = it & 15;
+      u[j] = qq / tpu;
+      t[j] = qq - u[j] * tpu;
+      const int i0 = t[j] * 4;
+      e[j] = meta[r[j]];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int nu = n0 + h * kBN + u[j] * d;
+        valid[j][h] = e[j].row >= 0 && nu < g.N;
+        part[j][h] = MODE == EPI_V ? 2 : (nu < kvd ? 1 : 2);
+        hidx[j][h] = (nu - (part[j][h] == 2 && MODE == EPI_KV ? kvd : 0)) / d;
       }
+      any_k[j] = (valid[j][0] && part[j][0] == 1) || (valid[j][1] && part[j][1] == 1);
+      cached[j] = e[j].delta != kFresh;
+      if (any_k[j]) rope_coef(g.rope, e[j].pos, i0, c1[j], s1[j]);
+      if (any_k[j] && cached[j]) rope_coef(g.rope, e[j].delta, i0, c2[j], s2[j]);
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      float a[4], b[4];
-      const float *src = Cs + r * ldc + h * kBN + u * d;
+      for (int h = 0; h < 2; ++h)
+        if (valid[j][h] && cached[j]) {
+          const T *c = (const T *)(part[j][h] == 2 ? g.v_cache : g.k_cache) + (size_t)e[j].cache * kvd +
+                       hidx[j][h] * d;
+          ra[j][h] = *reinterpret_cast<const uint2 *>(c + i0);
+          rb[j][h] = *reinterpret_cast<const uint2 *>(c + half + i0);
+        }
+    }
+    // compute and store
 #pragma unroll
-      for (int k = 0; k < 4; ++k) { a[k] = src[i0 + k]; b[k] = src[half + i0 + k]; }
-      float part_sum = 0.f;
-      if (valid[h]) {
-        if (part[h] == 1) rotate4(a, b, c1, s1);
-        T *f = (T *)g.fresh + (size_t)m * 2 * kvd + (part[h] - 1) * kvd + hidx[h] * d;
-        st4(f + i0, a);
-        st4(f + half + i0, b);
-        if (cached) {
-          float ca[4], cb[4];
-          ca[0] = __uint_as_float(ra[h].x << 16); ca[1] = __uint_as_float(ra[h].x & 0xffff0000u);
-          ca[2] = __uint_as_float(ra[h].y << 16); ca[3] = __uint_as_float(ra[h].y & 0xffff0000u);
-          cb[0] = __uint_as_float(rb[h].x << 16); cb[1] = __uint_as_float(rb[h].x & 0xffff0000u);
-          cb[2] = __uint_as_float(rb[h].y << 16); cb[3] = __uint_as_float(rb[h].y & 0xffff0000u);
-          if (part[h] == 1) {
-            // positional recovery of the cached key, kept in fp32 for the
-            // deviation and written back to the cache
-            rotate4(ca, cb, c2, s2);
-            T *c = (T *)g.k_cache + (size_t)e.cache * kvd + hidx[h] * d;
-            st4(c + i0, ca);
-            st4(c + half + i0, cb);
-          }
+    for (int j = 0; j < B; ++j) {
+      const int i0 = t[j] * 4;
+      const int m = m_base + r[j];
 #pragma unroll
-          for (int k = 0; k < 4; ++k) {
-            const float x = a[k] - ca[k], y = b[k] - cb[k];
-            part_sum += x * x + y * y;
+      for (int h = 0; h < 2; ++h) {
+        float a[4], b[4];
+        const float *src = Cs + r[j] * ldc + h * kBN + u[j] * d;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) { a[k] = src[i0 + k]; b[k] = src[half + i0 + k]; }
+        float part_sum = 0.f;
+        if (valid[j][h]) {
+          if (part[j][h] == 1) rotate4(a, b, c1[j], s1[j]);
+          T *f = (T *)g.fresh + (size_t)m * 2 * kvd + (part[j][h] - 1) * kvd + hidx[j][h] * d;
+          st4(f + i0, a);
+          st4(f + half + i0, b);
+          if (cached[j]) {
+            float ca[4], cb[4];
+            ca[0] = __uint_as_float(ra[j][h].x << 16); ca[1] = __uint_as_float(ra[j][h].x & 0xffff0000u);
+            ca[2] = __uint_as_float(ra[j][h].y << 16); ca[3] = __uint_as_float(ra[j][h].y & 0xffff0000u);
+            cb[0] = __uint_as_float(rb[j][h].x << 16); cb[1] = __uint_as_float(rb[j][h].x & 0xffff0000u);
+            cb[2] = __uint_as_float(rb[j][h].y << 16); cb[3] = __uint_as_float(rb[j][h].y & 0xffff0000u);
+            if (part[j][h] == 1) {
+              // positional recovery of the cached key, kept in fp32 for the
+              // deviation and written back to the cache
+              rotate4(ca, cb, c2[j], s2[j]);
+              T *c = (T *)g.k_cache + (size_t)e[j].cache * kvd + hidx[j][h] * d;
+              st4(c + i0, ca);
+              st4(c + half + i0, cb);
+            }
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const float x = a[k] - ca[k], y = b[k] - cb[k];
+              part_sum += x * x + y * y;
+            }
           }
         }
+        // fixed-order reduction over the head's tpu lanes (aligned groups)
+        for (int o = 1; o < tpu; o <<= 1) part_sum += __shfl_xor(part_sum, o, 64);
+        if (valid[j][h] && t[j] == 0)
+          g.dev_part[(size_t)m * 2 * g.nkv + (part[j][h] - 1) * g.nkv + hidx[j][h]] = part_sum;
       }
-      // fixed-order reduction over the head's tpu lanes (aligned groups)
-      for (int o = 1; o < tpu; o <<= 1) part_sum += __shfl_xor(part_sum, o, 64);
-      if (valid[h] && t == 0) g.dev_part[(size_t)m * 2 * g.nkv + (part[h] - 1) * g.nkv + hidx[h]] = part_sum;
     }
+  }
+}
+
+// Calls f(integral_constant<int, i>) for i = 0..N-1 (compile-time indices).
+template <int N, typename F>
+__device__ __forceinline__ void static_for_gemm(F &&f) {
+  if constexpr (N > 0) {
+    static_for_gemm<N - 1>(f);
+    f(std::integral_constant<int, N - 1>{});
   }
 }
 
@@ -488,28 +513,53 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
     const int m0 = mt * C::BM, n0 = nt * C::BN;
     // the epilogue's row metadata loads while the first copies are in flight
     mainloop(m0, n0, 0, KT, [&] { load_row_meta<MODE, C::BM>(meta, m0, M, g); });
-    // the epilogue runs once per wave row: the waves of row p stage their
-    // accumulators (D[row][col], row = 8*(e/4) + 4*(lane/32) + e%4), then every
-    // wave works through the staged rows one 128-column block at a time
-#pragma unroll 1
-    for (int p = 0; p < C::WM; ++p) {
-      __syncthreads();  // the ring (or the previous pass) is no longer read
-      if (wm == p) {
+    if constexpr ((MODE == EPI_KV || MODE == EPI_V) && C::BN == 2 * kBN && C::WM == 2 && C::MI == 4) {
+      // scoring projections: each of two passes stages half of every wave's rows
+      // (blocks i = 2p, 2p+1; D[row][col], row = 8*(e/4) + 4*(lane/32) + e%4), so
+      // after the first pass half the accumulators are dead and the epilogue
+      // items can go two per batch. Staged row r is tile row
+      // (r / 64) * 128 + 64 p + r % 64.
+      static_for_gemm<2>([&](auto P) __attribute__((always_inline)) {
+        constexpr int p = decltype(P)::value;
+        __syncthreads();  // the ring (or the previous pass) is no longer read
 #pragma unroll
-        for (int i = 0; i < C::MI; ++i)
+        for (int ii = 0; ii < 2; ++ii)
 #pragma unroll
           for (int j = 0; j < C::NI; ++j)
 #pragma unroll
             for (int e = 0; e < 16; ++e) {
-              const int row = i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+              const int row = wm * 64 + ii * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
               const int col = wn * C::TN + j * 32 + (lane & 31);
-              Cs[row * C::LDC + col] = acc[i][j][e];
+              Cs[row * C::LDC + col] = acc[2 * p + ii][j][e];
             }
-      }
-      __syncthreads();
-      if constexpr ((MODE == EPI_KV || MODE == EPI_V) && C::BN == 2 * kBN) {
-        epilogue_pair<uint16_t, C::EROWS, MODE, C::THREADS>(Cs, C::LDC, meta + p * C::TM, m0 + p * C::TM, n0, g);
-      } else {
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll 1
+        for (int hr = 0; hr < 2; ++hr)
+          epilogue_pair<uint16_t, 64, MODE, C::THREADS, 2>(Cs + hr * 64 * C::LDC, C::LDC, meta + hr * 128 + 64 * p,
+                                                           m0 + hr * 128 + 64 * p, n0, g);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    } else {
+      // the epilogue runs once per wave row: the waves of row p stage their
+      // accumulators (D[row][col], row = 8*(e/4) + 4*(lane/32) + e%4), then every
+      // wave works through the staged rows one 128-column block at a time
+#pragma unroll 1
+      for (int p = 0; p < C::WM; ++p) {
+        __syncthreads();  // the ring (or the previous pass) is no longer read
+        if (wm == p) {
+#pragma unroll
+          for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) {
+                const int row = i * 32 + (e >> 2) * 8 + (lane >> 5) * 4 + (e & 3);
+                const int col = wn * C::TN + j * 32 + (lane & 31);
+                Cs[row * C::LDC + col] = acc[i][j][e];
+              }
+        }
+        __syncthreads();
 #pragma unroll 1
         for (int cb = 0; cb < C::BN / kBN; ++cb)
           epilogue<uint16_t, C::EROWS, MODE, C::THREADS, C::EPI_B>(Cs + cb * kBN, C::LDC, meta + p * C::TM,
