@@ -180,17 +180,18 @@ __device__ __forceinline__ void epilogue(const float *Cs, int ldc, const EpiRow 
   }
 }
 
-// Score modes (EPI_KV, EPI_V) on a 256-column tile: each item covers the same
-// (row, 4 rotation pairs) of both 128-column blocks, so the two blocks share the
-// rotation coefficients and one round trip of loads.
+// Projection modes other than the encode on a 256-column tile: each item covers
+// the same (row, 4 rotation pairs) of both 128-column blocks, so the two blocks
+// share the rotation coefficients and one round trip of loads.
 template <typename T, int ROWS, int MODE, int NT, int B>
 __device__ __forceinline__ void epilogue_pair(const float *Cs, int ldc, const EpiRow *meta, int m_base,
                                               int n0, const GemmArgs &g) {
   constexpr int ITEMS = ROWS * 16 / NT;
   static_assert(ROWS * 16 % NT == 0 && ITEMS % B == 0, "items split evenly");
+  constexpr bool SCORE = MODE == EPI_KV || MODE == EPI_V;  // fresh K/V + deviation
   const int d = g.d, half = d >> 1;
   const int tpu = d >> 3;
-  const int kvd = g.nkv * d;
+  const int kvd = g.nkv * d, qd = g.nh * d;
 #pragma unroll 1
   for (int kb = 0; kb < ITEMS; kb += B) {
     int r[B], u[B], t[B], part[B][2], hidx[B][2];
@@ -213,13 +214,23 @@ __device__ __forceinline__ void epilogue_pair(const float *Cs, int ldc, const Ep
       for (int h = 0; h < 2; ++h) {
         const int nu = n0 + h * kBN + u[j] * d;
         valid[j][h] = e[j].row >= 0 && nu < g.N;
-        part[j][h] = MODE == EPI_V ? 2 : (nu < kvd ? 1 : 2);
-        hidx[j][h] = (nu - (part[j][h] == 2 && MODE == EPI_KV ? kvd : 0)) / d;
+        // part of the unit (0 = Q, 1 = K, 2 = V) and its head index
+        if (MODE == EPI_Q) {
+          part[j][h] = 0;
+          hidx[j][h] = nu / d;
+        } else if (MODE == EPI_QK) {
+          part[j][h] = nu < qd ? 0 : 1;
+          hidx[j][h] = (nu - (nu < qd ? 0 : qd)) / d;
+        } else {
+          part[j][h] = MODE == EPI_V ? 2 : (nu < kvd ? 1 : 2);
+          hidx[j][h] = (nu - (part[j][h] == 2 && MODE == EPI_KV ? kvd : 0)) / d;
+        }
       }
-      any_k[j] = (valid[j][0] && part[j][0] == 1) || (valid[j][1] && part[j][1] == 1);
-      cached[j] = e[j].delta != kFresh;
+      // units roped at the row's position (Q and K)
+      any_k[j] = (valid[j][0] && part[j][0] <= 1) || (valid[j][1] && part[j][1] <= 1);
+      cached[j] = SCORE && e[j].delta != kFresh;
       if (any_k[j]) rope_coef(g.rope, e[j].pos, i0, c1[j], s1[j]);
-      if (any_k[j] && cached[j]) rope_coef(g.rope, e[j].delta, i0, c2[j], s2[j]);
+      if (MODE == EPI_KV && any_k[j] && cached[j]) rope_coef(g.rope, e[j].delta, i0, c2[j], s2[j]);
 #pragma unroll
       for (int h = 0; h < 2; ++h)
         if (valid[j][h] && cached[j]) {
@@ -241,7 +252,21 @@ __device__ __forceinline__ void epilogue_pair(const float *Cs, int ldc, const Ep
 #pragma unroll
         for (int k = 0; k < 4; ++k) { a[k] = src[i0 + k]; b[k] = src[half + i0 + k]; }
         float part_sum = 0.f;
-        if (valid[j][h]) {
+        if (valid[j][h] && !SCORE) {
+          rotate4(a, b, c1[j], s1[j]);
+          if (part[j][h] == 0) {
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { a[k] *= g.q_scale; b[k] *= g.q_scale; }
+            T *q = (T *)g.q_out + (size_t)m * qd + hidx[j][h] * d;
+            st4(q + i0, a);
+            st4(q + half + i0, b);
+          } else {
+            // fresh key of a selected row, straight into its cache row
+            T *o = (T *)g.k_cache + (size_t)e[j].cache * kvd + hidx[j][h] * d;
+            st4(o + i0, a);
+            st4(o + half + i0, b);
+          }
+        } else if (valid[j][h]) {
           if (part[j][h] == 1) rotate4(a, b, c1[j], s1[j]);
           T *f = (T *)g.fresh + (size_t)m * 2 * kvd + (part[j][h] - 1) * kvd + hidx[j][h] * d;
           st4(f + i0, a);
@@ -267,10 +292,12 @@ __device__ __forceinline__ void epilogue_pair(const float *Cs, int ldc, const Ep
             }
           }
         }
-        // fixed-order reduction over the head's tpu lanes (aligned groups)
-        for (int o = 1; o < tpu; o <<= 1) part_sum += __shfl_xor(part_sum, o, 64);
-        if (valid[j][h] && t[j] == 0)
-          g.dev_part[(size_t)m * 2 * g.nkv + (part[j][h] - 1) * g.nkv + hidx[j][h]] = part_sum;
+        if (SCORE) {
+          // fixed-order reduction over the head's tpu lanes (aligned groups)
+          for (int o = 1; o < tpu; o <<= 1) part_sum += __shfl_xor(part_sum, o, 64);
+          if (valid[j][h] && t[j] == 0)
+            g.dev_part[(size_t)m * 2 * g.nkv + (part[j][h] - 1) * g.nkv + hidx[j][h]] = part_sum;
+        }
       }
     }
   }
@@ -513,8 +540,8 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
     const int m0 = mt * C::BM, n0 = nt * C::BN;
     // the epilogue's row metadata loads while the first copies are in flight
     mainloop(m0, n0, 0, KT, [&] { load_row_meta<MODE, C::BM>(meta, m0, M, g); });
-    if constexpr ((MODE == EPI_KV || MODE == EPI_V) && C::BN == 2 * kBN && C::WM == 2 && C::MI == 4) {
-      // scoring projections: each of two passes stages half of every wave's rows
+    if constexpr (MODE != EPI_ENC && C::BN == 2 * kBN && C::WM == 2 && C::MI == 4) {
+      // each of two passes stages half of every wave's rows
       // (blocks i = 2p, 2p+1; D[row][col], row = 8*(e/4) + 4*(lane/32) + e%4), so
       // after the first pass half the accumulators are dead and the epilogue
       // items can go two per batch. Staged row r is tile row
