@@ -251,12 +251,16 @@ int srp_stack_workspace_size(const srp_dims *dims, const srp_batch *batch,
  *   attn[j]) on its selected rows (srp_residual_rmsnorm, eps rms_eps), so hidden
  *   ends as the stack's output. sel_idx, sel_offsets and attn_out end as the last
  *   layer's; every layer's fused cache stays in its k_cache / v_cache.
- *   Loads: every host cache is copied on copy_stream in layer order, each layer's
- *   pair followed by an event that `stream` waits for before that layer, so the copy
- *   of layer l+1 runs while layer l computes. The copies start after the work
- *   enqueued on `stream` before the call (which may still use the destinations).
- *   copy_stream == stream (e.g. both NULL) puts the copies in line. Work is only enqueued: synchronising with `stream`
- *   covers the copies too. The host caches must stay valid until then.
+ *   Loads: the host key caches are copied on copy_stream in layer order and the
+ *   value caches on a second copy stream that the library creates once per device
+ *   (default priority, kept until the process ends), each layer's copies followed by
+ *   events that `stream` waits for before that layer, so the loads of layer l+1 run
+ *   while layer l computes and one copy engine's idle time between transfers
+ *   overlaps the other's transfer. The copies start after the work enqueued on
+ *   `stream` before the call (which may still use the destinations).
+ *   copy_stream == stream (e.g. both NULL) puts all copies in line. Work is only
+ *   enqueued: synchronising with `stream` covers the copies too. The host caches
+ *   must stay valid until then.
  * Errors as for srp_fuse_layer; nothing is enqueued when an argument check fails. */
 int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_select *first,
                    int32_t n_layers, const srp_layer *layers, void *hidden, float rms_eps,

@@ -491,6 +491,28 @@ int srp_stack_workspace_size(const srp_dims *dims, const srp_batch *batch, const
   return SRP_OK;
 }
 
+// A second copy stream per device for the stack executor's value loads (created on
+// first use with the default priority, kept until the process ends): with the keys
+// on the caller's copy stream and the values on this one, one copy engine's idle
+// time between transfers overlaps the other's transfer.
+static hipError_t value_copy_stream(hipStream_t *out) {
+  static std::mutex mu;
+  static std::map<int, hipStream_t> streams;
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(mu);
+  auto it = streams.find(dev);
+  if (it == streams.end()) {
+    hipStream_t st;
+    e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+    if (e != hipSuccess) return e;
+    it = streams.emplace(dev, st).first;
+  }
+  *out = it->second;
+  return hipSuccess;
+}
+
 int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_select *first,
                    int32_t n_layers, const srp_layer *layers, void *hidden, float rms_eps,
                    int32_t *sel_idx, int32_t *sel_offsets, void *attn_out, void *workspace,
@@ -527,22 +549,30 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
   hipStream_t s = (hipStream_t)stream, cs = (hipStream_t)copy_stream;
   const size_t cache_bytes = (size_t)T * dims->n_kv_heads * dims->head_dim * (dims->dtype == SRP_BF16 ? 2 : 4);
 
-  // one event per loaded layer, created for this call (concurrent calls never share
-  // one) and released once its wait is enqueued; ev.back() orders the copies after
-  // the work already on the compute stream, which may still use the destinations
-  std::vector<hipEvent_t> ev(n_layers + 1, nullptr);
+  // one event per loaded layer and copy stream, created for this call (concurrent
+  // calls never share one) and released once its wait is enqueued; ev.back() orders
+  // the copies after the work already on the compute stream, which may still use
+  // the destinations
+  std::vector<hipEvent_t> ev(n_layers + 1, nullptr), ev_v(n_layers, nullptr);
   auto release = [&]() {
     for (hipEvent_t e : ev)
+      if (e) (void)hipEventDestroy(e);
+    for (hipEvent_t e : ev_v)
       if (e) (void)hipEventDestroy(e);
   };
   bool loads = false;
   for (int l = 0; l < n_layers; ++l) loads |= layers[l].k_host != nullptr;
   if (loads && b.block_rows > 0)
     return fail(SRP_E_UNSUPPORTED, "host loads fill contiguous caches (block_rows must be 0)");
+  // on a side stream the values go to a second copy stream; in line (cs == s)
+  // both copies stay on the compute stream
+  hipStream_t vs = cs;
   if (loads && cache_bytes > 0 && cs != s) {
-    hipError_t e = hipEventCreateWithFlags(&ev[n_layers], hipEventDisableTiming);
+    hipError_t e = value_copy_stream(&vs);
+    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev[n_layers], hipEventDisableTiming);
     if (e == hipSuccess) e = hipEventRecord(ev[n_layers], s);
     if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[n_layers], 0);
+    if (e == hipSuccess) e = hipStreamWaitEvent(vs, ev[n_layers], 0);
     if (e != hipSuccess) {
       release();
       return fail(SRP_E_HIP, "ordering the loads: %s", hipGetErrorString(e));
@@ -551,9 +581,11 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
   for (int l = 0; l < n_layers; ++l) {
     if (!layers[l].k_host || cache_bytes == 0) continue;
     hipError_t e = hipEventCreateWithFlags(&ev[l], hipEventDisableTiming);
+    if (e == hipSuccess && vs != cs) e = hipEventCreateWithFlags(&ev_v[l], hipEventDisableTiming);
     if (e == hipSuccess) e = hipMemcpyAsync(layers[l].k_cache, layers[l].k_host, cache_bytes, hipMemcpyHostToDevice, cs);
-    if (e == hipSuccess) e = hipMemcpyAsync(layers[l].v_cache, layers[l].v_host, cache_bytes, hipMemcpyHostToDevice, cs);
+    if (e == hipSuccess) e = hipMemcpyAsync(layers[l].v_cache, layers[l].v_host, cache_bytes, hipMemcpyHostToDevice, vs);
     if (e == hipSuccess) e = hipEventRecord(ev[l], cs);
+    if (e == hipSuccess && ev_v[l]) e = hipEventRecord(ev_v[l], vs);
     if (e != hipSuccess) {
       release();
       return fail(SRP_E_HIP, "loading layer %d: %s", l, hipGetErrorString(e));
@@ -562,7 +594,8 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
   int rc = SRP_OK;
   for (int l = 0; l < n_layers && rc == SRP_OK; ++l) {
     if (ev[l]) {
-      const hipError_t e = hipStreamWaitEvent(s, ev[l], 0);
+      hipError_t e = hipStreamWaitEvent(s, ev[l], 0);
+      if (e == hipSuccess && ev_v[l]) e = hipStreamWaitEvent(s, ev_v[l], 0);
       if (e != hipSuccess) {
         rc = fail(SRP_E_HIP, "waiting for layer %d: %s", l, hipGetErrorString(e));
         break;
