@@ -690,9 +690,13 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
     else
       fix_sum<kMaxSplit, C::BN, LDC>(base, sp.split, Cs);
     __syncthreads();
+    if constexpr (MODE != EPI_ENC && C::BN == 2 * kBN) {
+      epilogue_pair<uint16_t, kFixRows, MODE, 256, 1>(Cs, LDC, meta, m0, n0, g);
+    } else {
 #pragma unroll 1
-    for (int cb = 0; cb < C::BN / kBN; ++cb)
-      epilogue<uint16_t, kFixRows, MODE, 256, 1>(Cs + cb * kBN, LDC, meta, m0, n0 + cb * kBN, g);
+      for (int cb = 0; cb < C::BN / kBN; ++cb)
+        epilogue<uint16_t, kFixRows, MODE, 256, 1>(Cs + cb * kBN, LDC, meta, m0, n0 + cb * kBN, g);
+    }
   }
 }
 
