@@ -4,8 +4,10 @@
 // candidates and fresh rows for K/V, the selected rows for Q), W rows are output
 // features. The bf16 kernel uses v_mfma_f32_32x32x16_bf16 with fp32 accumulation;
 // the fp32 kernel is a plain FMA tiling for fp32 workloads. Both stage the
-// accumulator tile in LDS and run the same epilogue, which works on whole heads so
-// that each rotation pair (i, i + d/2) sits in one thread.
+// accumulator tile in LDS for an epilogue that works on whole heads, so that each
+// rotation pair (i, i + d/2) sits in one thread; the bf16 kernel's items cover both
+// 128-column blocks of its 256-column tile (shared rotation coefficients, one
+// round trip of loads), the fp32 kernel and the encode mode go block by block.
 #include <type_traits>
 
 #include "kernels.hpp"
