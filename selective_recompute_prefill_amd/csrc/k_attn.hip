@@ -184,6 +184,13 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   uint32_t voff[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) voff[c] = KT + qi * 128 + (((2 * c + gph) ^ ((qi >> 1) & 7)) * 16);
+  // the same lane offsets 64 KB further on: fragment reads of the slots that lie
+  // beyond the 16-bit immediate offset of an LDS read start from these registers
+  uint32_t koff_hi[NS], voff_hi[4];
+#pragma unroll
+  for (int ks = 0; ks < NS; ++ks) koff_hi[ks] = koff[ks] + 65536u;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) voff_hi[c] = voff[c] + 65536u;
 
   // S^T of the first tile (both 32-key halves) into s, starting from c0; K
   // fragments two steps ahead, kept in that order by the scheduling barriers
@@ -282,7 +289,9 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
       __attribute__((always_inline)) {
     const char *St = slot_ptr(NSLOT);
     auto kfrag = [&](int t) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8 *>(St + koff[t >> 1] + (t & 1) * 32 * (D * 2));
+      const uint32_t so = (uint32_t)(uintptr_t)(lds_void *)St;
+      const uint32_t a = so >= 65536u ? koff_hi[t >> 1] + (so - 65536u) : koff[t >> 1] + so;
+      return *(const __attribute__((address_space(3))) bf16x8 *)(uintptr_t)(a + (t & 1) * 32 * (D * 2));
     };
     bf16x8 kf[PFD + 1];
 #pragma unroll
@@ -318,7 +327,9 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
       __attribute__((always_inline)) {
     const char *St = slot_ptr(SLOT);
     auto vfrag = [&](int t) __attribute__((always_inline)) {
-      return *reinterpret_cast<const bf16x8 *>(St + voff[t / (D / 32)] + (t % (D / 32)) * 32 * 128);
+      const uint32_t so = (uint32_t)(uintptr_t)(lds_void *)St;
+      const uint32_t a = so >= 65536u ? voff_hi[t / (D / 32)] + (so - 65536u) : voff[t / (D / 32)] + so;
+      return *(const __attribute__((address_space(3))) bf16x8 *)(uintptr_t)(a + (t % (D / 32)) * 32 * 128);
     };
     if (kb_next < key_start || kb_next + kBK - 1 > w_first) {
 #pragma unroll
