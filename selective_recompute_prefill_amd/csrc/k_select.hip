@@ -723,11 +723,19 @@ __global__ __launch_bounds__(1024) void select_lds_kernel(SelectArgs a, Workspac
   uint8_t fr[PER];
   uint32_t cmask = 0;
   int my_cand = 0;
+  // every global load first (the LDS stores below could alias them as far as the
+  // compiler knows, which would make each load wait for the previous store)
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = tid + j * nt;
-    const uint8_t f = i < n ? w.eflag[e0 + i] : 0;
-    const uint32_t key = i < n ? w.keys[e0 + i] : 0u;
+    fr[j] = i < n ? w.eflag[e0 + i] : 0;
+    kr[j] = i < n ? w.keys[e0 + i] : 0u;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + j * nt;
+    const uint8_t f = fr[j];
+    const uint32_t key = kr[j];
     const bool cand = (f & kCand) != 0;
     fr[j] = f;
     kr[j] = cand ? key : 0u;
@@ -947,12 +955,24 @@ __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Worksp
   uint8_t fr[PER];
   uint32_t cmask = 0;
   int my_ctx = 0, my_cand = 0;
+  // every global load first (the LDS stores below could alias them as far as the
+  // compiler knows, which would make each load wait for the previous store)
+  int dlv[PER];
+  uint8_t rfv[PER];
+  float scv[PER];
 #pragma unroll
   for (int j = 0; j < PER; ++j) {
     const int i = tid + j * nt;
-    const int dl = i < n ? w.row_delta[rq0 + i] : kFresh;
-    const uint8_t rf = (i < n && a.cand) ? w.rowflag[rq0 + i] : 0;
-    const float sc = i < n ? a.scores[rq0 + i] : 0.f;
+    dlv[j] = i < n ? w.row_delta[rq0 + i] : kFresh;
+    rfv[j] = (i < n && a.cand) ? w.rowflag[rq0 + i] : 0;
+    scv[j] = i < n ? a.scores[rq0 + i] : 0.f;
+  }
+#pragma unroll
+  for (int j = 0; j < PER; ++j) {
+    const int i = tid + j * nt;
+    const int dl = dlv[j];
+    const uint8_t rf = rfv[j];
+    const float sc = scv[j];
     const bool fresh = dl == kFresh;
     const bool cand = i < n && !fresh && (a.cand ? rf == kCand : true);
     fr[j] = fresh ? kFreshF : (cand ? kCand : 0);
