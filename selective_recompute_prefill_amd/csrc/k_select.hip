@@ -1001,7 +1001,19 @@ __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Worksp
       const int m = k_from_ratio(a.cap_ratio, n_ctx, n_cand, a.k_ceil);
       if (n_sel > m) {
         // the key storage held the span counters: reload the keys of the chosen rows
-        for (int i = tid; i < n; i += nt) keys_s[i] = (fl_s[i] & kSel) ? score_key(a.scores[rq0 + i]) : 0u;
+        // (all loads before the LDS stores, as above)
+        float scv[PER];
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int i = tid + j * nt;
+          scv[j] = (i < n && (fl_s[i] & kSel)) ? a.scores[rq0 + i] : 0.f;
+        }
+        __syncthreads();  // every thread has read its flags before keys_s changes
+#pragma unroll
+        for (int j = 0; j < PER; ++j) {
+          const int i = tid + j * nt;
+          if (i < n) keys_s[i] = (fl_s[i] & kSel) ? score_key(scv[j]) : 0u;
+        }
         __syncthreads();
         lds_mark_top(keys_s, fl_s, n, kSel, kCap, m, n_sel, hist, sh, digit_info);
         chosen = kCap;
