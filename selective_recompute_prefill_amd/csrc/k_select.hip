@@ -1025,6 +1025,23 @@ __global__ __launch_bounds__(1024) void score_select_kernel(SelectArgs a, Worksp
   }
   __syncthreads();
   for (int i = tid; i < n; i += nt) w.rowflag[rq0 + i] = (fl_s[i] & chosen) ? kCand : 0;
+  if (gridDim.x == 1) {
+    // a single request: the R list (chosen rows and fresh rows in row order) right
+    // here instead of three grid-wide passes
+    int lo, hi;
+    my_segment(n, lo, hi);
+    int c = 0;
+    for (int i = lo; i < hi; ++i) c += (fl_s[i] & (chosen | kFreshF)) ? 1 : 0;
+    int total;
+    int p = block_excl_scan(c, sh, &total);
+    for (int i = lo; i < hi; ++i)
+      if (fl_s[i] & (chosen | kFreshF)) w.rlist[p++] = rq0 + i;
+    if (tid == 0) {
+      w.roff[0] = 0;
+      w.roff[1] = total;
+      w.ctr[kCtrREntries] = total;
+    }
+  }
 }
 
 __global__ __launch_bounds__(1024) void finalize_kernel(SelectArgs a, Workspace w, int32_t *sel_offsets) {
@@ -1093,7 +1110,8 @@ hipError_t launch_prepare(const SelectArgs &a, const Workspace &w, hipStream_t s
   }
   if (a.mode == SRP_SEL_SCORES)
     hipLaunchKernelGGL(score_select_kernel, dim3(a.n_req), dim3(1024), 0, s, a, w);
-  if (a.listed) {
+  // the external-score selection of a single request writes the R list itself
+  if (a.listed && !(a.mode == SRP_SEL_SCORES && a.n_req == 1)) {
     const int bpr = blocks_per_req(a.max_req_rows);
     hipLaunchKernelGGL(r_count_kernel, dim3(a.n_req * bpr), dim3(1024), 0, s, a, w, bpr);
     hipLaunchKernelGGL(r_scan_kernel, dim3(1), dim3(1024), 0, s, a, w, bpr);
