@@ -126,23 +126,19 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   // depends on the lane for these row groups). Rows past key_end are clamped to
   // the last valid row; such keys come after every query of the tile and are masked.
   const int k_lrow = lane / KCH, k_logical = (lane % KCH) ^ ((KROWS * w + k_lrow) & (KCH - 1));
-  const uint32_t k_lane_off = (uint32_t)(k_lrow * row_bytes + k_logical * 16);
+  const uint32_t k_chunk_off = (uint32_t)(k_logical * 16), row_bytes32 = (uint32_t)row_bytes;
   const int v_lrow = lane >> 3, v_logical = (lane & 7) ^ (((8 * w + v_lrow) >> 1) & 7);
   const uint32_t v_lane_off = (uint32_t)(v_lrow * vrow_bytes + v_logical * 16);
   auto issue = [&](auto SLOT, int blk) __attribute__((always_inline)) {
     const int kb = key_base + blk * kBK;
     char *st = slot_ptr(SLOT);
-    const bool partial = kb + kBK > key_end;
     static_for<KJ>([&](auto J) __attribute__((always_inline)) {
       const int i = w + kAW * decltype(J)::value;
-      const char *src;
-      if (!partial) {
-        src = Kg + (size_t)(kb + KROWS * i) * row_bytes + k_lane_off;
-      } else {
-        const int row = min(kb + KROWS * i + k_lrow, key_end - 1);
-        src = Kg + (size_t)row * row_bytes + k_logical * 16;
-      }
-      dma16(src, st + i * 1024);
+      // lane row min(kb + KROWS i + k_lrow, key_end - 1) as a wave-uniform first
+      // row plus a small per-lane step (24-bit multiply, no 64-bit lane math)
+      const int r0 = min(kb + KROWS * i, key_end - 1);
+      const uint32_t lo = __umul24((uint32_t)min(k_lrow, key_end - 1 - r0), row_bytes32) + k_chunk_off;
+      dma16(Kg + (size_t)r0 * row_bytes + lo, st + i * 1024);
     });
     static_for<VJ>([&](auto J) __attribute__((always_inline)) {
       const int i = w + kAW * decltype(J)::value;
