@@ -67,7 +67,8 @@ typedef enum { SRP_DEV_KV = 0, SRP_DEV_V = 1 } srp_dev_mode;
  * n_heads*d query rows, then n_kv_heads*d key rows, then n_kv_heads*d value rows,
  * each row one output feature (so Q = X W_q^T). Rotary embedding: rotate-half
  * pairing (i, i + d/2), angle p * rope_base^(-2i/d). Supported: head_dim 64 or
- * 128, n_heads a multiple of n_kv_heads, hidden a multiple of 64. */
+ * 128, n_heads a multiple of n_kv_heads with at most 8 query heads per KV head
+ * (SRP_E_UNSUPPORTED beyond), hidden a multiple of 64. */
 typedef struct {
   int32_t hidden;
   int32_t n_heads;

@@ -130,7 +130,9 @@ struct AttnArgs {
   void *out;               // [n_sel][nh][d]
 };
 hipError_t launch_attention(const AttnArgs &a, hipStream_t s);
-// Selected rows per attention tile for this shape (a multiple of 32).
+// Selected rows per attention tile for this shape: bf16 packs (query, head)
+// pairs of a KV group into 256 columns, floor(256 / G) queries for G = nh / nkv
+// <= 8 (so at least 32); fp32 takes 32.
 int attn_tile_rows(int dtype, int nh, int nkv);
 
 hipError_t launch_residual_rmsnorm(int dtype, int H, void *hidden, const void *attn,

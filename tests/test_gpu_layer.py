@@ -129,6 +129,15 @@ def test_mini_bf16_gqa5():
     run_case(inputs.small_spec(hidden=640, n_heads=5, n_kv_heads=1), what="mini-gqa5")
 
 
+@pytest.mark.parametrize("nh,nkv,d", [(4, 4, 128), (6, 2, 64), (16, 2, 64)])
+def test_mini_bf16_gqa_groups(nh, nkv, d):
+    """Other query-head groups: G = 1 (256 queries per attention tile), 3 (85
+    queries, one spare column) and 8 (32 queries), with a ragged head block in
+    the Q projection for 6 x 64."""
+    run_case(inputs.small_spec(hidden=nh * d, n_heads=nh, n_kv_heads=nkv, head_dim=d),
+             what=f"mini-g{nh // nkv}-d{d}")
+
+
 def test_mini_grouping():
     run_case(inputs.small_spec(window=8, tau=4, ratio=0.3), what="mini-grouping")
 
