@@ -1,7 +1,7 @@
 """GPU parity at the edges of the input space: a request larger than the LDS-resident
 selection holds (the global-memory selection path, with and without grouping), an
-empty batch, empty / one-row / cache-only / query-only requests in one batch, and
-a batch without any cached row. Compared with the fp64 oracle as in the other
+empty batch, empty / one-row / cache-only / query-only requests in one batch, a
+batch without any cached row, and more requests than one 1024-thread block covers. Compared with the fp64 oracle as in the other
 parity tests."""
 import copy
 import sys
@@ -138,3 +138,16 @@ def test_no_cached_rows():
     got, want, _ = run_case(spec, w=w, lay=w.layout, kc_st=kc, vc_st=vc, sel_kw=dict(ratio=0.5),
                             what="all fresh")
     assert len(got["sel_idx"]) == w.layout.total_rows  # everything recomputed
+
+
+def test_more_requests_than_one_block():
+    """1100 requests (every hundredth long, the rest three cached rows and one
+    fresh one): the CSR offsets and the attention tile list are built in two
+    passes of a 1024-thread block."""
+    requests = [[(120, 0), (40, -1)] if i % 100 == 0 else [(3, 0), (1, -1)] for i in range(1100)]
+    spec, w = custom_workload(requests, seed=9)
+    kc, vc = oracle_caches(w)
+    _say(f"[gpu] {len(requests)} requests, T={w.layout.total_rows}")
+    got, _, _ = run_case(spec, w=w, lay=w.layout, kc_st=kc, vc_st=vc, sel_kw=dict(ratio=0.34),
+                         what="1100 requests")
+    assert len(got["sel_offsets"]) == 1101
