@@ -325,8 +325,8 @@ def main():
         print("--pipeline loads contiguous caches; it does not combine with --paged", file=sys.stderr)
         sys.exit(2)
     if args.gpus != 1:
-        print(f"bench.py runs on one GPU only (asked for {args.gpus}): this build has no "
-              f"multi-GPU path", file=sys.stderr)
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}): the library has no "
+              f"multi-GPU path; its value is one GPU's throughput", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -341,7 +341,7 @@ def main():
         return
     S.lib()  # fail loudly if the library is not built
     dev = "cuda"
-    spec = inputs.CONFIGS[args.workload]
+    spec = inputs.WORKLOADS[args.workload]
     if args.ratio is not None:
         spec = spec.replace(ratio=args.ratio, ratios=())
     print(f"[bench] generating {spec.name}", file=sys.stderr, flush=True)

@@ -22,7 +22,7 @@ the CacheClip paper's latency table, 15% as CacheBlend's quality floor):
   draw_scores, a stream of their own: units of 1-6 rows at a lognormal(0, 0.5)
   level with 2% per-row jitter.
 
-Storage: fp32 configs keep float32 arrays; bf16 configs keep uint16 bit patterns
+Storage: fp32 workloads keep float32 arrays; bf16 workloads keep uint16 bit patterns
 (value rounded to float32, then to bfloat16, each round-to-nearest-even). The
 encode input X + eps*n is returned in float64 and is never rounded.
 
@@ -95,8 +95,8 @@ class Spec:
         return dataclasses.replace(self, **kw)
 
 
-# The five workloads of the graded configuration list, by id.
-CONFIGS: Dict[int, Spec] = {
+# The five workloads (shapes, sizes and ratios of the pages' setups), by id.
+WORKLOADS: Dict[int, Spec] = {
     0: Spec("tiny-fp32", 256, 4, 2, 64, "f32", prefix=32, chunk_lens=(128,) * 4,
             n_query=32, ratio=0.20, seed=SEED_BASE + 0),
     1: Spec("llama3-8b-layer", 4096, 32, 8, 128, "bf16", prefix=0,

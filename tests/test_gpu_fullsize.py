@@ -82,30 +82,30 @@ def _compare_layer(spec, lay, got, hidden_st, wq_st, kc_st, vc_st, want, okw, wh
     assert rel.max() < 1e-4, f"{what}: deviation rel err {rel.max():.2e}"
 
 
-def test_config1_llama8b_layer():
-    spec = inputs.CONFIGS[1]
+def test_llama3_8b_layer():
+    spec = inputs.WORKLOADS[1]
     w = inputs.generate(spec)
     lay = w.layout
     kc, vc = oracle_caches(w)
     wq = w.layers[0].w_qkv
-    _say(f"[gpu] config1 T={lay.total_rows}")
+    _say(f"[gpu] llama3-8b T={lay.total_rows}")
     got = _gpu_layer(spec, lay, w.hidden, wq, kc, vc, spec.ratio)
     okw = dict(ratio=spec.ratio, window=0, tau=0)
     want = oracle_layer(spec, lay, w.hidden, wq, kc, vc, **okw)
     assert len(got["sel_idx"]) == 461 + 64
-    _compare_layer(spec, lay, got, w.hidden, wq, kc, vc, want, okw, "config1", sample=False)
+    _compare_layer(spec, lay, got, w.hidden, wq, kc, vc, want, okw, "llama3-8b", sample=False)
 
 
-def test_config2_16k_grouped_layer():
-    spec = inputs.CONFIGS[2]
+def test_14b_16k_grouped_layer():
+    spec = inputs.WORKLOADS[2]
     w = inputs.generate(spec)
     lay = w.layout
     kc, vc = oracle_caches(w)
     wq = w.layers[0].w_qkv
     req, src = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
-    _say(f"[gpu] config2 T={lay.total_rows} (top-k run)")
+    _say(f"[gpu] 14b-16k T={lay.total_rows} (top-k run)")
     got0 = _gpu_layer(spec, lay, w.hidden, wq, kc, vc, spec.ratio)  # no grouping: the top-k set
-    _say("[gpu] config2 grouped run")
+    _say("[gpu] 14b-16k grouped run")
     got = _gpu_layer(spec, lay, w.hidden, wq, kc, vc, spec.ratio, window=8, tau=4)
     okw = dict(ratio=spec.ratio, window=8, tau=4)
     want = oracle_layer(spec, lay, w.hidden, wq, kc, vc, attn_sample=np.zeros(0, np.int64), **okw)
@@ -114,27 +114,27 @@ def test_config2_16k_grouped_layer():
     s0_gpu = np.setdiff1d(got0["sel_idx"], fresh)
     assert len(s0_gpu) == 3283
     check_selection(np.union1d(s0_gpu, fresh), dict(sel_idx=np.union1d(want["s0"], fresh),
-                                                    kth=want["kth"], dev=want["dev"]), req, "config2 top-k")
+                                                    kth=want["kth"], dev=want["dev"]), req, "14b-16k top-k")
     # grouping of the GPU's own top-k set
     seq = np.nonzero(src >= 0)[0]
     kept = ref.group_windows(np.searchsorted(seq, s0_gpu), len(seq), 8, 4)
     assert np.array_equal(got["sel_idx"], np.union1d(seq[np.asarray(kept)], fresh))
-    _compare_layer(spec, lay, got, w.hidden, wq, kc, vc, want, okw, "config2")
+    _compare_layer(spec, lay, got, w.hidden, wq, kc, vc, want, okw, "14b-16k")
 
 
-def test_config2_16k_scores_span_completion():
+def test_14b_16k_scores_span_completion():
     """The 16K layer with rows chosen from external scores (SpecCache's settings:
     K = ceil(0.2 N), spans of at most 16 at tau_smooth 0.4, completion at tau_cover
     0.7, a budget of 25%): the choice is exact, caches and sampled attention rows
     within tolerance."""
-    spec = inputs.CONFIGS[2]
+    spec = inputs.WORKLOADS[2]
     w = inputs.generate(spec)
     lay = w.layout
     kc, vc = oracle_caches(w)
     wq = w.layers[0].w_qkv
     sc = inputs.draw_scores(lay.total_rows, 22)
     kw = dict(span_max=16, tau_smooth=0.4, tau_cover=0.7, cap_ratio=0.25)
-    _say(f"[gpu] config2 scores T={lay.total_rows}")
+    _say(f"[gpu] 14b-16k scores T={lay.total_rows}")
     got = _gpu_layer(spec, lay, w.hidden, wq, kc, vc, spec.ratio, mode=S.SRP_SEL_SCORES,
                      scores=torch.as_tensor(sc, device="cuda"), k_rule=S.SRP_K_CEIL, **kw)
     okw = dict(ratio=spec.ratio, window=0, tau=0, mode="scores", scores=sc.astype(np.float64),
@@ -143,7 +143,7 @@ def test_config2_16k_scores_span_completion():
     want = oracle_layer(spec, lay, w.hidden, wq, kc, vc, attn_sample=sp, **okw)
     assert np.array_equal(got["sel_idx"], want["sel_idx"])
     assert len(want["sel_idx"]) > len(want["s0"]) + 96  # completion added rows
-    _compare_layer(spec, lay, got, w.hidden, wq, kc, vc, want, okw, "config2 scores", sample=True,
+    _compare_layer(spec, lay, got, w.hidden, wq, kc, vc, want, okw, "14b-16k scores", sample=True,
                    exact=True)
 
 
@@ -155,15 +155,15 @@ def _csr(rows, req_offsets):
     return rows.astype(np.int32), np.asarray(off, np.int32)
 
 
-def test_config3_gradual_filtering_stack():
-    spec = inputs.CONFIGS[3]
+def test_70b_gradual_filtering_stack():
+    spec = inputs.WORKLOADS[3]
     w = inputs.generate(spec)
     lay = w.layout
     T = lay.total_rows
     x0 = ref.widen(w.hidden, "bf16")
     wq64 = [ref.widen(w.layers[l].w_qkv, "bf16") for l in range(spec.n_layers)]
     # caches of layer l: full-prefill hidden of layer l plus fresh noise
-    _say("[gpu] config3: oracle full-prefill stack for the layer caches")
+    _say("[gpu] 70b-stack: oracle full-prefill stack for the layer caches")
     xs = [x0]
     for l in range(spec.n_layers - 1):
         full = ref.full_prefill_layer(hidden=xs[l], w_qkv=wq64[l], req_offsets=lay.req_offsets,
@@ -173,7 +173,7 @@ def test_config3_gradual_filtering_stack():
         xs.append(ref.residual_rmsnorm(xs[l], full["attn_out"].reshape(T, -1)))
     caches = [oracle_caches(w, l, None if l == 0 else xs[l]) for l in range(spec.n_layers)]
     rb = lambda y: ref.widen(inputs.store(y, "bf16"), "bf16")
-    _say("[gpu] config3: oracle selective stack")
+    _say("[gpu] 70b-stack: oracle selective stack")
     outs = ref.fuse_stack(hidden=x0, layers=[dict(w_qkv=wq64[l], k_cache=ref.widen(caches[l][0], "bf16"),
                                                   v_cache=ref.widen(caches[l][1], "bf16"))
                                              for l in range(spec.n_layers)],
@@ -195,12 +195,12 @@ def test_config3_gradual_filtering_stack():
             c, co = _csr(cand, lay.req_offsets)
             kw.update(cand=ints(c), cand_offsets=ints(co))
             okw["cand"] = cand
-        _say(f"[gpu] config3 layer {l}")
+        _say(f"[gpu] 70b-stack layer {l}")
         got = _gpu_layer(spec, lay, h_st, w.layers[l].w_qkv, caches[l][0], caches[l][1], **kw)
         _compare_layer(spec, lay, got, h_st, w.layers[l].w_qkv, caches[l][0], caches[l][1], o, okw,
-                       f"config3 layer {l}", sample=False)
+                       f"70b-stack layer {l}", sample=False)
     # the whole stack freely on the GPU: sets shrink and keep their sizes
-    _say("[gpu] config3 free-running stack")
+    _say("[gpu] 70b-stack free-running stack")
     call = LayerCall(spec, lay)
     h = upload(w.hidden, "bf16")
     prev = None
@@ -252,16 +252,16 @@ def _request_slice(lay, r):
     return a, b, sub
 
 
-def test_config4_batched_sampled_requests_and_ratio_sweep():
-    spec = inputs.CONFIGS[4]
+def test_8b_batch16x8k_sampled_requests_and_ratio_sweep():
+    spec = inputs.WORKLOADS[4]
     w = inputs.generate(spec)
     lay = w.layout
-    _say("[gpu] config4: oracle pool caches")
+    _say("[gpu] batch16x8k: oracle pool caches")
     kc, vc = _pool_caches(w)
     wq = w.layers[0].w_qkv
     results = {}
     for ratio in inputs.BATCH_RATIOS:
-        _say(f"[gpu] config4 ratio {ratio}")
+        _say(f"[gpu] batch16x8k ratio {ratio}")
         results[ratio] = _gpu_layer(spec, lay, w.hidden, wq, kc, vc, ratio)
     for r in (0, 7, 15):
         a, b, sub = _request_slice(lay, r)
@@ -276,12 +276,12 @@ def test_config4_batched_sampled_requests_and_ratio_sweep():
             cand = np.arange(b - a)
             w_r = dict(sel_idx=ref.topk_rows(want["dev"], cand, k), dev=want["dev"],
                        kth=np.array([np.sort(want["dev"])[::-1][k - 1]]))
-            check_selection(gs, w_r, req, f"config4 request {r} ratio {ratio}")
+            check_selection(gs, w_r, req, f"batch16x8k request {r} ratio {ratio}")
         got = results[0.2]
         s0, s1 = got["sel_offsets"][r], got["sel_offsets"][r + 1]
         sub_got = dict(sel_idx=got["sel_idx"][s0:s1] - a, sel_offsets=np.array([0, s1 - s0]),
                        attn_out=got["attn_out"][s0:s1], dev=got["dev"][a:b],
                        k_cache=got["k_cache"][a:b], v_cache=got["v_cache"][a:b])
-        _say(f"[gpu] config4 request {r} outputs")
+        _say(f"[gpu] batch16x8k request {r} outputs")
         _compare_layer(spec, sub, sub_got, w.hidden[a:b], wq, kc[a:b], vc[a:b], want, okw,
-                       f"config4 request {r}")
+                       f"batch16x8k request {r}")

@@ -109,8 +109,8 @@ def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel
 # small shapes (several tiles, ragged tails, two requests)
 # --------------------------------------------------------------------------- #
 
-def test_config0_tiny_fp32():
-    run_case(inputs.CONFIGS[0], what="config0")
+def test_tiny_fp32_workload():
+    run_case(inputs.WORKLOADS[0], what="tiny-fp32")
 
 
 def test_mini_bf16_two_requests():

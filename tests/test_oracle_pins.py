@@ -117,7 +117,7 @@ def _layer_kwargs(spec, w, x, wq, kc, vc, **kw):
 def test_deviation_closed_form():
     # cached = R(src) W (x + eps n) moved by R(pos - src); fresh = R(pos) W x, so the
     # deviation is eps * sqrt(|W_k n|^2 + |W_v n|^2) exactly (orthogonal R).
-    spec = inputs.CONFIGS[0]
+    spec = inputs.WORKLOADS[0]
     w, x, wq, kc, vc = _unrounded_layer(spec)
     out = ref.fuse_layer(**_layer_kwargs(spec, w, x, wq, kc, vc))
     ld = w.layers[0]
@@ -356,7 +356,7 @@ def test_batch_equals_concatenated_requests():
 def test_selection_tracks_noise_scale():
     # The deviation of a layer-1 token is eps * |W n|: with eps lognormal(-3, 1) the
     # top-k set must be dominated by the largest-eps tokens.
-    spec = inputs.CONFIGS[0]
+    spec = inputs.WORKLOADS[0]
     w, x, wq, kc, vc = _unrounded_layer(spec)
     out = ref.fuse_layer(**_layer_kwargs(spec, w, x, wq, kc, vc))
     rows = np.nonzero(w.cache_row_of >= 0)[0]
