@@ -143,3 +143,10 @@ def test_validate_rejects_shared_pool_rows():
     with pytest.raises(S.SrpError) as e:
         S.srp_validate_batch(call.batch)
     assert e.value.code == S.SRP_E_BATCH
+
+
+def test_paged_head_dim_64_gqa8():
+    """Head dim 64 with eight query heads per KV head: the gathered K rows, the V
+    transpose from the pool and the projection epilogue at the other head size."""
+    spec = inputs.small_spec(hidden=1024, n_heads=16, n_kv_heads=2, head_dim=64)
+    run_both(spec, lambda: dict(ratio=0.25), "d64 g8")
