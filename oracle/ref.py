@@ -23,7 +23,8 @@ function and listed, with every other reading, in the design notes of the repo.
 Parity status: every function is pinned by the CPU tests (closed forms, brute
 force, library cross-checks, the grouping figure; for span completion, hand-worked
 cases, a characterisation of the segmentation and a cross-check of the external-score
-mode against deviation-ranked top-k). The intermediate layers of the
+mode against deviation-ranked top-k; for the chain step, hand-worked rows; for bf16
+widening, hand-decoded bit patterns and torch's conversion of every pattern). The intermediate layers of the
 multi-layer chain are pinned only through the invariants of the single layer and
 the all-recompute reduction of the whole stack.
 """

@@ -443,3 +443,76 @@ def test_gradual_filtering_shrinks():
     n_ctx = [int(cr[lay.req_offsets[r]:lay.req_offsets[r + 1]].sum()) for r in range(lay.n_req)]
     assert len(set(outs[0]["sel_idx"].tolist()) - fresh) == sum(
         ref.topk_count(0.3, n, n) for n in n_ctx)
+
+
+# --------------------------------------------------------------------------- #
+# chain step and storage widening
+# --------------------------------------------------------------------------- #
+
+def test_residual_rmsnorm_golden(golden_dir):
+    # hand-worked rows (tests/golden/rmsnorm.json): the residual adds, the mean (not
+    # the sum) of squares is taken, eps sits inside the square root
+    with open(os.path.join(golden_dir, "rmsnorm.json")) as fh:
+        g = json.load(fh)
+    for case in g["cases"]:
+        x = np.asarray([case["x"]], np.float64)
+        o = np.asarray([case["o"]], np.float64)
+        got = ref.residual_rmsnorm(x, o, case["eps"])[0]
+        np.testing.assert_allclose(got, case["expected"], rtol=1e-14, atol=0, err_msg=case["what"])
+
+
+def test_residual_rmsnorm_rows_are_independent_and_scale_free():
+    # each row is normalised on its own (a batch equals its rows one by one); with
+    # eps = 0 the output has unit RMS and does not change when y is scaled
+    rng = np.random.default_rng(17)
+    x = rng.standard_normal((5, 24)) * np.array([1e-2, 1, 3, 50, 7])[:, None]
+    o = rng.standard_normal((5, 24))
+    both = ref.residual_rmsnorm(x, o, 0.0)
+    for i in range(5):
+        np.testing.assert_array_equal(both[i], ref.residual_rmsnorm(x[i:i + 1], o[i:i + 1], 0.0)[0])
+    np.testing.assert_allclose(np.sqrt((both ** 2).mean(axis=1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(ref.residual_rmsnorm(3.5 * x, 3.5 * o, 0.0), both, rtol=1e-14)
+
+
+def test_widen_bf16_bit_patterns():
+    # bfloat16 = the upper 16 bits of an IEEE binary32: sign, 8 exponent bits, 7
+    # mantissa bits; hand-decoded patterns
+    cases = {
+        0x3F80: 1.0,                       # exponent 127, mantissa 0
+        0xC000: -2.0,                      # sign, exponent 128
+        0x4049: 3.140625,                  # 2 * (1 + 1/2 + 1/16 + 1/128)
+        0x3E80: 0.25,                      # exponent 125
+        0x0000: 0.0,
+        0x0001: 2.0 ** -133,               # smallest subnormal: 2^-126 * 2^-7
+        0x007F: (127 / 128) * 2.0 ** -126,  # largest subnormal
+        0x0080: 2.0 ** -126,               # smallest normal
+        0x7F7F: (2 - 2 ** -7) * 2.0 ** 127,  # largest finite
+        0x7F80: np.inf,
+        0xFF80: -np.inf,
+    }
+    bits = np.array(list(cases), np.uint16)
+    got = ref.widen(bits, "bf16")
+    assert got.dtype == np.float64
+    np.testing.assert_array_equal(got, np.array(list(cases.values())))
+    neg_zero = ref.widen(np.array([0x8000], np.uint16), "bf16")[0]
+    assert neg_zero == 0.0 and np.signbit(neg_zero)
+
+
+def test_widen_bf16_matches_torch_for_every_pattern():
+    # every non-NaN bit pattern against torch's own bfloat16 -> float64 conversion
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    want = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    got = ref.widen(bits, "bf16")
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    np.testing.assert_array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def test_widen_f32_is_exact():
+    x = np.array([1.0, -0.0, 3.4028234663852886e38, 1.401298464324817e-45, np.inf], np.float32)
+    got = ref.widen(x, "f32")
+    assert got.dtype == np.float64
+    np.testing.assert_array_equal(got, x.astype(np.float64))
+    with pytest.raises(ValueError):
+        ref.widen(x, "fp8")
