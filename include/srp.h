@@ -33,6 +33,9 @@ extern "C" {
 
 typedef struct ihipStream_t *srp_stream_t; /* hipStream_t */
 
+/* Status codes. A call reports failure by a negative return value, as the
+ * CacheBlend walkthrough's loader does ("Implementation": fetch_kv returns -1 when a
+ * chunk's cache is missing); the codes below tell the failures apart. */
 typedef enum {
   SRP_OK = 0,
   SRP_E_INVALID = -1,     /* bad argument (shape, dtype, ratio, null pointer...)  */
@@ -164,7 +167,12 @@ typedef struct {
   int32_t fresh_all;   /* 0 or 1                                                */
 } srp_select;
 
-/* Bytes of scratch that srp_fuse_layer needs for these arguments. */
+/* Bytes of device scratch that srp_fuse_layer needs for these arguments (written
+ * to *bytes). No passage of the pages defines this call: it is the engineering
+ * convention that keeps allocation off the hot path (the caller allocates once and
+ * reuses the buffer across layers, as the per-layer calls of the CacheBlend
+ * walkthrough's "Implementation" run back to back). Host arithmetic only; the same
+ * argument checks as srp_fuse_layer, with the same error codes. */
 int srp_workspace_size(const srp_dims *dims, const srp_batch *batch,
                        const srp_select *sel, size_t *bytes);
 
@@ -209,11 +217,19 @@ int srp_encode_kv(const srp_dims *dims, int32_t n_rows, int32_t max_position,
 int srp_rerotate_kv(const srp_dims *dims, const srp_batch *batch, void *k_cache,
                     srp_stream_t stream);
 
-/* Chain step between stacked layers (gradual filtering): for every selected row
+/* Chain step between stacked layers (CacheBlend walkthrough, "The chicken-and-egg
+ * problem": the rows a layer recomputes carry their hidden state into the next
+ * layer, which checks only them; "The system": the fusor runs the layers one after
+ * another). The pages give no block internals; the step taken is a unit-weight
+ * RMSNorm after the residual. For every selected row
  * j = sel_idx[s], s < sel_offsets[n_req]:
  *   hidden[j] <- y / sqrt(mean(y^2) + eps),  y = hidden[j] + attn_out[s]
- * (unit-weight RMSNorm after the residual; requires n_heads * head_dim == hidden).
- * sel_capacity bounds sel_offsets[n_req] (normally T). */
+ * (requires n_heads * head_dim == hidden, else SRP_E_INVALID). hidden [T, hidden]
+ * is updated in place; attn_out [sel_capacity, n_heads, head_dim] holds the layer's
+ * attention rows in sel_idx order; sel_idx / sel_offsets are device arrays as
+ * srp_fuse_layer writes them. sel_capacity bounds sel_offsets[n_req] (normally T);
+ * rows past it are ignored. Enqueued on `stream`; SRP_E_INVALID on a NULL pointer,
+ * n_req < 1 or eps < 0. */
 int srp_residual_rmsnorm(const srp_dims *dims, void *hidden, const void *attn_out,
                          const int32_t *sel_idx, const int32_t *sel_offsets,
                          int32_t n_req, int32_t sel_capacity, float eps,
@@ -235,8 +251,12 @@ typedef struct {
   double ratio;       /* the layer's recompute ratio, in [0, 1]                        */
 } srp_layer;
 
-/* Bytes of scratch that srp_fuse_stack needs (srp_workspace_size plus the carried
- * candidate list). */
+/* Bytes of device scratch that srp_fuse_stack needs (written to *bytes):
+ * srp_workspace_size plus room for the candidate list carried from layer to layer
+ * (CacheBlend walkthrough, "Implementation": the per-layer dictionary passes the
+ * indices chosen by one layer to the next). The allocation itself is the same
+ * engineering convention as srp_workspace_size. Host arithmetic only; errors as for
+ * srp_workspace_size. */
 int srp_stack_workspace_size(const srp_dims *dims, const srp_batch *batch,
                              const srp_select *first, size_t *bytes);
 
@@ -277,7 +297,12 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
 int srp_controller_ratio(double full_layer_ms, double load_ms, double r_floor, double *ratio);
 
 /* Debug check of a batch's device arrays against the rules of srp_batch (copies
- * them to the host and synchronises). SRP_OK or SRP_E_BATCH with a message. */
+ * them to the host and synchronises `stream`). SRP_OK or SRP_E_BATCH with a
+ * message. No passage of the pages defines it: it is the engineering counterpart of
+ * the synchronisation point that the CacheBlend walkthrough's "Implementation" puts
+ * before each layer (synchronize), a place where device-side layout errors can be
+ * reported to the host instead of giving undefined results. The only entry point
+ * that blocks the host. */
 int srp_validate_batch(const srp_batch *batch, srp_stream_t stream);
 
 /* Stage timing (the pages report per-stage latency breakdowns of this path, e.g.
@@ -293,10 +318,15 @@ int srp_profile_begin(int32_t max_calls);
 int srp_profile_end(float *ms, int32_t max_calls, int32_t *n_calls);
 const char *srp_profile_stage_name(int32_t i);
 
-/* Message for the last failing call on this thread ("" if none). */
+/* Message for the last failing call on this thread ("" if none; the pointer stays
+ * valid until the thread's next libsrp call). Engineering convention that goes with
+ * the negative status codes (CacheBlend walkthrough, "Implementation": fetch_kv
+ * reports a miss as -1): the code says what kind of failure, this says which
+ * argument. */
 const char *srp_last_error(void);
 
-/* Library version string. */
+/* Library version string (static storage). Engineering convention; no passage of
+ * the pages defines it. */
 const char *srp_version(void);
 
 #ifdef __cplusplus

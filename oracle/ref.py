@@ -99,13 +99,23 @@ def row_layout(req_offsets, chunk_offsets, chunk_src_pos, total_rows: int):
 # --------------------------------------------------------------------------- #
 
 
-def project(x: np.ndarray, w_qkv: np.ndarray, n_heads: int, n_kv: int, d: int):
-    """Q, K, V = x W_q^T, x W_k^T, x W_v^T (rows of w_qkv: Q, then K, then V)."""
+def project_q(x: np.ndarray, w_qkv: np.ndarray, n_heads: int, n_kv: int, d: int):
+    """Q = x W_q^T (rows of w_qkv: Q, then K, then V), shaped [n, heads, d]."""
+    qd = n_heads * d
+    return (x @ w_qkv[:qd].T).reshape(x.shape[0], n_heads, d)
+
+
+def project_kv(x: np.ndarray, w_qkv: np.ndarray, n_heads: int, n_kv: int, d: int):
+    """K, V = x W_k^T, x W_v^T (rows of w_qkv: Q, then K, then V)."""
     qd, kvd = n_heads * d, n_kv * d
-    wq, wk, wv = w_qkv[:qd], w_qkv[qd:qd + kvd], w_qkv[qd + kvd:qd + 2 * kvd]
+    wk, wv = w_qkv[qd:qd + kvd], w_qkv[qd + kvd:qd + 2 * kvd]
     n = x.shape[0]
-    return ((x @ wq.T).reshape(n, n_heads, d), (x @ wk.T).reshape(n, n_kv, d),
-            (x @ wv.T).reshape(n, n_kv, d))
+    return (x @ wk.T).reshape(n, n_kv, d), (x @ wv.T).reshape(n, n_kv, d)
+
+
+def project(x: np.ndarray, w_qkv: np.ndarray, n_heads: int, n_kv: int, d: int):
+    """Q, K, V = x W_q^T, x W_k^T, x W_v^T."""
+    return (project_q(x, w_qkv, n_heads, n_kv, d),) + project_kv(x, w_qkv, n_heads, n_kv, d)
 
 
 def encode_kv(x: np.ndarray, w_qkv: np.ndarray, pos: np.ndarray, n_heads: int,
@@ -113,7 +123,7 @@ def encode_kv(x: np.ndarray, w_qkv: np.ndarray, pos: np.ndarray, n_heads: int,
     """Offline chunk cache: K = R(pos) W_k x and V = W_v x for each row, at the
     positions the rows are encoded at (CacheClip walkthrough, Figure 4, offline
     phase; chunk-local positions)."""
-    _, k, v = project(x, w_qkv, n_heads, n_kv, d)
+    k, v = project_kv(x, w_qkv, n_heads, n_kv, d)
     return rope(k, pos, base), v
 
 
@@ -391,7 +401,7 @@ def fuse_layer(*, hidden, w_qkv, k_cache, v_cache, req_offsets, chunk_offsets,
 
     # 2c. the rows recomputed: C plus fresh rows
     rec = np.nonzero(is_cand | fresh)[0]
-    _, kf, vf = project(hidden[rec], w_qkv, n_heads, n_kv, d)
+    kf, vf = project_kv(hidden[rec], w_qkv, n_heads, n_kv, d)
     kf = rope(kf, pos[rec], rope_base)
     k_new = np.zeros_like(k_cache)
     v_new = np.zeros_like(v_cache)
@@ -440,7 +450,7 @@ def fuse_layer(*, hidden, w_qkv, k_cache, v_cache, req_offsets, chunk_offsets,
     if sel_override is not None:
         missing = np.setdiff1d(sel, rec)
         if len(missing):  # an override may name rows that were not recomputed
-            _, km, vm = project(hidden[missing], w_qkv, n_heads, n_kv, d)
+            km, vm = project_kv(hidden[missing], w_qkv, n_heads, n_kv, d)
             k_new[missing], v_new[missing] = rope(km, pos[missing], rope_base), vm
     k_out = k_tilde.copy()
     v_out = v_cache.copy()
@@ -452,12 +462,12 @@ def fuse_layer(*, hidden, w_qkv, k_cache, v_cache, req_offsets, chunk_offsets,
     #    (attn_sample: positions into the selection whose rows are evaluated;
     #    the others are left NaN -- a cost cut for large tests)
     if attn_sample is None:
-        q, _, _ = project(hidden[sel], w_qkv, n_heads, n_kv, d)
+        q = project_q(hidden[sel], w_qkv, n_heads, n_kv, d)
         q = rope(q, pos[sel], rope_base)
         attn = attention(q, sel, k_out, v_out, req, pos)
     else:
         idx = np.asarray(attn_sample, np.int64)
-        q, _, _ = project(hidden[sel[idx]], w_qkv, n_heads, n_kv, d)
+        q = project_q(hidden[sel[idx]], w_qkv, n_heads, n_kv, d)
         q = rope(q, pos[sel[idx]], rope_base)
         attn = np.full((len(sel), n_heads, d), np.nan)
         attn[idx] = attention(q, sel[idx], k_out, v_out, req, pos)

@@ -20,7 +20,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 # pass warns that it does not know it).
 FLAGS = ["-O3", f"--offload-arch={ARCH}", "-fPIC", "-std=c++17",
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         "-Wno-unused-result", "-munsafe-fp-atomics"]
+         "-Wno-unused-result"]
 
 
 def _compile(src: str, build_dir: str = BUILD_DIR, extra=()) -> str:

@@ -89,10 +89,19 @@ def visible_vmax(v_cache: np.ndarray, rows: np.ndarray, req_offsets, n_heads: in
 
 
 def check_selection(gpu_sel: np.ndarray, ref_out: dict, req_of_row: np.ndarray, what: str):
-    """The GPU's selected set equals the oracle's except for near-ties: every row in
-    the symmetric difference is a candidate whose oracle deviation lies within
-    NEAR_TIE (relative) of its request's k-th largest. Returns the swapped rows."""
-    a, b = set(gpu_sel.tolist()), set(ref_out["sel_idx"].tolist())
+    """The GPU's selected set equals the oracle's except for near-ties: each request
+    selects exactly as many rows as in the oracle's result, and every row in the
+    symmetric difference is a candidate whose oracle deviation lies within NEAR_TIE
+    (relative) of its request's k-th largest. Returns the swapped rows."""
+    ga = np.asarray(gpu_sel, np.int64)
+    gb = np.asarray(ref_out["sel_idx"], np.int64)
+    n_req = int(req_of_row.max(initial=-1)) + 1
+    ca = np.bincount(req_of_row[ga], minlength=n_req)
+    cb = np.bincount(req_of_row[gb], minlength=n_req)
+    bad = np.nonzero(ca != cb)[0]
+    assert len(bad) == 0, (f"{what}: request {int(bad[0])} selects {int(ca[bad[0]])} rows, the "
+                           f"oracle {int(cb[bad[0]])}")
+    a, b = set(ga.tolist()), set(gb.tolist())
     sym = sorted(a ^ b)
     for j in sym:
         r = int(req_of_row[j])
@@ -101,6 +110,29 @@ def check_selection(gpu_sel: np.ndarray, ref_out: dict, req_of_row: np.ndarray, 
         assert np.isfinite(dj) and np.isfinite(dk) and dk > 0, f"{what}: row {j} differs and is not a scored candidate"
         assert abs(dj - dk) / dk < NEAR_TIE, f"{what}: row {j} differs (dev {dj} vs k-th {dk})"
     return sym
+
+
+def attn_tile_rows(dtype: str, n_heads: int, n_kv: int) -> int:
+    """Selected rows per attention work-group tile of the library for this shape:
+    bf16 packs the (query, head) pairs of a KV group into 256 columns, so
+    floor(256 / G) queries for G = n_heads / n_kv; fp32 takes 32."""
+    return 256 // (n_heads // n_kv) if dtype == "bf16" else 32
+
+
+def tile_sample(sel_offsets, tile_rows: int, extra: int = 16, seed: int = 0) -> np.ndarray:
+    """Positions into sel_idx that hit every attention tile: the first and last row
+    of each tile of each request (tiles are runs of tile_rows selected rows from the
+    request's first one), plus `extra` seeded positions inside tiles."""
+    off = np.asarray(sel_offsets, np.int64)
+    pos = []
+    for r in range(len(off) - 1):
+        a, b = int(off[r]), int(off[r + 1])
+        for t in range(a, b, tile_rows):
+            pos += [t, min(t + tile_rows, b) - 1]
+    n = int(off[-1])
+    if n and extra:
+        pos += np.random.default_rng(seed).integers(0, n, extra).tolist()
+    return np.unique(np.asarray(pos, np.int64))
 
 
 def csr_ok(sel: np.ndarray, off: np.ndarray, req_offsets: np.ndarray):

@@ -28,9 +28,58 @@ def _say(msg):
     sys.stdout.flush()
 
 
+# Fill value of the pool rows a paged run must never touch.
+POISON = 1000.0
+
+
+def paged_call(spec, lay, block_rows, seg_block, table):
+    """A LayerCall whose batch addresses its caches through a block table."""
+    call = LayerCall(spec, lay)
+    call.seg_block = ints(seg_block)
+    call.block_table = ints(table)
+    call.batch = S.make_batch(call.req_offsets, call.chunk_offsets, call.chunk_src_pos, call.positions,
+                              total_rows=lay.total_rows, max_req_rows=call.max_req_rows,
+                              max_position=lay.max_position, block_rows=block_rows,
+                              seg_block=call.seg_block, block_table=call.block_table)
+    return call
+
+
+def to_pool(a, slot, pool_rows, dtype):
+    """Cache rows placed at their pool rows; every other pool row holds POISON."""
+    pool = inputs.store(np.full((pool_rows,) + a.shape[1:], POISON), dtype)
+    pool[slot] = a
+    return pool
+
+
+def gpu_run(spec, lay, sel, hid, wq, kc_st, vc_st, paged=None):
+    """One srp_fuse_layer call; returns (results, K cache, V cache) in row order.
+    paged = (block_rows, seed): the caches live in a shuffled block pool (each
+    segment padded to whole blocks, Cache-Craft summary, section 4) whose padding
+    rows must come back untouched."""
+    if paged is None:
+        call = LayerCall(spec, lay)
+        kc, vc = upload(kc_st, spec.dtype), upload(vc_st, spec.dtype)
+        call.fuse(sel, hid, wq, kc, vc)
+        torch.cuda.synchronize()
+        return call.results(), download(kc), download(vc)
+    B, seed = paged
+    seg_block, table, slot, pool_rows = inputs.paged_layout(lay, B, seed)
+    call = paged_call(spec, lay, B, seg_block, table)
+    S.srp_validate_batch(call.batch)
+    kp = upload(to_pool(kc_st, slot, pool_rows, spec.dtype), spec.dtype)
+    vp = upload(to_pool(vc_st, slot, pool_rows, spec.dtype), spec.dtype)
+    call.fuse(sel, hid, wq, kp, vp)
+    torch.cuda.synchronize()
+    kp, vp = download(kp), download(vp)
+    pad = np.setdiff1d(np.arange(pool_rows), slot)
+    poison = inputs.store(np.full(1, POISON), spec.dtype)[0]
+    assert np.all(kp[pad] == poison) and np.all(vp[pad] == poison), "paged run touched padding rows"
+    return call.results(), kp[slot], vp[slot]
+
+
 def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel_kw=None,
-             oracle_kw=None, check_group_s0=True, what=""):
-    """Run one layer on both sides and check every output."""
+             oracle_kw=None, check_group_s0=True, what="", paged=None):
+    """Run one layer on both sides and check every output (paged: see gpu_run)."""
     w = w or inputs.generate(spec)
     lay = lay or w.layout
     if kc_st is None:
@@ -45,16 +94,11 @@ def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel
     okw.update(oracle_kw or {})
     want = oracle_layer(spec, lay, hidden_st, wq_st, kc_st, vc_st, **okw)
 
-    _say(f"[gpu] {what or spec.name}: T={lay.total_rows} ratio={ratio} {sel_kw}")
-    call = LayerCall(spec, lay)
+    _say(f"[gpu] {what or spec.name}: T={lay.total_rows} ratio={ratio} {sel_kw}"
+         + (f" paged {paged}" if paged else ""))
     hid = upload(hidden_st, spec.dtype)
     wq = upload(wq_st, spec.dtype)
-    kc = upload(kc_st, spec.dtype)
-    vc = upload(vc_st, spec.dtype)
-    call.fuse(call.select(ratio, **sel_kw), hid, wq, kc, vc)
-    torch.cuda.synchronize()
-    got = call.results()
-    k_out, v_out = download(kc), download(vc)
+    got, k_out, v_out = gpu_run(spec, lay, S.make_select(ratio, **sel_kw), hid, wq, kc_st, vc_st, paged)
 
     req, _ = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
     csr_ok(got["sel_idx"], got["sel_offsets"], lay.req_offsets)
@@ -62,13 +106,10 @@ def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel
         # the choice from given scores is exact on both sides (fp32 ranks, fp64 spans)
         assert np.array_equal(got["sel_idx"], want["sel_idx"]), what + ": selection from scores differs"
     elif sel_kw.get("window", 0) > 0 and check_group_s0:
-        # compare the top-k sets, then the grouping of the GPU's own top-k set
-        call0 = LayerCall(spec, lay)
-        kc0, vc0 = upload(kc_st, spec.dtype), upload(vc_st, spec.dtype)
+        # compare the top-k sets (sizes per request included), then the grouping of
+        # the GPU's own top-k set
         kw0 = dict(sel_kw, window=0, tau=0)
-        call0.fuse(call0.select(ratio, **kw0), hid, wq, kc0, vc0)
-        torch.cuda.synchronize()
-        s0_gpu = call0.results()["sel_idx"]
+        s0_gpu = gpu_run(spec, lay, S.make_select(ratio, **kw0), hid, wq, kc_st, vc_st, paged)[0]["sel_idx"]
         ref0 = oracle_layer(spec, lay, hidden_st, wq_st, kc_st, vc_st, **dict(okw, window=0, tau=0))
         check_selection(s0_gpu, ref0, req, what + " top-k")
         _, src = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
@@ -83,6 +124,7 @@ def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel
         expect = np.concatenate(expect).astype(np.int64) if expect else np.zeros(0, np.int64)
         assert np.array_equal(got["sel_idx"], expect), what + ": grouping of the GPU top-k differs"
     else:
+        # per-request sizes equal the oracle's, swapped rows are near-ties
         check_selection(got["sel_idx"], want, req, what)
     if not np.array_equal(got["sel_idx"], want["sel_idx"]):
         want = oracle_layer(spec, lay, hidden_st, wq_st, kc_st, vc_st, sel_override=got["sel_idx"], **okw)
@@ -102,7 +144,7 @@ def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel
     if scored.any():
         rel = np.abs(got["dev"][scored] - want["dev"][scored]) / np.maximum(want["dev"][scored], 1e-30)
         assert rel.max() < 1e-4, f"{what}: deviation rel err {rel.max():.2e}"
-    return got, want, call
+    return got, want, (k_out, v_out)
 
 
 # --------------------------------------------------------------------------- #
@@ -273,7 +315,7 @@ def test_deterministic_bitwise():
 SPEC_SPANS = dict(span_max=16, tau_smooth=0.4, tau_cover=0.7)
 
 
-def _scores_case(spec, scores, sel_kw, what, w=None, kc=None, vc=None, cand=None):
+def _scores_case(spec, scores, sel_kw, what, w=None, kc=None, vc=None, cand=None, paged=None):
     w = w or inputs.generate(spec)
     if kc is None:
         kc, vc = oracle_caches(w)
@@ -289,7 +331,7 @@ def _scores_case(spec, scores, sel_kw, what, w=None, kc=None, vc=None, cand=None
         okw["cand"] = c
     skw.setdefault("window", 0)
     skw.setdefault("tau", 0)
-    return run_case(spec, w=w, kc_st=kc, vc_st=vc, sel_kw=skw, oracle_kw=okw, what=what)
+    return run_case(spec, w=w, kc_st=kc, vc_st=vc, sel_kw=skw, oracle_kw=okw, what=what, paged=paged)
 
 
 def test_scores_topk_only():
