@@ -12,12 +12,10 @@ from selective_recompute_prefill_amd import inputs
 # Tolerances: rel-L2 and max-abs per output, by storage dtype.
 TOL = {"bf16": (1e-2, 3e-2), "f32": (1e-5, 1e-5)}
 # The fixed max-abs bound holds for unit-scale operands (|K|, |V| below about 4 on
-# the workloads' selections). bf16 rounding errors grow with the magnitude of the
-# operands (a store of v errs by up to |v| 2^-9; rounded queries and probabilities
-# perturb an attention row in proportion to its values), so where large-magnitude
-# rows stay in the cache the bound scales: max-abs <= bound * max(1, mag / MAG_UNIT),
-# mag = the stored value itself for K/V, the largest |V| among the row's visible keys
-# for attention.
+# the workloads' selections). A bf16 store of a value v errs by up to |v| 2^-9, so
+# where large-magnitude rows stay in the cache (a choice by external scores) the
+# bound on cache rows scales: max-abs <= bound * max(1, |v| / MAG_UNIT), which is
+# 3.8 times the storage rounding. Attention rows there use the derived bound below.
 MAG_UNIT = 4.0
 NEAR_TIE = 1e-4  # relative deviation gap below which two candidates may swap
 
@@ -74,18 +72,68 @@ def assert_close(got: np.ndarray, want: np.ndarray, dtype: str, what: str, mag=N
                                     f"|value| {abs(float(want.flat[worst])):.3g} (<= {bw:.3e})")
 
 
-def visible_vmax(v_cache: np.ndarray, rows: np.ndarray, req_offsets, n_heads: int) -> np.ndarray:
-    """[len(rows), n_heads, 1]: the largest |V| of head h's KV group over the keys row
-    j sees (its request's rows up to j; positions ascend with rows in a request)."""
-    nkv = v_cache.shape[1]
-    m = np.abs(v_cache).max(axis=2)  # [T, nkv]
-    pm = np.empty_like(m)
-    for r in range(len(req_offsets) - 1):
-        a, b = int(req_offsets[r]), int(req_offsets[r + 1])
-        if b > a:
-            pm[a:b] = np.maximum.accumulate(m[a:b], axis=0)
-    g = (np.arange(n_heads) * nkv) // n_heads
-    return pm[np.asarray(rows, np.int64)][:, g][:, :, None]
+# Attention with a choice by external scores (high-noise rows stay in the cache).
+# The kernel rounds to bf16 (u = 2^-9, round to nearest even) the queries, the keys
+# and values as the cache stores them, the probabilities that enter the PV product,
+# and the output. To first order the output error of row j, head h is
+#   sum_i p_i (v_i - o) ds_i + sum_i p_i v_i (g_i + e_i) + o n,
+# ds_i = (q (a) . k_i + q . k_i (b_i)) / sqrt(d) with relative rounding errors a (of
+# the query, shared by every key), b_i, g_i, e_i, n. Taking them independent and
+# uniform on [-u, u] (variance u^2 / 3) gives a standard deviation per output element
+# (attn_sigma). Where the fixed max-abs bound does not hold, an element may err by up
+# to ATTN_Z of those deviations: a simulation of these rounding points reproduces the
+# kernel's errors and stays within 5.2 deviations wherever they exceed 3e-2.
+BF16_U = 2.0 ** -9
+ATTN_Z = 8.0
+
+
+def attn_sigma(q: np.ndarray, K: np.ndarray, V: np.ndarray, o: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """Standard deviation [nh, d] of the bf16 rounding error of one attention row (model
+    above): q [nh, d] the row's roped query, K/V [T, nkv, d] the fused caches, o
+    [nh, d] the exact output, keys the rows it sees. All from the oracle (fp64)."""
+    nh, d = q.shape
+    nkv = K.shape[1]
+    cs = 1.0 / np.sqrt(d)
+    out = np.zeros_like(o)
+    for h in range(nh):
+        g = (h * nkv) // nh
+        k, v = K[keys, g], V[keys, g]
+        s = (k @ q[h]) * cs
+        p = np.exp(s - s.max())
+        p /= p.sum()
+        dv = v - o[h][None, :]
+        gq = cs * (k.T @ (p[:, None] * dv))                     # d(o) / d(q), [d, d]
+        q_term = ((q[h] ** 2)[:, None] * gq ** 2).sum(0)
+        k_term = cs ** 2 * (((p ** 2) * ((k * q[h][None, :]) ** 2).sum(1))[:, None] * dv ** 2).sum(0)
+        pv_term = 2.0 * ((p ** 2)[:, None] * v ** 2).sum(0)
+        out[h] = np.sqrt(BF16_U ** 2 / 3.0 * (q_term + k_term + pv_term + o[h] ** 2))
+    return out
+
+
+def assert_attention_bf16_scores(got: np.ndarray, want: np.ndarray, q: np.ndarray, K: np.ndarray,
+                                 V: np.ndarray, rows: np.ndarray, req_offsets, positions, what: str):
+    """Attention rows of a choice by external scores: rel-L2 <= 1e-2 overall; max-abs
+    <= 3e-2, or <= ATTN_Z x attn_sigma where that is larger (computed only for rows
+    that exceed 3e-2). got/want/q: [n, nh, d] for the selected rows `rows`."""
+    rl, ma = TOL["bf16"]
+    got = np.asarray(got, np.float64)
+    assert got.shape == want.shape and np.isfinite(got).all(), what
+    if want.size == 0:
+        return
+    rel = np.linalg.norm(got - want) / max(np.linalg.norm(want), 1e-300)
+    assert rel <= rl, f"{what}: rel-L2 {rel:.3e} (<= {rl})"
+    err = np.abs(got - want)
+    req_of = np.searchsorted(np.asarray(req_offsets), rows, side="right") - 1
+    pos = np.asarray(positions)
+    for i in np.nonzero(err.reshape(len(rows), -1).max(axis=1) > ma)[0]:
+        j, r = int(rows[i]), int(req_of[i])
+        span = np.arange(int(req_offsets[r]), int(req_offsets[r + 1]))
+        keys = span[pos[span] <= pos[j]]
+        bound = np.maximum(ma, ATTN_Z * attn_sigma(q[i], K, V, want[i], keys))
+        worst = np.unravel_index(int(np.argmax(err[i] - bound)), bound.shape)
+        assert err[i][worst] <= bound[worst], (
+            f"{what}: row {j} head {worst[0]} abs err {err[i][worst]:.3e} at |value| "
+            f"{abs(want[i][worst]):.3g} (<= max(3e-2, {ATTN_Z:g} sigma) = {bound[worst]:.3e})")
 
 
 def check_selection(gpu_sel: np.ndarray, ref_out: dict, req_of_row: np.ndarray, what: str):

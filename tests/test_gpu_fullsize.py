@@ -21,8 +21,8 @@ from selective_recompute_prefill_amd import inputs
 from selective_recompute_prefill_amd import srp as S
 from selective_recompute_prefill_amd.device import LayerCall, download, ints, upload
 
-from parity import (assert_close, attn_tile_rows, check_selection, csr_ok, oracle_caches,
-                    oracle_layer, tile_sample, visible_vmax)
+from parity import (assert_attention_bf16_scores, assert_close, attn_tile_rows, check_selection, csr_ok,
+                    oracle_caches, oracle_layer, tile_sample)
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -67,11 +67,13 @@ def _compare_layer(spec, lay, got, hidden_st, wq_st, kc_st, vc_st, want, okw, wh
     assert_close(ref.widen(got["v_cache"], dt), want["v_cache"], dt, what + " V", mag(want["v_cache"]))
     ga = ref.widen(got["attn_out"], dt)
     rows = got["sel_idx"] if sp is None else got["sel_idx"][sp]
-    amag = visible_vmax(want["v_cache"], rows, lay.req_offsets, spec.n_heads) if scaled else None
-    if sp is not None:
-        assert_close(ga[sp], want["attn_out"][sp], dt, what + " attention (sampled rows)", amag)
+    g_rows, w_rows = (ga, want["attn_out"]) if sp is None else (ga[sp], want["attn_out"][sp])
+    label = what + (" attention" if sp is None else " attention (every tile)")
+    if scaled and dt == "bf16":
+        assert_attention_bf16_scores(g_rows, w_rows, want["q"], want["k_cache"], want["v_cache"], rows,
+                                     lay.req_offsets, lay.positions, label)
     else:
-        assert_close(ga, want["attn_out"], dt, what + " attention", amag)
+        assert_close(g_rows, w_rows, dt, label)
     scored = np.isfinite(want["dev"])
     rel = np.abs(got["dev"][:lay.total_rows][scored] - want["dev"][scored]) / want["dev"][scored]
     assert rel.max() < 1e-4, f"{what}: deviation rel err {rel.max():.2e}"

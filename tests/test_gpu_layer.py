@@ -17,8 +17,8 @@ from selective_recompute_prefill_amd import inputs
 from selective_recompute_prefill_amd import srp as S
 from selective_recompute_prefill_amd.device import LayerCall, download, ints, upload
 
-from parity import (assert_close, check_selection, csr_ok, oracle_caches, oracle_layer,
-                    visible_vmax)
+from parity import (assert_attention_bf16_scores, assert_close, check_selection, csr_ok, oracle_caches,
+                    oracle_layer)
 
 pytestmark = pytest.mark.gpu
 
@@ -136,8 +136,13 @@ def run_case(spec, w=None, lay=None, hidden_st=None, kc_st=None, vc_st=None, sel
     mag = lambda a: np.abs(a) if scaled else None
     assert_close(ref.widen(k_out, dt), want["k_cache"], dt, what + " K cache", mag(want["k_cache"]))
     assert_close(ref.widen(v_out, dt), want["v_cache"], dt, what + " V cache", mag(want["v_cache"]))
-    amag = visible_vmax(want["v_cache"], want["sel_idx"], lay.req_offsets, spec.n_heads) if scaled else None
-    assert_close(ref.widen(got["attn_out"], dt), want["attn_out"], dt, what + " attention", amag)
+    if scaled and dt == "bf16":
+        assert_attention_bf16_scores(ref.widen(got["attn_out"], dt), want["attn_out"], want["q"],
+                                     want["k_cache"], want["v_cache"], want["sel_idx"], lay.req_offsets,
+                                     lay.positions, what + " attention")
+    else:
+        assert_close(ref.widen(got["attn_out"], dt), want["attn_out"], dt, what + " attention",
+                     mag(want["attn_out"]))
     # deviations of scored rows (fp32 on the GPU)
     scored = np.isfinite(want["dev"])
     assert np.array_equal(np.isfinite(got["dev"][:lay.total_rows]), scored)

@@ -37,3 +37,33 @@ def test_tile_sample_hits_every_tile():
         end = min(t + tr, off[r + 1])
         assert t in sp and end - 1 in sp
     assert sp.max() < off[-1] and len(sp) == 2 * len(tiles)
+
+
+def test_attn_sigma_matches_monte_carlo():
+    # the first-order deviation of the bf16 rounding model equals the spread of the
+    # exact output under random relative errors of that model (uniform on [-u, u])
+    from parity import BF16_U, attn_sigma
+    rng = np.random.default_rng(4)
+    nh, nkv, d, n = 2, 1, 16, 24
+    q = rng.standard_normal((nh, d)) * 2.0
+    K = rng.standard_normal((n, nkv, d)) * 1.5
+    V = rng.standard_normal((n, nkv, d)) * 3.0
+    keys = np.arange(n)
+
+    def out(eq, ek, ep, ev, eo):
+        o = np.zeros((nh, d))
+        for h in range(nh):
+            s = (K[:, 0] * (1 + ek[h])) @ (q[h] * (1 + eq[h])) / np.sqrt(d)
+            p = np.exp(s - s.max())
+            o[h] = ((p * (1 + ep[h])) @ (V[:, 0] * (1 + ev[h]))) / p.sum()
+        return o * (1 + eo)
+
+    zero = lambda: (np.zeros((nh, d)), np.zeros((nh, n, d)), np.zeros((nh, n)), np.zeros((nh, n, d)),
+                    np.zeros((nh, d)))
+    o0 = out(*zero())
+    uni = lambda shape: rng.uniform(-BF16_U, BF16_U, shape)
+    samples = np.stack([out(uni((nh, d)), uni((nh, n, d)), uni((nh, n)), uni((nh, n, d)), uni((nh, d))) - o0
+                        for _ in range(3000)])
+    sig = attn_sigma(q, K, V, o0, keys)
+    ratio = samples.std(axis=0) / sig
+    assert 0.85 < np.median(ratio) < 1.15 and ratio.min() > 0.7 and ratio.max() < 1.3, ratio
