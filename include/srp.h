@@ -201,6 +201,26 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch,
                    int32_t *sel_offsets, void *attn_out, float *dev_out,
                    void *workspace, size_t workspace_bytes, srp_stream_t stream);
 
+/* srp_fuse_layer without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). Same arguments, outputs and errors as srp_fuse_layer minus
+ * workspace / workspace_bytes. Its scratch space (the layer's workspace with 16
+ * split-K partial-tile slots instead of 256, and a rotary table built on the device
+ * for the call's head_dim, rope_base and max_position) lives in a static device
+ * array of 128 MiB that every GPU the library runs on holds until the process
+ * ends; the call allocates nothing. A layer whose scratch exceeds 128 MiB gets
+ * SRP_E_WORKSPACE before anything is enqueued (bf16, head_dim 128: about 5,600 rows
+ * at hidden 8192 with 64/8 heads, 7,600 at 5120 with 40/8, 8,600 at 4096 with
+ * 32/8). Every call on one GPU uses that GPU's
+ * one array, which keeps the last call's contents (the next call sets everything it
+ * reads before reading it): calls that overlap on one GPU (different streams or
+ * threads) race and must be serialised by the caller. */
+int srp_fuse_layer_noalloc(const srp_dims *dims, const srp_batch *batch,
+                           const srp_select *sel, const void *hidden, const void *w_qkv,
+                           void *k_cache, void *v_cache, int32_t *sel_idx,
+                           int32_t *sel_offsets, void *attn_out, float *dev_out,
+                           srp_stream_t stream);
+
 /* Offline chunk encoding (CacheClip walkthrough, Figure 4, offline phase: each
  * chunk's KV cache is computed once, at chunk-local positions):
  *   k_out[j] = R(positions[j]) W_k hidden[j],  v_out[j] = W_v hidden[j]

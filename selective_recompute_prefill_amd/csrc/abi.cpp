@@ -204,28 +204,30 @@ int srp_workspace_size(const srp_dims *dims, const srp_batch *batch, const srp_s
   return SRP_OK;
 }
 
-int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_select *sel,
-                   const void *hidden, const void *w_qkv, void *k_cache, void *v_cache,
-                   int32_t *sel_idx, int32_t *sel_offsets, void *attn_out, float *dev_out,
-                   void *workspace, size_t workspace_bytes, srp_stream_t stream) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// Argument checks of srp_fuse_layer that do not involve the workspace.
+int check_fuse_args(const srp_dims *dims, const srp_batch *batch, const srp_select *sel,
+                    const void *hidden, const void *w_qkv, const void *k_cache, const void *v_cache,
+                    const int32_t *sel_idx, const int32_t *sel_offsets, const void *attn_out) {
   CHECK(check_dims(dims));
   CHECK(check_batch(batch));
   CHECK(check_select(sel));
   CHECK(check_select_batch(batch, sel));
-  const srp_dims &d = *dims;
-  const srp_batch &b = *batch;
-  const int T = b.total_rows;
-  if (T > 0 && (!hidden || !w_qkv || !k_cache || !v_cache || !sel_idx || !attn_out))
+  if (batch->total_rows > 0 && (!hidden || !w_qkv || !k_cache || !v_cache || !sel_idx || !attn_out))
     return fail(SRP_E_INVALID, "tensor arguments must not be NULL");
   if (!sel_offsets) return fail(SRP_E_INVALID, "sel_offsets must not be NULL");
-  const size_t need = carve(d, b, nullptr).bytes;
-  if (!workspace || workspace_bytes < need)
-    return fail(SRP_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
-  hipStream_t s = (hipStream_t)stream;
-  RopeTable rt;
-  CHECK(get_table(d.head_dim, d.rope_base, b.max_position, &rt));
-  const Workspace w = carve(d, b, (char *)workspace);
+  return SRP_OK;
+}
+
+// The launch sequence of one fused layer on a carved workspace and a rotary table.
+int fuse_layer_launch(const srp_dims &d, const srp_batch &b, const srp_select *sel, const void *hidden,
+                      const void *w_qkv, void *k_cache, void *v_cache, int32_t *sel_idx,
+                      int32_t *sel_offsets, void *attn_out, float *dev_out, const Workspace &w,
+                      const RopeTable &rt, hipStream_t s) {
+  const int T = b.total_rows;
   const int kvd = d.n_kv_heads * d.head_dim, qd = d.n_heads * d.head_dim;
   const size_t es = d.dtype == SRP_BF16 ? 2 : 4;
 
@@ -311,7 +313,7 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   g.dev_part = w.dev_part;
   g.row_slot = w.row_slot;
   g.part = w.gemm_part;
-  g.part_cap = w.gemm_part ? kGemmParts : 0;
+  g.part_cap = w.gemm_part ? w.gemm_parts : 0;
   marks.mark(1);
   SRP_HIP(launch_gemm(g, s));
   marks.mark(2);
@@ -377,6 +379,126 @@ int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_selec
   if (T > 0) SRP_HIP(launch_attention(aa, s));
   marks.mark(6);
   return SRP_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int srp_fuse_layer(const srp_dims *dims, const srp_batch *batch, const srp_select *sel,
+                   const void *hidden, const void *w_qkv, void *k_cache, void *v_cache,
+                   int32_t *sel_idx, int32_t *sel_offsets, void *attn_out, float *dev_out,
+                   void *workspace, size_t workspace_bytes, srp_stream_t stream) {
+  g_err.clear();
+  CHECK(check_fuse_args(dims, batch, sel, hidden, w_qkv, k_cache, v_cache, sel_idx, sel_offsets, attn_out));
+  const size_t need = carve(*dims, *batch, nullptr).bytes;
+  if (!workspace || workspace_bytes < need)
+    return fail(SRP_E_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+  RopeTable rt;
+  CHECK(get_table(dims->head_dim, dims->rope_base, batch->max_position, &rt));
+  return fuse_layer_launch(*dims, *batch, sel, hidden, w_qkv, k_cache, v_cache, sel_idx, sel_offsets,
+                           attn_out, dev_out, carve(*dims, *batch, (char *)workspace), rt,
+                           (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ------------------------------------------------------------------------- //
+// no-allocation variant: the workspace and the rotary table live in `scratch`, a
+// file-scope device array of kScratchBytes that every GPU the library runs on
+// holds until the process ends. Host code never uses the array's name as an
+// address (in host code it only stands in for the symbol): its device address on
+// each device comes from hipGetSymbolAddress on the first call there.
+// ------------------------------------------------------------------------- //
+namespace {
+
+constexpr size_t kScratchBytes = (size_t)128 << 20;
+// split-K partial-tile slots the variant carves (4 MiB; the workspace variant: 256)
+constexpr int kScratchParts = 16;
+constexpr int kMaxDevices = 64;
+
+struct ScratchDev {
+  char *ptr = nullptr;      // device address of `scratch` on this device
+  int table_d = 0;          // the rotary table at the front of the array: head dim,
+  double table_base = 0.0;  // base
+  int table_cap = 0;        // and positions covered (0: none built)
+};
+std::mutex g_smu;
+ScratchDev g_sdev[kMaxDevices];
+
+// cos / sin of p * base^(-2i/d) for p < n_pos, i < d/2, evaluated in double and
+// rounded to float (the same expressions as the host-built tables).
+__global__ void rope_table_kernel(float *cos_t, float *sin_t, int half, int d, double base, int n_pos) {
+  const long n = (long)n_pos * half;
+  for (long t = (long)blockIdx.x * blockDim.x + threadIdx.x; t < n; t += (long)gridDim.x * blockDim.x) {
+    const int p = (int)(t / half), i = (int)(t - (long)p * half);
+    const double f = pow(base, -2.0 * i / d);
+    const double th = (double)p * f;
+    cos_t[t] = (float)cos(th);
+    sin_t[t] = (float)sin(th);
+  }
+}
+
+size_t table_bytes(int d, int cap) { return align_up((size_t)cap * (d / 2) * sizeof(float), 256) * 2; }
+
+}  // namespace
+
+static __device__ __align__(256) char scratch[kScratchBytes];
+
+extern "C" {
+
+int srp_fuse_layer_noalloc(const srp_dims *dims, const srp_batch *batch, const srp_select *sel,
+                           const void *hidden, const void *w_qkv, void *k_cache, void *v_cache,
+                           int32_t *sel_idx, int32_t *sel_offsets, void *attn_out, float *dev_out,
+                           srp_stream_t stream) {
+  g_err.clear();
+  CHECK(check_fuse_args(dims, batch, sel, hidden, w_qkv, k_cache, v_cache, sel_idx, sel_offsets, attn_out));
+  const srp_dims &d = *dims;
+  const srp_batch &b = *batch;
+  hipStream_t s = (hipStream_t)stream;
+  // host-checkable size limit first: the table of this call's positions plus the
+  // workspace (a table kept from an earlier call may be larger, checked below)
+  const int cap0 = (b.max_position + 1023) / 1024 * 1024;
+  const size_t ws_bytes = carve(d, b, nullptr, kScratchParts).bytes;
+  if (table_bytes(d.head_dim, cap0) + ws_bytes > kScratchBytes)
+    return fail(SRP_E_WORKSPACE,
+                "this layer needs %zu bytes of scratch; srp_fuse_layer_noalloc has %zu (use srp_fuse_layer with a workspace)",
+                table_bytes(d.head_dim, cap0) + ws_bytes, kScratchBytes);
+  int dev = 0;
+  SRP_HIP(hipGetDevice(&dev));
+  if (dev < 0 || dev >= kMaxDevices) return fail(SRP_E_UNSUPPORTED, "device %d beyond the %d the variant tracks", dev, kMaxDevices);
+  std::lock_guard<std::mutex> lk(g_smu);
+  ScratchDev &sd = g_sdev[dev];
+  if (!sd.ptr) {
+    // once per device, with that device current
+    void *p = nullptr;
+    SRP_HIP(hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)));
+    if (!p) return fail(SRP_E_HIP, "hipGetSymbolAddress returned no address for the scratch array");
+    sd.ptr = (char *)p;
+  }
+  // the table is rebuilt only when this call needs another one (or more positions)
+  const bool rebuild = sd.table_cap == 0 || sd.table_d != d.head_dim || sd.table_base != d.rope_base ||
+                       sd.table_cap < b.max_position;
+  int cap = rebuild ? cap0 : sd.table_cap;
+  // a larger kept table that leaves too little room is rebuilt at this call's size
+  if (!rebuild && table_bytes(d.head_dim, cap) + ws_bytes > kScratchBytes) cap = cap0;
+  const bool build = rebuild || cap != sd.table_cap;
+  const size_t tb = table_bytes(d.head_dim, cap);
+  const int half = d.head_dim / 2;
+  float *cos_t = (float *)sd.ptr, *sin_t = (float *)(sd.ptr + tb / 2);
+  if (build) {
+    const long n = (long)cap * half;
+    const unsigned grid = (unsigned)std::min<long>((n + 255) / 256, 4096);
+    hipLaunchKernelGGL(rope_table_kernel, dim3(grid), dim3(256), 0, s, cos_t, sin_t, half, d.head_dim,
+                       d.rope_base, cap);
+    SRP_HIP(hipGetLastError());
+    sd.table_d = d.head_dim;
+    sd.table_base = d.rope_base;
+    sd.table_cap = cap;
+  }
+  const RopeTable rt{cos_t, sin_t, half, cap};
+  return fuse_layer_launch(d, b, sel, hidden, w_qkv, k_cache, v_cache, sel_idx, sel_offsets, attn_out,
+                           dev_out, carve(d, b, sd.ptr + tb, kScratchParts), rt, s);
 }
 
 int srp_profile_begin(int32_t max_calls) {

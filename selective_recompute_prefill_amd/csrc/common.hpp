@@ -205,6 +205,7 @@ struct Workspace {
   float *gemm_part;    // bf16: [kGemmParts][kGemmPartFloats] split-K partial tiles
   int32_t *row_slot;   // paged cache: [T] pool row of each batch row (else NULL)
   void *k_lin, *v_lin; // paged cache: [T][kvdim] fused K (and fp32 V) gathered in row order
+  int gemm_parts;      // partial-tile slots at gemm_part (0: no split of the last round)
   size_t bytes;
 };
 // split-K partial tiles of the projection GEMMs' last round
@@ -259,8 +260,9 @@ __device__ __forceinline__ void vt_chunk(int r0, int g, int T, int D, int nkv, c
   }
 }
 
-// Lays the workspace out from `base` (nullptr: just measure).
-inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base) {
+// Lays the workspace out from `base` (nullptr: just measure), with `parts`
+// split-K partial-tile slots for bf16 projections.
+inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base, int parts = kGemmParts) {
   const size_t T = (size_t)(b.total_rows > 0 ? b.total_rows : 1);
   const size_t nr = (size_t)b.n_req;
   const size_t es = d.dtype == SRP_BF16 ? 2 : 4;
@@ -296,7 +298,8 @@ inline Workspace carve(const srp_dims &d, const srp_batch &b, char *base) {
   w.vt = d.dtype == SRP_BF16 ? take((size_t)d.n_kv_heads * d.head_dim * vt_stride(b.total_rows) * 2) : nullptr;
   w.tiles = (int32_t *)take((size_t)3 * max_attn_tiles((int)T, (int)nr) * 4);
   w.ctr = (int32_t *)take(16 * 4);
-  w.gemm_part = d.dtype == SRP_BF16 ? (float *)take((size_t)kGemmParts * kGemmPartFloats * 4) : nullptr;
+  w.gemm_parts = d.dtype == SRP_BF16 ? parts : 0;
+  w.gemm_part = w.gemm_parts > 0 ? (float *)take((size_t)w.gemm_parts * kGemmPartFloats * 4) : nullptr;
   if (b.block_rows > 0) {
     w.row_slot = (int32_t *)take(T * 4);
     w.k_lin = take(T * kvd * es);

@@ -19,7 +19,7 @@ SRP_SEL_TOPK, SRP_SEL_GIVEN, SRP_SEL_SCORES = 0, 1, 2
 SRP_K_ROUND, SRP_K_CEIL = 0, 1
 SRP_DEV_KV, SRP_DEV_V = 0, 1
 
-EXPORTS = ("srp_workspace_size", "srp_fuse_layer", "srp_encode_kv", "srp_rerotate_kv",
+EXPORTS = ("srp_workspace_size", "srp_fuse_layer", "srp_fuse_layer_noalloc", "srp_encode_kv", "srp_rerotate_kv",
            "srp_residual_rmsnorm", "srp_stack_workspace_size", "srp_fuse_stack",
            "srp_controller_ratio", "srp_validate_batch", "srp_profile_begin", "srp_profile_end",
            "srp_profile_stage_name", "srp_last_error", "srp_version")
@@ -79,6 +79,8 @@ def lib() -> ctypes.CDLL:
         L.srp_workspace_size.argtypes = [P(Dims), P(Batch), P(Select), P(sz)]
         L.srp_fuse_layer.argtypes = [P(Dims), P(Batch), P(Select), vp, vp, vp, vp, vp, vp, vp, vp,
                                      vp, sz, vp]
+        L.srp_fuse_layer_noalloc.argtypes = [P(Dims), P(Batch), P(Select), vp, vp, vp, vp, vp, vp, vp,
+                                             vp, vp]
         L.srp_encode_kv.argtypes = [P(Dims), i32, i32, vp, vp, vp, vp, vp, vp]
         L.srp_rerotate_kv.argtypes = [P(Dims), P(Batch), vp, vp]
         L.srp_residual_rmsnorm.argtypes = [P(Dims), vp, vp, vp, vp, i32, i32, ctypes.c_float, vp]
@@ -92,7 +94,7 @@ def lib() -> ctypes.CDLL:
         L.srp_profile_end.argtypes = [P(ctypes.c_float), i32, P(i32)]
         L.srp_profile_stage_name.argtypes = [i32]
         L.srp_profile_stage_name.restype = ctypes.c_char_p
-        for f in ("srp_workspace_size", "srp_fuse_layer", "srp_encode_kv", "srp_rerotate_kv",
+        for f in ("srp_workspace_size", "srp_fuse_layer", "srp_fuse_layer_noalloc", "srp_encode_kv", "srp_rerotate_kv",
                   "srp_residual_rmsnorm", "srp_stack_workspace_size", "srp_fuse_stack",
                   "srp_controller_ratio", "srp_validate_batch", "srp_profile_begin",
                   "srp_profile_end"):
@@ -165,6 +167,16 @@ def srp_fuse_layer(dims: Dims, batch: Batch, sel: Select, hidden, w_qkv, k_cache
         ctypes.byref(dims), ctypes.byref(batch), ctypes.byref(sel), _ptr(hidden), _ptr(w_qkv),
         _ptr(k_cache), _ptr(v_cache), _ptr(sel_idx), _ptr(sel_offsets), _ptr(attn_out),
         _ptr(dev_out), _ptr(workspace), int(workspace_bytes), _stream(stream)))
+
+
+def srp_fuse_layer_noalloc(dims: Dims, batch: Batch, sel: Select, hidden, w_qkv, k_cache, v_cache,
+                           sel_idx, sel_offsets, attn_out, dev_out, stream=None) -> int:
+    """srp_fuse_layer on the library's static scratch array (no workspace, no
+    allocation); calls that overlap on one GPU race."""
+    return _check(lib().srp_fuse_layer_noalloc(
+        ctypes.byref(dims), ctypes.byref(batch), ctypes.byref(sel), _ptr(hidden), _ptr(w_qkv),
+        _ptr(k_cache), _ptr(v_cache), _ptr(sel_idx), _ptr(sel_offsets), _ptr(attn_out),
+        _ptr(dev_out), _stream(stream)))
 
 
 def srp_encode_kv(dims: Dims, n_rows: int, max_position: int, hidden, w_qkv, positions, k_out,

@@ -199,3 +199,14 @@ def test_struct_layouts_match_header():
     assert S.Select.scores.offset == 56 and S.Select.fresh_all.offset == 88
     assert ctypes.sizeof(S.Select) == 96
     assert S.Layer.ratio.offset == 40 and ctypes.sizeof(S.Layer) == 48
+
+
+def test_noalloc_rejects_a_layer_beyond_its_scratch_before_any_hip_call():
+    # the 16K-row layer at hidden 5120 needs more than the 128 MiB static scratch:
+    # rejected on the host (the pointers are never dereferenced)
+    d = S.make_dims(5120, 40, 8, 128, 1e4, S.SRP_BF16)
+    b = S.Batch(1, 2, 16512, 16512, 16512, 8, 8, 8, 8, 0, None, None)
+    rc = S.lib().srp_fuse_layer_noalloc(ctypes.byref(d), ctypes.byref(b), ctypes.byref(S.make_select(0.2)),
+                                        8, 8, 8, 8, 8, 8, 8, None, None)
+    assert rc == S.SRP_E_WORKSPACE
+    assert "srp_fuse_layer with a workspace" in S.lib().srp_last_error().decode()
