@@ -269,6 +269,11 @@ typedef struct {
                          NULL: k_cache already holds the cache                        */
   const void *v_host; /* same for V; given exactly when k_host is                      */
   double ratio;       /* the layer's recompute ratio, in [0, 1]                        */
+  int32_t mode;       /* layers >= 1 (CacheBlend walkthrough, "Implementation": the
+                         per-layer check_flag): SRP_SEL_TOPK (0) checks the layer, ranking
+                         the previous layer's selection by KV deviation at `ratio`;
+                         SRP_SEL_GIVEN recomputes exactly the previous layer's selection
+                         (ratio unused). Layer 0 selects with `first` instead.          */
 } srp_layer;
 
 /* Bytes of device scratch that srp_fuse_stack needs (written to *bytes):
@@ -286,9 +291,11 @@ int srp_stack_workspace_size(const srp_dims *dims, const srp_batch *batch,
  * soon as its cache has landed in GPU memory; Cache-Craft summary, section 4: the
  * caches of later layers are loaded ahead).
  *   Layer 0 selects with `first` (its ratio field is ignored; layers[0].ratio
- *   applies); layer l >= 1 ranks by KV deviation only the previous layer's selection
- *   (fresh rows are always recomputed) at layers[l].ratio, with first's dev_mode,
- *   k_rule and fresh_all. After every layer hidden[j] <- RMSNorm(hidden[j] +
+ *   applies); layer l >= 1 starts from the previous layer's selection (fresh rows
+ *   are always recomputed) and, with layers[l].mode SRP_SEL_TOPK, ranks it by KV
+ *   deviation at layers[l].ratio with first's dev_mode, k_rule and fresh_all, or,
+ *   with SRP_SEL_GIVEN, recomputes it as it is (check on the first layers, then pass
+ *   the indices on). After every layer hidden[j] <- RMSNorm(hidden[j] +
  *   attn[j]) on its selected rows (srp_residual_rmsnorm, eps rms_eps), so hidden
  *   ends as the stack's output. sel_idx, sel_offsets and attn_out end as the last
  *   layer's; every layer's fused cache stays in its k_cache / v_cache.

@@ -483,7 +483,8 @@ def fuse_stack(*, hidden, layers: Sequence[dict], req_offsets, chunk_offsets,
                ratios: Sequence[float], window: int = 0, tau: int = 0,
                dev_mode: str = "kv", rms_eps: float = 1e-6,
                round_hidden=None, k_rule: str = "round", fresh_all: bool = False,
-               first_kw: Optional[dict] = None) -> List[Dict[str, np.ndarray]]:
+               first_kw: Optional[dict] = None,
+               modes: Optional[Sequence[str]] = None) -> List[Dict[str, np.ndarray]]:
     """Gradual filtering across stacked layers (CacheBlend walkthrough, "The
     chicken-and-egg problem": layer 1 scores every token, each later layer scores
     only the previous layer's selection, so the set only shrinks; the fusor is
@@ -492,7 +493,10 @@ def fuse_stack(*, hidden, layers: Sequence[dict], req_offsets, chunk_offsets,
     the selection are not read again. round_hidden, if given, is applied to the new
     hidden rows (the storage rounding of a bf16 model's hidden state). k_rule and
     fresh_all apply to every layer; first_kw holds further selection settings of
-    layer 1 only (e.g. mode "scores" with its scores and span settings)."""
+    layer 1 only (e.g. mode "scores" with its scores and span settings). modes[l]
+    for l >= 1 is the layer's check flag (CacheBlend walkthrough, "Implementation":
+    a layer either checks, "topk", or reuses the indices it is handed, "given");
+    None = every layer checks."""
     x = hidden.copy()
     outs = []
     cand = None
@@ -502,7 +506,8 @@ def fuse_stack(*, hidden, layers: Sequence[dict], req_offsets, chunk_offsets,
                        chunk_offsets=chunk_offsets, chunk_src_pos=chunk_src_pos,
                        positions=positions, n_heads=n_heads, n_kv=n_kv,
                        head_dim=head_dim, rope_base=rope_base, ratio=ratios[l],
-                       **dict(dict(mode="topk", window=window if l == 0 else 0, tau=tau,
+                       **dict(dict(mode="topk" if l == 0 or modes is None else modes[l],
+                                   window=window if l == 0 else 0, tau=tau,
                                    dev_mode=dev_mode, cand=cand, k_rule=k_rule,
                                    fresh_all=fresh_all),
                               **((first_kw or {}) if l == 0 else {})))

@@ -653,6 +653,8 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
   for (int l = 0; l < n_layers; ++l) {
     const srp_layer &L = layers[l];
     if (!(L.ratio >= 0.0 && L.ratio <= 1.0)) return fail(SRP_E_INVALID, "layer %d: ratio must lie in [0, 1]", l);
+    if (l > 0 && L.mode != SRP_SEL_TOPK && L.mode != SRP_SEL_GIVEN)
+      return fail(SRP_E_INVALID, "layer %d: mode must be SRP_SEL_TOPK or SRP_SEL_GIVEN", l);
     if ((L.k_host == nullptr) != (L.v_host == nullptr))
       return fail(SRP_E_INVALID, "layer %d: k_host and v_host go together", l);
     if (T > 0 && (!L.w_qkv || !L.k_cache || !L.v_cache))
@@ -727,7 +729,7 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
     sl.ratio = layers[l].ratio;
     if (l > 0) {
       sl = srp_select{};
-      sl.mode = SRP_SEL_TOPK;
+      sl.mode = layers[l].mode;
       sl.ratio = layers[l].ratio;
       sl.dev_mode = first->dev_mode;
       sl.k_rule = first->k_rule;

@@ -61,7 +61,7 @@ class Select(ctypes.Structure):
 class Layer(ctypes.Structure):
     _fields_ = [("w_qkv", ctypes.c_void_p), ("k_cache", ctypes.c_void_p),
                 ("v_cache", ctypes.c_void_p), ("k_host", ctypes.c_void_p),
-                ("v_host", ctypes.c_void_p), ("ratio", ctypes.c_double)]
+                ("v_host", ctypes.c_void_p), ("ratio", ctypes.c_double), ("mode", ctypes.c_int32)]
 
 
 _lib: Optional[ctypes.CDLL] = None
@@ -198,11 +198,14 @@ def srp_residual_rmsnorm(dims: Dims, hidden, attn_out, sel_idx, sel_offsets, n_r
                                              int(sel_capacity), float(eps), _stream(stream)))
 
 
-def make_layer(w_qkv, k_cache, v_cache, ratio: float, k_host=None, v_host=None) -> Layer:
+def make_layer(w_qkv, k_cache, v_cache, ratio: float, k_host=None, v_host=None,
+               mode=SRP_SEL_TOPK) -> Layer:
     """Layer descriptor for srp_fuse_stack; k_host / v_host are host tensors in
     page-locked memory (torch pin_memory=True) or None when the device caches are
-    already filled."""
-    return Layer(_ptr(w_qkv), _ptr(k_cache), _ptr(v_cache), _ptr(k_host), _ptr(v_host), float(ratio))
+    already filled; mode (layers after the first): SRP_SEL_TOPK checks the layer,
+    SRP_SEL_GIVEN recomputes the previous layer's selection as it is."""
+    return Layer(_ptr(w_qkv), _ptr(k_cache), _ptr(v_cache), _ptr(k_host), _ptr(v_host), float(ratio),
+                 int(mode))
 
 
 def srp_stack_workspace_size(dims: Dims, batch: Batch, first: Select) -> int:

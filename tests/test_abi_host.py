@@ -198,7 +198,7 @@ def test_struct_layouts_match_header():
     assert S.Select.ratio.offset == 8 and S.Select.cand.offset == 32
     assert S.Select.scores.offset == 56 and S.Select.fresh_all.offset == 88
     assert ctypes.sizeof(S.Select) == 96
-    assert S.Layer.ratio.offset == 40 and ctypes.sizeof(S.Layer) == 48
+    assert S.Layer.ratio.offset == 40 and S.Layer.mode.offset == 48 and ctypes.sizeof(S.Layer) == 56
 
 
 def test_noalloc_rejects_a_layer_beyond_its_scratch_before_any_hip_call():

@@ -39,8 +39,10 @@ def _stack_spec(**kw):
     return inputs.small_spec("stack", **base)
 
 
-def _serial(spec, lay, call, w, caches, first_kw):
-    """The reference chain: one srp_fuse_layer + srp_residual_rmsnorm per layer."""
+def _serial(spec, lay, call, w, caches, first_kw, modes=None):
+    """The reference chain: one srp_fuse_layer + srp_residual_rmsnorm per layer
+    (modes[l] for l >= 1: SRP_SEL_TOPK checks the layer, SRP_SEL_GIVEN passes the
+    previous selection on)."""
     T = lay.total_rows
     h = upload(w.hidden, "bf16")
     kcs, vcs = [], []
@@ -53,7 +55,8 @@ def _serial(spec, lay, call, w, caches, first_kw):
         else:
             prev_i.copy_(call.sel_idx)
             prev_o.copy_(call.sel_offsets)
-            sel = call.select(spec.layer_ratios()[l], cand=prev_i, cand_offsets=prev_o)
+            mode = S.SRP_SEL_TOPK if modes is None else modes[l]
+            sel = call.select(spec.layer_ratios()[l], mode=mode, cand=prev_i, cand_offsets=prev_o)
         call.fuse(sel, h, upload(w.layers[l].w_qkv, "bf16"), kc, vc, dev_out=False)
         S.srp_residual_rmsnorm(call.dims, h, call.attn_out, call.sel_idx, call.sel_offsets, lay.n_req, T)
         kcs.append(kc)
@@ -64,7 +67,7 @@ def _serial(spec, lay, call, w, caches, first_kw):
                 hidden=download(h), k=[download(k) for k in kcs], v=[download(v) for v in vcs])
 
 
-def _stacked(spec, lay, w, caches, first_kw, copy_stream):
+def _stacked(spec, lay, w, caches, first_kw, copy_stream, modes=None):
     """The same chain through srp_fuse_stack with the caches in pinned host memory."""
     T = lay.total_rows
     call = LayerCall(spec, lay)
@@ -81,7 +84,8 @@ def _stacked(spec, lay, w, caches, first_kw, copy_stream):
         keep += [kh, vh, wq]
         kcs.append(kc)
         vcs.append(vc)
-        layers.append(S.make_layer(wq, kc, vc, spec.layer_ratios()[l], k_host=kh, v_host=vh))
+        layers.append(S.make_layer(wq, kc, vc, spec.layer_ratios()[l], k_host=kh, v_host=vh,
+                                   mode=S.SRP_SEL_TOPK if modes is None else modes[l]))
     S.srp_fuse_stack(call.dims, call.batch, first, layers, h, 1e-6, call.sel_idx, call.sel_offsets,
                      call.attn_out, ws, ws_n, None, copy_stream)
     torch.cuda.synchronize()
@@ -98,19 +102,25 @@ def _same(a, b, what):
         assert np.array_equal(a["v"][l], b["v"][l]), f"{what}: V cache of layer {l} differs"
 
 
-@pytest.mark.parametrize("first", ["topk", "grouped"])
+@pytest.mark.parametrize("first", ["topk", "grouped", "check-two-layers"])
 def test_stack_equals_serial_layers_and_oracle(first):
+    """check-two-layers: layers 1 and 2 check (rank by deviation), layers 3 and 4
+    recompute the indices layer 2 chose (CacheBlend walkthrough, "Implementation":
+    the per-layer check_flag with the carried indices)."""
     spec = _stack_spec()
     w = inputs.generate(spec)
     lay = w.layout
     caches = [oracle_caches(w, l) for l in range(spec.n_layers)]
     first_kw = dict(window=8, tau=4) if first == "grouped" else {}
+    modes = None
+    if first == "check-two-layers":
+        modes = [S.SRP_SEL_TOPK, S.SRP_SEL_TOPK, S.SRP_SEL_GIVEN, S.SRP_SEL_GIVEN]
     _say(f"[gpu] stack {first}: T={lay.total_rows}, {spec.n_layers} layers")
-    ser = _serial(spec, lay, LayerCall(spec, lay), w, caches, first_kw)
+    ser = _serial(spec, lay, LayerCall(spec, lay), w, caches, first_kw, modes)
     side = torch.cuda.Stream()
-    piped = _stacked(spec, lay, w, caches, first_kw, side)
+    piped = _stacked(spec, lay, w, caches, first_kw, side, modes)
     _same(piped, ser, "copy stream")
-    inline = _stacked(spec, lay, w, caches, first_kw, None)
+    inline = _stacked(spec, lay, w, caches, first_kw, None, modes)
     _same(inline, ser, "copies in line")
 
     # the oracle's stack on the same stored inputs (hidden rounded to bf16 between layers)
@@ -124,7 +134,11 @@ def test_stack_equals_serial_layers_and_oracle(first):
                           chunk_src_pos=lay.chunk_src_pos, positions=lay.positions,
                           n_heads=spec.n_heads, n_kv=spec.n_kv_heads, head_dim=spec.head_dim,
                           rope_base=spec.rope_base, ratios=spec.layer_ratios(),
-                          window=first_kw.get("window", 0), tau=first_kw.get("tau", 0), round_hidden=rb)
+                          window=first_kw.get("window", 0), tau=first_kw.get("tau", 0), round_hidden=rb,
+                          modes=None if modes is None else ["topk" if m == S.SRP_SEL_TOPK else "given"
+                                                            for m in modes])
+    if modes is not None:  # the passed-on layers keep layer 2's rows
+        assert np.array_equal(outs[3]["sel_idx"], outs[1]["sel_idx"])
     last = outs[-1]
     req, _ = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
     csr_ok(piped["sel_idx"], piped["sel_offsets"], lay.req_offsets)

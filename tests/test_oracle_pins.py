@@ -516,3 +516,64 @@ def test_widen_f32_is_exact():
     np.testing.assert_array_equal(got, x.astype(np.float64))
     with pytest.raises(ValueError):
         ref.widen(x, "fp8")
+
+
+def _chain_layers(spec, w, x):
+    lay = w.layout
+    src = inputs.encode_positions(lay)
+    cr = src >= 0
+    layers = []
+    for l in range(spec.n_layers):
+        wq = ref.widen(w.layers[l].w_qkv, "f32")
+        kc = np.zeros((lay.total_rows, spec.n_kv_heads, spec.head_dim))
+        vc = np.zeros_like(kc)
+        kc[cr], vc[cr] = ref.encode_kv(w.encode_input(l, x_full=x)[cr], wq, src[cr],
+                                       spec.n_heads, spec.n_kv_heads, spec.head_dim, 1e4)
+        layers.append(dict(w_qkv=wq, k_cache=kc, v_cache=vc))
+    return layers
+
+
+def test_given_layers_after_a_full_check_equal_the_full_stack():
+    # check_flag off on layers 2 and 3 (CacheBlend walkthrough, "Implementation"):
+    # they recompute the rows handed to them; after a first layer that recomputes
+    # every row, the whole chain is a full prefill stack, computed here directly
+    spec = inputs.small_spec(dtype="f32", hidden=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                             chunk_lens=(30, 41), prefix=0, n_query=7, n_req=1, n_layers=3,
+                             ratios=(1.0, 0.1, 0.0))
+    w = inputs.generate(spec)
+    lay = w.layout
+    x = inputs.stored_to_f64(w.hidden, "f32")
+    layers = _chain_layers(spec, w, x)
+    outs = ref.fuse_stack(hidden=x, layers=layers, req_offsets=lay.req_offsets,
+                          chunk_offsets=lay.chunk_offsets, chunk_src_pos=lay.chunk_src_pos,
+                          positions=lay.positions, n_heads=spec.n_heads, n_kv=spec.n_kv_heads,
+                          head_dim=spec.head_dim, rope_base=1e4, ratios=spec.layer_ratios(),
+                          modes=("topk", "given", "given"))
+    h = x.copy()
+    for l in range(spec.n_layers):
+        assert len(outs[l]["sel_idx"]) == lay.total_rows
+        _, _, o = _full_prefill_torch(h, layers[l]["w_qkv"], spec, lay.req_offsets, lay.positions)
+        np.testing.assert_allclose(outs[l]["attn_out"], o, atol=1e-10)
+        y = torch.from_numpy(h + o.reshape(h.shape[0], -1))
+        h = (y / torch.sqrt((y * y).mean(1, keepdim=True) + 1e-6)).numpy()
+
+
+def test_given_layers_keep_the_last_checked_selection():
+    # check on layers 1-2, then pass the indices on: layers 3 and 4 select exactly
+    # layer 2's rows although their own ratio would keep fewer
+    spec = inputs.small_spec(dtype="f32", hidden=256, n_heads=4, n_kv_heads=2, head_dim=64,
+                             n_layers=4, ratios=(0.3, 0.15, 0.05, 0.05))
+    w = inputs.generate(spec)
+    lay = w.layout
+    x = inputs.stored_to_f64(w.hidden, "f32")
+    layers = _chain_layers(spec, w, x)
+    kw = dict(hidden=x, layers=layers, req_offsets=lay.req_offsets, chunk_offsets=lay.chunk_offsets,
+              chunk_src_pos=lay.chunk_src_pos, positions=lay.positions, n_heads=spec.n_heads,
+              n_kv=spec.n_kv_heads, head_dim=spec.head_dim, rope_base=1e4, ratios=spec.layer_ratios())
+    given = ref.fuse_stack(modes=("topk", "topk", "given", "given"), **kw)
+    checked = ref.fuse_stack(**kw)
+    for l in (0, 1):  # identical up to the last check layer
+        np.testing.assert_array_equal(given[l]["sel_idx"], checked[l]["sel_idx"])
+    for l in (2, 3):
+        np.testing.assert_array_equal(given[l]["sel_idx"], given[1]["sel_idx"])
+        assert len(checked[l]["sel_idx"]) < len(given[l]["sel_idx"])
