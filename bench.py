@@ -62,15 +62,15 @@ def parse():
                    help="only run a plain device-to-device copy of MIB MiB five times (the "
                         "reference for scaling the HBM byte counters) and exit")
     p.add_argument("--summarize-trace", metavar="CSV",
-                   help="print a markdown table of a rocprofv3 kernel CSV (--stats summary, or the "
-                        "per-dispatch kernel trace, see --trace-skip) and exit")
-    p.add_argument("--trace-skip", type=int, default=0,
-                   help="with a per-dispatch kernel trace: leave out each kernel's first N "
-                        "dispatches (the warm-up calls)")
+                   help="print the markdown + JSON record of a rocprofv3 per-dispatch kernel trace "
+                        "(kernel_trace.csv) over the last --calls layer calls and exit")
+    p.add_argument("--calls", type=int, default=0,
+                   help="layer calls a summary covers: the timed ones, 2 x steps x layers (the timed "
+                        "pass and the stage-timing pass)")
     p.add_argument("--summarize-pmc", nargs=4, metavar=("FETCH", "WRITE", "COPY_FETCH", "COPY_WRITE"),
-                   help="print the per-launch HBM traffic summary from four rocprofv3 --pmc "
-                        "counter CSVs (kernel FETCH_SIZE, kernel WRITE_SIZE, copy FETCH_SIZE, "
-                        "copy WRITE_SIZE; the copy runs use --copy-calibration) and exit")
+                   help="print the per-call HBM traffic record from four rocprofv3 --pmc counter "
+                        "CSVs (kernel FETCH_SIZE, kernel WRITE_SIZE, copy FETCH_SIZE, copy WRITE_SIZE; "
+                        "the copy runs use --copy-calibration) over the last --calls layer calls and exit")
     p.add_argument("--copy-mib", type=int, default=1024, help="size the copy runs used")
     return p.parse_args()
 
@@ -125,14 +125,23 @@ def algorithmic_work(spec, lay, sel, ratio_rows):
     }
 
 
-# Kernels whose HBM traffic is reported, with the sources their code comes from:
-# a recorded traffic figure is used only while these files are unchanged.
-TRAFFIC_KERNELS = {
-    "attn_bf16_kernel<128>": ("attn_bf16_kernel<128>", ["k_attn.hip", "kernels.hpp", "common.hpp"]),
-    "gemm_bf16_kernel<EPI_KV>": ("gemm_bf16_kernel<0,", ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
-    "gemm_bf16_kernel<EPI_Q>": ("gemm_bf16_kernel<1,", ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
+# The kernels of each MFMA stage (rocprofv3 names; a stage's time per layer call is
+# the sum of its kernels), with the sources their code comes from: a recorded
+# profile figure is used only while these files are unchanged.
+STAGE_KERNELS = {
+    "kv_proj": ([r"gemm_bf16_kernel<(0|3),", r"gemm_fixup_kernel<(0|3),"],
+                ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
+    "q_proj": ([r"gemm_bf16_kernel<(1|4),", r"gemm_fixup_kernel<(1|4),"],
+               ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
+    "attention": ([r"attn_bf16_kernel<"], ["k_attn.hip", "kernels.hpp", "common.hpp"]),
 }
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_14b_16k_grouped.md")
+# Kernels launched exactly once per srp_fuse_layer call, ahead of every stage
+# kernel of the call: they mark where the last layer calls begin. The trace records
+# every kernel, so it cuts at the call's first kernel (row metadata); the counter
+# runs record only the MFMA stages, and cut at the K/V projection.
+TRACE_ANCHOR = r"row_meta_kernel"
+PMC_ANCHOR = r"gemm_bf16_kernel<(0|3),"
+PROFILES = os.path.join(ROOT, "profiles")
 
 
 def source_hash(files):
@@ -144,18 +153,56 @@ def source_hash(files):
     return h.hexdigest()[:16]
 
 
-def recorded_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the recorded counter runs, or None
-    when there is no record or the kernel's sources changed since."""
+def profile_label(args, spec):
+    """File-name label of the workload a profile record covers."""
+    base = {1: "llama3_8b_layer", 2: "14b_16k", 3: "70b_4layer_gradual", 4: "8b_batch16x8k"}[args.workload]
+    if args.workload == 2:
+        base += "_scores" if args.select == "scores" else "_grouped"
+    if args.workload == 4 or args.ratio is not None:
+        base += f"_r{spec.layer_ratios()[0]:g}"
+    if args.dev == "v":
+        base += "_vonly"
+    if args.paged:
+        base += "_paged"
+    return base
+
+
+def _json_block(path):
     try:
-        text = open(TRAFFIC_FILE).read()
-        rec = json.loads(text.split("```json", 1)[1].split("```", 1)[0])
+        text = open(path).read()
+        return json.loads(text.split("```json", 1)[1].split("```", 1)[0])
     except (OSError, IndexError, ValueError):
         return None
-    ent = rec.get("kernels", {}).get(kernel)
-    if not ent or ent.get("source_hash") != source_hash(TRAFFIC_KERNELS[kernel][1]):
+
+
+def recorded_stage(label, kind, stage):
+    """A stage's recorded figure (kind "trace": avg_ms per layer call; "traffic":
+    bytes per layer call) for workload `label`, or None when there is no record or
+    the stage's kernel sources changed since it was taken."""
+    rec = _json_block(os.path.join(PROFILES, f"{'kernel_trace' if kind == 'trace' else 'hbm_traffic'}_{label}.md"))
+    ent = (rec or {}).get("stages", {}).get(stage)
+    if not ent or ent.get("source_hash") != source_hash(STAGE_KERNELS[stage][1]):
         return None
-    return ent["bytes_per_launch"]
+    return ent.get("avg_ms" if kind == "trace" else "bytes_per_call")
+
+
+def _stage_of(name):
+    import re
+    for st, (pats, _) in STAGE_KERNELS.items():
+        if any(re.search(p, name) for p in pats):
+            return st
+    return None
+
+
+def _window(events, n_calls, anchor):
+    """The dispatches of the last n_calls layer calls: events = [(order key, kernel
+    name, value)], cut at the n_calls-th last launch of the anchor kernel."""
+    import re
+    anchors = sorted(k for k, n, _ in events if re.search(anchor, n))
+    if len(anchors) < n_calls:
+        raise SystemExit(f"only {len(anchors)} layer calls in the record, {n_calls} asked for")
+    t0 = anchors[-n_calls]
+    return [(k, n, v) for k, n, v in events if k >= t0]
 
 
 def _pmc_rows(path):
@@ -169,7 +216,7 @@ def _pmc_rows(path):
 
 
 def _per_dispatch(rows, counter):
-    """{dispatch id: (kernel name, summed counter value)} for one counter."""
+    """[(dispatch id, kernel name, summed counter value)] for one counter."""
     out = {}
     for r in rows:
         if r["Counter_Name"] != counter:
@@ -177,69 +224,74 @@ def _per_dispatch(rows, counter):
         d = int(r["Dispatch_Id"])
         name, v = out.get(d, (r["Kernel_Name"], 0.0))
         out[d] = (name, v + float(r["Counter_Value"]))
-    return out
+    return [(d, n, v) for d, (n, v) in out.items()]
 
 
-def summarize_pmc(fetch, write, cfetch, cwrite, copy_mib):
-    """Markdown + JSON record of HBM traffic per launch: the kernels' FETCH_SIZE
-    and WRITE_SIZE (KiB per dispatch, averaged over their dispatches), each scaled
-    by true bytes / counter bytes of the plain copy."""
+def summarize_pmc(fetch, write, cfetch, cwrite, copy_mib, n_calls):
+    """Markdown + JSON record of HBM traffic per layer call of each MFMA stage, from
+    FETCH_SIZE and WRITE_SIZE (KiB per dispatch) over the last n_calls layer calls,
+    each scaled by true bytes / counter bytes of a plain device-to-device copy."""
     import numpy as np
     true_kib = copy_mib * 1024.0
 
     def copy_factor(path, counter):
-        d = _per_dispatch(_pmc_rows(path), counter)
-        vals = [v for n, v in d.values() if "copy" in n.lower()]
+        vals = [v for _, n, v in _per_dispatch(_pmc_rows(path), counter) if "copy" in n.lower()]
         return true_kib / float(np.median(vals)), float(np.median(vals))
 
     f_fac, f_raw = copy_factor(cfetch, "FETCH_SIZE")
     w_fac, w_raw = copy_factor(cwrite, "WRITE_SIZE")
-    fd, wd = _per_dispatch(_pmc_rows(fetch), "FETCH_SIZE"), _per_dispatch(_pmc_rows(write), "WRITE_SIZE")
+    fd = _window(_per_dispatch(_pmc_rows(fetch), "FETCH_SIZE"), n_calls, PMC_ANCHOR)
+    wd = _window(_per_dispatch(_pmc_rows(write), "WRITE_SIZE"), n_calls, PMC_ANCHOR)
     rec = {"copy_mib": copy_mib, "copy_fetch_kib": f_raw, "copy_write_kib": w_raw,
-           "fetch_factor": f_fac, "write_factor": w_fac, "kernels": {}}
-    lines = ["| kernel | launches | FETCH_SIZE KiB | WRITE_SIZE KiB | HBM bytes / launch (scaled) |",
+           "fetch_factor": f_fac, "write_factor": w_fac, "layer_calls": n_calls, "stages": {}}
+    lines = ["| stage | kernels | FETCH_SIZE KiB / call | WRITE_SIZE KiB / call | HBM bytes / call (scaled) |",
              "|---|---|---|---|---|"]
-    for label, (match, files) in TRAFFIC_KERNELS.items():
-        fv = [v for n, v in fd.values() if match in n]
-        wv = [v for n, v in wd.values() if match in n]
+    for st, (_, files) in STAGE_KERNELS.items():
+        fv = [v for _, n, v in fd if _stage_of(n) == st]
+        wv = [v for _, n, v in wd if _stage_of(n) == st]
         if not fv or not wv:
             continue
-        f_kib, w_kib = float(np.mean(fv)), float(np.mean(wv))
+        f_kib, w_kib = sum(fv) / n_calls, sum(wv) / n_calls
         total = (f_kib * f_fac + w_kib * w_fac) * 1024.0
-        rec["kernels"][label] = {"fetch_kib": f_kib, "write_kib": w_kib, "launches": len(fv),
-                                 "bytes_per_launch": total, "source_hash": source_hash(files)}
-        lines.append(f"| {label} | {len(fv)} | {f_kib:.0f} | {w_kib:.0f} | {total:.4g} |")
+        names = sorted({n.split("(")[0].replace("void ", "") for _, n, _ in fd if _stage_of(n) == st})
+        rec["stages"][st] = {"fetch_kib": f_kib, "write_kib": w_kib, "bytes_per_call": total,
+                             "kernels": names, "source_hash": source_hash(files)}
+        lines.append(f"| {st} | {', '.join(names)} | {f_kib:.0f} | {w_kib:.0f} | {total:.4g} |")
     head = [f"Copy calibration: a {copy_mib} MiB device-to-device copy reads FETCH_SIZE "
             f"{f_raw:.0f} KiB and WRITE_SIZE {w_raw:.0f} KiB for {true_kib:.0f} KiB each way: "
-            f"factors {f_fac:.4f} (fetch) and {w_fac:.4f} (write).", ""]
+            f"factors {f_fac:.4f} (fetch) and {w_fac:.4f} (write). Figures are per layer call, "
+            f"over the last {n_calls} layer calls of the run.", ""]
     return "\n".join(head + lines + ["", "```json", json.dumps(rec, indent=1), "```", ""])
 
 
-def summarize_trace(stats_csv, skip=0):
+def summarize_trace(trace_csv, n_calls):
+    """Markdown table + JSON record of a rocprofv3 per-dispatch kernel trace over the
+    last n_calls layer calls: every kernel's calls and durations, and each MFMA
+    stage's time per layer call (the sum of its kernels)."""
     import csv
-    with open(stats_csv) as fh:
+    with open(trace_csv) as fh:
         rows = list(csv.DictReader(fh))
-    if rows and "Start_Timestamp" in rows[0]:
-        # per-dispatch trace: aggregate per kernel, without its first `skip` calls
-        per = {}
-        for r in sorted(rows, key=lambda r: int(r["Dispatch_Id"])):
-            per.setdefault(r["Kernel_Name"], []).append(
-                int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-        agg = []
-        for name, d in per.items():
-            d = d[skip:] if len(d) > skip else d
-            agg.append((name, len(d), sum(d), min(d), max(d)))
-        total = sum(a[2] for a in agg) or 1
-        rows = [{"Name": n, "Calls": c, "TotalDurationNs": t, "AverageNs": t / c, "MinNs": mn,
-                 "MaxNs": mx, "Percentage": 100.0 * t / total}
-                for n, c, t, mn, mx in sorted(agg, key=lambda a: -a[2])]
-    lines = ["| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
-    for r in rows[:16]:
-        nm = r["Name"] if len(r["Name"]) < 70 else r["Name"][:67] + "..."
-        lines.append(f"| {nm} | {r['Calls']} | {float(r['TotalDurationNs']) / 1e6:.3f} | "
-                     f"{float(r['AverageNs']) / 1e3:.1f} | {float(r['MinNs']) / 1e3:.1f} | "
-                     f"{float(r['MaxNs']) / 1e3:.1f} | {float(r['Percentage']):.1f} |")
-    return "\n".join(lines) + "\n"
+    ev = _window([(int(r["Start_Timestamp"]), r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+                  for r in rows], n_calls, TRACE_ANCHOR)
+    per = {}
+    for _, n, d in ev:
+        per.setdefault(n, []).append(d)
+    total = sum(sum(d) for d in per.values()) or 1
+    lines = [f"Kernels of the last {n_calls} layer calls:", "",
+             "| kernel | calls | total ms | avg us | min us | max us | % |", "|---|---|---|---|---|---|---|"]
+    for name, d in sorted(per.items(), key=lambda kv: -sum(kv[1])):
+        nm = name if len(name) < 70 else name[:67] + "..."
+        lines.append(f"| {nm} | {len(d)} | {sum(d) / 1e6:.3f} | {sum(d) / len(d) / 1e3:.1f} | "
+                     f"{min(d) / 1e3:.1f} | {max(d) / 1e3:.1f} | {100.0 * sum(d) / total:.1f} |")
+    rec = {"layer_calls": n_calls, "kernel_ms_per_call": round(total / 1e6 / n_calls, 5), "stages": {}}
+    lines += ["", "| stage | ms per layer call |", "|---|---|"]
+    for st, (_, files) in STAGE_KERNELS.items():
+        tot = sum(sum(d) for n, d in per.items() if _stage_of(n) == st)
+        if tot:
+            rec["stages"][st] = {"avg_ms": tot / 1e6 / n_calls, "source_hash": source_hash(files)}
+            lines.append(f"| {st} | {tot / 1e6 / n_calls:.4f} |")
+    lines.append(f"| all kernels | {total / 1e6 / n_calls:.4f} |")
+    return "\n".join(lines + ["", "```json", json.dumps(rec, indent=1), "```", ""])
 
 
 def copy_calibration(mib):
@@ -316,10 +368,10 @@ SCORES_SETTINGS = dict(k_rule="ceil", span_max=16, tau_smooth=0.4, tau_cover=0.7
 def main():
     args = parse()
     if args.summarize_trace:
-        print(summarize_trace(args.summarize_trace, args.trace_skip), end="")
+        print(summarize_trace(args.summarize_trace, args.calls), end="")
         return
     if args.summarize_pmc:
-        print(summarize_pmc(*args.summarize_pmc, args.copy_mib), end="")
+        print(summarize_pmc(*args.summarize_pmc, args.copy_mib, args.calls), end="")
         return
     if args.paged and args.pipeline:
         print("--pipeline loads contiguous caches; it does not combine with --paged", file=sys.stderr)
@@ -448,6 +500,10 @@ def main():
 
     for l in range(nl):
         call.ensure_workspace(call.select(ratios[l], **(sel_kw if l == 0 else {})))
+    # every layer's selection (an untimed pass on a spare cache copy): the
+    # algorithmic work of each layer follows from it
+    layer_sel = capture_selections(call, nl, ratios, sel_kw, hiddens[0].clone(),
+                                   [(c[0].clone(), c[1].clone()) for c in caches], wqs, lay, T)
     print(f"[bench] warmup {args.warmup}", file=sys.stderr, flush=True)
     for i in range(args.warmup):
         step(args.steps + i)
@@ -470,43 +526,60 @@ def main():
         step(i)
     stage_ms = S.srp_profile_end(args.steps * nl)
     ms_per_layer = ms_per_step / nl
-    res = call.results()
-    sel = res["sel_idx"]
+    sel = layer_sel[-1]
 
     names = [S.srp_profile_stage_name(i) for i in range(S.SRP_N_STAGES)]
     st = np.asarray(stage_ms, np.float64).reshape(args.steps, nl, S.SRP_N_STAGES)
-    # per-stage work of the first layer (the layer the metric is quoted on)
-    sel0 = sel if nl == 1 else _first_layer_sel(call, spec, lay, hidden0, wqs, pristine, sel_kw, ratios)
-    if by_scores:  # only the chosen rows (and fresh rows) are projected
-        n_rc = int((src[sel0] >= 0).sum())
-        rows = {"n_ctx": n_ctx, "n_rec": len(sel0), "n_rec_ctx": n_rc, "scores": True}
-    else:  # the first layer projects every row to K/V
-        rows = {"n_ctx": n_ctx, "n_rec": T, "v_only": args.dev == "v"}
-    work = algorithmic_work(spec, lay, sel0, rows)
+    # per-stage work of every layer: the first projects every row to K/V (or, with
+    # external scores, the chosen rows); a later layer its candidates (the previous
+    # selection) and the fresh rows
+    works = []
+    for l in range(nl):
+        if l == 0 and by_scores:
+            n_rc = int((src[layer_sel[0]] >= 0).sum())
+            rows = {"n_ctx": n_ctx, "n_rec": len(layer_sel[0]), "n_rec_ctx": n_rc, "scores": True}
+        elif l == 0:
+            rows = {"n_ctx": n_ctx, "n_rec": T, "v_only": args.dev == "v"}
+        else:
+            prev = layer_sel[l - 1]
+            rows = {"n_ctx": n_ctx, "n_rec": len(prev), "n_rec_ctx": int((src[prev] >= 0).sum())}
+        works.append(algorithmic_work(spec, lay, layer_sel[l], rows))
     stages = {}
     peak_fl = PEAK_BF16_TFLOPS if spec.dtype == "bf16" else PEAK_F32_TFLOPS
     for i, nm in enumerate(names):
-        ms = float(st[:, 0, i].mean())
-        wk = work[nm]
-        ent = {"ms": round(ms, 4)}
-        if "flops" in wk:
-            tf = wk["flops"] / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
-            ent.update(flops=wk["flops"], tflops=round(tf, 1), frac_mfma=round(tf / peak_fl, 4))
-        if "bytes" in wk:
-            gbs = wk["bytes"] / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
-            ent.update(bytes=wk["bytes"], gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        # totals over the layers of a step; per layer call = total / layers
+        ms = float(st[:, :, i].mean(axis=0).sum())
+        ent = {"ms": round(ms / nl, 4)}
+        fl = sum(w[nm].get("flops", 0.0) for w in works)
+        by = sum(w[nm].get("bytes", 0.0) for w in works)
+        if "flops" in works[0][nm]:
+            tf = fl / (ms * 1e-3) / 1e12 if ms > 0 else 0.0
+            ent.update(flops=fl / nl, tflops=round(tf, 1), frac_mfma=round(tf / peak_fl, 4))
+        if "bytes" in works[0][nm]:
+            gbs = by / (ms * 1e-3) / 1e9 if ms > 0 else 0.0
+            ent.update(bytes=by / nl, gbs=round(gbs, 1), frac_hbm=round(gbs / PEAK_HBM_GBS, 4))
+        if nl > 1:
+            ent["per_layer_ms"] = [round(float(x), 4) for x in st[:, :, i].mean(axis=0)]
         stages[nm] = ent
-    # dominant kernel: the longest MFMA stage
+    # dominant kernel: the longest MFMA stage. Its achieved rate is the stage's
+    # algorithmic flops per layer call over its time per layer call, from the
+    # library's stage events in this run; the same flops over the committed rocprofv3
+    # trace's time per layer call of this workload are reported beside it.
+    label = profile_label(args, spec)
     dom = max(("kv_proj", "q_proj", "attention"), key=lambda n: stages[n]["ms"])
-    roof = {"kernel": {"kv_proj": "gemm_bf16_kernel<EPI_KV>", "q_proj": "gemm_bf16_kernel<EPI_Q>",
-                       "attention": "attn_bf16_kernel<128>"}[dom],
+    roof = {"stage": dom,
+            "kernel": {"kv_proj": "gemm_bf16_kernel<EPI_KV> + fix-up", "q_proj": "gemm_bf16_kernel<EPI_Q> + fix-up",
+                       "attention": "attn_bf16_kernel<128>"}[dom] if spec.dtype == "bf16" else dom,
             "bound": "mfma", "achieved": stages[dom]["tflops"], "peak": peak_fl, "unit": "TFLOP/s",
-            "frac": stages[dom]["frac_mfma"], "traffic": None,
-            "flops_per_launch": work[dom]["flops"], "avg_launch_ms": stages[dom]["ms"]}
-
-    if args.workload == 2 and args.ratio is None and not by_scores and not args.paged and args.dev == "kv":
-        # HBM bytes per launch from the recorded counter runs of this workload
-        roof["traffic"] = recorded_traffic(roof["kernel"])
+            "frac": stages[dom]["frac_mfma"], "traffic": recorded_stage(label, "traffic", dom),
+            "flops_per_launch": stages[dom]["flops"], "avg_launch_ms": stages[dom]["ms"],
+            "timing": "hipEvents of the library's stage marks, on the layer's stream, over the timed steps"}
+    prof_ms = recorded_stage(label, "trace", dom)
+    if prof_ms:
+        ach = stages[dom]["flops"] / (prof_ms * 1e-3) / 1e12
+        roof.update(profile_avg_launch_ms=round(prof_ms, 4), profile_achieved=round(ach, 1),
+                    profile_frac=round(ach / peak_fl, 4),
+                    profile=f"profiles/kernel_trace_{label}.md")
 
     value = n_ctx / (ms_per_layer * 1e-3)
     pipe = None
@@ -538,6 +611,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "ms_per_layer": round(ms_per_layer, 4),
         "n_selected": int(len(sel)),
+        **({"n_selected_per_layer": [int(len(x)) for x in layer_sel]} if nl > 1 else {}),
         "n_ctx": n_ctx,
         "roofline": roof,
         "stages": stages,
@@ -662,13 +736,27 @@ def _to_f64(a, dtype):
     return (a.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
 
-def _first_layer_sel(call, spec, lay, hidden0, wqs, pristine, sel_kw, ratios):
-    """Selection of the stack's first layer (re-run once on a spare cache copy)."""
+def capture_selections(call, nl, ratios, sel_kw, h, caches, wqs, lay, T):
+    """Each layer's selected rows in one untimed pass of the step (hidden state and
+    caches are scratch copies)."""
     import torch
-    kc, vc = pristine[0][0][0].clone(), pristine[0][0][1].clone()
-    call.fuse(call.select(ratios[0], **sel_kw), hidden0, wqs[0], kc, vc, dev_out=False)
-    torch.cuda.synchronize()
-    return call.results()["sel_idx"]
+    from selective_recompute_prefill_amd import srp as S
+    out = []
+    prev_idx = torch.empty_like(call.sel_idx)
+    prev_off = torch.empty_like(call.sel_offsets)
+    for l in range(nl):
+        if l == 0:
+            sel = call.select(ratios[0], **sel_kw)
+        else:
+            prev_idx.copy_(call.sel_idx)
+            prev_off.copy_(call.sel_offsets)
+            sel = call.select(ratios[l], cand=prev_idx, cand_offsets=prev_off)
+        call.fuse(sel, h, wqs[l], caches[l][0], caches[l][1], dev_out=False)
+        if l + 1 < nl:
+            S.srp_residual_rmsnorm(call.dims, h, call.attn_out, call.sel_idx, call.sel_offsets, lay.n_req, T)
+        torch.cuda.synchronize()
+        out.append(call.results()["sel_idx"])
+    return out
 
 
 if __name__ == "__main__":

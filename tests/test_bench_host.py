@@ -1,7 +1,9 @@
-"""Host-side checks of the bench's HBM-traffic bookkeeping (no GPU): the counter
-summary scales each kernel's FETCH_SIZE and WRITE_SIZE by what the same counters
-read for a plain copy of known size, and a recorded figure is used only while the
-kernel's sources are unchanged."""
+"""Host-side checks of the bench's profile bookkeeping (no GPU): the counter
+summary scales each stage's FETCH_SIZE and WRITE_SIZE by what the same counters
+read for a plain copy of known size, both summaries cover only the last layer
+calls of a run (cut at the anchor kernel launched once per call), a stage's
+figure is the sum of its kernels per call, and a recorded figure is used only
+while the stage's kernel sources are unchanged."""
 import csv
 import json
 import os
@@ -11,6 +13,11 @@ import pytest
 
 sys.path.insert(0, os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
 import bench  # noqa: E402
+
+ATTN = "void srp::attn_bf16_kernel<128>(srp::AttnArgs)"
+GEMM = "void srp::gemm_bf16_kernel<0, srp::GemmCfg<256, 256, 2, 4, 2, 64> >(srp::GemmArgs)"
+FIX = "void srp::gemm_fixup_kernel<0, srp::GemmCfg<256, 256, 2, 4, 2, 64> >(srp::GemmArgs)"
+META = "srp::row_meta_kernel(srp::SelectArgs, srp::Workspace)"
 
 
 def _counter_csv(path, rows):
@@ -25,17 +32,19 @@ def _counter_csv(path, rows):
 
 @pytest.fixture
 def pmc_dirs(tmp_path):
-    attn = "void srp::attn_bf16_kernel<128>(srp::AttnArgs)"
-    gemm = "void srp::gemm_bf16_kernel<0, srp::GemmCfg<256, 256, 2, 4, 2, 64> >(srp::GemmArgs)"
-    # two launches each; counters split over two rows (per-XCD instances) that add up
-    _counter_csv(tmp_path / "fetch", [
-        (1, attn, "FETCH_SIZE", 300.0), (1, attn, "FETCH_SIZE", 100.0),
-        (2, gemm, "FETCH_SIZE", 1000.0),
-        (3, attn, "FETCH_SIZE", 600.0),
-        (4, gemm, "FETCH_SIZE", 3000.0)])
-    _counter_csv(tmp_path / "write", [
-        (1, attn, "WRITE_SIZE", 50.0), (2, gemm, "WRITE_SIZE", 70.0),
-        (3, attn, "WRITE_SIZE", 150.0), (4, gemm, "WRITE_SIZE", 130.0)])
+    # three layer calls (K/V GEMM, fix-up, attention: the counter runs record only
+    # the MFMA stages and cut at the K/V GEMM); the first is a warm-up that the
+    # summary of the last two leaves out; counters split over two rows (per-XCD
+    # instances) add up
+    fetch, write = [], []
+    for c, (fa, fg, ff) in enumerate([(9999.0, 9999.0, 9999.0), (400.0, 1000.0, 40.0), (600.0, 3000.0, 60.0)]):
+        d = 10 * c
+        fetch += [(d + 1, GEMM, "FETCH_SIZE", fg / 2), (d + 1, GEMM, "FETCH_SIZE", fg / 2),
+                  (d + 2, FIX, "FETCH_SIZE", ff), (d + 3, ATTN, "FETCH_SIZE", fa)]
+        write += [(d + 1, GEMM, "WRITE_SIZE", 100.0), (d + 2, FIX, "WRITE_SIZE", 20.0),
+                  (d + 3, ATTN, "WRITE_SIZE", 100.0)]
+    _counter_csv(tmp_path / "fetch", fetch)
+    _counter_csv(tmp_path / "write", write)
     # a 1 MiB copy: FETCH_SIZE reads half the bytes, WRITE_SIZE all of them
     _counter_csv(tmp_path / "cfetch", [(1, "__amd_rocclr_copyBuffer", "FETCH_SIZE", 512.0)])
     _counter_csv(tmp_path / "cwrite", [(1, "__amd_rocclr_copyBuffer", "WRITE_SIZE", 1024.0)])
@@ -46,36 +55,53 @@ def _record(md):
     return json.loads(md.split("```json", 1)[1].split("```", 1)[0])
 
 
-def test_summary_scales_by_the_copy_calibration(pmc_dirs):
-    md = bench.summarize_pmc(str(pmc_dirs / "fetch"), str(pmc_dirs / "write"), str(pmc_dirs / "cfetch"),
-                             str(pmc_dirs / "cwrite"), 1)
-    rec = _record(md)
+def _pmc(pmc_dirs, calls=2):
+    return bench.summarize_pmc(str(pmc_dirs / "fetch"), str(pmc_dirs / "write"), str(pmc_dirs / "cfetch"),
+                               str(pmc_dirs / "cwrite"), 1, calls)
+
+
+def test_traffic_summary_scales_by_the_copy_calibration(pmc_dirs):
+    rec = _record(_pmc(pmc_dirs))
     assert rec["fetch_factor"] == pytest.approx(2.0) and rec["write_factor"] == pytest.approx(1.0)
-    attn = rec["kernels"]["attn_bf16_kernel<128>"]
-    # mean fetch (400 + 600) / 2 = 500 KiB x 2, mean write (50 + 150) / 2 = 100 KiB x 1
-    assert attn["launches"] == 2
-    assert attn["bytes_per_launch"] == pytest.approx((500 * 2 + 100) * 1024)
-    kv = rec["kernels"]["gemm_bf16_kernel<EPI_KV>"]
-    assert kv["bytes_per_launch"] == pytest.approx((2000 * 2 + 100) * 1024)
-    # a kernel with no dispatches in the counter files is left out
-    assert "gemm_bf16_kernel<EPI_Q>" not in rec["kernels"]
-    assert attn["source_hash"] == bench.source_hash(bench.TRAFFIC_KERNELS["attn_bf16_kernel<128>"][1])
+    attn = rec["stages"]["attention"]
+    # last two calls: fetch (400 + 600) / 2 = 500 KiB x 2, write 100 KiB x 1
+    assert attn["bytes_per_call"] == pytest.approx((500 * 2 + 100) * 1024)
+    # the K/V stage adds its fix-up kernel: fetch (1040 + 3060) / 2, write 120
+    kv = rec["stages"]["kv_proj"]
+    assert kv["bytes_per_call"] == pytest.approx((2050 * 2 + 120) * 1024)
+    assert "q_proj" not in rec["stages"]  # no dispatches of it
+    assert attn["source_hash"] == bench.source_hash(bench.STAGE_KERNELS["attention"][1])
+    with pytest.raises(SystemExit):
+        _pmc(pmc_dirs, calls=4)  # more calls than the record holds
 
 
-def test_recorded_traffic_only_for_unchanged_sources(pmc_dirs, tmp_path, monkeypatch):
-    md = bench.summarize_pmc(str(pmc_dirs / "fetch"), str(pmc_dirs / "write"), str(pmc_dirs / "cfetch"),
-                             str(pmc_dirs / "cwrite"), 1)
-    f = tmp_path / "traffic.md"
-    f.write_text("# traffic\n\n" + md)
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
-    assert bench.recorded_traffic("attn_bf16_kernel<128>") == pytest.approx((500 * 2 + 100) * 1024)
-    # the record of a kernel whose sources changed since is not used
+def test_trace_summary_per_layer_call(tmp_path):
+    rows, t = [], 0
+    for c, (kv, fx, at) in enumerate([(900, 90, 900), (300, 20, 500), (340, 40, 700)]):
+        for name, dur in [(META, 5), (GEMM, kv), (FIX, fx), (ATTN, at)]:
+            rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur * 1000})
+            t += dur * 1000 + 10
+    path = tmp_path / "kernel_trace.csv"
+    with open(path, "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        wr.writerows(rows)
+    rec = _record(bench.summarize_trace(str(path), 2))
+    assert rec["stages"]["kv_proj"]["avg_ms"] == pytest.approx((300 + 20 + 340 + 40) / 2 / 1000)
+    assert rec["stages"]["attention"]["avg_ms"] == pytest.approx(0.6)
+    assert rec["kernel_ms_per_call"] == pytest.approx((5 + 300 + 20 + 500 + 5 + 340 + 40 + 700) / 2 / 1000)
+
+
+def test_recorded_figures_only_for_unchanged_sources(pmc_dirs, tmp_path, monkeypatch):
+    monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
+    md = _pmc(pmc_dirs)
+    (tmp_path / "hbm_traffic_demo.md").write_text("# traffic\n\n" + md)
+    assert bench.recorded_stage("demo", "traffic", "attention") == pytest.approx((500 * 2 + 100) * 1024)
+    # the record of a stage whose sources changed since is not used
     rec = _record(md)
-    rec["kernels"]["attn_bf16_kernel<128>"]["source_hash"] = "0" * 16
-    f.write_text("```json\n" + json.dumps(rec) + "\n```\n")
-    assert bench.recorded_traffic("attn_bf16_kernel<128>") is None
-    assert bench.recorded_traffic("gemm_bf16_kernel<EPI_KV>") == pytest.approx((2000 * 2 + 100) * 1024)
+    rec["stages"]["attention"]["source_hash"] = "0" * 16
+    (tmp_path / "hbm_traffic_demo.md").write_text("```json\n" + json.dumps(rec) + "\n```\n")
+    assert bench.recorded_stage("demo", "traffic", "attention") is None
+    assert bench.recorded_stage("demo", "traffic", "kv_proj") == pytest.approx((2050 * 2 + 120) * 1024)
     # no record at all
-    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(tmp_path / "missing.md"))
-    assert bench.recorded_traffic("attn_bf16_kernel<128>") is None
-
+    assert bench.recorded_stage("missing", "trace", "attention") is None

@@ -495,3 +495,65 @@ def test_residual_rmsnorm():
     S.srp_residual_rmsnorm(call.dims, hd, upload(attn, "bf16"), ints(sel), ints([0, 300]), 1, T)
     torch.cuda.synchronize()
     assert_close(ref.widen(download(hd), "bf16"), want, "bf16", "rmsnorm")
+
+
+# --------------------------------------------------------------------------- #
+# guard bands: nothing is written past an output's capacity, inputs stay intact
+# --------------------------------------------------------------------------- #
+
+CANARY = 0x5A
+
+
+@pytest.mark.parametrize("dtype,sel_kw", [("bf16", dict(ratio=0.3, window=8, tau=4)), ("f32", dict(ratio=0.3)),
+                                          ("bf16", dict(ratio=0.2, dev_mode=S.SRP_DEV_V))])
+def test_guard_bands_untouched(dtype, sel_kw):
+    """Every output buffer (caches, sel_idx, sel_offsets, attn_out, dev_out, the
+    workspace) sits inside a larger byte buffer filled with a canary pattern; after
+    the call the bytes before and after each stay the canary, and the read-only
+    inputs (hidden, W_qkv, the layout arrays) are bit-for-bit unchanged."""
+    spec = inputs.small_spec(dtype=dtype)
+    w = inputs.generate(spec)
+    lay = w.layout
+    kc, vc = oracle_caches(w)
+    T = lay.total_rows
+    pad = 4096
+
+    def guarded(nbytes):
+        buf = torch.full((nbytes + 2 * pad,), CANARY, dtype=torch.uint8, device="cuda")
+        return buf, buf[pad:pad + nbytes]
+
+    def typed(view, dt, shape):
+        return view.view(dt).view(shape)
+
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    es = 2 if dtype == "bf16" else 4
+    kv_shape = (T, spec.n_kv_heads, spec.head_dim)
+    call = LayerCall(spec, lay)
+    sel = S.make_select(**sel_kw)
+    n_ws = S.srp_workspace_size(call.dims, call.batch, sel)
+    bufs = {}
+    for name, nbytes in [("k", T * spec.kvdim * es), ("v", T * spec.kvdim * es), ("sel_idx", T * 4),
+                         ("sel_off", (lay.n_req + 1) * 4), ("attn", T * spec.qdim * es), ("dev", T * 4),
+                         ("ws", n_ws)]:
+        bufs[name] = guarded(nbytes)
+    k = typed(bufs["k"][1], td, kv_shape)
+    v = typed(bufs["v"][1], td, kv_shape)
+    k.copy_(upload(kc, dtype))
+    v.copy_(upload(vc, dtype))
+    hid, wq = upload(w.hidden, dtype), upload(w.layers[0].w_qkv, dtype)
+    hid0, wq0 = hid.clone(), wq.clone()
+    layout0 = [t.clone() for t in (call.req_offsets, call.chunk_offsets, call.chunk_src_pos, call.positions)]
+    _say(f"[gpu] guard bands {dtype} {sel_kw}")
+    S.srp_fuse_layer(call.dims, call.batch, sel, hid, wq, k, v, typed(bufs["sel_idx"][1], torch.int32, (T,)),
+                     typed(bufs["sel_off"][1], torch.int32, (lay.n_req + 1,)),
+                     typed(bufs["attn"][1], td, (T, spec.n_heads, spec.head_dim)),
+                     typed(bufs["dev"][1], torch.float32, (T,)), bufs["ws"][1], n_ws)
+    torch.cuda.synchronize()
+    for name, (buf, _) in bufs.items():
+        head, tail = buf[:pad].cpu().numpy(), buf[-pad:].cpu().numpy()
+        assert np.all(head == CANARY) and np.all(tail == CANARY), f"{name}: guard band overwritten"
+    assert torch.equal(hid, hid0) and torch.equal(wq, wq0), "an input was written"
+    for a, b in zip(layout0, (call.req_offsets, call.chunk_offsets, call.chunk_src_pos, call.positions)):
+        assert torch.equal(a, b), "a layout array was written"
+    n_sel = int(typed(bufs["sel_off"][1], torch.int32, (lay.n_req + 1,))[-1])
+    assert 0 < n_sel <= T
