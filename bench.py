@@ -630,7 +630,9 @@ def main():
 def bench_pipeline(args, spec, lay, call, wqs, pristine, host, hidden0, sel_kw, ratios, T, n_ctx):
     """The stack through srp_fuse_stack three ways: caches already on the device, caches
     copied from page-locked host memory in line on the compute stream, and copied on a
-    separate copy stream so that later layers' loads overlap earlier layers' recompute.
+    separate copy stream so that later layers' loads overlap earlier layers' recompute
+    (and, with two destination sets used in turn, the first layer's load overlaps the
+    previous stack).
     Also the measured host-to-device throughput, the profiled full-prefill time of a
     layer and the loading controller's ratio from them (CacheBlend walkthrough, "Making
     the recompute free"). The host-load times are PCIe-inclusive."""
@@ -647,7 +649,12 @@ def bench_pipeline(args, spec, lay, call, wqs, pristine, host, hidden0, sel_kw, 
             cp[l][0].copy_(host[l][0])
             cp[l][1].copy_(host[l][1])
     torch.cuda.synchronize()
-    dev_kv = [(torch.empty_like(pristine[0][l][0]), torch.empty_like(pristine[0][l][1])) for l in range(nl)]
+    # two sets of destination caches used in turn: a stack's copies are not ordered
+    # after earlier work, so the set a call fills must be free (the call before last
+    # used it: the host waits for that call's completion event before issuing)
+    dev_sets = [[(torch.empty_like(pristine[0][l][0]), torch.empty_like(pristine[0][l][1])) for l in range(nl)]
+                for _ in range(2)]
+    dev_kv = dev_sets[0]
     cache_bytes = sum(h[0].numel() * h[0].element_size() * 2 for h in host)
     side = torch.cuda.Stream()
     cur = torch.cuda.current_stream()
@@ -659,7 +666,8 @@ def bench_pipeline(args, spec, lay, call, wqs, pristine, host, hidden0, sel_kw, 
             layers = [S.make_layer(wqs[l], pristine[i % n_copies][l][0], pristine[i % n_copies][l][1], ratios[l])
                       for l in range(nl)]
         else:
-            layers = [S.make_layer(wqs[l], dev_kv[l][0], dev_kv[l][1], ratios[l], k_host=host[l][0],
+            dst = dev_sets[i % 2]
+            layers = [S.make_layer(wqs[l], dst[l][0], dst[l][1], ratios[l], k_host=host[l][0],
                                    v_host=host[l][1]) for l in range(nl)]
         return h, layers
 
@@ -667,17 +675,24 @@ def bench_pipeline(args, spec, lay, call, wqs, pristine, host, hidden0, sel_kw, 
         cs = side if mode == "pipelined" else None
         reps = args.steps
         prep = [run(mode, i) for i in range(args.warmup + reps)]
-        for i in range(args.warmup):
+        done = {}
+
+        def call_stack(i):
+            if i >= 2:
+                done.pop(i - 2).synchronize()  # the destination set of call i-2 is free
             h, layers = prep[i]
             S.srp_fuse_stack(call.dims, call.batch, first, layers, h, 1e-6, call.sel_idx, call.sel_offsets,
                              call.attn_out, ws, ws_n, None, cs)
+            done[i] = torch.cuda.Event()
+            done[i].record(cur)
+
+        for i in range(args.warmup):
+            call_stack(i)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(cur)
         for i in range(reps):
-            h, layers = prep[args.warmup + i]
-            S.srp_fuse_stack(call.dims, call.batch, first, layers, h, 1e-6, call.sel_idx, call.sel_offsets,
-                             call.attn_out, ws, ws_n, None, cs)
+            call_stack(args.warmup + i)
         e1.record(cur)
         torch.cuda.synchronize()
         return e0.elapsed_time(e1) / reps

@@ -303,12 +303,15 @@ int srp_stack_workspace_size(const srp_dims *dims, const srp_batch *batch,
  *   value caches on a second copy stream that the library creates once per device
  *   (default priority, kept until the process ends), each layer's copies followed by
  *   events that `stream` waits for before that layer, so the loads of layer l+1 run
- *   while layer l computes and one copy engine's idle time between transfers
- *   overlaps the other's transfer. The copies start after the work enqueued on
- *   `stream` before the call (which may still use the destinations).
- *   copy_stream == stream (e.g. both NULL) puts all copies in line. Work is only
- *   enqueued: synchronising with `stream` covers the copies too. The host caches
- *   must stay valid until then.
+ *   while layer l computes and the two copy engines share the link. The copies are
+ *   not ordered after earlier work: when the call is made, no pending work on any
+ *   stream may still use a destination k_cache / v_cache (a caller issuing stacks
+ *   back to back alternates two sets of destinations, or waits for the call before
+ *   last). Making a copy stream wait for pending work on the compute stream was
+ *   measured to stall the host inside hipMemcpyAsync for milliseconds at times, which
+ *   idles the GPU. copy_stream == stream (e.g. both NULL) puts all copies in line,
+ *   ordered as usual. Work is only enqueued: synchronising with `stream` covers the
+ *   copies too. The host caches must stay valid until then.
  * Errors as for srp_fuse_layer; nothing is enqueued when an argument check fails. */
 int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_select *first,
                    int32_t n_layers, const srp_layer *layers, void *hidden, float rms_eps,

@@ -674,10 +674,11 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
   const size_t cache_bytes = (size_t)T * dims->n_kv_heads * dims->head_dim * (dims->dtype == SRP_BF16 ? 2 : 4);
 
   // one event per loaded layer and copy stream, created for this call (concurrent
-  // calls never share one) and released once its wait is enqueued; ev.back() orders
-  // the copies after the work already on the compute stream, which may still use
-  // the destinations
-  std::vector<hipEvent_t> ev(n_layers + 1, nullptr), ev_v(n_layers, nullptr);
+  // calls never share one) and released once its wait is enqueued. The copy
+  // streams wait for nothing: a copy stream made to wait for work still pending on
+  // the compute stream can stall the host inside hipMemcpyAsync for milliseconds
+  // (measured), which idles the GPU; the caller keeps the destinations free instead.
+  std::vector<hipEvent_t> ev(n_layers, nullptr), ev_v(n_layers, nullptr);
   auto release = [&]() {
     for (hipEvent_t e : ev)
       if (e) (void)hipEventDestroy(e);
@@ -693,14 +694,7 @@ int srp_fuse_stack(const srp_dims *dims, const srp_batch *batch, const srp_selec
   hipStream_t vs = cs;
   if (loads && cache_bytes > 0 && cs != s) {
     hipError_t e = value_copy_stream(&vs);
-    if (e == hipSuccess) e = hipEventCreateWithFlags(&ev[n_layers], hipEventDisableTiming);
-    if (e == hipSuccess) e = hipEventRecord(ev[n_layers], s);
-    if (e == hipSuccess) e = hipStreamWaitEvent(cs, ev[n_layers], 0);
-    if (e == hipSuccess) e = hipStreamWaitEvent(vs, ev[n_layers], 0);
-    if (e != hipSuccess) {
-      release();
-      return fail(SRP_E_HIP, "ordering the loads: %s", hipGetErrorString(e));
-    }
+    if (e != hipSuccess) return fail(SRP_E_HIP, "the value copy stream: %s", hipGetErrorString(e));
   }
   for (int l = 0; l < n_layers; ++l) {
     if (!layers[l].k_host || cache_bytes == 0) continue;
