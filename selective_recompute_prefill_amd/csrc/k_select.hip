@@ -1064,6 +1064,31 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Work
   const int nR = roff[a.n_req];
   constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
   const int chunks = kvdim / V;
+  if (!a.fresh_all) {
+    // selected rows only: output slot s of request r is entry roff[r] + (s -
+    // sel_offsets[r]) of the per-request selection
+    const int total = sel_offsets[a.n_req];
+    for (int s = wave; s < total; s += nwaves) {
+      const int r = upper_index(sel_offsets, a.n_req + 1, s);
+      const int q = roff[r] + (s - sel_offsets[r]);
+      const int row = w.tsel_row[q], e = w.tsel_ent[q];
+      if (lane == 0) {
+        sel_idx[s] = row;
+        w.sel_ent[s] = e;
+      }
+      const T *f = (const T *)w.fresh_kv + (size_t)e * 2 * kvdim;
+      const int cr = w.row_slot ? w.row_slot[row] : row;  // cache row
+      for (int c = lane; c < chunks; c += 64) {
+        if (!a.v_only)
+          *reinterpret_cast<uint4 *>(k_cache + (size_t)cr * kvdim + c * V) =
+              *reinterpret_cast<const uint4 *>(f + c * V);
+        *reinterpret_cast<uint4 *>(v_cache + (size_t)cr * kvdim + c * V) =
+            *reinterpret_cast<const uint4 *>(f + kvdim + c * V);
+      }
+    }
+    return;
+  }
+  // fresh K/V of every recomputed row (the selected ones also fill sel_idx)
   for (int q = wave; q < nR; q += nwaves) {
     const int r = upper_index(roff, a.n_req + 1, q);
     const int i = q - roff[r];
@@ -1077,11 +1102,8 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Work
         w.sel_ent[out] = e;
       }
     }
-    if (a.fresh_all) {
-      e = q;
-      row = a.listed ? w.rlist[q] : q;
-    }
-    if (e < 0) continue;
+    e = q;
+    row = a.listed ? w.rlist[q] : q;
     const T *f = (const T *)w.fresh_kv + (size_t)e * 2 * kvdim;
     const int cr = w.row_slot ? w.row_slot[row] : row;  // cache row
     for (int c = lane; c < chunks; c += 64) {
@@ -1140,8 +1162,9 @@ hipError_t launch_select(const SelectArgs &a, const Workspace &w, int32_t *sel_o
 hipError_t launch_compact_scatter(const SelectArgs &a, const Workspace &w, int dtype, int kvdim,
                                   int32_t *sel_idx, const int32_t *sel_offsets, void *k_cache,
                                   void *v_cache, hipStream_t s) {
+  // a wave per row up to 64K waves (the selection's size is known on the device only)
   int grid = (a.T * 64 + 255) / 256;
-  grid = grid < 2048 ? (grid > 0 ? grid : 1) : 2048;
+  grid = grid < 16384 ? (grid > 0 ? grid : 1) : 16384;
   if (dtype == SRP_BF16)
     hipLaunchKernelGGL(compact_scatter_kernel<uint16_t>, dim3(grid), dim3(256), 0, s, a, w, kvdim,
                        sel_idx, sel_offsets, (uint16_t *)k_cache, (uint16_t *)v_cache);
