@@ -168,9 +168,11 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   // Scores are in base-2 units (queries carry log2(e)/sqrt(d)). The score chains
   // start at -m, so they come out of the MFMA already relative to the reference
   // max m, which is raised only when a tile's max exceeds it by more than 8:
-  // probabilities stay below 2^8 and rescales are rare. l is this lane's share
-  // of the row sum (its keys of each 16-key step); the two lanes of a column are
-  // added at the end.
+  // probabilities stay below 2^8 and rescales are rare. The check follows the
+  // exponentials instead of a max before them: a probability of at least 2^8 makes
+  // its lane's sum over the tile at least 256, and only then (rarely) is the exact
+  // max taken and the tile redone. l is this lane's share of the row sum (its keys
+  // of each 16-key step); the two lanes of a column are added at the end.
   float m = 0.f, l = 0.f;
   floatx16 cneg;  // -m in every element: the first accumulator of each score chain
   const bf16x2 ones = {(__bf16)1.0f, (__bf16)1.0f};
@@ -227,26 +229,6 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
     for (int e = 0; e < 16; e += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, s[1][e]), s[1][e + 1]);
     return pair_max(x);
   };
-  // lazy rescale after the max mx of the next tile (relative to m): only when it
-  // rises by more than 8, after the PV product of the current tile
-  auto rescale = [&](floatx16 (&s)[2], float mx) __attribute__((always_inline)) {
-    const bool up = mx > 8.f;
-    if (__any(up)) {
-      const float dlt = up ? mx : 0.f;
-      const float alpha = __builtin_amdgcn_exp2f(-dlt);
-      m += dlt;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) cneg[e] = -m;
-      l *= alpha;
-#pragma unroll
-      for (int b = 0; b < D / 32; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) { s[0][e] -= dlt; s[1][e] -= dlt; }
-    }
-  };
-
   using I0 = std::integral_constant<int, 0>;
   using I1 = std::integral_constant<int, 1>;
   using I2 = std::integral_constant<int, 2>;
@@ -281,7 +263,7 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   // 32-63, taken in turn so neither waits on its own previous MFMA) with the
   // probabilities of tile j: step t exponentiates elements
   // 2(t%4), 2(t%4)+1 of k-step c = t/4 (half c/2, elements 8(c%2)+...).
-  auto part1 = [&](auto NSLOT, floatx16 (&cur)[2], floatx16 (&nxt)[2], u32x4 (&pw)[4])
+  auto part1 = [&](auto NSLOT, floatx16 (&cur)[2], floatx16 (&nxt)[2], u32x4 (&pw)[4], float &lt)
       __attribute__((always_inline)) {
     const char *St = slot_ptr(NSLOT);
     auto kfrag = [&](int t) __attribute__((always_inline)) {
@@ -308,17 +290,57 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
         const bf16x2 pr = {(__bf16)__builtin_amdgcn_exp2f(cur[c / 2][(c % 2) * 8 + jj]),
                            (__bf16)__builtin_amdgcn_exp2f(cur[c / 2][(c % 2) * 8 + jj + 1])};
         uint32_t word = __builtin_bit_cast(uint32_t, pr);
-        l = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, l, false);
+        lt = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lt, false);
         // the empty asm pins the work to this step (it would otherwise sink to
         // its first use, the PV MFMAs)
-        asm volatile("" : "+v"(word), "+v"(l));
+        asm volatile("" : "+v"(word), "+v"(lt));
         pw[c][v % 4] = word;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  // Part 2: the PV MFMAs of tile j with the column max of tile j+1 (masked first
-  // when the tile needs it)
+  // After the exponentials of tile j (scores cur): when some lane's sum over the
+  // tile reached 256, the tile's exact column max decides a rescale as in the
+  // lazy scheme (raise m where it exceeds 8; O, l and the next tile's scores follow)
+  // and the tile's probabilities are formed again. Wave-uniform and rare.
+  auto check_tile = [&](floatx16 (&cur)[2], floatx16 (&nxt)[2], u32x4 (&pw)[4], float &lt)
+      __attribute__((always_inline)) {
+    if (__any(lt >= 256.f)) {
+      float x = __builtin_fmaxf(cur[0][0], cur[0][1]);
+#pragma unroll
+      for (int e = 2; e < 16; e += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, cur[0][e]), cur[0][e + 1]);
+#pragma unroll
+      for (int e = 0; e < 16; e += 2) x = __builtin_fmaxf(__builtin_fmaxf(x, cur[1][e]), cur[1][e + 1]);
+      x = pair_max(x);
+      const bool up = x > 8.f;
+      if (__any(up)) {
+        const float dlt = up ? x : 0.f;
+        const float alpha = __builtin_amdgcn_exp2f(-dlt);
+        m += dlt;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) cneg[e] = -m;
+        l *= alpha;
+#pragma unroll
+        for (int b = 0; b < D / 32; ++b)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) acc[b][e] *= alpha;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) { nxt[0][e] -= dlt; nxt[1][e] -= dlt; }
+        lt = 0.f;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int c = v / 4, jj = 2 * (v % 4);
+          const bf16x2 pr = {(__bf16)__builtin_amdgcn_exp2f(cur[c / 2][(c % 2) * 8 + jj] - dlt),
+                             (__bf16)__builtin_amdgcn_exp2f(cur[c / 2][(c % 2) * 8 + jj + 1] - dlt)};
+          lt = __builtin_amdgcn_fdot2_f32_bf16(pr, ones, lt, false);
+          pw[c][v % 4] = __builtin_bit_cast(uint32_t, pr);
+        }
+      }
+    }
+    l += lt;
+  };
+  // Part 2: the PV MFMAs of tile j, with the mask of tile j+1 when it needs one
+  // (its VALU work now lies in part 1, which the other wave of the SIMD runs meanwhile)
   auto part2 = [&](auto SLOT, floatx16 (&nxt)[2], const u32x4 (&pw)[4], int kb_next)
       __attribute__((always_inline)) {
     const char *St = slot_ptr(SLOT);
@@ -340,7 +362,6 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
     bf16x8 vf[PFD + 1];
 #pragma unroll
     for (int t = 0; t < PFD; ++t) vf[t] = vfrag(t);
-    float x = -INFINITY;
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int t = 0; t < NPV; ++t) {
@@ -348,15 +369,8 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
       const int b = t % (D / 32);
       acc[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[t % (PFD + 1)], __builtin_bit_cast(bf16x8, pw[t / (D / 32)]),
                                                        acc[b], 0, 0, 0);
-#pragma unroll
-      for (int u = 0; u < 32 / NPV; u += 2) {
-        const int v = t * (32 / NPV) + u;  // 0..31
-        x = __builtin_fmaxf(x, __builtin_fmaxf(nxt[v / 16][v % 16], nxt[v / 16][v % 16 + 1]));
-      }
-      asm volatile("" : "+v"(x));
       __builtin_amdgcn_sched_barrier(0);
     }
-    return pair_max(x);
   };
   // iteration j: tile j's scores are in `cur`, tile j+1's go to `nxt`. A wave's
   // last tile runs the same code (its score MFMAs read a stale slot and their
@@ -384,15 +398,16 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
     const bool second = !lead;
     if (!second && j >= 1 && j + 3 < nblk) issue(FREE3{}, j + 3);
     u32x4 pw[4];
-    if (j < nact) part1(NEXT{}, cur, nxt, pw);
+    if (j < nact) {
+      float lt = 0.f;
+      part1(NEXT{}, cur, nxt, pw, lt);
+      check_tile(cur, nxt, pw, lt);
+    }
     if (second && j + 1 < nblk) {
       barrier_after(j);
       if (j + 4 < nblk) issue(FREE4{}, j + 4);
     }
-    if (j < nact) {
-      const float mx = part2(SLOT, nxt, pw, key_base + (j + 1) * kBK);
-      if (j + 1 < nact) rescale(nxt, mx);
-    }
+    if (j < nact) part2(SLOT, nxt, pw, key_base + (j + 1) * kBK);
     if (!second && j + 1 < nblk) barrier_after(j);
   };
   // unrolled by ten so slots and score buffers are both constants
