@@ -125,22 +125,27 @@ def algorithmic_work(spec, lay, sel, ratio_rows):
     }
 
 
-# The kernels of each MFMA stage (rocprofv3 names; a stage's time per layer call is
-# the sum of its kernels), with the sources their code comes from: a recorded
-# profile figure is used only while these files are unchanged.
+# The kernels of each stage of a layer call (rocprofv3 names; a stage's time per
+# layer call is the sum of its kernels), with the sources their code comes from: a
+# recorded profile figure is used only while these files are unchanged.
+_SEL_SRC = ["k_select.hip", "k_misc.hip", "kernels.hpp", "common.hpp"]
 STAGE_KERNELS = {
+    "prepare": ([r"row_meta_kernel", r"mark_cand_kernel", r"score_select_kernel", r"r_count_kernel",
+                 r"r_scan_kernel", r"r_write_kernel", r"rerotate_kernel"], _SEL_SRC),
     "kv_proj": ([r"gemm_bf16_kernel<(0|3),", r"gemm_fixup_kernel<(0|3),"],
                 ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
+    "select": ([r"keys_kernel", r"select_lds_kernel", r"\bselect_kernel", r"finalize_kernel"], _SEL_SRC),
+    "scatter": ([r"compact_scatter_kernel"], _SEL_SRC),
     "q_proj": ([r"gemm_bf16_kernel<(1|4),", r"gemm_fixup_kernel<(1|4),"],
                ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
     "attention": ([r"attn_bf16_kernel<"], ["k_attn.hip", "kernels.hpp", "common.hpp"]),
 }
-# Kernels launched exactly once per srp_fuse_layer call, ahead of every stage
-# kernel of the call: they mark where the last layer calls begin. The trace records
-# every kernel, so it cuts at the call's first kernel (row metadata); the counter
-# runs record only the MFMA stages, and cut at the K/V projection.
-TRACE_ANCHOR = r"row_meta_kernel"
-PMC_ANCHOR = r"gemm_bf16_kernel<(0|3),"
+MFMA_STAGES = ("kv_proj", "q_proj", "attention")
+# Kernels launched exactly once per srp_fuse_layer call, ahead of the rest of the
+# call: the first of them that a record holds marks where the last layer calls
+# begin (the row metadata opens every call with rows; counter runs that record only
+# the MFMA stages cut at the K/V projection).
+ANCHORS = (r"row_meta_kernel", r"gemm_bf16_kernel<(0|3),")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
@@ -194,14 +199,18 @@ def _stage_of(name):
     return None
 
 
-def _window(events, n_calls, anchor):
+def _window(events, n_calls):
     """The dispatches of the last n_calls layer calls: events = [(order key, kernel
-    name, value)], cut at the n_calls-th last launch of the anchor kernel."""
+    name, value)], cut at the n_calls-th last launch of the first anchor kernel the
+    record holds."""
     import re
-    anchors = sorted(k for k, n, _ in events if re.search(anchor, n))
-    if len(anchors) < n_calls:
-        raise SystemExit(f"only {len(anchors)} layer calls in the record, {n_calls} asked for")
-    t0 = anchors[-n_calls]
+    for anchor in ANCHORS:
+        marks = sorted(k for k, n, _ in events if re.search(anchor, n))
+        if marks:
+            break
+    if len(marks) < n_calls:
+        raise SystemExit(f"only {len(marks)} layer calls in the record, {n_calls} asked for")
+    t0 = marks[-n_calls]
     return [(k, n, v) for k, n, v in events if k >= t0]
 
 
@@ -240,8 +249,8 @@ def summarize_pmc(fetch, write, cfetch, cwrite, copy_mib, n_calls):
 
     f_fac, f_raw = copy_factor(cfetch, "FETCH_SIZE")
     w_fac, w_raw = copy_factor(cwrite, "WRITE_SIZE")
-    fd = _window(_per_dispatch(_pmc_rows(fetch), "FETCH_SIZE"), n_calls, PMC_ANCHOR)
-    wd = _window(_per_dispatch(_pmc_rows(write), "WRITE_SIZE"), n_calls, PMC_ANCHOR)
+    fd = _window(_per_dispatch(_pmc_rows(fetch), "FETCH_SIZE"), n_calls)
+    wd = _window(_per_dispatch(_pmc_rows(write), "WRITE_SIZE"), n_calls)
     rec = {"copy_mib": copy_mib, "copy_fetch_kib": f_raw, "copy_write_kib": w_raw,
            "fetch_factor": f_fac, "write_factor": w_fac, "layer_calls": n_calls, "stages": {}}
     lines = ["| stage | kernels | FETCH_SIZE KiB / call | WRITE_SIZE KiB / call | HBM bytes / call (scaled) |",
@@ -272,7 +281,7 @@ def summarize_trace(trace_csv, n_calls):
     with open(trace_csv) as fh:
         rows = list(csv.DictReader(fh))
     ev = _window([(int(r["Start_Timestamp"]), r["Kernel_Name"], int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
-                  for r in rows], n_calls, TRACE_ANCHOR)
+                  for r in rows], n_calls)
     per = {}
     for _, n, d in ev:
         per.setdefault(n, []).append(d)
@@ -561,12 +570,22 @@ def main():
         if nl > 1:
             ent["per_layer_ms"] = [round(float(x), 4) for x in st[:, :, i].mean(axis=0)]
         stages[nm] = ent
+    # the committed profile records of this workload, stage by stage: kernel time per
+    # layer call from the trace, fabric bytes per layer call from the counter runs
+    label = profile_label(args, spec)
+    for nm, ent in stages.items():
+        pms, pby = recorded_stage(label, "trace", nm), recorded_stage(label, "traffic", nm)
+        if pms:
+            ent["profile_ms"] = round(pms, 4)
+        if pby is not None:
+            ent["counter_bytes"] = round(pby)
+            if pms:
+                ent["counter_gbs"] = round(pby / (pms * 1e-3) / 1e9, 1)
     # dominant kernel: the longest MFMA stage. Its achieved rate is the stage's
     # algorithmic flops per layer call over its time per layer call, from the
     # library's stage events in this run; the same flops over the committed rocprofv3
     # trace's time per layer call of this workload are reported beside it.
-    label = profile_label(args, spec)
-    dom = max(("kv_proj", "q_proj", "attention"), key=lambda n: stages[n]["ms"])
+    dom = max(MFMA_STAGES, key=lambda n: stages[n]["ms"])
     roof = {"stage": dom,
             "kernel": {"kv_proj": "gemm_bf16_kernel<EPI_KV> + fix-up", "q_proj": "gemm_bf16_kernel<EPI_Q> + fix-up",
                        "attention": "attn_bf16_kernel<128>"}[dom] if spec.dtype == "bf16" else dom,

@@ -69,7 +69,7 @@ def test_traffic_summary_scales_by_the_copy_calibration(pmc_dirs):
     # the K/V stage adds its fix-up kernel: fetch (1040 + 3060) / 2, write 120
     kv = rec["stages"]["kv_proj"]
     assert kv["bytes_per_call"] == pytest.approx((2050 * 2 + 120) * 1024)
-    assert "q_proj" not in rec["stages"]  # no dispatches of it
+    assert "q_proj" not in rec["stages"] and "select" not in rec["stages"]  # no dispatches of them
     assert attn["source_hash"] == bench.source_hash(bench.STAGE_KERNELS["attention"][1])
     with pytest.raises(SystemExit):
         _pmc(pmc_dirs, calls=4)  # more calls than the record holds
