@@ -798,12 +798,14 @@ hipError_t launch_gemm(const GemmArgs &g0, hipStream_t s) {
   const int bm = bf ? C::BM : kBM32, bn = bf ? C::BN : kBN;
   const long tiles = (long)((g.M_cap + bm - 1) / bm) * ((g.N + bn - 1) / bn);
   if (tiles <= 0) return hipSuccess;
-  // resident work-groups (256 CUs x work-groups per CU), a multiple of the 8 XCDs
+  // resident work-groups (256 CUs x work-groups per CU), a multiple of the 8 XCDs.
+  // With room for partial tiles the grid stays whole, so that a launch of fewer
+  // tiles than work-groups splits them along K (all of them form the last round).
+  if (!bf || !g.part) g.part_cap = 0;
   const long resident = bf ? 256L * C::PER_CU : 512L;
-  long grid = tiles < resident ? tiles : resident;
+  long grid = tiles < resident && g.part_cap == 0 ? tiles : resident;
   grid = (grid + 7) / 8 * 8;
   g.grid_main = (int)grid;
-  if (!bf || !g.part) g.part_cap = 0;
   const dim3 gr((unsigned)grid), bl(bf ? C::THREADS : 256);
   // fix-up: with M known here the split plan is known too (no launch without a
   // split); with M on the device, as many items as the plan can have for M_cap
