@@ -219,7 +219,12 @@ constexpr int kCtrVtChunks = 3;  // V transpose chunks claimed (zeroed by the se
 inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 inline int blocks_per_req(int max_req_rows) { return (max_req_rows + 1023) / 1024 > 0 ? (max_req_rows + 1023) / 1024 : 1; }
-inline int max_attn_tiles(int T, int n_req) { return T / kQT + n_req + 1; }
+// The selection's finalize may cut the longest attention tiles of an
+// under-filled launch into halves of their queries, adding at most
+// kAttnExtraTiles tiles; key blocks of the attention are kAttnBK rows.
+constexpr int kAttnExtraTiles = 64;
+constexpr int kAttnBK = 64;
+inline int max_attn_tiles(int T, int n_req) { return T / kQT + n_req + 1 + kAttnExtraTiles; }
 // Row stride of the transposed V copy: T rounded up to 64 plus one zeroed tile, so
 // a key tile that starts inside the batch never reads past the copy.
 inline int vt_stride(int T) { return (T + 63) / 64 * 64 + 64; }

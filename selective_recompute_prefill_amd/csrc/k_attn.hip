@@ -34,7 +34,7 @@ __device__ __forceinline__ void static_for(F &&f) {
   }
 }
 
-constexpr int kBK = 64;          // keys per LDS stage
+constexpr int kBK = kAttnBK;     // keys per LDS stage
 constexpr int kAW = 8;           // waves per work-group (two per SIMD)
 constexpr int kACols = 32 * kAW; // (query, head) columns per work-group
 
@@ -91,6 +91,7 @@ __global__ __launch_bounds__(64 * kAW, 1) void attn_bf16_kernel(AttnArgs a) {
   if (slot >= n_tiles) return;
   const int G = a.nh / a.nkv;
   const int q0 = a.tiles[3 * slot], nq = a.tiles[3 * slot + 1], r = a.tiles[3 * slot + 2];
+  if (nq <= 0) return;  // the empty second half of a one-row tile
   // key tiles are aligned to 64 rows (the V^T key order repeats every 16 rows
   // and the copies stay 128-byte aligned); rows of the first tile before the
   // request's first row are masked

@@ -342,21 +342,67 @@ __device__ void finalize_body(const SelectArgs &a, const Workspace &w, int32_t *
   // tile i of request r is emitted at E = (tiles of any request with index > i)
   // + (requests before r that also have a tile i): descending tile index first,
   // so the longest causal ranges start first.
-  for (int f = tid; f < tcarry; f += 1024) {
-    const int r = upper_index(tpre, nr + 1, f);
+  const int tr = a.tile_rows;
+  auto place = [&](int f, int &E, int &q0, int &nq, int &r) {
+    r = upper_index(tpre, nr + 1, f);
     const int i = f - tpre[r];
-    int E = 0;
+    E = 0;
     for (int q = 0; q < nr; ++q) {
       const int t = ntile[q];
       E += t - 1 - i > 0 ? t - 1 - i : 0;
       if (q < r && t > i) ++E;
     }
     const int c = w.sel_cnt[r];
-    const int tr = a.tile_rows;
-    w.tiles[3 * E + 0] = sel_offsets[r] + i * tr;
-    w.tiles[3 * E + 1] = c - i * tr < tr ? c - i * tr : tr;
+    q0 = sel_offsets[r] + i * tr;
+    nq = c - i * tr < tr ? c - i * tr : tr;
+  };
+  auto put = [&](int E, int q0, int nq, int r) {
+    w.tiles[3 * E + 0] = q0;
+    w.tiles[3 * E + 1] = nq;
     w.tiles[3 * E + 2] = r;
+  };
+  const int wmax = 256 / a.nkv;
+  if (tcarry >= wmax) {
+    for (int f = tid; f < tcarry; f += 1024) {
+      int E, q0, nq, r;
+      place(f, E, q0, nq, r);
+      put(E, q0, nq, r);
+    }
+    return;
   }
+  // An under-filled launch (fewer tiles than one work-group per CU, 256 CUs, for
+  // each KV head) is evened out. A tile's key blocks run from its request's first
+  // row, rounded down to a block, to its last query. Let H be the number of tiles
+  // longer than 1.15 times a CU's share of all key blocks, at most the room left:
+  // the first H tiles in emission order (the longest) each become two tiles of
+  // half their queries (the second empty for a one-row tile), in their place.
+  // (Thirds ran no faster than halves: with fewer queries a work-group's time per
+  // key block stops falling.)
+  const int f = tid;
+  int E = 0, q0 = 0, nq = 0, r = 0, nb = 0;
+  if (f < tcarry) {
+    place(f, E, q0, nq, r);
+    const int *roff = a.listed ? w.roff : a.req_offsets;
+    const int last = w.tsel_row[roff[r] + (q0 - sel_offsets[r]) + nq - 1];
+    nb = (last + 1 - (a.req_offsets[r] & ~(kAttnBK - 1)) + kAttnBK - 1) / kAttnBK;
+  }
+  int total, longer;
+  block_excl_scan(nb, sh, &total);
+  const long long thr = (long long)total * a.nkv * 115 / (256 * 100);
+  block_excl_scan(f < tcarry && nb > thr ? 1 : 0, sh, &longer);
+  const int room = min(wmax - tcarry, kAttnExtraTiles);
+  const int H = min(longer, room > 0 ? room : 0);
+  if (f < tcarry) {
+    const int P = E + (E < H ? E : H);
+    if (E < H) {
+      const int h1 = (nq + 1) / 2;
+      put(P, q0, h1, r);
+      put(P + 1, q0 + h1, nq - h1, r);
+    } else {
+      put(P, q0, nq, r);
+    }
+  }
+  if (tid == 0) w.ctr[kCtrTiles] = tcarry + H;
 }
 
 // ------------------------------------------------------------------------- //

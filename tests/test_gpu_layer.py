@@ -17,7 +17,7 @@ from selective_recompute_prefill_amd import inputs
 from selective_recompute_prefill_amd import srp as S
 from selective_recompute_prefill_amd.device import LayerCall, download, ints, upload
 
-from parity import (assert_attention_bf16_scores, assert_close, check_selection, csr_ok, oracle_caches,
+from parity import (assert_attention_bf16_scores, assert_close, attn_tile_rows, check_selection, csr_ok, oracle_caches,
                     oracle_layer)
 
 pytestmark = pytest.mark.gpu
@@ -294,6 +294,34 @@ def test_candidate_list_topk_and_given():
         run_case(spec, w=w, kc_st=kc, vc_st=vc,
                  sel_kw=dict(ratio=0.15, mode=mode, cand=c_t, cand_offsets=o_t),
                  oracle_kw=dict(mode=omode, cand=cand), what=f"cand-{omode}")
+
+
+def test_one_row_tail_tiles_of_an_underfilled_launch():
+    """Selections of 2 tiles + 1 row per request (64-row tiles at G = 4): the
+    one-row tiles have the longest key ranges, come first in the tile list and are
+    cut in two by the finalize's evening-out of under-filled launches (the second
+    half empty); every attention row must still match the oracle."""
+    spec = inputs.small_spec()
+    w = inputs.generate(spec)
+    kc, vc = oracle_caches(w)
+    lay = w.layout
+    tile = attn_tile_rows(spec.dtype, spec.n_heads, spec.n_kv_heads)
+    _, src = ref.row_layout(lay.req_offsets, lay.chunk_offsets, lay.chunk_src_pos, lay.total_rows)
+    rng = np.random.default_rng(11)
+    cand, off = [], [0]
+    for r in range(lay.n_req):
+        rows = np.arange(lay.req_offsets[r], lay.req_offsets[r + 1])
+        cached = rows[src[rows] >= 0]
+        n_fresh = len(rows) - len(cached)
+        need = 2 * tile + 1 - n_fresh
+        assert 0 < need <= len(cached)
+        cand.append(np.sort(rng.choice(cached, need, replace=False)))
+        off.append(off[-1] + need)
+    cand = np.concatenate(cand)
+    got, want, _ = run_case(spec, w=w, kc_st=kc, vc_st=vc,
+                            sel_kw=dict(mode=S.SRP_SEL_GIVEN, cand=ints(cand), cand_offsets=ints(off)),
+                            oracle_kw=dict(mode="given", cand=cand), what="one-row tail tiles")
+    assert np.all(np.diff(got["sel_offsets"]) == 2 * tile + 1)
 
 
 def test_deterministic_bitwise():
