@@ -48,6 +48,7 @@ def _serial(spec, lay, call, w, caches, first_kw, modes=None):
     kcs, vcs = [], []
     prev_i = torch.empty_like(call.sel_idx)
     prev_o = torch.empty_like(call.sel_offsets)
+    steps = []  # each chain step's hidden before and after, with the layer's output
     for l in range(spec.n_layers):
         kc, vc = upload(caches[l][0], "bf16"), upload(caches[l][1], "bf16")
         if l == 0:
@@ -58,13 +59,18 @@ def _serial(spec, lay, call, w, caches, first_kw, modes=None):
             mode = S.SRP_SEL_TOPK if modes is None else modes[l]
             sel = call.select(spec.layer_ratios()[l], mode=mode, cand=prev_i, cand_offsets=prev_o)
         call.fuse(sel, h, upload(w.layers[l].w_qkv, "bf16"), kc, vc, dev_out=False)
+        torch.cuda.synchronize()
+        before = download(h)
         S.srp_residual_rmsnorm(call.dims, h, call.attn_out, call.sel_idx, call.sel_offsets, lay.n_req, T)
+        torch.cuda.synchronize()
+        r = call.results()
+        steps.append(dict(before=before, after=download(h), attn=r["attn_out"], sel_idx=r["sel_idx"]))
         kcs.append(kc)
         vcs.append(vc)
     torch.cuda.synchronize()
     r = call.results()
     return dict(sel_idx=r["sel_idx"], sel_offsets=r["sel_offsets"], attn=r["attn_out"],
-                hidden=download(h), k=[download(k) for k in kcs], v=[download(v) for v in vcs])
+                hidden=download(h), k=[download(k) for k in kcs], v=[download(v) for v in vcs], steps=steps)
 
 
 def _stacked(spec, lay, w, caches, first_kw, copy_stream, modes=None):
@@ -94,6 +100,21 @@ def _stacked(spec, lay, w, caches, first_kw, copy_stream, modes=None):
                 hidden=download(h), k=[download(k) for k in kcs], v=[download(v) for v in vcs])
 
 
+def _check_chain_steps(ser):
+    """Each chain step of the serial run against the oracle's residual RMSNorm on the
+    same stored inputs: the selected rows within the bf16 tolerance of one layer, every
+    other row unchanged."""
+    for l, st in enumerate(ser["steps"]):
+        s = st["sel_idx"]
+        x = ref.widen(st["before"], "bf16")
+        want = ref.residual_rmsnorm(x[s], ref.widen(st["attn"], "bf16").reshape(len(s), -1))
+        got = ref.widen(st["after"], "bf16")
+        assert_close(got[s], want, "bf16", f"chain step {l}")
+        rest = np.ones(len(x), bool)
+        rest[s] = False
+        assert np.array_equal(st["after"][rest], st["before"][rest]), f"chain step {l}: unselected rows changed"
+
+
 def _same(a, b, what):
     for key in ("sel_idx", "sel_offsets", "attn", "hidden"):
         assert np.array_equal(a[key], b[key]), f"{what}: {key} differs"
@@ -117,6 +138,7 @@ def test_stack_equals_serial_layers_and_oracle(first):
         modes = [S.SRP_SEL_TOPK, S.SRP_SEL_TOPK, S.SRP_SEL_GIVEN, S.SRP_SEL_GIVEN]
     _say(f"[gpu] stack {first}: T={lay.total_rows}, {spec.n_layers} layers")
     ser = _serial(spec, lay, LayerCall(spec, lay), w, caches, first_kw, modes)
+    _check_chain_steps(ser)
     side = torch.cuda.Stream()
     piped = _stacked(spec, lay, w, caches, first_kw, side, modes)
     _same(piped, ser, "copy stream")
@@ -153,7 +175,8 @@ def test_stack_equals_serial_layers_and_oracle(first):
         x[s] = rb(ref.residual_rmsnorm(o["hidden_in"][s], o["attn_out"].reshape(len(s), -1)))
     # the hidden state went through every layer's chain step: each adds its layer's
     # output error (and a bf16 rounding) to the residual, so the max-abs bound is one
-    # layer's bound per chained layer; rel-L2 keeps the single-layer bound
+    # layer's bound per chained layer; rel-L2 keeps the single-layer bound (every step
+    # on its own inputs is held to one layer's bound by _check_chain_steps)
     got_h = ref.widen(piped["hidden"], "bf16")
     err = np.abs(got_h - x)
     assert np.linalg.norm(got_h - x) / np.linalg.norm(x) <= 1e-2
@@ -168,6 +191,7 @@ def test_stack_single_layer_without_host_caches():
     lay = w.layout
     caches = [oracle_caches(w, 0)]
     ser = _serial(spec, lay, LayerCall(spec, lay), w, caches, {})
+    _check_chain_steps(ser)
     call = LayerCall(spec, lay)
     first = call.select(0.2)
     h = upload(w.hidden, "bf16")
