@@ -112,7 +112,33 @@ hipError_t launch_gather_rows(int T, size_t row_bytes, const int32_t *row_slot, 
 }
 
 // hidden[j] <- y / sqrt(mean(y^2) + eps), y = hidden[j] + attn[s], j = sel_idx[s].
-// One work-group per selected row; fixed-order reduction.
+// One work-group per selected row; fixed-order reduction. A thread takes 8
+// consecutive elements per 2048 (16-byte loads); rows of up to kNormRegs * 2048
+// elements keep y in registers between the sum and the scaling, longer ones load
+// it again.
+constexpr int kNormRegs = 4;
+__device__ __forceinline__ void ld8(const uint16_t *p, float v[8]) {
+  const uint4 u = *reinterpret_cast<const uint4 *>(p);
+  const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    v[2 * k] = __uint_as_float(w[k] << 16);
+    v[2 * k + 1] = __uint_as_float(w[k] & 0xffff0000u);
+  }
+}
+__device__ __forceinline__ void ld8(const float *p, float v[8]) {
+  const float4 a = *reinterpret_cast<const float4 *>(p), b = *reinterpret_cast<const float4 *>(p + 4);
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void st8(uint16_t *p, const float v[8]) {
+  st4(p, v);
+  st4(p + 4, v + 4);
+}
+__device__ __forceinline__ void st8(float *p, const float v[8]) {
+  st4(p, v);
+  st4(p + 4, v + 4);
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(int H, T *hidden, const T *attn,
                                                               const int32_t *sel_idx,
@@ -120,30 +146,65 @@ __global__ __launch_bounds__(256) void residual_rmsnorm_kernel(int H, T *hidden,
   __shared__ float red[4];
   const int total = *total_dev;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const bool in_regs = H <= kNormRegs * 2048;
   for (int s = blockIdx.x; s < total; s += gridDim.x) {
     const int j = sel_idx[s];
     T *x = hidden + (size_t)j * H;
     const T *o = attn + (size_t)s * H;
     float ss = 0.f;
-    for (int i = tid * 4; i < H; i += 1024) {
-      float a[4], b[4];
-      ld4(x + i, a);
-      ld4(o + i, b);
+    float y[kNormRegs][8];
+    if (in_regs) {
+      // every load issued before the first use (past the row end: a valid element,
+      // its value dropped below)
+      float a[kNormRegs][8], b[kNormRegs][8];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) { const float y = a[k] + b[k]; ss = fmaf(y, y, ss); }
+      for (int c = 0; c < kNormRegs; ++c) {
+        const int i = min(tid * 8 + c * 2048, H - 8);
+        ld8(x + i, a[c]);
+        ld8(o + i, b[c]);
+      }
+#pragma unroll
+      for (int c = 0; c < kNormRegs; ++c) {
+        const int i = tid * 8 + c * 2048;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          y[c][k] = i < H ? a[c][k] + b[c][k] : 0.f;
+          ss = fmaf(y[c][k], y[c][k], ss);
+        }
+      }
+    } else {
+      for (int i = tid * 8; i < H; i += 2048) {
+        float a[8], b[8];
+        ld8(x + i, a);
+        ld8(o + i, b);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) { const float v = a[k] + b[k]; ss = fmaf(v, v, ss); }
+      }
     }
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
     if (lane == 0) red[w] = ss;
     __syncthreads();
     const float tot = (red[0] + red[1]) + (red[2] + red[3]);
     const float sc = 1.f / sqrtf(tot / (float)H + eps);
-    for (int i = tid * 4; i < H; i += 1024) {
-      float a[4], b[4];
-      ld4(x + i, a);
-      ld4(o + i, b);
+    if (in_regs) {
 #pragma unroll
-      for (int k = 0; k < 4; ++k) a[k] = (a[k] + b[k]) * sc;
-      st4(x + i, a);
+      for (int c = 0; c < kNormRegs; ++c) {
+        const int i = tid * 8 + c * 2048;
+        if (i < H) {
+#pragma unroll
+          for (int k = 0; k < 8; ++k) y[c][k] *= sc;
+          st8(x + i, y[c]);
+        }
+      }
+    } else {
+      for (int i = tid * 8; i < H; i += 2048) {
+        float a[8], b[8];
+        ld8(x + i, a);
+        ld8(o + i, b);
+#pragma unroll
+        for (int k = 0; k < 8; ++k) a[k] = (a[k] + b[k]) * sc;
+        st8(x + i, a);
+      }
     }
     __syncthreads();
   }

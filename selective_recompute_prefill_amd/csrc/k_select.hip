@@ -15,25 +15,29 @@ namespace srp {
 // ------------------------------------------------------------------------- //
 // row metadata
 // ------------------------------------------------------------------------- //
+__device__ __forceinline__ void row_meta(const SelectArgs &a, const Workspace &w, int j) {
+  const int c = upper_index(a.chunk_offsets, a.n_chunks + 1, j);
+  const int src0 = a.chunk_src_pos[c];
+  w.row_delta[j] = src0 >= 0 ? a.positions[j] - (src0 + j - a.chunk_offsets[c]) : kFresh;
+  w.row_req[j] = upper_index(a.req_offsets, a.n_req + 1, j);
+  if (a.block_rows > 0)
+    w.row_slot[j] = paged_row(PagedMap{a.block_rows, a.seg_block, a.block_table}, c, j - a.chunk_offsets[c]);
+  w.rowflag[j] = 0;
+  if (a.dev_out) a.dev_out[j] = __int_as_float(0x7fc00000);
+}
+
 __global__ void row_meta_kernel(SelectArgs a, Workspace w) {
-  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < a.T; j += gridDim.x * blockDim.x) {
-    const int c = upper_index(a.chunk_offsets, a.n_chunks + 1, j);
-    const int src0 = a.chunk_src_pos[c];
-    w.row_delta[j] = src0 >= 0 ? a.positions[j] - (src0 + j - a.chunk_offsets[c]) : kFresh;
-    w.row_req[j] = upper_index(a.req_offsets, a.n_req + 1, j);
-    if (a.block_rows > 0)
-      w.row_slot[j] = paged_row(PagedMap{a.block_rows, a.seg_block, a.block_table}, c, j - a.chunk_offsets[c]);
-    w.rowflag[j] = 0;
-    if (a.dev_out) a.dev_out[j] = __int_as_float(0x7fc00000);
-  }
+  for (int j = blockIdx.x * blockDim.x + threadIdx.x; j < a.T; j += gridDim.x * blockDim.x) row_meta(a, w, j);
+}
+
+__device__ __forceinline__ void mark_cand(const SelectArgs &a, const Workspace &w, int i) {
+  const int row = a.cand[i];
+  if (row >= 0 && row < a.T && w.row_delta[row] != kFresh) w.rowflag[row] = kCand;
 }
 
 __global__ void mark_cand_kernel(SelectArgs a, Workspace w) {
   const int n = a.cand_offsets[a.n_req];
-  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) {
-    const int row = a.cand[i];
-    if (row >= 0 && row < a.T && w.row_delta[row] != kFresh) w.rowflag[row] = kCand;
-  }
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) mark_cand(a, w, i);
 }
 
 // R = candidate rows plus fresh rows, compacted per request (3 passes over blocks
@@ -80,6 +84,39 @@ __global__ __launch_bounds__(1024) void r_write_kernel(SelectArgs a, Workspace w
   int tot;
   const int p = block_excl_scan(v, sh, &tot);
   if (v) w.rlist[w.blkcnt[blockIdx.x] + p] = j;
+}
+
+// The same three steps (row metadata, candidate marks, R list) in one work-group
+// of 1024 threads, for batches of at most kPrepOneGroup rows: one launch instead of
+// five, each of which costs more in launch and drain than in work at these sizes.
+constexpr int kPrepOneGroup = 16384;
+__global__ __launch_bounds__(1024) void prepare_one_group_kernel(SelectArgs a, Workspace w) {
+  __shared__ int sh[17];
+  const int tid = threadIdx.x;
+  for (int j = tid; j < a.T; j += 1024) row_meta(a, w, j);
+  __threadfence_block();
+  __syncthreads();
+  const int n = a.cand_offsets[a.n_req];
+  for (int i = tid; i < n; i += 1024) mark_cand(a, w, i);
+  __threadfence_block();
+  __syncthreads();
+  int carry = 0;
+  for (int r = 0; r < a.n_req; ++r) {
+    if (tid == 0) w.roff[r] = carry;
+    const int end = a.req_offsets[r + 1];
+    for (int base = a.req_offsets[r]; base < end; base += 1024) {
+      const int j = base + tid;
+      const int v = j < end ? (int)in_r(w, j) : 0;
+      int tot;
+      const int p = block_excl_scan(v, sh, &tot);
+      if (v) w.rlist[carry + p] = j;
+      carry += tot;
+    }
+  }
+  if (tid == 0) {
+    w.roff[a.n_req] = carry;
+    w.ctr[kCtrREntries] = carry;
+  }
 }
 
 // ------------------------------------------------------------------------- //
@@ -1166,6 +1203,10 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Work
 // launchers
 // ------------------------------------------------------------------------- //
 hipError_t launch_prepare(const SelectArgs &a, const Workspace &w, hipStream_t s) {
+  if (a.cand && a.listed && a.mode != SRP_SEL_SCORES && a.T > 0 && a.T <= kPrepOneGroup) {
+    hipLaunchKernelGGL(prepare_one_group_kernel, dim3(1), dim3(1024), 0, s, a, w);
+    return hipGetLastError();
+  }
   if (a.T > 0) {
     int grid = (a.T + 255) / 256;
     grid = grid < 4096 ? grid : 4096;
