@@ -130,7 +130,8 @@ def algorithmic_work(spec, lay, sel, ratio_rows):
 # recorded profile figure is used only while these files are unchanged.
 _SEL_SRC = ["k_select.hip", "k_misc.hip", "kernels.hpp", "common.hpp"]
 STAGE_KERNELS = {
-    "prepare": ([r"row_meta_kernel", r"mark_cand_kernel", r"score_select_kernel", r"r_count_kernel",
+    "prepare": ([r"row_meta_kernel", r"prepare_one_group_kernel", r"mark_cand_kernel", r"score_select_kernel",
+                 r"r_count_kernel",
                  r"r_scan_kernel", r"r_write_kernel", r"rerotate_kernel"], _SEL_SRC),
     "kv_proj": ([r"gemm_bf16_kernel<(0|3),", r"gemm_fixup_kernel<(0|3),"],
                 ["k_gemm.hip", "kernels.hpp", "common.hpp"]),
@@ -145,7 +146,7 @@ MFMA_STAGES = ("kv_proj", "q_proj", "attention")
 # call: the first of them that a record holds marks where the last layer calls
 # begin (the row metadata opens every call with rows; counter runs that record only
 # the MFMA stages cut at the K/V projection).
-ANCHORS = (r"row_meta_kernel", r"gemm_bf16_kernel<(0|3),")
+ANCHORS = (r"row_meta_kernel|prepare_one_group_kernel", r"gemm_bf16_kernel<(0|3),")
 PROFILES = os.path.join(ROOT, "profiles")
 
 
