@@ -705,6 +705,10 @@ __global__ __launch_bounds__(256) void gemm_fixup_kernel(GemmArgs g) {
 // 256x256 tiles, 8 waves of 128x64, two 64-deep ring slots (128 KB), one
 // work-group per CU
 using GemmBig = GemmCfg<256, 256, 2, 4, 2, 64>;
+// 256x128 tiles, 8 waves of 64x64, three 64-deep ring slots (144 KB): about 15%
+// less efficient per flop, but twice the tiles, for host-sized launches whose
+// 256x256 tiles would leave most of a round idle
+using GemmMid = GemmCfg<256, 128, 4, 2, 3, 64>;
 
 // ------------------------------------------------------------------------- //
 // fp32 kernel: 64x128 tile, BK 16, each thread 4 rows x 8 columns.
@@ -791,9 +795,18 @@ __global__ __launch_bounds__(256, 2) void gemm_f32_kernel(GemmArgs g) {
   }
 }
 
-hipError_t launch_gemm(const GemmArgs &g0, hipStream_t s) {
-  using C = GemmBig;
-  GemmArgs g = g0;
+// Time of a launch of `tiles` tiles on `grid` work-groups in units of one tile's
+// time: whole rounds, then the split last round (a piece plus the fix-up) or one
+// more round.
+inline float launch_cost(int tiles, int grid, int part_cap) {
+  constexpr float kFixCost = 0.07f;
+  const SplitPlan sp = split_plan(tiles, grid, part_cap);
+  if (sp.split >= 2) return (float)(sp.full / grid) + 1.f / (float)sp.split + kFixCost;
+  return (float)((tiles + grid - 1) / grid);
+}
+
+template <typename C>
+hipError_t launch_gemm_cfg(GemmArgs g, hipStream_t s) {
   const bool bf = g.dtype == SRP_BF16;
   const int bm = bf ? C::BM : kBM32, bn = bf ? C::BN : kBN;
   const long tiles = (long)((g.M_cap + bm - 1) / bm) * ((g.N + bn - 1) / bn);
@@ -839,6 +852,21 @@ hipError_t launch_gemm(const GemmArgs &g0, hipStream_t s) {
   }
 #undef SRP_GEMM_LAUNCH
   return hipGetLastError();
+}
+
+hipError_t launch_gemm(const GemmArgs &g, hipStream_t s) {
+  // bf16 with M known on the host: 256x128 tiles when the estimate says they end
+  // the launch at least 10% sooner (a 256x128 tile takes about 0.59 of a 256x256
+  // one); M on the device (sized for M_cap) keeps 256x256.
+  if (g.dtype == SRP_BF16 && !g.M_dev && g.part) {
+    const int M = g.M_host;
+    const long big = (long)((M + GemmBig::BM - 1) / GemmBig::BM) * ((g.N + GemmBig::BN - 1) / GemmBig::BN);
+    const long mid = (long)((M + GemmMid::BM - 1) / GemmMid::BM) * ((g.N + GemmMid::BN - 1) / GemmMid::BN);
+    if (big > 0 && big < (1L << 30) &&
+        0.59f * launch_cost((int)mid, 256, g.part_cap) < 0.9f * launch_cost((int)big, 256, g.part_cap))
+      return launch_gemm_cfg<GemmMid>(g, s);
+  }
+  return launch_gemm_cfg<GemmBig>(g, s);
 }
 
 }  // namespace srp
