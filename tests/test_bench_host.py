@@ -92,6 +92,27 @@ def test_trace_summary_per_layer_call(tmp_path):
     assert rec["kernel_ms_per_call"] == pytest.approx((5 + 300 + 20 + 500 + 5 + 340 + 40 + 700) / 2 / 1000)
 
 
+def test_trace_window_counts_calls_opened_by_either_prepare_kernel(tmp_path):
+    # a stack: the first layer call opens with the row metadata kernel, later ones
+    # (candidate lists) with the one-group prepare kernel; both mark a call
+    prep = "srp::prepare_one_group_kernel(srp::SelectArgs, srp::Workspace)"
+    rows, t = [], 0
+    for c, opener in enumerate([META, prep, prep, META, prep, prep]):
+        for name, dur in [(opener, 5), (GEMM, 100 + c), (ATTN, 200)]:
+            rows.append({"Kernel_Name": name, "Start_Timestamp": t, "End_Timestamp": t + dur * 1000})
+            t += dur * 1000 + 10
+    path = tmp_path / "kernel_trace.csv"
+    with open(path, "w", newline="") as fh:
+        wr = csv.DictWriter(fh, fieldnames=["Kernel_Name", "Start_Timestamp", "End_Timestamp"])
+        wr.writeheader()
+        wr.writerows(rows)
+    rec = _record(bench.summarize_trace(str(path), 3))  # the last three calls
+    assert rec["stages"]["kv_proj"]["avg_ms"] == pytest.approx((103 + 104 + 105) / 3 / 1000)
+    assert rec["stages"]["prepare"]["avg_ms"] == pytest.approx(0.005)
+    with pytest.raises(SystemExit):
+        bench.summarize_trace(str(path), 7)
+
+
 def test_recorded_figures_only_for_unchanged_sources(pmc_dirs, tmp_path, monkeypatch):
     monkeypatch.setattr(bench, "PROFILES", str(tmp_path))
     md = _pmc(pmc_dirs)
