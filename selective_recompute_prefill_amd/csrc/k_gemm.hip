@@ -419,6 +419,7 @@ __host__ __device__ inline SplitPlan split_plan(int tiles, int grid, int part_ca
 template <int MODE, typename C>
 __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmArgs g) {
   static_assert(C::BM * C::BN <= kGemmPartFloats, "partial tiles fit their slots");
+  static_assert(C::BK / 16 >= 3, "a stage's copies spread over three 16-deep steps");
   __shared__ __align__(16) char smem[C::SMEM];
   __shared__ EpiRow meta[C::BM];
   float *Cs = reinterpret_cast<float *>(smem);  // epilogue staging, EROWS x LDC fp32
@@ -488,11 +489,22 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
       else if (later == 1) wait_vmcnt<C::CPW>();
       else wait_vmcnt<0>();
       __builtin_amdgcn_s_barrier();
-      // the slot of tile kt+S-1 was last read in iteration kt-1
-      if (kt + C::S - 1 < nk) issue(kt + C::S - 1);
+      // the slot of tile kt+S-1 was last read in iteration kt-1. Its copies go out
+      // in three groups, before the first three 16-deep steps: issued all at once
+      // they stall the waves' MFMA issue while the copy unit drains them, and the
+      // last step's would land too late
+      const bool copy_next = kt + C::S - 1 < nk;
+      char *st_next = smem + ((kt + C::S - 1) % C::S) * C::STAGE;
       const char *as = smem + (kt % C::S) * C::STAGE, *bs = as + C::ATILE;
 #pragma unroll
       for (int ks = 0; ks < C::BK / 16; ++ks) {
+        if (ks < 3 && copy_next) {
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int j = (ks * C::CPW) / 3; j < ((ks + 1) * C::CPW) / 3; ++j)
+            dma16(src[j] + (size_t)(kt + C::S - 1) * (C::BK * 2), st_next + (w + C::WAVES * j) * 1024);
+          __builtin_amdgcn_sched_barrier(0);
+        }
         const uint32_t off = fr * (C::BK * 2) + (((2 * ks + fk) ^ fswz) * 16);
         bf16x8 af[C::MI], bfr[C::NI];
 #pragma unroll
