@@ -229,40 +229,61 @@ inline int max_attn_tiles(int T, int n_req) { return T / kQT + n_req + 1 + kAttn
 // a key tile that starts inside the batch never reads past the copy.
 inline int vt_stride(int T) { return (T + 63) / 64 * 64 + 64; }
 
-// One chunk of the transposed V copy for the attention's DMA loads: keys
-// r0..r0+63 of KV head g, with NT threads and a 128 x 66 u16 LDS tile. Row i of
-// head g holds vt[g][i][j] = v[slot(j)][g][i] (slot(j) = row_slot[j], or j when
-// row_slot is NULL); inside every 16-key group the keys are stored in the order
-// 0-3, 8-11, 4-7, 12-15 (the PV operand's lane order); keys at or past T are zero.
-template <int NT>
-__device__ __forceinline__ void vt_chunk(int r0, int g, int T, int D, int nkv, const uint16_t *v,
-                                         const int32_t *row_slot, uint16_t *vt, int vts,
-                                         uint16_t (*tile)[66]) {
+// Chunks of the transposed V copy for the attention's DMA loads. Chunk (r0, g)
+// covers keys r0..r0+63 of KV head g: row i of head g holds vt[g][i][j] =
+// v[slot(j)][g][i] (slot(j) = row_slot[j], or j when row_slot is NULL); inside
+// every 16-key group the keys are stored in the order 0-3, 8-11, 4-7, 12-15 (the
+// PV operand's lane order); keys at or past T are zero. A work-group of NT
+// threads does up to NCH chunks at once (n of them, chunk k at r0[k], g[k]): every
+// global load is issued before the first LDS write, each thread writes two keys of
+// one d per 32-bit LDS store, and each output 16 bytes comes from one LDS read.
+// tile: NCH x 128 rows x kVtPitch u16 of LDS.
+constexpr int kVtPitch = 72;  // u16 per LDS row (144 bytes: 16-byte aligned rows)
+template <int NT, int NCH>
+__device__ __forceinline__ void vt_chunks(int n, const int *r0, const int *g, int T, int D, int nkv,
+                                          const uint16_t *v, const int32_t *row_slot, uint16_t *vt, int vts,
+                                          uint16_t *tile) {
   typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
   const int tid = threadIdx.x, kvd = nkv * D, dch = D / 8;
-  for (int c = tid; c < 64 * dch; c += NT) {
-    const int key = c / dch, dc = c - key * dch;
-    const int row = r0 + key;
-    u32x4_t x = {0, 0, 0, 0};
-    if (row < T)
-      x = *reinterpret_cast<const u32x4_t *>(v + (size_t)(row_slot ? row_slot[row] : row) * kvd + g * D + dc * 8);
-    // stored position of this key: swap bits 2 and 3 of its index
-    const int pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+  constexpr int ITEMS = 32 * 16 / NT > 0 ? (32 * 16 + NT - 1) / NT : 1;  // (key pair, d chunk) items per thread
+  u32x4_t x[NCH][ITEMS][2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      tile[dc * 8 + 2 * i][pos] = (uint16_t)(x[i] & 0xffffu);
-      tile[dc * 8 + 2 * i + 1][pos] = (uint16_t)(x[i] >> 16);
+  for (int k = 0; k < NCH; ++k)
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int c = tid + it * NT, kp = c & 31, dc = c >> 5;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        x[k][it][h] = u32x4_t{0, 0, 0, 0};
+        const int row = k < n ? r0[k] + 2 * kp + h : T;
+        if (dc < dch && row < T)
+          x[k][it][h] =
+              *reinterpret_cast<const u32x4_t *>(v + (size_t)(row_slot ? row_slot[row] : row) * kvd + g[k] * D + dc * 8);
+      }
     }
-  }
-  __syncthreads();
-  for (int c = tid; c < D * 8; c += NT) {
-    const int dd = c >> 3, kc = c & 7;
-    u32x4_t y;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      y[i] = (uint32_t)tile[dd][kc * 8 + 2 * i] | ((uint32_t)tile[dd][kc * 8 + 2 * i + 1] << 16);
-    *reinterpret_cast<u32x4_t *>(vt + ((size_t)g * D + dd) * vts + r0 + kc * 8) = y;
-  }
+  for (int k = 0; k < NCH; ++k)
+#pragma unroll
+    for (int it = 0; it < ITEMS; ++it) {
+      const int c = tid + it * NT, kp = c & 31, dc = c >> 5;
+      if (dc >= dch) continue;
+      // stored position of key 2kp (bits 2 and 3 of its index swapped); key 2kp+1 follows
+      const int key = 2 * kp, pos = (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+      uint16_t *t = tile + ((size_t)k * 128 + dc * 8) * kVtPitch + pos;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const uint32_t a = x[k][it][0][i], b = x[k][it][1][i];
+        *reinterpret_cast<uint32_t *>(t + (2 * i) * kVtPitch) = (a & 0xffffu) | (b << 16);
+        *reinterpret_cast<uint32_t *>(t + (2 * i + 1) * kVtPitch) = (a >> 16) | (b & 0xffff0000u);
+      }
+    }
+  __syncthreads();
+  for (int k = 0; k < n; ++k)
+    for (int c = tid; c < D * 8; c += NT) {
+      const int dd = c >> 3, kc = c & 7;
+      const u32x4_t y = *reinterpret_cast<const u32x4_t *>(tile + ((size_t)k * 128 + dd) * kVtPitch + kc * 8);
+      *reinterpret_cast<u32x4_t *>(vt + ((size_t)g[k] * D + dd) * vts + r0[k] + kc * 8) = y;
+    }
 }
 
 // Lays the workspace out from `base` (nullptr: just measure), with `parts`

@@ -616,18 +616,25 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
   if constexpr (MODE == EPI_Q || MODE == EPI_QK) {
     if (g.vt_dst) {
       __shared__ int claim;
+      constexpr int NCH = 4;  // chunks per claim, their loads in flight together
       const int rows_n = g.vt_stride / 64, n_chunks = rows_n * g.nkv;
-      auto tile = reinterpret_cast<uint16_t (*)[66]>(smem);
-      static_assert(128 * 66 * 2 <= C::SMEM, "the transpose tile fits the ring");
+      static_assert(NCH * 128 * kVtPitch * 2 <= C::SMEM, "the transpose tiles fit the ring");
       for (;;) {
-        if (tid == 0) claim = atomicAdd(g.vt_ctr, 1);
+        if (tid == 0) claim = atomicAdd(g.vt_ctr, NCH);
         __syncthreads();
         const int c = claim;
         if (c >= n_chunks) break;
-        const int hg = c / rows_n;
-        vt_chunk<C::THREADS>((c - hg * rows_n) * 64, hg, g.vt_T, g.d, g.nkv, (const uint16_t *)g.vt_src,
-                             g.vt_slot, (uint16_t *)g.vt_dst, g.vt_stride, tile);
-        __syncthreads();  // the tile and `claim` are reused by the next chunk
+        int r0[NCH], hg[NCH];
+#pragma unroll
+        for (int k = 0; k < NCH; ++k) {
+          const int ck = c + k < n_chunks ? c + k : c;
+          hg[k] = ck / rows_n;
+          r0[k] = (ck - hg[k] * rows_n) * 64;
+        }
+        const int n = n_chunks - c < NCH ? n_chunks - c : NCH;
+        vt_chunks<C::THREADS, NCH>(n, r0, hg, g.vt_T, g.d, g.nkv, (const uint16_t *)g.vt_src, g.vt_slot,
+                                   (uint16_t *)g.vt_dst, g.vt_stride, reinterpret_cast<uint16_t *>(smem));
+        __syncthreads();  // the tiles and `claim` are reused by the next claim
       }
     }
   }
