@@ -1136,6 +1136,35 @@ __global__ __launch_bounds__(1024) void finalize_kernel(SelectArgs a, Workspace 
 // compaction to sel_idx and scatter of the fresh K/V rows (one wave per entry);
 // with fresh_all every recomputed entry's fresh K/V goes to its row instead
 // ------------------------------------------------------------------------- //
+// Copies one row's fresh K and V (16-byte chunks, a wave per row) into cache row
+// cr, two chunks per lane and operand at a time with all four loads issued before
+// the stores (the compiler cannot tell the scratch from the cache, so it would
+// otherwise wait on each load before the next).
+template <typename T>
+__device__ __forceinline__ void scatter_row(const T *f, int kvdim, bool v_only, T *k_cache, T *v_cache, int cr,
+                                            int lane) {
+  constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
+  const int chunks = kvdim / V;
+  T *kd = k_cache + (size_t)cr * kvdim, *vd = v_cache + (size_t)cr * kvdim;
+  for (int c = lane; c < chunks; c += 128) {
+    // the second chunk's loads come from a clamped (always valid) chunk
+    const int c2 = min(c + 64, chunks - 1);
+    uint4 k0 = {0, 0, 0, 0}, k1 = {0, 0, 0, 0};
+    if (!v_only) {
+      k0 = *reinterpret_cast<const uint4 *>(f + c * V);
+      k1 = *reinterpret_cast<const uint4 *>(f + c2 * V);
+    }
+    const uint4 v0 = *reinterpret_cast<const uint4 *>(f + kvdim + c * V);
+    const uint4 v1 = *reinterpret_cast<const uint4 *>(f + kvdim + c2 * V);
+    if (!v_only) *reinterpret_cast<uint4 *>(kd + c * V) = k0;
+    *reinterpret_cast<uint4 *>(vd + c * V) = v0;
+    if (c + 64 < chunks) {
+      if (!v_only) *reinterpret_cast<uint4 *>(kd + (c + 64) * V) = k1;
+      *reinterpret_cast<uint4 *>(vd + (c + 64) * V) = v1;
+    }
+  }
+}
+
 template <typename T>
 __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Workspace w, int kvdim,
                                                               int32_t *sel_idx, const int32_t *sel_offsets,
@@ -1145,8 +1174,6 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Work
   const int nwaves = (gridDim.x * blockDim.x) >> 6;
   const int *roff = a.listed ? w.roff : a.req_offsets;
   const int nR = roff[a.n_req];
-  constexpr int V = 16 / sizeof(T);  // elements per 16-byte chunk
-  const int chunks = kvdim / V;
   if (!a.fresh_all) {
     // selected rows only: output slot s of request r is entry roff[r] + (s -
     // sel_offsets[r]) of the per-request selection
@@ -1161,13 +1188,7 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Work
       }
       const T *f = (const T *)w.fresh_kv + (size_t)e * 2 * kvdim;
       const int cr = w.row_slot ? w.row_slot[row] : row;  // cache row
-      for (int c = lane; c < chunks; c += 64) {
-        if (!a.v_only)
-          *reinterpret_cast<uint4 *>(k_cache + (size_t)cr * kvdim + c * V) =
-              *reinterpret_cast<const uint4 *>(f + c * V);
-        *reinterpret_cast<uint4 *>(v_cache + (size_t)cr * kvdim + c * V) =
-            *reinterpret_cast<const uint4 *>(f + kvdim + c * V);
-      }
+      scatter_row(f, kvdim, a.v_only, k_cache, v_cache, cr, lane);
     }
     return;
   }
@@ -1189,13 +1210,7 @@ __global__ __launch_bounds__(256) void compact_scatter_kernel(SelectArgs a, Work
     row = a.listed ? w.rlist[q] : q;
     const T *f = (const T *)w.fresh_kv + (size_t)e * 2 * kvdim;
     const int cr = w.row_slot ? w.row_slot[row] : row;  // cache row
-    for (int c = lane; c < chunks; c += 64) {
-      if (!a.v_only)
-        *reinterpret_cast<uint4 *>(k_cache + (size_t)cr * kvdim + c * V) =
-            *reinterpret_cast<const uint4 *>(f + c * V);
-      *reinterpret_cast<uint4 *>(v_cache + (size_t)cr * kvdim + c * V) =
-          *reinterpret_cast<const uint4 *>(f + kvdim + c * V);
-    }
+    scatter_row(f, kvdim, a.v_only, k_cache, v_cache, cr, lane);
   }
 }
 
