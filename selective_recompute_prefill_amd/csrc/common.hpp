@@ -118,6 +118,14 @@ __device__ __forceinline__ int upper_index(const int32_t *a, int n, int x) {
   return lo;
 }
 
+// The same for a wave whose lanes hold the table (t = a[lane] for lane < n, n <= 64,
+// and a[0] <= x < a[n-1]): one ballot instead of dependent loads.
+__device__ __forceinline__ int upper_index_lanes(int t, int n, int x) {
+  const int lane = threadIdx.x & 63;
+  return __popcll(__ballot(lane >= 1 && lane < n && t <= x));
+}
+
+
 // ------------------------------------------------------------------------- //
 // rotary tables: cos/sin of p * base^(-2i/d), p < max_position, i < d/2,
 // computed in fp64 on the host and stored as fp32 [max_position][d/2].
