@@ -140,6 +140,23 @@ def test_no_cached_rows():
     assert len(got["sel_idx"]) == w.layout.total_rows  # everything recomputed
 
 
+@pytest.mark.parametrize("n_req", [63, 64])
+@pytest.mark.parametrize("fresh_all", [False, True])
+def test_request_table_in_lanes_boundary(n_req, fresh_all):
+    """63 and 64 requests of mixed sizes (empty ones included): below 64 the
+    scatter keeps the request tables one entry per lane and finds a row's
+    request with a ballot, from 64 on it searches them in memory."""
+    requests = [[] if i % 9 == 4 else [(5 + (i * 7) % 23, 0), (1 + i % 3, -1)] for i in range(n_req)]
+    spec, w = custom_workload(requests, seed=11)
+    kc, vc = oracle_caches(w)
+    sel_kw, okw = dict(ratio=0.3), {}
+    if fresh_all:
+        sel_kw["fresh_all"] = okw["fresh_all"] = True
+    got, _, _ = run_case(spec, w=w, lay=w.layout, kc_st=kc, vc_st=vc, sel_kw=sel_kw, oracle_kw=okw,
+                         what=f"{n_req} requests fresh_all={fresh_all}")
+    assert len(got["sel_offsets"]) == n_req + 1
+
+
 def test_more_requests_than_one_block():
     """1100 requests (every hundredth long, the rest three cached rows and one
     fresh one): the CSR offsets and the attention tile list are built in two
