@@ -445,25 +445,31 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
   const int fr = lane & 31, fk = lane >> 5;
   const uint32_t fswz = (fr / C::SWZ) % C::CH;
   floatx16 acc[C::MI][C::NI];
+  // 256x256 tiles run the two wave groups in turns (below); the encode's epilogue
+  // needs more registers than that schedule leaves, so it keeps the shared ring loop
+  constexpr bool kPingPong = C::S == 2 && C::WAVES == 8 && C::WM == 2 && C::BK == 64 && MODE != EPI_ENC;
 
   // acc = A[m0.., k0*32 ..] * B[n0.., ..]^T over nk k-tiles; `pre` runs once the
   // first copies are in flight
   auto mainloop = [&](int m0, int n0, int k0, int nk, auto pre) __attribute__((always_inline)) {
-    // wave w moves copies q = w + WAVES*j; A copies come first. Rows past M or
-    // N read a valid row (their results are never stored).
-    const char *src[C::CPW];
+    // copies are 1 KB operand pieces q of a stage, A's first; in the shared ring
+    // loop wave w moves q = w + WAVES*j. Rows past M or N read a valid row (their
+    // results are never stored).
     const int row0 = g.a_rows ? g.a_rows[m0] : m0;
-#pragma unroll
-    for (int j = 0; j < C::CPW; ++j) {
-      const int q = w + C::WAVES * j;
+    // source of copy q of the first k-tile (A copies first, then B)
+    auto copy_src = [&](int q) __attribute__((always_inline)) -> const char * {
       if (q < C::ACOPY) {
         const int m = m0 + C::RPC * q + lrow;
         const int row = m < M ? (g.a_rows ? g.a_rows[m] : m) : row0;
-        src[j] = A + (size_t)row * rowb + (size_t)k0 * (C::BK * 2) + lchunk * 16;
-      } else {
-        const int n = n0 + C::RPC * (q - C::ACOPY) + lrow;
-        src[j] = B + (size_t)(n < N ? n : N - 1) * rowb + (size_t)k0 * (C::BK * 2) + lchunk * 16;
+        return A + (size_t)row * rowb + (size_t)k0 * (C::BK * 2) + lchunk * 16;
       }
+      const int n = n0 + C::RPC * (q - C::ACOPY) + lrow;
+      return B + (size_t)(n < N ? n : N - 1) * rowb + (size_t)k0 * (C::BK * 2) + lchunk * 16;
+    };
+    const char *src[C::CPW];
+    if constexpr (!kPingPong) {
+#pragma unroll
+      for (int j = 0; j < C::CPW; ++j) src[j] = copy_src(w + C::WAVES * j);
     }
     auto issue = [&](int kt) __attribute__((always_inline)) {
       char *st = smem + (kt % C::S) * C::STAGE;
@@ -476,48 +482,164 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
       for (int j = 0; j < C::NI; ++j)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
+    if constexpr (kPingPong) {
+      // Waves 0-3 and 4-7 (one of each on every SIMD) take turns: while one group
+      // runs the MFMAs of 32 of a stage's 64 k-values from fragments it already
+      // holds, the other reads its fragments of the next 32 and moves operand data,
+      // so neither LDS reads nor global loads sit in a wave's MFMA stream. Both
+      // groups run the same stream (read, barrier, MFMAs, barrier), waves 4-7 one
+      // barrier later; numbering phases 4kt + p, group 0 reads stage kt in phases
+      // 4kt and 4kt+2, group 1 in 4kt+1 and 4kt+3.
+      // Group 0 reads only the top 128 A rows of a stage and group 1 only the
+      // bottom ones; both read all of B. So the three regions of a slot free at
+      // different phases, and every read phase fills a quarter of a later stage
+      // into a region already free: group 0 the first half of B (phase 4kt) and the
+      // bottom of A (4kt+2) of stage kt+1, group 1 the second half of B of stage
+      // kt+1 (4kt+1) and the top of A of stage kt+2 (4kt+3). A read phase stores
+      // the set its wave loaded into registers in its previous read phase, then
+      // loads the next one: global loads plus LDS stores move operand data faster
+      // than direct-to-LDS copies, and the compiler counts these loads itself.
+      static_assert(C::CPW == 8 && C::ACOPY == 32 && C::COPIES == 64, "four copies per set");
+      const bool g0 = w < C::WAVES / 2;
+      const int u = w & (C::WAVES / 2 - 1);
+      // set 0: group 0 the first half of B, group 1 the second half; set 1: group 0
+      // the bottom of A, group 1 the top. Set h holds copies qs[h] + u + 4i.
+      const int qs0 = g0 ? C::ACOPY : C::ACOPY + C::ACOPY / 2;
+      const int qs1 = g0 ? C::ACOPY / 2 : 0;
+      const char *sp[2][4];
 #pragma unroll
-    for (int p = 0; p < C::S - 1; ++p)
-      if (p < nk) issue(p);
-    pre();
-    for (int kt = 0; kt < nk; ++kt) {
-      // this tile's copies are done once at most those of the later tiles
-      // already in flight are outstanding
-      const int later = min(nk - 1 - kt, C::S - 2);
-      if (later >= 3) wait_vmcnt<3 * C::CPW>();
-      else if (later == 2) wait_vmcnt<2 * C::CPW>();
-      else if (later == 1) wait_vmcnt<C::CPW>();
-      else wait_vmcnt<0>();
-      __builtin_amdgcn_s_barrier();
-      // the slot of tile kt+S-1 was last read in iteration kt-1. Its copies go out
-      // in three groups, before the first three 16-deep steps: issued all at once
-      // they stall the waves' MFMA issue while the copy unit drains them, and the
-      // last step's would land too late
-      const bool copy_next = kt + C::S - 1 < nk;
-      char *st_next = smem + ((kt + C::S - 1) % C::S) * C::STAGE;
-      const char *as = smem + (kt % C::S) * C::STAGE, *bs = as + C::ATILE;
+      for (int i = 0; i < 4; ++i) {
+        sp[0][i] = copy_src(qs0 + u + 4 * i);
+        sp[1][i] = copy_src(qs1 + u + 4 * i);
+      }
+      // direct copies of set h into the slot of stage kt (prologue only)
+      auto copy_set = [&](int h, int kt) __attribute__((always_inline)) {
+        char *st = smem + (kt % C::S) * C::STAGE + ((h ? qs1 : qs0) + u) * 1024;
 #pragma unroll
-      for (int ks = 0; ks < C::BK / 16; ++ks) {
-        if (ks < 3 && copy_next) {
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int j = (ks * C::CPW) / 3; j < ((ks + 1) * C::CPW) / 3; ++j)
-            dma16(src[j] + (size_t)(kt + C::S - 1) * (C::BK * 2), st_next + (w + C::WAVES * j) * 1024);
-          __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < 4; ++i) {
+          dma16(sp[h][i], st + i * 4096);
+          sp[h][i] += C::BK * 2;
         }
-        const uint32_t off = fr * (C::BK * 2) + (((2 * ks + fk) ^ fswz) * 16);
-        bf16x8 af[C::MI], bfr[C::NI];
+      };
+      // the staged set in four scalars (an array under these conditions would be
+      // kept in scratch memory)
+      uint4 sg0 = {0, 0, 0, 0}, sg1 = sg0, sg2 = sg0, sg3 = sg0;
+      auto load_set = [&](int h) __attribute__((always_inline)) {
+        sg0 = *reinterpret_cast<const uint4 *>(sp[h][0]);
+        sg1 = *reinterpret_cast<const uint4 *>(sp[h][1]);
+        sg2 = *reinterpret_cast<const uint4 *>(sp[h][2]);
+        sg3 = *reinterpret_cast<const uint4 *>(sp[h][3]);
 #pragma unroll
-        for (int i = 0; i < C::MI; ++i)
-          af[i] = *reinterpret_cast<const bf16x8 *>(as + (wm * C::TM + i * 32) * (C::BK * 2) + off);
+        for (int i = 0; i < 4; ++i) sp[h][i] += C::BK * 2;
+      };
+      auto write_set = [&](int h, int kt) __attribute__((always_inline)) {
+        char *st = smem + (kt % C::S) * C::STAGE + ((h ? qs1 : qs0) + u) * 1024 + lane * 16;
+        *reinterpret_cast<uint4 *>(st) = sg0;
+        *reinterpret_cast<uint4 *>(st + 4096) = sg1;
+        *reinterpret_cast<uint4 *>(st + 8192) = sg2;
+        *reinterpret_cast<uint4 *>(st + 12288) = sg3;
+      };
+      bf16x8 af[2][C::MI], bfr[2][C::NI];
+      auto read_half = [&](int kt, int h) __attribute__((always_inline)) {
+        const char *as = smem + (kt % C::S) * C::STAGE, *bs = as + C::ATILE;
 #pragma unroll
-        for (int j = 0; j < C::NI; ++j)
-          bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + (wn * C::TN + j * 32) * (C::BK * 2) + off);
+        for (int s = 0; s < 2; ++s) {
+          const int ks = 2 * h + s;
+          const uint32_t off = fr * (C::BK * 2) + (((2 * ks + fk) ^ fswz) * 16);
 #pragma unroll
-        for (int i = 0; i < C::MI; ++i)
+          for (int i = 0; i < C::MI; ++i)
+            af[s][i] = *reinterpret_cast<const bf16x8 *>(as + (wm * C::TM + i * 32) * (C::BK * 2) + off);
 #pragma unroll
           for (int j = 0; j < C::NI; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+            bfr[s][j] = *reinterpret_cast<const bf16x8 *>(bs + (wn * C::TN + j * 32) * (C::BK * 2) + off);
+        }
+      };
+      auto sync = [&]() __attribute__((always_inline)) {
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // set 1 is stored at the second read phase of stage kt for stage kt + ydelta
+      const int ydelta = g0 ? 1 : 2;
+      if (nk > 0) {
+        copy_set(0, 0);
+        copy_set(1, 0);
+      }
+      pre();
+      if (!g0 && nk > 1) copy_set(1, 1);
+      wait_vmcnt<0>();
+      if (nk > 1) load_set(0);  // set 0 of stage 1, stored in the first read phase
+      sync();
+      if (!g0) sync();
+      for (int kt = 0; kt < nk; ++kt) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          read_half(kt, h);
+          if (h == 0) {
+            if (kt + 1 < nk) write_set(0, kt + 1);
+            if (kt + ydelta < nk) load_set(1);
+          } else {
+            if (kt + ydelta < nk) write_set(1, kt + ydelta);
+            if (kt + 2 < nk) load_set(0);
+          }
+          // fragments read and staged stores done before the phase's barrier
+          wait_lgkmcnt0();
+          sync();
+#pragma unroll
+          for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+              for (int j = 0; j < C::NI; ++j)
+                acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s][i], bfr[s][j], acc[i][j], 0, 0, 0);
+          sync();
+        }
+      }
+      if (g0) sync();
+    } else {
+#pragma unroll
+      for (int p = 0; p < C::S - 1; ++p)
+        if (p < nk) issue(p);
+      pre();
+      for (int kt = 0; kt < nk; ++kt) {
+        // this tile's copies are done once at most those of the later tiles
+        // already in flight are outstanding
+        const int later = min(nk - 1 - kt, C::S - 2);
+        if (later >= 3) wait_vmcnt<3 * C::CPW>();
+        else if (later == 2) wait_vmcnt<2 * C::CPW>();
+        else if (later == 1) wait_vmcnt<C::CPW>();
+        else wait_vmcnt<0>();
+        __builtin_amdgcn_s_barrier();
+        // the slot of tile kt+S-1 was last read in iteration kt-1. Its copies go out
+        // in three groups, before the first three 16-deep steps: issued all at once
+        // they stall the waves' MFMA issue while the copy unit drains them, and the
+        // last step's would land too late
+        const bool copy_next = kt + C::S - 1 < nk;
+        char *st_next = smem + ((kt + C::S - 1) % C::S) * C::STAGE;
+        const char *as = smem + (kt % C::S) * C::STAGE, *bs = as + C::ATILE;
+#pragma unroll
+        for (int ks = 0; ks < C::BK / 16; ++ks) {
+          if (ks < 3 && copy_next) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int j = (ks * C::CPW) / 3; j < ((ks + 1) * C::CPW) / 3; ++j)
+              dma16(src[j] + (size_t)(kt + C::S - 1) * (C::BK * 2), st_next + (w + C::WAVES * j) * 1024);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          const uint32_t off = fr * (C::BK * 2) + (((2 * ks + fk) ^ fswz) * 16);
+          bf16x8 af[C::MI], bfr[C::NI];
+#pragma unroll
+          for (int i = 0; i < C::MI; ++i)
+            af[i] = *reinterpret_cast<const bf16x8 *>(as + (wm * C::TM + i * 32) * (C::BK * 2) + off);
+#pragma unroll
+          for (int j = 0; j < C::NI; ++j)
+            bfr[j] = *reinterpret_cast<const bf16x8 *>(bs + (wn * C::TN + j * 32) * (C::BK * 2) + off);
+#pragma unroll
+          for (int i = 0; i < C::MI; ++i)
+#pragma unroll
+            for (int j = 0; j < C::NI; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfr[j], acc[i][j], 0, 0, 0);
+        }
       }
     }
   };
