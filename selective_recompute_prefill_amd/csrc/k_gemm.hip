@@ -495,10 +495,11 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
       // different phases, and every read phase fills a quarter of a later stage
       // into a region already free: group 0 the first half of B (phase 4kt) and the
       // bottom of A (4kt+2) of stage kt+1, group 1 the second half of B of stage
-      // kt+1 (4kt+1) and the top of A of stage kt+2 (4kt+3). A read phase stores
-      // the set its wave loaded into registers in its previous read phase, then
-      // loads the next one: global loads plus LDS stores move operand data faster
-      // than direct-to-LDS copies, and the compiler counts these loads itself.
+      // kt+1 (4kt+1) and the top of A of stage kt+2 (4kt+3). Each wave stages both
+      // of its sets in registers: a read phase stores one set, loaded two read
+      // phases earlier, and loads it again for the next stage. Global loads plus
+      // LDS stores move operand data faster than direct-to-LDS copies, and the
+      // compiler counts these loads itself.
       static_assert(C::CPW == 8 && C::ACOPY == 32 && C::COPIES == 64, "four copies per set");
       const bool g0 = w < C::WAVES / 2;
       const int u = w & (C::WAVES / 2 - 1);
@@ -506,38 +507,56 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
       // the bottom of A, group 1 the top. Set h holds copies qs[h] + u + 4i.
       const int qs0 = g0 ? C::ACOPY : C::ACOPY + C::ACOPY / 2;
       const int qs1 = g0 ? C::ACOPY / 2 : 0;
-      const char *sp[2][4];
+      // set 0 reads B rows n0.. of this tile: 32-bit byte offsets from the first;
+      // set 1 reads gathered A rows: full pointers
+      const char *Bt = B + (size_t)n0 * rowb;
+      uint32_t so0[4];
+      const char *pa[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        sp[0][i] = copy_src(qs0 + u + 4 * i);
-        sp[1][i] = copy_src(qs1 + u + 4 * i);
+        so0[i] = (uint32_t)(copy_src(qs0 + u + 4 * i) - Bt);
+        pa[i] = copy_src(qs1 + u + 4 * i);
       }
+      auto spp = [&](int h, int i) __attribute__((always_inline)) -> const char * {
+        return h ? pa[i] : Bt + so0[i];
+      };
+      auto advance = [&](int h, int i) __attribute__((always_inline)) {
+        if (h) pa[i] += C::BK * 2;
+        else so0[i] += C::BK * 2;
+      };
       // direct copies of set h into the slot of stage kt (prologue only)
       auto copy_set = [&](int h, int kt) __attribute__((always_inline)) {
         char *st = smem + (kt % C::S) * C::STAGE + ((h ? qs1 : qs0) + u) * 1024;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          dma16(sp[h][i], st + i * 4096);
-          sp[h][i] += C::BK * 2;
+          dma16(spp(h, i), st + i * 4096);
+          advance(h, i);
         }
       };
-      // the staged set in four scalars (an array under these conditions would be
+      // each set staged in four scalars (an array under these conditions would be
       // kept in scratch memory)
-      uint4 sg0 = {0, 0, 0, 0}, sg1 = sg0, sg2 = sg0, sg3 = sg0;
+      uint4 a0 = {0, 0, 0, 0}, a1 = a0, a2 = a0, a3 = a0, b0 = a0, b1 = a0, b2 = a0, b3 = a0;
       auto load_set = [&](int h) __attribute__((always_inline)) {
-        sg0 = *reinterpret_cast<const uint4 *>(sp[h][0]);
-        sg1 = *reinterpret_cast<const uint4 *>(sp[h][1]);
-        sg2 = *reinterpret_cast<const uint4 *>(sp[h][2]);
-        sg3 = *reinterpret_cast<const uint4 *>(sp[h][3]);
+        if (h == 0) {
+          a0 = *reinterpret_cast<const uint4 *>(spp(0, 0));
+          a1 = *reinterpret_cast<const uint4 *>(spp(0, 1));
+          a2 = *reinterpret_cast<const uint4 *>(spp(0, 2));
+          a3 = *reinterpret_cast<const uint4 *>(spp(0, 3));
+        } else {
+          b0 = *reinterpret_cast<const uint4 *>(spp(1, 0));
+          b1 = *reinterpret_cast<const uint4 *>(spp(1, 1));
+          b2 = *reinterpret_cast<const uint4 *>(spp(1, 2));
+          b3 = *reinterpret_cast<const uint4 *>(spp(1, 3));
+        }
 #pragma unroll
-        for (int i = 0; i < 4; ++i) sp[h][i] += C::BK * 2;
+        for (int i = 0; i < 4; ++i) advance(h, i);
       };
       auto write_set = [&](int h, int kt) __attribute__((always_inline)) {
         char *st = smem + (kt % C::S) * C::STAGE + ((h ? qs1 : qs0) + u) * 1024 + lane * 16;
-        *reinterpret_cast<uint4 *>(st) = sg0;
-        *reinterpret_cast<uint4 *>(st + 4096) = sg1;
-        *reinterpret_cast<uint4 *>(st + 8192) = sg2;
-        *reinterpret_cast<uint4 *>(st + 12288) = sg3;
+        *reinterpret_cast<uint4 *>(st) = h ? b0 : a0;
+        *reinterpret_cast<uint4 *>(st + 4096) = h ? b1 : a1;
+        *reinterpret_cast<uint4 *>(st + 8192) = h ? b2 : a2;
+        *reinterpret_cast<uint4 *>(st + 12288) = h ? b3 : a3;
       };
       bf16x8 af[2][C::MI], bfr[2][C::NI];
       auto read_half = [&](int kt, int h) __attribute__((always_inline)) {
@@ -568,20 +587,19 @@ __global__ __launch_bounds__(C::THREADS, C::PER_CU) void gemm_bf16_kernel(GemmAr
       pre();
       if (!g0 && nk > 1) copy_set(1, 1);
       wait_vmcnt<0>();
-      if (nk > 1) load_set(0);  // set 0 of stage 1, stored in the first read phase
+      // the first staged stage of each set
+      if (nk > 1) load_set(0);
+      if (ydelta < nk) load_set(1);
       sync();
       if (!g0) sync();
       for (int kt = 0; kt < nk; ++kt) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           read_half(kt, h);
-          if (h == 0) {
-            if (kt + 1 < nk) write_set(0, kt + 1);
-            if (kt + ydelta < nk) load_set(1);
-          } else {
-            if (kt + ydelta < nk) write_set(1, kt + ydelta);
-            if (kt + 2 < nk) load_set(0);
-          }
+          // set h: store its stage for this read phase, then load the one after
+          const int tgt = h == 0 ? kt + 1 : kt + ydelta;
+          if (tgt < nk) write_set(h, tgt);
+          if (tgt + 1 < nk) load_set(h);
           // fragments read and staged stores done before the phase's barrier
           wait_lgkmcnt0();
           sync();
