@@ -185,6 +185,14 @@ def test_mini_bf16_gqa_groups(nh, nkv, d):
              what=f"mini-g{nh // nkv}-d{d}")
 
 
+@pytest.mark.parametrize("hidden,nh", [(64, 1), (128, 2)])
+def test_mini_short_k(hidden, nh):
+    """Hidden sizes of one and two 64-deep stages: the projection's pipeline
+    prologue and its last stages overlap (stage 1 copied before any compute)."""
+    run_case(inputs.small_spec(hidden=hidden, n_heads=nh, n_kv_heads=1, head_dim=64),
+             what=f"mini-hidden{hidden}")
+
+
 def test_mini_grouping():
     run_case(inputs.small_spec(window=8, tau=4, ratio=0.3), what="mini-grouping")
 
