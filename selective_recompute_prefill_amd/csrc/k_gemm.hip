@@ -335,9 +335,10 @@ struct TileIter {
 // ------------------------------------------------------------------------- //
 // bf16 MFMA kernel: BM x BN tile, WM x WN waves, each wave owning a
 // (BM/WM) x (BN/WN) block of 32x32x16 MFMA tiles. Operand tiles of depth BK
-// stream into an S-slot LDS ring with direct-to-LDS copies (no staging
-// registers); each copy moves 1 KB, i.e. 1024 / (2 BK) whole row segments.
-// Row segments of at least 128 bytes (BK >= 64) keep the copies at full rate;
+// stream into an S-slot LDS ring in 1 KB pieces (1024 / (2 BK) whole row
+// segments each): 256x256 tiles stage them through registers while the two
+// wave groups take turns (the mainloop below), other tiles copy them with
+// direct-to-LDS loads. Row segments of at least 128 bytes (BK >= 64) keep the copies at full rate;
 // 64-byte segments (half cache lines) run at a third of it. With CH = BK / 8
 // chunks of 16 bytes per row, chunk c of row r is stored at
 // c ^ ((r / (16 / CH)) % CH): a 16-byte LDS read serves 16 lanes (64 banks) per
